@@ -1,0 +1,362 @@
+"""CPU oracle for the Medusa single-pass tree verification step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call
+this module: only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` use it.  It shares no code with the HIP library.
+
+Every function is the plain definition of what the step computes, in float64
+(inputs are upcast exactly), with no blocking, online softmax, splitting or
+fusion.  Sources (web pages on Medusa and tree-structured speculative
+verification):
+
+* "Medusa Explained: Multi-Head Speculative Decoding Guide" (aifetchly blog):
+  section "The Architectural Blueprint" (residual-block and softmax
+  equations of a Medusa head), "1. Combinatorial Tree Construction",
+  "2. Single-Pass Tree Attention Verification" (additive mask M_tree and the
+  5-candidate mask example, greedy longest-accepted-path rule).
+* "Multi-Token Prediction: Draft-Model-Free Speculative Decoding"
+  (globaltechdigest blog): "The 2D Tree Attention Mask" (boolean mask,
+  ancestor-or-self), the verification-engine code (parent array with -1
+  roots, index-order acceptance, longest path with first-wins ties) and the
+  Figure-1 text box (longest valid path plus one bonus token).
+* "Speculative Decoding & Medusa Tree Attention" (akmalkhaniub blog):
+  section 2, "The Acceptance Sampling Rule" (alpha = min(1, P_t/P_d) and the
+  residual distribution normalize(max(0, P_t - P_d))).
+
+Readings where the pages are silent (scale 1/sqrt(dh), contiguous GQA groups,
+tree K/V appended after the prefix, ties, the speculative rule applied node by
+node, sampling by inverse CDF) are stated next to the code that takes them.
+
+Parity pins: every function here is pinned by tests under ``tests/`` against
+worked examples printed on the pages, closed forms, invariants and brute-force
+references; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "silu", "medusa_heads", "topk_rows", "build_tree", "tree_attention",
+    "accept_greedy", "accept_speculative", "paths_to_parents",
+]
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# 1. Medusa heads  ("The Architectural Blueprint", residual-block equation)
+# --------------------------------------------------------------------------
+def silu(x: np.ndarray) -> np.ndarray:
+    """SiLU(x) = x * sigmoid(x) = x / (1 + exp(-x))."""
+    x = _f64(x)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def topk_rows(rows: np.ndarray, s: int) -> Dict[str, np.ndarray]:
+    """Top-s entries of each row: larger value first, equal values by lower index.
+
+    The order is a stable sort on (-value, index); returns ids (int64) and values.
+    """
+    rows = _f64(rows)
+    order = np.argsort(-rows, axis=-1, kind="stable")[..., :s]
+    return {"ids": order.astype(np.int64), "vals": np.take_along_axis(rows, order, axis=-1)}
+
+
+def medusa_heads(h, w_res, w_head, widths: Sequence[int]) -> Dict[str, np.ndarray]:
+    """Medusa heads for a batch of hidden states.
+
+    For head k:  u = W_res[k] h,  h_k = SiLU(u) + h,  logits_k = W_head[k] h_k
+    (the residual block has no bias, as in the page's equation), and
+    p_k = softmax(logits_k).  Head k's candidates are its top-``widths[k]``
+    logits (softmax is monotone, so the top of p_k is the top of logits_k).
+
+    Shapes: h [B,d]; w_res [K,d,d] stored (out, in); w_head [K,V,d].
+    Returns hk [B,K,d], logits [B,K,V], topk_ids/topk_vals [B,K,s_max]
+    (-1 / -inf padded past widths[k]), lse [B,K] = log sum exp(logits).
+    """
+    h, w_res, w_head = _f64(h), _f64(w_res), _f64(w_head)
+    B, d = h.shape
+    K, V, _ = w_head.shape
+    s_max = max(widths)
+    hk = np.empty((B, K, d))
+    logits = np.empty((B, K, V))
+    ids = np.full((B, K, s_max), -1, dtype=np.int64)
+    vals = np.full((B, K, s_max), -np.inf)
+    lse = np.empty((B, K))
+    for k in range(K):
+        for b in range(B):
+            u = w_res[k] @ h[b]
+            hk[b, k] = silu(u) + h[b]
+            z = w_head[k] @ hk[b, k]
+            logits[b, k] = z
+            t = topk_rows(z, widths[k])
+            ids[b, k, :widths[k]] = t["ids"]
+            vals[b, k, :widths[k]] = t["vals"]
+            m = z.max()
+            lse[b, k] = m + np.log(np.exp(z - m).sum())
+    return {"hk": hk, "logits": logits, "topk_ids": ids, "topk_vals": vals, "lse": lse}
+
+
+# --------------------------------------------------------------------------
+# 2. Tree assembly  ("1. Combinatorial Tree Construction"; the boolean
+#    ancestor-or-self mask of "The 2D Tree Attention Mask"; the parent-array
+#    walk of the verification-engine code)
+# --------------------------------------------------------------------------
+def paths_to_parents(paths: Sequence[Sequence[int]]):
+    """Convert root-to-node paths of node labels into (labels, parent array).
+
+    A label becomes a node the first time it is seen (in path order); its
+    parent is the previous label on that path, or -1 at the head of a path.
+    """
+    labels: List[int] = []
+    index: Dict[int, int] = {}
+    parents: List[int] = []
+    for path in paths:
+        prev = -1
+        for lab in path:
+            if lab not in index:
+                index[lab] = len(labels)
+                labels.append(lab)
+                parents.append(prev)
+            prev = index[lab]
+    return labels, parents
+
+
+def build_tree(parents: Sequence[int], cand: Optional[Sequence[np.ndarray]] = None,
+               widths: Optional[Sequence[int]] = None) -> Dict[str, object]:
+    """Depth, sibling rank, ancestor-or-self sets/bitmask and node tokens.
+
+    parents[i] is the parent of node i, -1 for a node that hangs directly off
+    the prefix; the array must be topological (-1 <= parents[i] < i).
+    depth[i] = 1 for parent -1, else depth[parent] + 1.  anc[i] = {i} plus
+    anc[parent].  rank[i] = number of earlier siblings.  With candidates
+    cand[k] ([B, >= s_k] token ids for depth k+1), node i's token is
+    cand[depth-1][b, rank], which requires rank < widths[depth-1].
+    The bitmask has W = ceil(N/32) uint32 words per node; bit j of word j//32
+    of row i is set iff j is in anc[i].
+    """
+    N = len(parents)
+    depth = np.zeros(N, dtype=np.int64)
+    rank = np.zeros(N, dtype=np.int64)
+    anc: List[List[int]] = []
+    for i in range(N):
+        p = int(parents[i])
+        if not (-1 <= p < i):
+            raise ValueError(f"node {i}: parent {p} is not in [-1, {i})")
+        depth[i] = 1 if p == -1 else depth[p] + 1
+        rank[i] = sum(1 for j in range(i) if int(parents[j]) == p)
+        anc.append(sorted(([i] + (anc[p] if p >= 0 else []))))
+    W = (N + 31) // 32
+    bits = np.zeros((N, W), dtype=np.uint32)
+    for i in range(N):
+        for j in anc[i]:
+            bits[i, j // 32] |= np.uint32(1) << np.uint32(j % 32)
+    out: Dict[str, object] = {"depth": depth, "rank": rank, "anc": anc, "mask_bits": bits}
+    if cand is not None:
+        B = np.asarray(cand[0]).shape[0]
+        tokens = np.zeros((B, N), dtype=np.int64)
+        for i in range(N):
+            k = int(depth[i]) - 1
+            if k >= len(cand):
+                raise ValueError(f"node {i} at depth {k + 1} has no candidate list")
+            w = widths[k] if widths is not None else np.asarray(cand[k]).shape[1]
+            if rank[i] >= w:
+                raise ValueError(f"node {i}: rank {rank[i]} >= width {w} at depth {k + 1}")
+            tokens[:, i] = np.asarray(cand[k])[:, rank[i]]
+        out["tokens"] = tokens
+    return out
+
+
+def mask_matrix(anc: Sequence[Sequence[int]]) -> np.ndarray:
+    """Dense boolean N x N mask: M[i, j] = j is an ancestor of i or j == i."""
+    N = len(anc)
+    m = np.zeros((N, N), dtype=bool)
+    for i, a in enumerate(anc):
+        m[i, list(a)] = True
+    return m
+
+
+# --------------------------------------------------------------------------
+# 3. Tree-masked GQA attention ("2. Single-Pass Tree Attention Verification":
+#    the tree is packed after the prefix and every node sees the prefix plus
+#    its ancestors and itself; additive mask 0 / -inf)
+# --------------------------------------------------------------------------
+def tree_attention(q, k_cache, v_cache, prefix_len, anc: Sequence[Sequence[int]],
+                   scale: Optional[float] = None,
+                   select: Optional[Sequence[tuple]] = None) -> Dict[str, np.ndarray]:
+    """Scaled dot-product attention of every tree node over prefix + ancestors.
+
+    q [B,N,Hq,dh]; k_cache/v_cache [B,Hkv,L_cap,dh] hold the prefix at rows
+    [0, L_b) and the tree's own K/V at rows [L_b, L_b+N) in node order.
+    Query head h reads KV head h // (Hq/Hkv).  For node i the visible keys are
+    all L_b prefix rows and the rows L_b + j for j in anc[i]; scores are
+    q.k * scale (default 1/sqrt(dh)), masked to -inf elsewhere, softmaxed,
+    and applied to V.  Returns out [B,N,Hq,dh] and lse [B,Hq,N] (natural log).
+
+    ``select`` = list of (b, h, i) computes only those outputs (others NaN).
+    """
+    q, k_cache, v_cache = _f64(q), k_cache, v_cache
+    B, N, Hq, dh = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(dh)
+    out = np.full((B, N, Hq, dh), np.nan)
+    lse = np.full((B, Hq, N), np.nan)
+    if select is None:
+        select = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(N)]
+    todo: Dict[tuple, List[tuple]] = {}
+    for b, h, i in select:
+        todo.setdefault((b, h // G), []).append((h, i))
+    for (b, g), items in todo.items():
+        L = int(prefix_len[b])
+        keys = _f64(k_cache[b, g, :L + N])
+        vals = _f64(v_cache[b, g, :L + N])
+        for h, i in items:
+            visible = np.zeros(L + N, dtype=bool)
+            visible[:L] = True
+            visible[[L + j for j in anc[i]]] = True
+            s = (keys @ q[b, i, h]) * scale
+            s = np.where(visible, s, -np.inf)
+            m = s.max()
+            e = np.exp(s - m)
+            z = e.sum()
+            out[b, i, h] = (e @ vals) / z
+            lse[b, h, i] = m + np.log(z)
+    return {"out": out, "lse": lse}
+
+
+# --------------------------------------------------------------------------
+# 4a. Greedy acceptance ("2. Single-Pass Tree Attention Verification", step 3:
+#     longest path whose every token equals the target's greedy choice;
+#     verification-engine code: index-order acceptance, first-wins ties;
+#     Figure-1 box: one bonus token from the target after the path)
+# --------------------------------------------------------------------------
+def _longest_path(parents, accepted):
+    """Deepest accepted node (first in index order on ties) and its root path."""
+    best, best_len = -1, 0
+    for i in range(len(parents)):
+        if not accepted[i]:
+            continue
+        path = []
+        c = i
+        while c != -1 and accepted[c]:
+            path.append(c)
+            c = int(parents[c])
+        if len(path) > best_len:
+            best, best_len = i, len(path)
+    path = []
+    c = best
+    while c != -1:
+        path.append(c)
+        c = int(parents[c])
+    return best, path[::-1]
+
+
+def _pack(paths_tokens, B, D):
+    acc_len = np.zeros(B, dtype=np.int64)
+    path_nodes = np.full((B, D), -1, dtype=np.int64)
+    out_tokens = np.full((B, D + 1), -1, dtype=np.int64)
+    for b, (path, toks, bonus) in enumerate(paths_tokens):
+        acc_len[b] = len(path)
+        path_nodes[b, :len(path)] = path
+        out_tokens[b, :len(path)] = toks
+        out_tokens[b, len(path)] = bonus
+    return acc_len, path_nodes, out_tokens
+
+
+def accept_greedy(target, node_tokens, parents, D: int) -> Dict[str, np.ndarray]:
+    """Greedy longest-accepted-path acceptance.
+
+    target [B, N+1, V]: row 0 is the distribution after the last prefix token,
+    row i+1 the one after node i.  pred[r] = argmax of row r (first index on
+    ties).  Node i (index order, parents first) is accepted iff its parent is
+    the prefix or an accepted node, and its token equals pred[parent row].
+    The committed path ends at the deepest accepted node (lowest index on
+    ties); the bonus token is pred at that node's row (row 0 if none).
+    """
+    target = _f64(target)
+    B, R, V = target.shape
+    N = len(parents)
+    pred = np.argmax(target, axis=-1)          # first maximal index
+    accepted = np.zeros((B, N), dtype=bool)
+    res = []
+    for b in range(B):
+        for i in range(N):
+            p = int(parents[i])
+            ok = (p == -1) or accepted[b, p]
+            accepted[b, i] = ok and int(node_tokens[b, i]) == int(pred[b, p + 1])
+        term, path = _longest_path(parents, accepted[b])
+        res.append((path, [int(node_tokens[b, n]) for n in path], int(pred[b, term + 1])))
+    acc_len, path_nodes, out_tokens = _pack(res, B, D)
+    return {"accept_len": acc_len, "path_nodes": path_nodes, "out_tokens": out_tokens,
+            "node_accept": accepted, "pred": pred}
+
+
+# --------------------------------------------------------------------------
+# 4b. Speculative acceptance ("The Acceptance Sampling Rule": accept x with
+#     probability min(1, P_t(x)/P_d(x)), else resample from
+#     normalize(max(0, P_t - P_d)); applied node by node on the tree)
+# --------------------------------------------------------------------------
+def _inverse_cdf(r: np.ndarray, u: float) -> int:
+    """First j with cumsum(r)[j] > u * sum(r); the last j with r_j > 0 if none."""
+    c = np.cumsum(r)
+    t = float(u) * c[-1]
+    hit = np.nonzero(c > t)[0]
+    if hit.size:
+        return int(hit[0])
+    pos = np.nonzero(r > 0)[0]
+    return int(pos[-1]) if pos.size else len(r) - 1
+
+
+def accept_speculative(p_target, p_draft, node_tokens, parents, uniforms,
+                       D: int) -> Dict[str, np.ndarray]:
+    """Speculative (rejection-sampling) acceptance over a candidate tree.
+
+    p_target/p_draft [B, N+1, V] probabilities (row 0 = after the prefix, row
+    i+1 = after node i); uniforms [B, N+1] in [0, 1).
+    alpha_i = min(1, P_t[parent row, x_i] / P_d[parent row, x_i]) (1 when
+    P_d = 0); node i passes iff u[b, i] < alpha_i and is accepted iff it
+    passes and its parent is the prefix or accepted.  The path ends at the
+    deepest accepted node e (lowest index on ties; e = prefix if none).  The
+    extra token is drawn with u[b, N] by inverse CDF from
+    normalize(max(0, P_t[e] - P_d[e])) when e has children (all of them were
+    rejected), falling back to P_t[e] when that residual is all zero, and
+    from P_t[e] when e is a leaf.
+    """
+    p_t, p_d = _f64(p_target), _f64(p_draft)
+    u = _f64(uniforms)
+    B, R, V = p_t.shape
+    N = len(parents)
+    has_child = np.zeros(N + 1, dtype=bool)    # index = row (node + 1); row 0 = prefix
+    for i in range(N):
+        has_child[int(parents[i]) + 1] = True
+    alpha = np.zeros((B, N))
+    accepted = np.zeros((B, N), dtype=bool)
+    res = []
+    for b in range(B):
+        for i in range(N):
+            p = int(parents[i])
+            x = int(node_tokens[b, i])
+            pt, pd = p_t[b, p + 1, x], p_d[b, p + 1, x]
+            alpha[b, i] = 1.0 if pd == 0.0 else min(1.0, pt / pd)
+            ok = (p == -1) or accepted[b, p]
+            accepted[b, i] = ok and (u[b, i] < alpha[b, i])
+        term, path = _longest_path(parents, accepted[b])
+        row = term + 1
+        if has_child[row]:
+            r = np.maximum(0.0, p_t[b, row] - p_d[b, row])
+            if r.sum() <= 0.0:
+                r = p_t[b, row]
+        else:
+            r = p_t[b, row]
+        tok = _inverse_cdf(r, u[b, N])
+        res.append((path, [int(node_tokens[b, n]) for n in path], tok))
+    acc_len, path_nodes, out_tokens = _pack(res, B, D)
+    return {"accept_len": acc_len, "path_nodes": path_nodes, "out_tokens": out_tokens,
+            "node_accept": accepted, "alpha": alpha}
