@@ -1,0 +1,332 @@
+"""Benchmark of the Medusa tree-verification step on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input, already resident in HBM:
+Medusa heads (residual block + vocabulary projection with top-k) -> candidate-tree assembly
+-> tree-masked GQA attention -> acceptance.  The default workload is the Llama-3-8B-shaped
+layer: batch 1, 32 query / 8 KV heads of 128 dims, a 4096-token prefix, the 64-node
+(4,3,2,1) tree, 4 Medusa heads over d=4096 and a 32000-token vocabulary, bf16, greedy
+acceptance against target logits whose argmax matches a child token with probability 0.6.
+
+Prints one JSON line: steps/s (and verified tree tokens/s), the roofline of the dominant
+kernel (the vocabulary-streaming head projection) timed with HIP events on the stream it
+runs on, and the CPU oracle timed on the host cores on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
+    python bench.py --copy-calibration      # plain device copy of known size (for counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6      # dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+F32_PEAK_TFLOPS = 157.3
+MALL_BYTES = 256 << 20         # Infinity Cache
+
+DESCR = {
+    "c1": "tiny-fp32: B=1, Hq=Hkv=4, dh=64, prefix 128, 8-node tree (two depth-4 chains), "
+          "heads d=256 V=1000 K=3, greedy",
+    "c2": "llama3-8b-layer: B=1, Hq=32, Hkv=8, dh=128, prefix 4096, 64-node (4,3,2,1) tree, "
+          "heads d=4096 V=32000 K=4 bf16, greedy (planted p=0.6)",
+    "c3": "70b-share-b8: B=8, Hq=64, Hkv=8, dh=128, prefix U[8192,32768], 64-node (4,3,2,1) tree, "
+          "heads d=8192 V=32000 K=4 bf16, greedy (planted p=0.6)",
+    "c4": "long-ctx-131k: B=1, Hq=64, Hkv=8, dh=128, prefix 131072, 212-node (4,4,4,2) tree, "
+          "attention only, bf16",
+    "c5": "spec-serving-b64: B=64, Hq=32, Hkv=8, dh=128, prefix U[512,8192], 64-node (4,3,2,1) "
+          "tree, speculative acceptance over V=128256 (fp32 probabilities)",
+}
+
+
+def _kernel_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel_key, src_path, launches_bytes=None):
+    """HBM traffic per launch from the committed counter summary, if it is still current."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel_key}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha") != _kernel_sha(src_path):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# --------------------------------------------------------------------------- inputs
+def make_inputs(wl, seed):
+    from medusa_tree_attention_verify_amd import workloads as W
+    x = {}
+    if wl.has_heads:
+        x.update(W.gen_heads(wl, seed))
+    x.update(W.gen_attention(wl, seed))
+    if wl.accept == "greedy":
+        x["target"] = W.gen_target_logits(wl, seed)
+    elif wl.accept == "speculative":
+        x.update(W.gen_speculative(wl, seed))
+    return x
+
+
+def step_bytes(wl, x):
+    """Algorithmic bytes / FLOPs of one step (weights, K/V and rows read once)."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    parts = {}
+    if wl.has_heads:
+        res = wl.K * wl.d * wl.d * esz + wl.B * wl.d * esz + wl.B * wl.K * wl.d * 4
+        head = wl.K * wl.V * wl.d * esz + wl.B * wl.K * wl.d * 4
+        parts["heads_residual"] = (res, 2.0 * wl.B * wl.K * wl.d * wl.d)
+        parts["heads_projection"] = (head, 2.0 * wl.B * wl.K * wl.V * wl.d)
+    L = x["prefix_len"].astype(np.int64)
+    N = wl.N
+    kv = int(np.sum((L + N) * wl.Hkv * wl.dh * esz * 2))
+    qo = 2 * wl.B * N * wl.Hq * wl.dh * esz
+    depth = []
+    for p in wl.parents:
+        depth.append(1 if p < 0 else depth[p] + 1)
+    flops = float(np.sum(4.0 * wl.dh * wl.Hq * (N * L + sum(depth))))
+    parts["attention"] = (kv + qo, flops)
+    if wl.accept == "greedy":
+        parts["accept"] = (wl.B * (N + 1) * wl.accept_V * esz, 0.0)
+    elif wl.accept == "speculative":
+        parts["accept"] = (wl.B * (2 * N * 4 + 2 * wl.accept_V * 4), 0.0)
+    return parts
+
+
+# --------------------------------------------------------------------------- CPU oracle
+def cpu_baseline(wl, x, seed, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    from threadpoolctl import threadpool_info
+
+    from medusa_tree_attention_verify_amd import workloads as W
+    from oracle import medusa_oracle as O
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    parents = list(wl.parents)
+    t_total = 0.0
+    steps = 0
+    sample = None
+    while True:
+        t0 = time.perf_counter()
+        cand = []
+        if wl.has_heads:
+            heads = O.medusa_heads(x["h"], x["w_res"], x["w_head"], list(wl.head_widths))
+            if wl.lm_width:
+                cand.append(np.stack([O.topk_rows(x["target"][b, 0], wl.lm_width)["ids"]
+                                      for b in range(wl.B)]))
+            cand += [heads["topk_ids"][:, k, :wl.head_widths[k]] for k in range(wl.K)]
+        elif wl.accept == "speculative":
+            cand = None
+        tree = O.build_tree(parents, cand, list(wl.depth_widths)) if cand else O.build_tree(parents)
+        t1 = time.perf_counter()
+        target = None
+        if wl.accept == "greedy":    # input generation (planting) is not timed
+            target = x["target"].copy()
+            if wl.plant_p > 0:
+                target = W.plant_greedy(target, parents, tree["tokens"], seed, wl.plant_p)
+            if wl.dtype == "bf16":
+                target = W.round_bf16(target)
+        t2 = time.perf_counter()
+        # attention: whole batch when it fits the budget, else a slice of the query rows
+        if sample is None:
+            sample = "1 full step"
+        O.tree_attention(x["q"], x["k_cache"], x["v_cache"], x["prefix_len"], tree["anc"])
+        if wl.accept == "greedy":
+            O.accept_greedy(target, tree["tokens"], parents, wl.D)
+        elif wl.accept == "speculative":
+            O.accept_speculative(x["p_target"], x["p_draft"], x["node_tokens"], parents,
+                                 x["uniforms"], wl.D)
+        t3 = time.perf_counter()
+        t_total += (t1 - t0) + (t3 - t2)
+        steps += 1
+        if t_total >= budget_s or steps >= 5:
+            break
+    return {"value": steps / t_total, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} full step(s) of the same workload (seed {seed}), "
+                      f"{t_total:.1f} s, NumPy fp64"}
+
+
+# --------------------------------------------------------------------------- main
+def copy_calibration(nbytes=1 << 30, reps=5):
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", choices=sorted(DESCR))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
+              "the path shards per sequence / KV head / vocabulary slice, but no multi-GPU "
+              "code is built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from medusa_tree_attention_verify_amd import _lib, ops
+    from medusa_tree_attention_verify_amd import workloads as W
+    from medusa_tree_attention_verify_amd.step import VerifyStep
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    _lib.lib()
+    torch.cuda.set_device(0)
+    wl = W.WORKLOADS[args.workload]
+    seed = args.seed or int(args.workload[1:])
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    t0 = time.time()
+    x = make_inputs(wl, seed)
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    parts = step_bytes(wl, x)
+    step_total = sum(b for b, _ in parts.values())
+
+    max_L = int(x["prefix_len"].max())
+    spec = wl.accept == "speculative"
+    step = VerifyStep(parents=wl.parents, depth_widths=wl.depth_widths, dtype=dt, B=wl.B,
+                      Hq=wl.Hq, Hkv=wl.Hkv, dh=wl.dh, max_L=max_L,
+                      heads={"d": wl.d, "V": wl.V, "K": wl.K, "widths": list(wl.head_widths)}
+                      if wl.has_heads else None,
+                      lm_width=wl.lm_width, accept=wl.accept, V=wl.accept_V,
+                      tokens_given=not wl.has_heads)
+    d = lambda a, t=dt: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
+    static = {}
+    if wl.has_heads:
+        static.update(h=d(x["h"]), w_res=d(x["w_res"]), w_head=d(x["w_head"]))
+    # Rotating copies of the per-step activations so that the 256 MB Infinity Cache cannot
+    # serve them as "HBM" reads: only needed when one step moves less than 2x the cache.
+    rot_bytes = parts["attention"][0] + (parts["accept"][0] if "accept" in parts else 0)
+    R = 1 if step_total >= 2 * MALL_BYTES else int(np.ceil(2 * MALL_BYTES / max(rot_bytes, 1)))
+    R = min(R, 64)
+    base = {"q": d(x["q"]), "k_cache": d(x["k_cache"]), "v_cache": d(x["v_cache"]),
+            "prefix_len": d(x["prefix_len"], torch.int32)}
+    if spec:
+        base.update(target=d(x["p_target"], torch.float32), draft=d(x["p_draft"], torch.float32),
+                    uniforms=d(x["uniforms"], torch.float32),
+                    node_tokens=d(x["node_tokens"], torch.int32))
+    elif wl.accept == "greedy":
+        # the greedy target is planted against the node tokens this step produces: run the
+        # heads and the tree once (untimed) to get them
+        base["target"] = d(W.round_bf16(x["target"]) if wl.dtype == "bf16" else x["target"])
+        if wl.plant_p > 0:
+            c = step.bind(dict(static, **base))
+            for part in ("heads_residual", "heads_projection", "tree"):
+                c[part]()
+            torch.cuda.synchronize()
+            toks = step.tree["node_tokens"].cpu().numpy()
+            tgt = W.plant_greedy(x["target"].copy(), list(wl.parents), toks, seed, wl.plant_p)
+            base["target"] = d(W.round_bf16(tgt) if wl.dtype == "bf16" else tgt)
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
+    seqs = [step.sequence(step.bind(dict(static, **s))) for s in sets]
+    present = [p for p in step.PARTS if p in step.bind(dict(static, **base))]
+
+    def one_step(i, ev=None):
+        for j, call in enumerate(seqs[i % R]):
+            if ev is not None:
+                ev[j].record()
+            call()
+        if ev is not None:
+            ev[len(present)].record()
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(present) + 1)]
+           for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(K):
+        one_step(i, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    if int(step.status.item()) != 0:
+        raise RuntimeError(f"device status flags {int(step.status.item())}")
+    ms = start.elapsed_time(stop) / K
+    steps_per_s = 1000.0 / ms
+    seg = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(len(present))] for e in evs])
+    seg_mean = dict(zip(present, seg.mean(axis=0)))  # ms per part
+    parts_ms = {n: round(float(v), 4) for n, v in seg_mean.items()}
+
+    # dominant kernel: the vocabulary-streaming head projection (one kernel launch)
+    roof = None
+    if wl.has_heads:
+        b_head = parts["heads_projection"][0]
+        dur_s = seg_mean["heads_projection"] / 1000.0
+        ach = b_head / dur_s / 1e9
+        src = os.path.join(ROOT, "medusa_tree_attention_verify_amd", "csrc", "heads.hip")
+        roof = {"kernel": "gemv_bf16_kernel<head projection>", "bound": "hbm",
+                "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": _traffic("head_projection_c2", src),
+                "algorithmic_bytes": int(b_head), "avg_launch_us": round(seg_mean["heads_projection"] * 1000, 2)}
+    else:
+        b_att, f_att = parts["attention"]
+        dur_s = seg_mean["attention"] / 1000.0
+        if f_att / b_att > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+            ach = f_att / dur_s / 1e12
+            roof = {"kernel": "tree_attn_bf16_kernel + combine", "bound": "mfma",
+                    "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None}
+        else:
+            ach = b_att / dur_s / 1e9
+            roof = {"kernel": "tree_attn_bf16_kernel + combine", "bound": "hbm",
+                    "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    t_roof = sum(max(b / (HBM_PEAK_GBS * 1e9), f / (BF16_PEAK_TFLOPS * 1e12))
+                 for b, f in parts.values())
+    out = {
+        "metric": "tree-verify steps/s & verified tree tokens/s; % of HBM/MFMA roofline",
+        "value": round(steps_per_s, 2), "unit": "steps/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,s) weights/activations, planted target argmax)",
+        "config": {"workload": DESCR[args.workload], "global_batch": wl.B, "tree_nodes": wl.N,
+                   "seq_len": max_L, "rotating_input_sets": R},
+        "verified_tree_tokens_per_s": round(steps_per_s * wl.B * wl.N, 1),
+        "step_roofline_frac": round(t_roof / (ms / 1000.0), 4),
+        "step_algorithmic_bytes": int(step_total),
+        "parts_ms": parts_ms,
+        "roofline": roof,
+        "wall_s_timed_region": round(t_wall, 4),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        out["cpu_baseline"] = cpu_baseline(wl, x, seed, args.cpu_budget)
+        print(f"# cpu baseline took {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

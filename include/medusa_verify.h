@@ -1,0 +1,239 @@
+/*
+ * medusa_verify.h -- C ABI of the MI355X (gfx950) Medusa tree-verification library.
+ *
+ * One verify step of Medusa decoding, split into the operations below:
+ *
+ *   (a1) Medusa residual block   h_k = SiLU(W_res^(k) h) + h
+ *   (a2) Medusa head projection  logits_k = W_head^(k) h_k, its top-s_k tokens and log-sum-exp
+ *   (a3) candidate-tree assembly from a parent array -> per-node ancestor-or-self bitmask
+ *   (a4/a5) tree-masked GQA attention of every tree node over the KV prefix plus its ancestors
+ *   (a6/a7) acceptance: greedy longest accepted path, or the speculative min(1, P_t/P_d) rule
+ *           with residual resampling, plus one extra ("bonus") token.
+ *
+ * Sources (web pages on the method):
+ *   [MX]  "Medusa Explained: Multi-Head Speculative Decoding Guide" (aifetchly blog):
+ *         "The Architectural Blueprint" (head equations), "1. Combinatorial Tree Construction",
+ *         "2. Single-Pass Tree Attention Verification" (mask M_tree, 5-candidate example,
+ *         greedy longest-path rule).
+ *   [MTP] "Multi-Token Prediction: Draft-Model-Free Speculative Decoding" (globaltechdigest
+ *         blog): "The 2D Tree Attention Mask", "Tree-Structured Attention Verification"
+ *         (figure box: longest valid path + 1 bonus token), and the verification-engine code
+ *         (parent array, -1 = root; index-order acceptance; longest path, first wins ties).
+ *   [SD]  "Speculative Decoding & Medusa Tree Attention" (akmalkhaniub blog), section 2,
+ *         "The Acceptance Sampling Rule" (alpha and the residual distribution).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers are DEVICE pointers (memory of the current HIP device) unless marked "host".
+ *   The caller owns every buffer.  The library never allocates, frees or synchronises;
+ *   scratch memory comes only through (ws, ws_bytes), sized by the matching *_workspace()
+ *   query (0 bytes is a valid answer).  ws must be 256-byte aligned.
+ * - stream is a hipStream_t passed as void* (NULL = the default stream).  Every call only
+ *   enqueues work on it and returns.
+ * - Host-side argument checks run first; on failure nothing is launched and a negative
+ *   mv_status is returned.  Data-dependent errors (a malformed parent array, a prefix that
+ *   does not fit the cache, a tree deeper than the output) cannot be seen by the host; they
+ *   are OR-ed as bit flags (MV_DEV_*) into *dev_status when dev_status is not NULL, and the
+ *   kernels still finish with every access in bounds (outputs of the offending item are then
+ *   unspecified).  The caller zeroes dev_status before the call.
+ * - Layouts are row-major, innermost dimension last.  bf16 tensors hold raw bfloat16 bits.
+ * - Thread safety: no mutable global state.  Calls that share one workspace must be ordered
+ *   (the same stream does that).
+ * - Numerics: every dot product accumulates in fp32; the acceptance decisions and the
+ *   residual sampling are taken in fp64.
+ */
+#ifndef MEDUSA_VERIFY_H
+#define MEDUSA_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifndef MV_API
+#if defined(__GNUC__) || defined(__clang__)
+#define MV_API __attribute__((visibility("default")))
+#else
+#define MV_API
+#endif
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MV_OK = 0,
+  MV_ERR_INVALID_ARG = -1,   /* NULL required pointer, non-positive size, bad enum value */
+  MV_ERR_INVALID_TREE = -2,  /* reserved for host-validated tree specs (binding level) */
+  MV_ERR_UNSUPPORTED = -3,   /* a size or dtype this build does not implement (see each call) */
+  MV_ERR_WORKSPACE = -4,     /* ws is NULL/misaligned or ws_bytes is below the query */
+  MV_ERR_HIP = -5            /* a HIP launch or runtime call failed */
+} mv_status;
+
+typedef enum { MV_F32 = 0, MV_BF16 = 1 } mv_dtype;
+typedef enum { MV_ACCEPT_GREEDY = 0, MV_ACCEPT_SPECULATIVE = 1 } mv_accept_mode;
+
+/* Device-side error flags (OR-ed into *dev_status). */
+#define MV_DEV_BAD_PARENT   0x1  /* parents[i] outside [-1, i) (parents must be topological) */
+#define MV_DEV_BAD_RANK     0x2  /* a node's sibling rank is >= the candidate width of its depth */
+#define MV_DEV_TOO_DEEP     0x4  /* a node's depth exceeds D */
+#define MV_DEV_BAD_PREFIX   0x8  /* prefix_len[b] < 0, > max_L, or prefix_len[b] + N > L_cap */
+#define MV_DEV_BAD_TOKEN    0x10 /* a node token is outside [0, V) */
+
+/* Limits of this build. */
+#define MV_MAX_NODES 256   /* N: tree nodes */
+#define MV_MAX_DEPTH 16    /* D: tree depth */
+#define MV_MAX_TOPK  16    /* s: candidates per head / per depth */
+#define MV_MAX_BATCH_HEADS 32  /* B for the Medusa heads */
+#define MV_MAX_HEADS 16    /* K: Medusa heads */
+
+/* Human-readable text of a mv_status value (static storage). */
+MV_API const char* mv_status_string(int status);
+
+/* MV_OK when `device` is a gfx950 GPU, MV_ERR_UNSUPPORTED for another GPU, MV_ERR_HIP when
+ * the device cannot be queried. */
+MV_API int mv_device_check(int device);
+
+/* Library version, major*10000 + minor*100 + patch. */
+MV_API int mv_version(void);
+
+/* ---------------------------------------------------------------------------------------
+ * (a1)+(a2) Medusa heads.  [MX] "The Architectural Blueprint": every head k has one residual
+ * block without bias, h_k = SiLU(W_res^(k) h) + h, followed by a vocabulary projection whose
+ * softmax is the head's distribution; [MX] "1. Combinatorial Tree Construction": each head
+ * contributes its top-s_k tokens.  Softmax is monotone, so the top-s_k of the distribution are
+ * the top-s_k logits, and lse = log sum_v exp(logit_v) gives the distribution itself.
+ *
+ *   dt        MV_BF16 (weights, h and logits in bf16) or MV_F32.
+ *   B         batch (1..MV_MAX_BATCH_HEADS), d model width, V vocabulary, K heads (1..16).
+ *             bf16 needs d % 32 == 0; fp32 needs d % 4 == 0.
+ *   h         [B, d] dt.
+ *   w_res     [K, d, d] dt, W_res^(k)[out][in] (row-major, out-major).
+ *   w_head    [K, V, d] dt.
+ *   hk        [B, K, d] fp32 output of the residual block, or NULL.  (It is always kept in ws.)
+ *   s_per_head host [K], 1 <= s_k <= s_max <= MV_MAX_TOPK, s_max <= V.
+ *   logits    [B, K, V] dt output, or NULL (then the logits are never written to memory).
+ *   topk_ids  int32, topk_vals fp32: element (b, k, r) at  b*ld_topk + k*s_max + r, r < s_max;
+ *             ld_topk >= K*s_max (0 means K*s_max).  Rank r orders larger logit first, equal
+ *             logits by lower token id.  Slots r >= s_k hold id -1 and value -inf.
+ *   lse       [B, K] fp32 natural-log log-sum-exp of each head's logits, or NULL.
+ *   ws        workspace from mv_medusa_heads_workspace(dt, B, d, V, K, s_max).  The residual
+ *             call leaves the head input there for the projection call, so the two calls of
+ *             one step must get the same ws (mv_medusa_heads does both).
+ * Values are accumulated in fp32.  With bf16 weights, h_k stays fp32: the projection feeds it
+ * to the bf16 matrix cores as the sum of two bf16 numbers (high part + remainder), which keeps
+ * about 16 significant bits of h_k in every product.
+ * ------------------------------------------------------------------------------------- */
+MV_API size_t mv_medusa_heads_workspace(int dt, int B, int d, int V, int K, int s_max);
+
+MV_API int mv_medusa_residual(int dt, int B, int d, int K, const void* h, const void* w_res,
+                       float* hk, void* ws, size_t ws_bytes, void* stream);
+
+MV_API int mv_medusa_head_topk(int dt, int B, int d, int V, int K, const int* s_per_head, int s_max,
+                        const void* w_head, void* logits, int32_t* topk_ids, float* topk_vals,
+                        int ld_topk, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+MV_API int mv_medusa_heads(int dt, int B, int d, int V, int K, const int* s_per_head, int s_max,
+                    const void* h, const void* w_res, const void* w_head, float* hk,
+                    void* logits, int32_t* topk_ids, float* topk_vals, int ld_topk, float* lse,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Top-s entries of each of R rows of a logit matrix (the same selection rule as the heads),
+ * for candidates that come from logits the caller already has -- e.g. the base model's own
+ * head ("Head 0", which predicts the next token in [MX] "The Architectural Blueprint").
+ *   x      row r starts at x + r*ldx elements (dt), V entries per row.
+ *   ids    int32, vals fp32 (vals may be NULL): row r at r*ld_out, s entries.
+ * 1 <= s <= MV_MAX_TOPK, s <= V.  No workspace. */
+MV_API int mv_topk_rows(int dt, int R, int V, int s, const void* x, long long ldx, int32_t* ids,
+                 float* vals, int ld_out, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * (a3) Candidate-tree assembly.  [MTP] verification-engine code: the tree is a parent array,
+ * -1 marking a node that hangs directly off the prefix (several such roots form a forest);
+ * [MTP] "The 2D Tree Attention Mask": node i may see node j iff j is an ancestor of i or
+ * j == i; [MX] "2. Single-Pass Tree Attention Verification" gives the same mask in additive
+ * form.  [MX] "1. Combinatorial Tree Construction": the depth-k nodes are the top-s_k tokens
+ * of the head for depth k.
+ *
+ *   N        1..MV_MAX_NODES nodes, parents [N] int32, topological: -1 <= parents[i] < i.
+ *   anc_mask [N, W] uint32 output, W = ceil(N/32): bit (j % 32) of word j/32 of row i is set
+ *            iff j is an ancestor of i or j == i.
+ *   depth    [N] int32 output (1 for a node whose parent is -1), or NULL.
+ *   cand     [B, D, s_max] int32 candidate tokens per depth, or NULL (then node_tokens is
+ *            not written).  Node i takes cand[b][depth_i - 1][rank_i], rank_i = number of
+ *            earlier nodes with the same parent.  s_per_depth (host [D], or NULL = s_max each)
+ *            bounds rank_i; D <= MV_MAX_DEPTH.
+ *   node_tokens [B, N] int32 output (may be NULL when cand is NULL).
+ *   dev_status  MV_DEV_BAD_PARENT / MV_DEV_BAD_RANK / MV_DEV_TOO_DEEP flags, or NULL.
+ * ------------------------------------------------------------------------------------- */
+MV_API int mv_build_tree_mask(int N, const int32_t* parents, int B, int D, int s_max,
+                       const int* s_per_depth, const int32_t* cand, uint32_t* anc_mask,
+                       int32_t* depth, int32_t* node_tokens, int32_t* dev_status,
+                       void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * (a4)+(a5) Tree-masked GQA attention.  [MX] "2. Single-Pass Tree Attention Verification":
+ * the tree is flattened into one packed sequence after the prefix and each node attends to
+ * the whole prefix plus its ancestors (additive mask 0 / -inf); [MTP] "The 2D Tree Attention
+ * Mask" adds the node itself.  Scores are scaled dot products, softmax over the visible keys.
+ *
+ *   dt       MV_BF16 or MV_F32 (q, caches and out share it).  dh in {64, 128}.
+ *   q        [B, N, Hq, dh]; query head h reads KV head h / (Hq/Hkv).  Hq % Hkv == 0.
+ *   k_cache, v_cache [B, Hkv, L_cap, dh]: rows [0, L_b) of sequence b are the prefix and rows
+ *            [L_b, L_b + N) hold the tree's own keys/values in node order; L_b =
+ *            prefix_len[b] (device int32 [B]), 0 <= L_b <= max_L, L_b + N <= L_cap.
+ *   anc_mask [N, ceil(N/32)] uint32 from mv_build_tree_mask.
+ *   scale    softmax scale; <= 0 selects 1/sqrt(dh).
+ *   out      [B, N, Hq, dh] dt output.  lse [B, Hq, N] fp32 natural-log output, or NULL.
+ *   ws       workspace from mv_tree_attn_verify_workspace() with the same sizes: the prefix
+ *            is split into chunks processed by separate workgroups and merged afterwards.
+ *   dev_status MV_DEV_BAD_PREFIX when a prefix length is out of range (it is then clamped).
+ * ------------------------------------------------------------------------------------- */
+MV_API size_t mv_tree_attn_verify_workspace(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L);
+
+MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, int L_cap, int max_L,
+                        const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* prefix_len, const uint32_t* anc_mask, float scale,
+                        void* out, float* lse, int32_t* dev_status, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * (a6)+(a7) Acceptance and the extra token.  Row 0 of target/draft is the distribution after
+ * the last prefix token; row i+1 the one after node i.  Node i (index order) is tested
+ * against the row of its parent and is accepted iff it passes and its parent is -1 or
+ * accepted.  The committed path ends at the deepest accepted node, the lowest index winning
+ * ties ([MTP] engine code keeps the first longest path); one extra token follows it
+ * ([MTP] figure box "longest valid path + 1 bonus token").
+ *
+ * MV_ACCEPT_GREEDY ([MX] "2. Single-Pass Tree Attention Verification", step 3): target holds
+ *   logits (dt); node i passes iff its token equals the argmax of its parent's row (lowest
+ *   index on ties).  The extra token is the argmax of the terminal's row.
+ * MV_ACCEPT_SPECULATIVE ([SD] "The Acceptance Sampling Rule"): target, draft hold fp32
+ *   probabilities; alpha_i = min(1, P_t(x_i)/P_d(x_i)) at the parent's row (1 when
+ *   P_d(x_i) = 0); node i passes iff uniforms[b][i] < alpha_i.  The extra token is drawn
+ *   with uniforms[b][N] by inverse CDF (first v whose running sum exceeds u * total, over
+ *   token order) from normalize(max(0, P_t - P_d)) of the terminal's row when the terminal
+ *   has children (all of them rejected), from P_t when that residual is all zero, and from
+ *   P_t of the terminal's row when the terminal is a leaf.  Decisions and sums are in fp64.
+ *
+ *   target_dt MV_BF16 or MV_F32 for greedy; must be MV_F32 for speculative.
+ *   parents [N], node_tokens [B, N] int32; target [B, N+1, V]; draft [B, N+1, V] fp32 and
+ *   uniforms [B, N+1] fp32 in [0, 1) (speculative only, else NULL).
+ *   D        max tree depth (size of the outputs), 1..MV_MAX_DEPTH.
+ *   accept_len [B] int32; path_nodes [B, D] int32 (-1 padded); out_tokens [B, D+1] int32
+ *            (accepted tokens, then the extra token, then -1).
+ *   node_accept [B, N] uint8 (1 = accepted) or NULL; alpha [B, N] fp32 (speculative) or NULL.
+ *   dev_status MV_DEV_BAD_PARENT / MV_DEV_TOO_DEEP / MV_DEV_BAD_TOKEN flags, or NULL.
+ * ------------------------------------------------------------------------------------- */
+MV_API size_t mv_accept_paths_workspace(int mode, int B, int N, int V);
+
+MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D, const int32_t* parents,
+                    const int32_t* node_tokens, const void* target, const float* draft,
+                    const float* uniforms, int32_t* accept_len, int32_t* path_nodes,
+                    int32_t* out_tokens, uint8_t* node_accept, float* alpha,
+                    int32_t* dev_status, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEDUSA_VERIFY_H */

@@ -1,0 +1,102 @@
+"""ctypes loader of ``libmedusa_verify.so`` (the gfx950 HIP library built in-tree).
+
+Only argument marshalling lives here.  If the library has not been built the import of any
+operation fails loudly: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmedusa_verify.so")
+
+MV_OK = 0
+MV_ERR_INVALID_ARG = -1
+MV_ERR_INVALID_TREE = -2
+MV_ERR_UNSUPPORTED = -3
+MV_ERR_WORKSPACE = -4
+MV_ERR_HIP = -5
+
+MV_F32 = 0
+MV_BF16 = 1
+MV_ACCEPT_GREEDY = 0
+MV_ACCEPT_SPECULATIVE = 1
+
+MV_DEV_BAD_PARENT = 0x1
+MV_DEV_BAD_RANK = 0x2
+MV_DEV_TOO_DEEP = 0x4
+MV_DEV_BAD_PREFIX = 0x8
+MV_DEV_BAD_TOKEN = 0x10
+
+MV_MAX_NODES = 256
+MV_MAX_DEPTH = 16
+MV_MAX_TOPK = 16
+MV_MAX_BATCH_HEADS = 32
+MV_MAX_HEADS = 16
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_Z = ctypes.c_size_t
+_F = ctypes.c_float
+_LL = ctypes.c_longlong
+_IP = ctypes.POINTER(ctypes.c_int)
+
+# (name, restype, argtypes) of every symbol that include/medusa_verify.h declares.
+SIGNATURES = [
+    ("mv_status_string", ctypes.c_char_p, [_I]),
+    ("mv_device_check", _I, [_I]),
+    ("mv_version", _I, []),
+    ("mv_medusa_heads_workspace", _Z, [_I, _I, _I, _I, _I, _I]),
+    ("mv_medusa_residual", _I, [_I, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
+    ("mv_medusa_head_topk", _I, [_I, _I, _I, _I, _I, _IP, _I, _P, _P, _P, _P, _I, _P, _P, _Z, _P]),
+    ("mv_medusa_heads", _I, [_I, _I, _I, _I, _I, _IP, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                             _Z, _P]),
+    ("mv_topk_rows", _I, [_I, _I, _I, _I, _P, _LL, _P, _P, _I, _P]),
+    ("mv_build_tree_mask", _I, [_I, _P, _I, _I, _I, _IP, _P, _P, _P, _P, _P, _P]),
+    ("mv_tree_attn_verify_workspace", _Z, [_I, _I, _I, _I, _I, _I, _I]),
+    ("mv_tree_attn_verify", _I, [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _F, _P, _P,
+                                 _P, _P, _Z, _P]),
+    ("mv_accept_paths_workspace", _Z, [_I, _I, _I, _I]),
+    ("mv_accept_paths", _I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                             _P, _Z, _P]),
+]
+
+_lib = None
+
+
+class MVError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises ImportError when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().mv_status_string(int(status)).decode()
+
+
+def check(fn: str, status: int) -> None:
+    if status != MV_OK:
+        raise MVError(fn, status)
+
+
+def int_array(values):
+    vals = [int(v) for v in values]
+    return (ctypes.c_int * max(1, len(vals)))(*vals)

@@ -1,0 +1,431 @@
+// Acceptance on gfx950: greedy longest accepted path, or the speculative rule with residual
+// resampling, plus the extra token that follows the committed path.
+//
+// Sources: "Medusa Explained: Multi-Head Speculative Decoding Guide", "2. Single-Pass Tree
+// Attention Verification" (step 3: longest path whose every token equals the target's greedy
+// choice); "Speculative Decoding & Medusa Tree Attention", section 2, "The Acceptance
+// Sampling Rule" (accept with probability min(1, P_t/P_d), else sample from
+// normalize(max(0, P_t - P_d))); "Multi-Token Prediction: Draft-Model-Free Speculative
+// Decoding", the verification engine (nodes tested in index order, a node counts only under
+// an accepted parent, the first longest path wins) and the figure box (longest valid path
+// plus one bonus token).
+//
+// Greedy: the target rows are scanned once by many workgroups (row segments -> partial
+// argmax), then one workgroup per sequence merges them and walks the tree.
+// Speculative: one workgroup per sequence gathers the 2N probabilities it needs, decides,
+// walks and picks the terminal row; the terminal row is then summed in segments by many
+// workgroups (fp64) and a last pass per sequence locates the inverse-CDF position.
+//
+// Decision exactness: u < P_t/P_d is evaluated as u*P_d < P_t in fp64; the product of two
+// fp32 numbers is exact in fp64, so the decision is the exact real-number comparison.
+
+#include <math.h>
+
+#include <algorithm>
+
+#include "mv_device.h"
+#include "mv_host.h"
+
+namespace mv {
+namespace {
+
+struct AcceptParams {
+  int B, N, V, D, R, S, segLen;
+  const int32_t* parents;
+  const int32_t* tokens;
+  const void* target;
+  const float* draft;
+  const float* uniforms;
+  int32_t* accept_len;
+  int32_t* path_nodes;
+  int32_t* out_tokens;
+  uint8_t* node_accept;
+  float* alpha;
+  int32_t* status;
+  float* amax_v;  // greedy partials [B*R][S]
+  int* amax_i;
+  int* term;      // speculative: [B][4] = {terminal row, residual?, accepted length, -}
+  double* seg_r;  // speculative: [B][S] segment sums of the residual / of P_t
+  double* seg_t;
+  int* seg_lr;    // last index with a positive entry in the segment (-1 if none)
+  int* seg_lt;
+};
+
+// ---- greedy: partial argmax of one row segment.
+template <bool BF16>
+__global__ __launch_bounds__(256) void row_argmax_kernel(const AcceptParams p) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int s = blockIdx.x % p.S;
+  const size_t row = blockIdx.x / p.S;
+  const int j0 = s * p.segLen, j1 = min(p.V, j0 + p.segLen);
+  const size_t off = row * p.V;
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  if constexpr (BF16) {
+    const uint16_t* x = static_cast<const uint16_t*>(p.target) + off;
+    if ((p.V & 7) == 0) {
+      for (int j = j0 + threadIdx.x * 8; j < j1; j += 256 * 8) {
+        const uint4 w = load_nt_u4(x + j);
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = __uint_as_float((e & 1) ? (wd[e >> 1] & 0xffff0000u) : (wd[e >> 1] << 16));
+          if (v > bv) { bv = v; bi = j + e; }
+        }
+      }
+    } else {
+      for (int j = j0 + threadIdx.x; j < j1; j += 256) {
+        const float v = bf16_to_f32(x[j]);
+        if (v > bv) { bv = v; bi = j; }
+      }
+    }
+  } else {
+    const float* x = static_cast<const float*>(p.target) + off;
+    if ((p.V & 3) == 0) {
+      for (int j = j0 + threadIdx.x * 4; j < j1; j += 256 * 4) {
+        const float4 w = load_nt_f4(x + j);
+        if (w.x > bv) { bv = w.x; bi = j; }
+        if (w.y > bv) { bv = w.y; bi = j + 1; }
+        if (w.z > bv) { bv = w.z; bi = j + 2; }
+        if (w.w > bv) { bv = w.w; bi = j + 3; }
+      }
+    } else {
+      for (int j = j0 + threadIdx.x; j < j1; j += 256) {
+        const float v = x[j];
+        if (v > bv) { bv = v; bi = j; }
+      }
+    }
+  }
+  block_argbest(bv, bi, sv, si);
+  if (threadIdx.x == 0) {
+    p.amax_v[row * p.S + s] = bv;
+    p.amax_i[row * p.S + s] = bi;
+  }
+}
+
+// ---- per-sequence decisions, accepted set, terminal node, committed path.
+template <bool SPEC>
+__global__ __launch_bounds__(256) void accept_path_kernel(const AcceptParams p) {
+  __shared__ int par[MV_MAX_NODES];
+  __shared__ int pred[MV_MAX_NODES + 1];
+  __shared__ int pass[MV_MAX_NODES];
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int b = blockIdx.x, tid = threadIdx.x, N = p.N, R = p.R;
+  if (tid < N) par[tid] = p.parents[tid];
+  if constexpr (!SPEC) {
+    for (int r = tid; r < R; r += 256) {
+      float bv = -INFINITY;
+      int bi = INT_MAX;
+      const size_t q = (static_cast<size_t>(b) * R + r) * p.S;
+      for (int s = 0; s < p.S; ++s) {
+        const float v = p.amax_v[q + s];
+        const int i = p.amax_i[q + s];
+        if (kv_better(v, i, bv, bi)) { bv = v; bi = i; }
+      }
+      pred[r] = bi;
+    }
+  }
+  __syncthreads();
+  int flags = 0;
+  if (tid < N) {
+    const int pn = par[tid];
+    int ok = 0;
+    if (pn < -1 || pn >= tid) {
+      flags |= MV_DEV_BAD_PARENT;
+    } else {
+      const int tok = p.tokens[static_cast<size_t>(b) * N + tid];
+      if (tok < 0 || tok >= p.V) {
+        flags |= MV_DEV_BAD_TOKEN;
+        if (SPEC && p.alpha) p.alpha[static_cast<size_t>(b) * N + tid] = 0.f;
+      } else if constexpr (SPEC) {
+        const size_t o = (static_cast<size_t>(b) * R + (pn + 1)) * p.V + tok;
+        const double pt = static_cast<const float*>(p.target)[o];
+        const double pd = p.draft[o];
+        const double u = p.uniforms[static_cast<size_t>(b) * R + tid];
+        const double a = pd == 0.0 ? 1.0 : fmin(1.0, pt / pd);
+        ok = pd == 0.0 ? (u < 1.0) : (u < 1.0 && u * pd < pt);
+        if (p.alpha) p.alpha[static_cast<size_t>(b) * N + tid] = static_cast<float>(a);
+      } else {
+        ok = tok == pred[pn + 1];
+      }
+    }
+    pass[tid] = ok;
+  }
+  __syncthreads();
+  int accepted = 0, dep = 0;
+  if (tid < N) {
+    int c = tid, ok = 1;
+    while (c != -1) {
+      ok &= pass[c];
+      ++dep;
+      const int nx = par[c];
+      if (nx < -1 || nx >= c) { ok = 0; break; }
+      c = nx;
+    }
+    accepted = ok;
+    if (p.node_accept) p.node_accept[static_cast<size_t>(b) * N + tid] = static_cast<uint8_t>(ok);
+  }
+  float bv = accepted ? static_cast<float>(dep) : -INFINITY;
+  int bi = accepted ? tid : INT_MAX;
+  block_argbest(bv, bi, sv, si);
+  const int term = bi == INT_MAX ? -1 : bi;
+  const int has_child = __syncthreads_or(tid < N && par[tid] == term);
+  if (tid == 0) {
+    int len = 0;
+    for (int c = term; c != -1 && len <= N; c = par[c]) ++len;
+    if (len > p.D) flags |= MV_DEV_TOO_DEEP;
+    const int D = p.D;
+    int32_t* pn_out = p.path_nodes + static_cast<size_t>(b) * D;
+    int32_t* tk_out = p.out_tokens + static_cast<size_t>(b) * (D + 1);
+    for (int k = 0; k < D; ++k) pn_out[k] = -1;
+    for (int k = 0; k <= D; ++k) tk_out[k] = -1;
+    int k = len - 1;
+    for (int c = term; c != -1 && k >= 0; c = par[c], --k) {
+      if (k < D) {
+        pn_out[k] = c;
+        tk_out[k] = p.tokens[static_cast<size_t>(b) * N + c];
+      }
+    }
+    const int lc = min(len, D);
+    p.accept_len[b] = lc;
+    if constexpr (SPEC) {
+      p.term[b * 4 + 0] = term + 1;
+      p.term[b * 4 + 1] = has_child;
+      p.term[b * 4 + 2] = lc;
+    } else {
+      tk_out[lc] = pred[term + 1];
+    }
+  }
+  if (flags && p.status) atomicOr(p.status, flags);
+}
+
+// ---- speculative: fp64 segment sums of the terminal row (residual and target).
+__global__ __launch_bounds__(256) void residual_segsum_kernel(const AcceptParams p) {
+  __shared__ double sd[4];
+  __shared__ int smx[4];
+  const int s = blockIdx.x % p.S, b = blockIdx.x / p.S;
+  const int row = p.term[b * 4 + 0], resid = p.term[b * 4 + 1];
+  const size_t off = (static_cast<size_t>(b) * p.R + row) * p.V;
+  const float* pt = static_cast<const float*>(p.target) + off;
+  const float* pd = p.draft + off;
+  const int j0 = s * p.segLen, j1 = min(p.V, j0 + p.segLen);
+  double sr = 0.0, st = 0.0;
+  int lr = -1, lt = -1;
+  for (int j = j0 + threadIdx.x; j < j1; j += 256) {
+    const double t = pt[j];
+    st += t;
+    if (t > 0.0) lt = j;
+    if (resid) {
+      const double r = fmax(0.0, t - static_cast<double>(pd[j]));
+      sr += r;
+      if (r > 0.0) lr = j;
+    }
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  double vals[2] = {sr, st};
+  int idx[2] = {lr, lt};
+  double outv[2];
+  int outi[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    double v = wave_sum_f64(vals[q]);
+    int mi = idx[q];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mi = max(mi, __shfl_xor(mi, o));
+    __syncthreads();
+    if (lane == 0) { sd[w] = v; smx[w] = mi; }
+    __syncthreads();
+    outv[q] = sd[0] + sd[1] + sd[2] + sd[3];
+    outi[q] = max(max(smx[0], smx[1]), max(smx[2], smx[3]));
+  }
+  if (threadIdx.x == 0) {
+    const size_t q = static_cast<size_t>(b) * p.S + s;
+    p.seg_r[q] = outv[0];
+    p.seg_t[q] = outv[1];
+    p.seg_lr[q] = outi[0];
+    p.seg_lt[q] = outi[1];
+  }
+}
+
+// ---- speculative: inverse-CDF position of u * Z in the chosen distribution.
+__global__ __launch_bounds__(256) void residual_sample_kernel(const AcceptParams p) {
+  __shared__ double pref[257];
+  __shared__ double sub[257];
+  __shared__ int sh[4];
+  __shared__ int found;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int row = p.term[b * 4 + 0], resid = p.term[b * 4 + 1], len = p.term[b * 4 + 2];
+  const size_t off = (static_cast<size_t>(b) * p.R + row) * p.V;
+  const float* pt = static_cast<const float*>(p.target) + off;
+  const float* pd = p.draft + off;
+  const size_t sq = static_cast<size_t>(b) * p.S;
+  if (tid == 0) {
+    double zr = 0.0;
+    for (int s = 0; s < p.S; ++s) zr += p.seg_r[sq + s];
+    const int use_r = resid && zr > 0.0;
+    double acc = 0.0;
+    for (int s = 0; s < p.S; ++s) {
+      pref[s] = acc;
+      acc += use_r ? p.seg_r[sq + s] : p.seg_t[sq + s];
+    }
+    pref[p.S] = acc;
+    const double t = static_cast<double>(p.uniforms[static_cast<size_t>(b) * p.R + p.N]) * acc;
+    int sstar = -1;
+    for (int s = 0; s < p.S; ++s)
+      if (pref[s + 1] > t) { sstar = s; break; }
+    int last = -1;
+    for (int s = 0; s < p.S; ++s) last = max(last, use_r ? p.seg_lr[sq + s] : p.seg_lt[sq + s]);
+    sh[0] = use_r;
+    sh[1] = sstar;
+    sh[2] = last;
+    sub[256] = t;
+    found = -1;
+  }
+  __syncthreads();
+  const int use_r = sh[0], sstar = sh[1];
+  const double t = sub[256];
+  int token = sh[2];
+  if (sstar >= 0) {
+    const int j0 = sstar * p.segLen, j1 = min(p.V, j0 + p.segLen);
+    const int per = (j1 - j0 + 255) / 256;
+    const int a0 = min(j1, j0 + tid * per), a1 = min(j1, a0 + per);
+    auto rv = [&](int j) -> double {
+      const double x = pt[j];
+      return use_r ? fmax(0.0, x - static_cast<double>(pd[j])) : x;
+    };
+    double mine = 0.0;
+    for (int j = a0; j < a1; ++j) mine += rv(j);
+    __syncthreads();
+    sub[tid] = mine;
+    __syncthreads();
+    if (tid == 0) {
+      double acc = pref[sstar];
+      for (int q = 0; q < 256; ++q) {
+        const double nx = acc + sub[q];
+        sub[q] = acc;  // exclusive prefix
+        acc = nx;
+      }
+    }
+    __syncthreads();
+    const double start = sub[tid];
+    const bool cross = a0 < a1 && start + mine > t;
+    // the first thread whose range crosses t scans it
+    int first = cross ? tid : INT_MAX;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o));
+    __syncthreads();
+    if ((tid & 63) == 0) sh[tid >> 6] = first;
+    __syncthreads();
+    const int ft = min(min(sh[0], sh[1]), min(sh[2], sh[3]));
+    if (tid == ft) {
+      double acc = start;
+      int hit = -1;
+      for (int j = a0; j < a1; ++j) {
+        acc += rv(j);
+        if (acc > t) { hit = j; break; }
+      }
+      found = hit;
+    }
+    __syncthreads();
+    if (found >= 0) token = found;
+    else token = use_r ? p.seg_lr[sq + sstar] : p.seg_lt[sq + sstar];
+  }
+  if (tid == 0) p.out_tokens[static_cast<size_t>(b) * (p.D + 1) + len] = token;
+}
+
+struct AcceptPlan {
+  int S = 1, segLen = 1;
+  size_t ws_bytes = 0;
+};
+
+AcceptPlan plan_accept(int mode, int B, int N, int V, void* ws, AcceptParams* p) {
+  AcceptPlan a;
+  const long long R = N + 1;
+  int S;
+  if (mode == MV_ACCEPT_GREEDY) {
+    S = static_cast<int>(std::max<long long>(1, (1024 + B * R - 1) / (B * R)));
+    S = std::min(S, std::max(1, V / 2048));
+    a.segLen = (ceil_div(V, S) + 7) / 8 * 8;
+  } else {
+    S = std::max(1, ceil_div(1024, B));
+    S = std::min(S, std::min(256, std::max(1, V / 1024)));
+    a.segLen = (ceil_div(V, S) + 3) / 4 * 4;
+  }
+  a.S = ceil_div(V, a.segLen);
+  Carver c(ws);
+  if (mode == MV_ACCEPT_GREEDY) {
+    float* av = c.take<float>(static_cast<size_t>(B) * R * a.S);
+    int* ai = c.take<int>(static_cast<size_t>(B) * R * a.S);
+    if (p) { p->amax_v = av; p->amax_i = ai; }
+  } else {
+    int* tm = c.take<int>(static_cast<size_t>(B) * 4);
+    double* sr = c.take<double>(static_cast<size_t>(B) * a.S);
+    double* st = c.take<double>(static_cast<size_t>(B) * a.S);
+    int* lr = c.take<int>(static_cast<size_t>(B) * a.S);
+    int* lt = c.take<int>(static_cast<size_t>(B) * a.S);
+    if (p) { p->term = tm; p->seg_r = sr; p->seg_t = st; p->seg_lr = lr; p->seg_lt = lt; }
+  }
+  a.ws_bytes = c.bytes();
+  return a;
+}
+
+}  // namespace
+}  // namespace mv
+
+using namespace mv;
+
+extern "C" {
+
+MV_API size_t mv_accept_paths_workspace(int mode, int B, int N, int V) {
+  if ((mode != MV_ACCEPT_GREEDY && mode != MV_ACCEPT_SPECULATIVE) || B < 1 || N < 1 || V < 1) return 0;
+  if (N > MV_MAX_NODES) return 0;
+  return plan_accept(mode, B, N, V, nullptr, nullptr).ws_bytes;
+}
+
+MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D,
+                           const int32_t* parents, const int32_t* node_tokens, const void* target,
+                           const float* draft, const float* uniforms, int32_t* accept_len,
+                           int32_t* path_nodes, int32_t* out_tokens, uint8_t* node_accept,
+                           float* alpha, int32_t* dev_status, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (mode != MV_ACCEPT_GREEDY && mode != MV_ACCEPT_SPECULATIVE) return MV_ERR_INVALID_ARG;
+  if (target_dt != MV_F32 && target_dt != MV_BF16) return MV_ERR_INVALID_ARG;
+  if (B < 1 || N < 1 || V < 1 || D < 1) return MV_ERR_INVALID_ARG;
+  if (N > MV_MAX_NODES || D > MV_MAX_DEPTH) return MV_ERR_UNSUPPORTED;
+  if (!parents || !node_tokens || !target || !accept_len || !path_nodes || !out_tokens)
+    return MV_ERR_INVALID_ARG;
+  if (mode == MV_ACCEPT_SPECULATIVE) {
+    if (target_dt != MV_F32) return MV_ERR_UNSUPPORTED;
+    if (!draft || !uniforms) return MV_ERR_INVALID_ARG;
+  }
+  const AcceptPlan need = plan_accept(mode, B, N, V, nullptr, nullptr);
+  MV_TRY(check_ws(ws, ws_bytes, need.ws_bytes));
+  AcceptParams p{};
+  p.B = B; p.N = N; p.V = V; p.D = D; p.R = N + 1;
+  p.parents = parents; p.tokens = node_tokens; p.target = target; p.draft = draft;
+  p.uniforms = uniforms; p.accept_len = accept_len; p.path_nodes = path_nodes;
+  p.out_tokens = out_tokens; p.node_accept = node_accept; p.alpha = alpha; p.status = dev_status;
+  const AcceptPlan a = plan_accept(mode, B, N, V, ws, &p);
+  p.S = a.S;
+  p.segLen = a.segLen;
+  hipStream_t st = as_stream(stream);
+  if (mode == MV_ACCEPT_GREEDY) {
+    const long long blocks = static_cast<long long>(B) * p.R * a.S;
+    if (blocks > (1LL << 31) - 1) return MV_ERR_UNSUPPORTED;
+    if (target_dt == MV_BF16) row_argmax_kernel<true><<<static_cast<int>(blocks), 256, 0, st>>>(p);
+    else row_argmax_kernel<false><<<static_cast<int>(blocks), 256, 0, st>>>(p);
+    MV_TRY(launch_status());
+    accept_path_kernel<false><<<B, 256, 0, st>>>(p);
+    return launch_status();
+  }
+  accept_path_kernel<true><<<B, 256, 0, st>>>(p);
+  MV_TRY(launch_status());
+  residual_segsum_kernel<<<B * a.S, 256, 0, st>>>(p);
+  MV_TRY(launch_status());
+  residual_sample_kernel<<<B, 256, 0, st>>>(p);
+  return launch_status();
+}
+
+}  // extern "C"

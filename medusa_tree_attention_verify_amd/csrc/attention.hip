@@ -1,0 +1,479 @@
+// Tree-masked GQA attention on gfx950.
+//
+// Sources: "Medusa Explained: Multi-Head Speculative Decoding Guide", "2. Single-Pass Tree
+// Attention Verification" (the candidate tree is packed after the prefix and every node sees
+// the whole prefix plus its ancestors; mask M_tree is 0 there and -inf elsewhere);
+// "Multi-Token Prediction: Draft-Model-Free Speculative Decoding", "The 2D Tree Attention
+// Mask" (ancestor-or-self, so every node also sees itself).
+//
+// bf16 path.  For one (sequence b, KV head g) the G query heads of the group and the N tree
+// nodes form M = N*G query rows that share every key, so they are packed into the MFMA tile:
+// a wave owns 32 query rows, a workgroup 32*NWV.  The prefix is split into chunks handled by
+// separate workgroups (split-KV); the chunk that ends the prefix also takes the N tree keys,
+// where the per-node ancestor bitmask replaces the dense mask.  Per 32-key tile:
+//   * K and V come from HBM with coalesced 16-byte loads (prefetched one tile ahead into
+//     registers) and land in LDS: K row-major, V transposed with its keys permuted so that
+//     the P.V operand of every lane is one 16-byte LDS read;
+//   * S^T = K Q^T is one 32x32 output tile of v_mfma_f32_32x32x16_bf16 per wave; in its
+//     output layout a lane holds 16 keys of one query, so the softmax max/sum need one
+//     cross-lane step (lanes l and l+32);
+//   * online softmax in the exp2 domain (scale * log2(e) folded into the scores);
+//   * O^T += V^T P^T, P rounded to bf16, accumulated in fp32.
+// A second kernel merges the chunk partials with their (max, sum) pairs.
+//
+// fp32 path: a vector-ALU kernel, one wave per query row, no chunking (the fp32 configuration
+// is a small check case).
+
+#include <math.h>
+
+#include <algorithm>
+
+#include "mv_device.h"
+#include "mv_host.h"
+
+namespace mv {
+namespace {
+
+struct AttnParams {
+  int B, N, Hq, Hkv, G, M, L_cap, max_L, CK, nchunks, qtiles, W, total;
+  float scale_log2;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* prefix_len;
+  const uint32_t* anc;
+  void* out;
+  float* lse;
+  float* part_o;
+  float2* part_ml;
+  int32_t* status;
+};
+
+constexpr int kXcds = 8;  // MI355X: workgroups are handed to the 8 XCDs round-robin
+
+__device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool report) {
+  const int hi = min(p.max_L, p.L_cap - p.N);
+  if (Lb < 0 || Lb > hi) {
+    if (report && p.status) atomicOr(p.status, MV_DEV_BAD_PREFIX);
+    Lb = max(0, min(Lb, hi));
+  }
+  return Lb;
+}
+
+// Slot of key k (0..31) in a transposed V tile row: the keys that one lane feeds to one
+// P.V MFMA become 8 consecutive slots.
+__device__ __forceinline__ int v_slot(int k) {
+  const int kk = k & 15;
+  return (k >> 4) * 16 + ((kk & 7) >> 2) * 8 + ((kk >> 3) << 2) + (kk & 3);
+}
+
+template <int DH, int NWV>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 8))) void tree_attn_bf16_kernel(const AttnParams p) {
+  constexpr int NT = NWV * 64;
+  constexpr int KP = DH + 8;  // K tile pitch (elements)
+  constexpr int VP = 32 + 8;  // V^T tile pitch (elements)
+  constexpr int KS = DH / 16;
+  constexpr int DB = DH / 32;
+  constexpr int DG = DH / 8;  // 16-byte pieces per key row
+  constexpr int PPT = 32 * DG / NT;
+  static_assert((32 * DG) % NT == 0, "tile pieces must split evenly");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][32 * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DH * VP];
+
+  // XCD-aware order: consecutive logical tiles (the query tiles of one KV chunk) run on one XCD.
+  const int per = (p.total + kXcds - 1) / kXcds;
+  const int lid = static_cast<int>(blockIdx.x % kXcds) * per + static_cast<int>(blockIdx.x / kXcds);
+  if (lid >= p.total) return;
+  int r = lid;
+  const int qt = r % p.qtiles;
+  r /= p.qtiles;
+  const int c = r % p.nchunks;
+  r /= p.nchunks;
+  const int g = r % p.Hkv;
+  const int b = r / p.Hkv;
+
+  const int Lb = clamp_prefix(p, p.prefix_len[b], threadIdx.x == 0 && qt == 0 && c == 0 && g == 0);
+  const int ncb = max(1, (Lb + p.CK - 1) / p.CK);
+  if (c >= ncb) return;
+  const int kbeg = c * p.CK, kend = min(Lb, kbeg + p.CK);
+  const bool last = c == ncb - 1;
+  const int ntp = kend > kbeg ? (kend - kbeg + 31) / 32 : 0;
+  const int ntiles = ntp + (last ? (p.N + 31) / 32 : 0);
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int m = qt * (NWV * 32) + wv * 32 + l32;
+  const bool qvalid = m < p.M;
+  const int node = qvalid ? m / p.G : 0;
+  const int h = g * p.G + (qvalid ? m % p.G : 0);
+
+  const uint16_t* qp = static_cast<const uint16_t*>(p.q);
+  bf16x8 qreg[KS];
+  {
+    const uint16_t* qrow = qp + (static_cast<size_t>(b * p.N + node) * p.Hq + h) * DH;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 t4 = qvalid ? *reinterpret_cast<const uint4*>(qrow + ks * 16 + half * 8) : make_uint4(0, 0, 0, 0);
+      qreg[ks] = as_bf16x8(t4);
+    }
+  }
+  const size_t kvbase = (static_cast<size_t>(b) * p.Hkv + g) * p.L_cap * DH;
+  const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + kvbase;
+  const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + kvbase;
+
+  uint4 kreg[PPT], vreg[PPT];
+  auto tile_rows = [&](int t, int& row0, int& nv) {
+    if (t < ntp) {
+      row0 = kbeg + t * 32;
+      nv = min(32, kend - row0);
+    } else {
+      const int tt = t - ntp;
+      row0 = Lb + tt * 32;
+      nv = min(32, p.N - tt * 32);
+    }
+  };
+  auto gload = [&](int t) {
+    int row0, nv;
+    tile_rows(t, row0, nv);
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int pc = tid + i * NT, key = pc / DG, dg = pc % DG;
+      if (key < nv) {
+        const size_t o = static_cast<size_t>(row0 + key) * DH + dg * 8;
+        kreg[i] = load_nt_u4(Kg + o);
+        vreg[i] = load_nt_u4(Vg + o);
+      } else {
+        kreg[i] = make_uint4(0, 0, 0, 0);
+        vreg[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int pc = tid + i * NT, key = pc / DG, dg = pc % DG;
+      *reinterpret_cast<uint4*>(&Ks[buf][key * KP + dg * 8]) = kreg[i];
+      // The lane holding key^1 (same d range) is lane ^ DG; two keys share one 32-bit word.
+      const uint32_t mine[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+      uint32_t other[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) other[q] = __shfl_xor(mine[q], DG);
+      const bool odd = key & 1;
+      const int slot = v_slot(key & ~1);
+      uint32_t* vt = reinterpret_cast<uint32_t*>(&Vt[buf][0]);
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int e = odd ? e4 + 4 : e4;
+        const uint32_t wm = mine[e >> 1], wo = other[e >> 1];
+        const uint32_t hm = (e & 1) ? (wm >> 16) : (wm & 0xffffu);
+        const uint32_t ho = (e & 1) ? (wo >> 16) : (wo & 0xffffu);
+        const uint32_t word = odd ? (ho | (hm << 16)) : (hm | (ho << 16));
+        vt[((dg * 8 + e) * VP + slot) >> 1] = word;
+      }
+    }
+  };
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  gload(0);
+  swrite(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) gload(t + 1);
+    f32x16 sacc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 a = *reinterpret_cast<const uint4*>(&Ks[buf][l32 * KP + ks * 16 + half * 8]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qreg[ks], sacc, 0, 0, 0);
+    }
+    int row0, nv;
+    tile_rows(t, row0, nv);
+    const bool tree = t >= ntp;
+    const uint32_t ancw = (tree && qvalid) ? p.anc[static_cast<size_t>(node) * p.W + (t - ntp)] : 0u;
+    // 32x32 output layout: lane holds query l32 and keys 8*(v/4) + 4*half + v%4.
+    float sv[16];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int kl = 8 * (v >> 2) + 4 * half + (v & 3);
+      const bool ok = kl < nv && (!tree || ((ancw >> kl) & 1u));
+      sv[v] = ok ? sacc[v] * p.scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, sv[v]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float lsum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      sv[v] = exp2f(sv[v] - m_use);
+      lsum += sv[v];
+    }
+    lsum += __shfl_xor(lsum, 32);
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+    const uint4 pw[2] = {
+        make_uint4(pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]), pack_bf16x2(sv[4], sv[5]),
+                   pack_bf16x2(sv[6], sv[7])),
+        make_uint4(pack_bf16x2(sv[8], sv[9]), pack_bf16x2(sv[10], sv[11]),
+                   pack_bf16x2(sv[12], sv[13]), pack_bf16x2(sv[14], sv[15]))};
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&Vt[buf][(db * 32 + l32) * VP + hf * 16 + half * 8]);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pw[hf]), oacc[db], 0, 0, 0);
+      }
+    }
+    if (t + 1 < ntiles) swrite(buf ^ 1);
+    __syncthreads();
+  }
+  if (!qvalid) return;
+  // Output layout of O^T: lane holds query l32, dims db*32 + 8*(v/4) + 4*half + v%4.
+  if (ncb == 1) {
+    const float inv = 1.f / l_run;
+    uint16_t* orow = static_cast<uint16_t*>(p.out) + (static_cast<size_t>(b * p.N + node) * p.Hq + h) * DH;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        const int d0 = db * 32 + 8 * vq + 4 * half;
+        uint2 w2;
+        w2.x = pack_bf16x2(oacc[db][vq * 4 + 0] * inv, oacc[db][vq * 4 + 1] * inv);
+        w2.y = pack_bf16x2(oacc[db][vq * 4 + 2] * inv, oacc[db][vq * 4 + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + d0) = w2;
+      }
+    if (p.lse && half == 0)
+      p.lse[(static_cast<size_t>(b) * p.Hq + h) * p.N + node] = (m_run + log2f(l_run)) * kLn2;
+  } else {
+    const size_t rowi = (static_cast<size_t>(b * p.Hq + h) * p.N + node) * p.nchunks + c;
+    float* po = p.part_o + rowi * DH;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        const int d0 = db * 32 + 8 * vq + 4 * half;
+        *reinterpret_cast<float4*>(po + d0) =
+            make_float4(oacc[db][vq * 4 + 0], oacc[db][vq * 4 + 1], oacc[db][vq * 4 + 2], oacc[db][vq * 4 + 3]);
+      }
+    if (half == 0) p.part_ml[rowi] = make_float2(m_run, l_run);
+  }
+}
+
+// Merge of the chunk partials: O = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c.
+template <int DH>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
+  const int rowid = blockIdx.x * 4 + (threadIdx.x >> 6);  // ((b*Hq + h)*N + i)
+  if (rowid >= p.B * p.Hq * p.N) return;
+  const int lane = threadIdx.x & 63;
+  const int i = rowid % p.N, h = (rowid / p.N) % p.Hq, b = rowid / (p.N * p.Hq);
+  const int Lb = clamp_prefix(p, p.prefix_len[b], false);
+  const int ncb = max(1, (Lb + p.CK - 1) / p.CK);
+  if (ncb == 1) return;
+  const size_t base = static_cast<size_t>(rowid) * p.nchunks;
+  float M = -INFINITY;
+  for (int c = 0; c < ncb; ++c) M = fmaxf(M, p.part_ml[base + c].x);
+  float L = 0.f, acc[DH / 64];
+#pragma unroll
+  for (int e = 0; e < DH / 64; ++e) acc[e] = 0.f;
+  for (int c = 0; c < ncb; ++c) {
+    const float2 ml = p.part_ml[base + c];
+    const float w = exp2f(ml.x - M);
+    L += w * ml.y;
+    const float* po = p.part_o + (base + c) * DH;
+#pragma unroll
+    for (int e = 0; e < DH / 64; ++e) acc[e] += w * po[lane + 64 * e];
+  }
+  const float inv = 1.f / L;
+  uint16_t* orow = static_cast<uint16_t*>(p.out) + (static_cast<size_t>(b * p.N + i) * p.Hq + h) * DH;
+#pragma unroll
+  for (int e = 0; e < DH / 64; ++e) orow[lane + 64 * e] = f32_to_bf16(acc[e] * inv);
+  if (p.lse && lane == 0) p.lse[(static_cast<size_t>(b) * p.Hq + h) * p.N + i] = (M + log2f(L)) * kLn2;
+}
+
+// fp32: one wave per query row (b, node i, head h); lanes run over keys for the scores and
+// over head dimensions for P.V.
+template <int DH>
+__global__ __launch_bounds__(256) void tree_attn_f32_kernel(const AttnParams p) {
+  const int rowid = blockIdx.x * 4 + (threadIdx.x >> 6);  // ((b*N + i)*Hq + h)
+  if (rowid >= p.B * p.N * p.Hq) return;
+  const int lane = threadIdx.x & 63;
+  const int h = rowid % p.Hq, i = (rowid / p.Hq) % p.N, b = rowid / (p.Hq * p.N);
+  const int g = h / p.G;
+  const int Lb = clamp_prefix(p, p.prefix_len[b], lane == 0 && i == 0 && h == 0);
+  const float* qrow = static_cast<const float*>(p.q) + static_cast<size_t>(rowid) * DH;
+  float qv[DH];
+#pragma unroll
+  for (int d = 0; d < DH; d += 4) {
+    const float4 t = *reinterpret_cast<const float4*>(qrow + d);
+    qv[d] = t.x; qv[d + 1] = t.y; qv[d + 2] = t.z; qv[d + 3] = t.w;
+  }
+  const size_t kvbase = (static_cast<size_t>(b) * p.Hkv + g) * p.L_cap * DH;
+  const float* Kg = static_cast<const float*>(p.k) + kvbase;
+  const float* Vg = static_cast<const float*>(p.v) + kvbase;
+  const uint32_t* ancrow = p.anc + static_cast<size_t>(i) * p.W;
+  const int nkeys = Lb + p.N;
+  float m_run = -INFINITY, l_run = 0.f, acc[DH / 64];
+#pragma unroll
+  for (int e = 0; e < DH / 64; ++e) acc[e] = 0.f;
+  for (int k0 = 0; k0 < nkeys; k0 += 64) {
+    const int kk = k0 + lane;
+    bool ok = kk < nkeys;
+    if (ok && kk >= Lb) {
+      const int j = kk - Lb;
+      ok = (ancrow[j >> 5] >> (j & 31)) & 1u;
+    }
+    float s = -INFINITY;
+    if (ok) {
+      const float* kr = Kg + static_cast<size_t>(kk) * DH;
+      float a = 0.f;
+#pragma unroll
+      for (int d = 0; d < DH; d += 4) {
+        const float4 t = *reinterpret_cast<const float4*>(kr + d);
+        a = fmaf(qv[d], t.x, a);
+        a = fmaf(qv[d + 1], t.y, a);
+        a = fmaf(qv[d + 2], t.z, a);
+        a = fmaf(qv[d + 3], t.w, a);
+      }
+      s = a * p.scale_log2;
+    }
+    const float tmax = wave_max(s);
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    const float pj = exp2f(s - m_use);
+    l_run = l_run * alpha + wave_sum(pj);
+    m_run = m_new;
+#pragma unroll
+    for (int e = 0; e < DH / 64; ++e) acc[e] *= alpha;
+    const int cnt = min(64, nkeys - k0);
+    for (int j = 0; j < cnt; ++j) {
+      const float pb = __shfl(pj, j);
+      if (pb != 0.f) {
+        const float* vr = Vg + static_cast<size_t>(k0 + j) * DH;
+#pragma unroll
+        for (int e = 0; e < DH / 64; ++e) acc[e] = fmaf(pb, vr[lane + 64 * e], acc[e]);
+      }
+    }
+  }
+  float* orow = static_cast<float*>(p.out) + static_cast<size_t>(rowid) * DH;
+  const float inv = 1.f / l_run;
+#pragma unroll
+  for (int e = 0; e < DH / 64; ++e) orow[lane + 64 * e] = acc[e] * inv;
+  if (p.lse && lane == 0) p.lse[(static_cast<size_t>(b) * p.Hq + h) * p.N + i] = (m_run + log2f(l_run)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------------------
+constexpr int kNWV = 4;  // waves per workgroup -> 128 query rows
+
+struct AttnPlan {
+  int qtiles = 1, CK = 256, nchunks = 1;
+  size_t ws_bytes = 0;
+};
+
+// Chunking: aim for ~2048 workgroups (8 per CU) while keeping chunks >= 256 keys, so that the
+// partial outputs stay small next to the K/V bytes of a chunk.
+AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L) {
+  AttnPlan a;
+  if (dt == MV_F32) return a;
+  const int M = N * (Hq / Hkv);
+  a.qtiles = ceil_div(M, kNWV * 32);
+  const long long base = static_cast<long long>(B) * Hkv * a.qtiles;
+  int want = static_cast<int>(std::max<long long>(1, (2048 + base - 1) / base));
+  const int cap = std::max(1, ceil_div(max_L, 256));
+  want = std::min(want, cap);
+  int ck = ceil_div(std::max(max_L, 1), want);
+  ck = std::max(256, (ck + 31) / 32 * 32);
+  a.CK = ck;
+  a.nchunks = std::max(1, ceil_div(max_L, ck));
+  if (a.nchunks > 1) {
+    Carver c(nullptr);
+    const size_t rows = static_cast<size_t>(B) * Hq * N * a.nchunks;
+    c.take<float>(rows * dh);
+    c.take<float2>(rows);
+    a.ws_bytes = c.bytes();
+  }
+  return a;
+}
+
+}  // namespace
+}  // namespace mv
+
+using namespace mv;
+
+extern "C" {
+
+MV_API size_t mv_tree_attn_verify_workspace(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L) {
+  if ((dt != MV_F32 && dt != MV_BF16) || B < 1 || N < 1 || Hq < 1 || Hkv < 1 || max_L < 0) return 0;
+  if (Hq % Hkv != 0 || (dh != 64 && dh != 128) || N > MV_MAX_NODES) return 0;
+  return plan_attn(dt, B, N, Hq, Hkv, dh, max_L).ws_bytes;
+}
+
+MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, int L_cap, int max_L,
+                               const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* prefix_len, const uint32_t* anc_mask, float scale,
+                               void* out, float* lse, int32_t* dev_status, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (dt != MV_F32 && dt != MV_BF16) return MV_ERR_INVALID_ARG;
+  if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || max_L < 0 || L_cap < N) return MV_ERR_INVALID_ARG;
+  if (!q || !k_cache || !v_cache || !prefix_len || !anc_mask || !out) return MV_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return MV_ERR_INVALID_ARG;
+  if (dh != 64 && dh != 128) return MV_ERR_UNSUPPORTED;
+  if (N > MV_MAX_NODES) return MV_ERR_UNSUPPORTED;
+  if (max_L > L_cap - N) return MV_ERR_INVALID_ARG;
+  const AttnPlan a = plan_attn(dt, B, N, Hq, Hkv, dh, max_L);
+  MV_TRY(check_ws(ws, ws_bytes, a.ws_bytes));
+  AttnParams p{};
+  p.B = B; p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.M = N * p.G;
+  p.L_cap = L_cap; p.max_L = max_L; p.CK = a.CK; p.nchunks = a.nchunks; p.qtiles = a.qtiles;
+  p.W = (N + 31) / 32;
+  p.scale_log2 = (scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(dh))) * kLog2e;
+  p.q = q; p.k = k_cache; p.v = v_cache; p.prefix_len = prefix_len; p.anc = anc_mask;
+  p.out = out; p.lse = lse; p.status = dev_status;
+  hipStream_t st = as_stream(stream);
+  if (dt == MV_F32) {
+    const int rows = B * N * Hq;
+    const int blocks = (rows + 3) / 4;
+    if (dh == 64) tree_attn_f32_kernel<64><<<blocks, 256, 0, st>>>(p);
+    else tree_attn_f32_kernel<128><<<blocks, 256, 0, st>>>(p);
+    return launch_status();
+  }
+  if (a.nchunks > 1) {
+    Carver c(ws);
+    const size_t rows = static_cast<size_t>(B) * Hq * N * a.nchunks;
+    p.part_o = c.take<float>(rows * dh);
+    p.part_ml = c.take<float2>(rows);
+  }
+  const long long total = static_cast<long long>(B) * Hkv * a.nchunks * a.qtiles;
+  if (total > (1LL << 30)) return MV_ERR_UNSUPPORTED;
+  p.total = static_cast<int>(total);
+  const int grid = ceil_div(total, kXcds) * kXcds;
+  if (dh == 64) tree_attn_bf16_kernel<64, kNWV><<<grid, kNWV * 64, 0, st>>>(p);
+  else tree_attn_bf16_kernel<128, kNWV><<<grid, kNWV * 64, 0, st>>>(p);
+  MV_TRY(launch_status());
+  if (a.nchunks > 1) {
+    const int rows = B * Hq * N;
+    const int blocks = (rows + 3) / 4;
+    if (dh == 64) attn_combine_kernel<64><<<blocks, 256, 0, st>>>(p);
+    else attn_combine_kernel<128><<<blocks, 256, 0, st>>>(p);
+    MV_TRY(launch_status());
+  }
+  return MV_OK;
+}
+
+}  // extern "C"

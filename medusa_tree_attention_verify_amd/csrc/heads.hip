@@ -1,0 +1,541 @@
+// Medusa heads on gfx950: the residual block h_k = SiLU(W_res^(k) h) + h and the vocabulary
+// projection logits_k = W_head^(k) h_k with its top-s_k tokens and log-sum-exp.
+//
+// Source: "Medusa Explained: Multi-Head Speculative Decoding Guide", section "The
+// Architectural Blueprint" (residual block without bias, softmax over the projection) and
+// "1. Combinatorial Tree Construction" (each head offers its top-s_k tokens).
+//
+// Both products are matrix-vector products over a handful of batch rows, so they are bound by
+// streaming the weights once from HBM.  They run on the bf16 matrix cores anyway: one
+// v_mfma_f32_16x16x32_bf16 takes a 16-row x 32-column weight tile straight from the load
+// registers and reduces over the 32 columns in hardware, which leaves the vector ALUs free and
+// needs no cross-lane reduction in the streaming loop.  The 16 MFMA columns carry the batch:
+// columns 0-7 hold the high bf16 part of up to 8 batch vectors and columns 8-15 the bf16
+// remainder (x - hi), so an fp32 vector enters the product with ~16 significant bits and the
+// sum of the two column halves is the fp32-accurate dot product.  bf16 inputs have a zero
+// remainder.  The vector side is pre-arranged in the exact register layout of the MFMA B
+// operand ("packed"), so the streaming loop does one coalesced 16-byte load per lane for it.
+//
+// Each workgroup owns 32 weight rows; its NW waves split the reduction dimension and meet in
+// LDS.  The projection's epilogue keeps only a per-workgroup top-s and (max, sum-exp) pair per
+// batch row; the last workgroup of each head (completion counter) merges them, so the logits
+// never have to be written.
+
+#include <math.h>
+
+#include "mv_device.h"
+#include "mv_host.h"
+
+namespace mv {
+namespace {
+
+constexpr int kRows = 32;  // weight rows per workgroup
+
+struct GemvParams {
+  int B, d, R, K, T, nrb;   // R = rows per head, T = d / 32, nrb = ceil(R / kRows)
+  const void* W;            // [K][R][d]
+  const u32x4* bsrc;        // packed B operand (bf16 path)
+  long long bsrc_hstride;   // per-head stride of bsrc in u32x4 units (0 = shared)
+  const float* xsrc;        // fp32 path: vector source, [B][xstride] with per-head offset
+  long long x_bstride, x_hstride;
+  // residual epilogue
+  const void* h;
+  float* hk_ws;
+  float* hk_out;
+  uint16_t* bpack_out;
+  unsigned* cnt;
+  // projection epilogue
+  void* logits;
+  float* pval;
+  int* pidx;
+  float* pm;
+  float* pl;
+  int32_t* topk_ids;
+  float* topk_vals;
+  int ld_topk;
+  float* lse;
+  int s_max;
+  int s[MV_MAX_HEADS];
+};
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* base, size_t i) {
+  if constexpr (BF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[i]);
+  else return static_cast<const float*>(base)[i];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_elem(void* base, size_t i, float v) {
+  if constexpr (BF16) static_cast<uint16_t*>(base)[i] = f32_to_bf16(v);
+  else static_cast<float*>(base)[i] = v;
+}
+
+// ---- residual epilogue: h_k = SiLU(u) + h; keep fp32 h_k and (bf16 path) its packed form.
+template <bool BF16, int BC>
+__device__ void residual_epilogue(const GemvParams& p, int k, int row0, float (*ys)[BC]) {
+  const int nct = BC / 8;
+  for (int idx = threadIdx.x; idx < kRows * BC; idx += blockDim.x) {
+    const int row = idx / BC, b = idx % BC, j = row0 + row;
+    if (j >= p.d) continue;
+    float v = 0.f;
+    if (b < p.B) {
+      const float u = ys[row][b];
+      const float silu = u / (1.0f + expf(-u));
+      v = silu + load_elem<BF16>(p.h, static_cast<size_t>(b) * p.d + j);
+      const size_t o = (static_cast<size_t>(b) * p.K + k) * p.d + j;
+      p.hk_ws[o] = v;
+      if (p.hk_out) p.hk_out[o] = v;
+    }
+    if constexpr (BF16) {
+      const uint16_t hi = (b < p.B) ? f32_to_bf16(v) : 0;
+      const uint16_t lo = (b < p.B) ? f32_to_bf16(v - bf16_to_f32(hi)) : 0;
+      const int t = j >> 5, g = (j >> 3) & 3, e = j & 7, ct = b >> 3, bb = b & 7;
+      const size_t base = ((static_cast<size_t>(k) * p.T + t) * nct + ct) * 64;
+      p.bpack_out[(base + g * 16 + bb) * 8 + e] = hi;
+      p.bpack_out[(base + g * 16 + 8 + bb) * 8 + e] = lo;
+    }
+  }
+}
+
+// ---- merge of the per-workgroup partials of head k (run by the last workgroup of head k).
+__device__ void heads_merge(const GemvParams& p, int k, float* sv, int* si) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int nrb = p.nrb, s = p.s[k], smax = p.s_max;
+  for (int b = 0; b < p.B; ++b) {
+    const size_t base = (static_cast<size_t>(k) * p.B + b) * nrb;
+    float m = -INFINITY;
+    for (int j = tid; j < nrb; j += nt) m = fmaxf(m, load_agent(p.pm + base + j));
+    m = block_max(m, sv);
+    float l = 0.f;
+    for (int j = tid; j < nrb; j += nt)
+      l += load_agent(p.pl + base + j) * expf(load_agent(p.pm + base + j) - m);
+    l = block_sum(l, sv);
+    float pv = INFINITY;
+    int pi = -1;
+    for (int r = 0; r < smax; ++r) {
+      float bv = -INFINITY;
+      int bi = INT_MAX;
+      if (r < s) {
+        for (int j = tid; j < nrb * s; j += nt) {
+          const size_t q = (base + j / s) * smax + (j % s);
+          const int ii = load_agent(p.pidx + q);
+          const float vv = load_agent(p.pval + q);
+          if (ii >= 0 && kv_after(vv, ii, pv, pi) && kv_better(vv, ii, bv, bi)) {
+            bv = vv;
+            bi = ii;
+          }
+        }
+      }
+      block_argbest(bv, bi, sv, si);
+      if (tid == 0) {
+        const size_t o = static_cast<size_t>(b) * p.ld_topk + static_cast<size_t>(k) * smax + r;
+        const bool ok = r < s && bi != INT_MAX;
+        p.topk_ids[o] = ok ? bi : -1;
+        p.topk_vals[o] = ok ? bv : -INFINITY;
+      }
+      pv = bv;
+      pi = bi;
+    }
+    if (tid == 0 && p.lse) p.lse[static_cast<size_t>(b) * p.K + k] = m + logf(l);
+  }
+  if (tid == 0) p.cnt[k] = 0u;  // re-arm the counter for the next launch
+}
+
+// ---- projection epilogue: optional logits, per-workgroup top-s and (max, sum exp), merge.
+template <bool BF16, int NW, int BC>
+__device__ void head_epilogue(const GemvParams& p, int k, int rb, float (*ys)[BC]) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  __shared__ int last;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row0 = rb * kRows;
+  if (p.logits) {
+    for (int idx = threadIdx.x; idx < kRows * BC; idx += blockDim.x) {
+      const int row = idx / BC, b = idx % BC, j = row0 + row;
+      if (b < p.B && j < p.R)
+        store_elem<BF16>(p.logits, (static_cast<size_t>(b) * p.K + k) * p.R + j, ys[row][b]);
+    }
+  }
+  const int s = p.s[k];
+  for (int b = w; b < p.B; b += NW) {
+    const int j = row0 + lane;
+    float val = (lane < kRows && j < p.R) ? ys[lane][b] : -INFINITY;
+    const float m = wave_max(val);
+    const float l = wave_sum(val == -INFINITY ? 0.f : expf(val - m));
+    const size_t q = (static_cast<size_t>(k) * p.B + b) * p.nrb + rb;
+    if (lane == 0) {
+      p.pm[q] = m;
+      p.pl[q] = l;
+    }
+    for (int r = 0; r < s; ++r) {
+      float bv = val;
+      int bi = (val == -INFINITY) ? INT_MAX : j;
+      wave_argbest(bv, bi);
+      if (lane == 0) {
+        p.pval[q * p.s_max + r] = bv;
+        p.pidx[q * p.s_max + r] = (bi == INT_MAX) ? -1 : bi;
+      }
+      if (bi == j) val = -INFINITY;
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last = (atomicAdd(&p.cnt[k], 1u) == static_cast<unsigned>(p.nrb - 1));
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  heads_merge(p, k, sv, si);
+}
+
+// ---- bf16 weights: MFMA streaming loop.
+template <int NW, int NCT, int MODE>
+__global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(const GemvParams p) {
+  constexpr int RT = kRows / 16, BC = 8 * NCT, U = 4;
+  __shared__ float red[NW][kRows][16 * NCT + 1];
+  __shared__ float ys[kRows][BC];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int k = blockIdx.y, rb = blockIdx.x, row0 = rb * kRows;
+  if (MODE == 0 && rb == 0 && threadIdx.x < MV_MAX_HEADS) p.cnt[threadIdx.x] = 0u;
+
+  const uint16_t* Wk = static_cast<const uint16_t*>(p.W) + static_cast<size_t>(k) * p.R * p.d;
+  const u32x4* arow[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = min(row0 + rt * 16 + (lane & 15), p.R - 1);
+    arow[rt] = reinterpret_cast<const u32x4*>(Wk + static_cast<size_t>(r) * p.d) + (lane >> 4);
+  }
+  const u32x4* bk = p.bsrc + k * p.bsrc_hstride + lane;
+
+  f32x4 acc[RT][NCT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int t0 = (w * p.T) / NW, t1 = ((w + 1) * p.T) / NW;
+  int t = t0;
+  for (; t + U <= t1; t += U) {
+    u32x4 a[U][RT], bv[U][NCT];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) a[u][rt] = __builtin_nontemporal_load(arow[rt] + (t + u) * 4);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) bv[u][ct] = bk[((t + u) * NCT + ct) * 64];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, a[u][rt]), __builtin_bit_cast(bf16x8, bv[u][ct]),
+              acc[rt][ct], 0, 0, 0);
+  }
+  for (; t < t1; ++t) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const u32x4 a = __builtin_nontemporal_load(arow[rt] + t * 4);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bk[(t * NCT + ct) * 64]),
+            acc[rt][ct], 0, 0, 0);
+    }
+  }
+  // D layout of a 16x16 MFMA tile: lane holds rows 4*(lane/16) + v, column lane % 16.
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        red[w][rt * 16 + (lane >> 4) * 4 + v][ct * 16 + (lane & 15)] = acc[rt][ct][v];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kRows * BC; idx += blockDim.x) {
+    const int row = idx / BC, b = idx % BC, ct = b >> 3, bb = b & 7;
+    float s = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) s += red[ww][row][ct * 16 + bb] + red[ww][row][ct * 16 + 8 + bb];
+    ys[row][b] = s;
+  }
+  __syncthreads();
+  if constexpr (MODE == 0) residual_epilogue<true, BC>(p, k, row0, ys);
+  else head_epilogue<true, NW, BC>(p, k, rb, ys);
+}
+
+// ---- fp32 weights: vector-ALU loop, one wave per weight row.
+template <int NW, int MODE>
+__global__ __launch_bounds__(NW * 64) void gemv_f32_kernel(const GemvParams p) {
+  constexpr int BC = MV_MAX_BATCH_HEADS;
+  __shared__ float ys[kRows][BC];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int k = blockIdx.y, rb = blockIdx.x, row0 = rb * kRows;
+  if (MODE == 0 && rb == 0 && threadIdx.x < MV_MAX_HEADS) p.cnt[threadIdx.x] = 0u;
+  const float* Wk = static_cast<const float*>(p.W) + static_cast<size_t>(k) * p.R * p.d;
+  const float* X = p.xsrc + k * p.x_hstride;
+  for (int r = w; r < kRows; r += NW) {
+    const int row = row0 + r;
+    if (row >= p.R) continue;  // wave-uniform
+    float acc[BC];
+#pragma unroll
+    for (int b = 0; b < BC; ++b) acc[b] = 0.f;
+    const float* wr = Wk + static_cast<size_t>(row) * p.d;
+    for (int c = lane * 4; c < p.d; c += 256) {
+      const float4 wv = *reinterpret_cast<const float4*>(wr + c);
+#pragma unroll
+      for (int b = 0; b < BC; ++b) {
+        if (b < p.B) {
+          const float4 xv = *reinterpret_cast<const float4*>(X + b * p.x_bstride + c);
+          acc[b] = fmaf(wv.x, xv.x, fmaf(wv.y, xv.y, fmaf(wv.z, xv.z, fmaf(wv.w, xv.w, acc[b]))));
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < BC; ++b) {
+      if (b < p.B) {
+        const float s = wave_sum(acc[b]);
+        if (lane == 0) ys[r][b] = s;
+      }
+    }
+  }
+  __syncthreads();
+  if constexpr (MODE == 0) residual_epilogue<false, BC>(p, k, row0, ys);
+  else head_epilogue<false, NW, BC>(p, k, rb, ys);
+}
+
+// ---- h -> packed B operand (remainder part is zero for bf16 inputs).
+__global__ __launch_bounds__(256) void pack_h_kernel(const uint16_t* h, int B, int d, int nct,
+                                                     uint16_t* out) {
+  const int T = d / 32;
+  const long long total = static_cast<long long>(T) * nct * 64;
+  for (long long q = blockIdx.x * 256LL + threadIdx.x; q < total; q += gridDim.x * 256LL) {
+    const int lane = static_cast<int>(q & 63);
+    const long long tc = q >> 6;
+    const int ct = static_cast<int>(tc % nct), t = static_cast<int>(tc / nct);
+    const int col = lane & 15, g = lane >> 4, b = ct * 8 + (col & 7);
+    const bool use = col < 8 && b < B;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = t * 32 + g * 8 + e;
+      out[q * 8 + e] = use ? h[static_cast<size_t>(b) * d + j] : static_cast<uint16_t>(0);
+    }
+  }
+}
+
+// ---- top-s of each row of a logit matrix (one workgroup per row).
+template <bool BF16>
+__global__ __launch_bounds__(256) void topk_rows_kernel(int V, int s, const void* x, long long ldx,
+                                                        int32_t* ids, float* vals, int ld_out) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const size_t rowoff = static_cast<size_t>(blockIdx.x) * ldx;
+  float pv = INFINITY;
+  int pi = -1;
+  for (int r = 0; r < s; ++r) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int j = threadIdx.x; j < V; j += 256) {
+      const float v = load_elem<BF16>(x, rowoff + j);
+      if (kv_after(v, j, pv, pi) && kv_better(v, j, bv, bi)) {
+        bv = v;
+        bi = j;
+      }
+    }
+    block_argbest(bv, bi, sv, si);
+    if (threadIdx.x == 0) {
+      const size_t o = static_cast<size_t>(blockIdx.x) * ld_out + r;
+      ids[o] = bi == INT_MAX ? -1 : bi;
+      if (vals) vals[o] = bv;
+    }
+    pv = bv;
+    pi = bi;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------------------
+int nct_for(int B) { return B <= 8 ? 1 : (B <= 16 ? 2 : 4); }
+
+struct HeadsLayout {
+  float* hk = nullptr;
+  uint16_t* bpack_h = nullptr;
+  uint16_t* bpack_hk = nullptr;
+  unsigned* cnt = nullptr;
+  float* pval = nullptr;
+  int* pidx = nullptr;
+  float* pm = nullptr;
+  float* pl = nullptr;
+  size_t residual_bytes = 0;  // prefix used by the residual call
+  size_t bytes = 0;
+};
+
+// Workspace layout.  The residual call's buffers come first so that it can check its part
+// without knowing V and s_max.
+HeadsLayout heads_layout(void* ws, int dt, int B, int d, int V, int K, int s_max) {
+  HeadsLayout L;
+  Carver c(ws);
+  const int nct = nct_for(B);
+  const size_t T = static_cast<size_t>(d) / 32;
+  L.hk = c.take<float>(static_cast<size_t>(B) * K * d);
+  if (dt == MV_BF16) {
+    L.bpack_h = c.take<uint16_t>(T * nct * 64 * 8);
+    L.bpack_hk = c.take<uint16_t>(static_cast<size_t>(K) * T * nct * 64 * 8);
+  }
+  L.cnt = c.take<unsigned>(MV_MAX_HEADS);
+  L.residual_bytes = c.bytes();
+  const size_t nrb = static_cast<size_t>(ceil_div(V, kRows));
+  const size_t np = static_cast<size_t>(K) * B * nrb;
+  L.pval = c.take<float>(np * s_max);
+  L.pidx = c.take<int>(np * s_max);
+  L.pm = c.take<float>(np);
+  L.pl = c.take<float>(np);
+  L.bytes = c.bytes();
+  return L;
+}
+
+int check_common(int dt, int B, int d, int K) {
+  if (dt != MV_F32 && dt != MV_BF16) return MV_ERR_INVALID_ARG;
+  if (B < 1 || d < 1 || K < 1) return MV_ERR_INVALID_ARG;
+  if (B > MV_MAX_BATCH_HEADS || K > MV_MAX_HEADS) return MV_ERR_UNSUPPORTED;
+  if (dt == MV_BF16 && d % 32 != 0) return MV_ERR_UNSUPPORTED;
+  if (dt == MV_F32 && d % 4 != 0) return MV_ERR_UNSUPPORTED;
+  return MV_OK;
+}
+
+// Waves per workgroup: enough waves in flight to cover HBM latency (about 8 per SIMD over the
+// chip's 1024 SIMDs), while each wave keeps at least 8 k-steps of streaming.
+int pick_nw(long long nblocks, int T, int cap) {
+  int nw = 1;
+  while (nw * 2 <= cap && nblocks * nw < 8192 && T / (nw * 2) >= 8) nw *= 2;
+  return nw;
+}
+
+template <int MODE>
+int launch_gemv(int dt, const GemvParams& p, int K, hipStream_t st) {
+  const dim3 grid(p.nrb, K);
+  if (dt == MV_F32) {
+    const int nw = pick_nw(static_cast<long long>(p.nrb) * K, 1 << 30, 4);
+    switch (nw) {
+      case 1: gemv_f32_kernel<1, MODE><<<grid, 64, 0, st>>>(p); break;
+      case 2: gemv_f32_kernel<2, MODE><<<grid, 128, 0, st>>>(p); break;
+      default: gemv_f32_kernel<4, MODE><<<grid, 256, 0, st>>>(p); break;
+    }
+    return launch_status();
+  }
+  const int nct = nct_for(p.B);
+  const int nw = pick_nw(static_cast<long long>(p.nrb) * K, p.T, 16 / nct > 8 ? 8 : 16 / nct);
+#define MV_GEMV_CASE(NW_, NCT_) \
+  if (nw == NW_ && nct == NCT_) { gemv_bf16_kernel<NW_, NCT_, MODE><<<grid, NW_ * 64, 0, st>>>(p); return launch_status(); }
+  MV_GEMV_CASE(1, 1) MV_GEMV_CASE(2, 1) MV_GEMV_CASE(4, 1) MV_GEMV_CASE(8, 1)
+  MV_GEMV_CASE(1, 2) MV_GEMV_CASE(2, 2) MV_GEMV_CASE(4, 2) MV_GEMV_CASE(8, 2)
+  MV_GEMV_CASE(1, 4) MV_GEMV_CASE(2, 4) MV_GEMV_CASE(4, 4)
+#undef MV_GEMV_CASE
+  return MV_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+}  // namespace mv
+
+using namespace mv;
+
+extern "C" {
+
+MV_API size_t mv_medusa_heads_workspace(int dt, int B, int d, int V, int K, int s_max) {
+  if (check_common(dt, B, d, K) != MV_OK || V < 1 || s_max < 1) return 0;
+  return heads_layout(nullptr, dt, B, d, V, K, s_max).bytes;
+}
+
+MV_API int mv_medusa_residual(int dt, int B, int d, int K, const void* h, const void* w_res,
+                              float* hk, void* ws, size_t ws_bytes, void* stream) {
+  MV_TRY(check_common(dt, B, d, K));
+  if (!h || !w_res) return MV_ERR_INVALID_ARG;
+  HeadsLayout need = heads_layout(nullptr, dt, B, d, 1, K, 1);
+  MV_TRY(check_ws(ws, ws_bytes, need.residual_bytes));
+  HeadsLayout L = heads_layout(ws, dt, B, d, 1, K, 1);
+  hipStream_t st = as_stream(stream);
+  GemvParams p{};
+  p.B = B; p.d = d; p.R = d; p.K = K; p.T = d / 32; p.nrb = ceil_div(d, kRows);
+  p.W = w_res; p.h = h; p.hk_ws = L.hk; p.hk_out = hk; p.cnt = L.cnt;
+  if (dt == MV_BF16) {
+    const int nct = nct_for(B);
+    const long long total = static_cast<long long>(d / 32) * nct * 64;
+    const int blocks = static_cast<int>((total + 255) / 256);
+    pack_h_kernel<<<blocks, 256, 0, st>>>(static_cast<const uint16_t*>(h), B, d, nct, L.bpack_h);
+    MV_TRY(launch_status());
+    p.bsrc = reinterpret_cast<const u32x4*>(L.bpack_h);
+    p.bsrc_hstride = 0;
+    p.bpack_out = L.bpack_hk;
+  } else {
+    p.xsrc = static_cast<const float*>(h);
+    p.x_bstride = d;
+    p.x_hstride = 0;
+  }
+  return launch_gemv<0>(dt, p, K, st);
+}
+
+MV_API int mv_medusa_head_topk(int dt, int B, int d, int V, int K, const int* s_per_head,
+                               int s_max, const void* w_head, void* logits, int32_t* topk_ids,
+                               float* topk_vals, int ld_topk, float* lse, void* ws,
+                               size_t ws_bytes, void* stream) {
+  MV_TRY(check_common(dt, B, d, K));
+  if (V < 1 || !s_per_head || !w_head || !topk_ids || !topk_vals) return MV_ERR_INVALID_ARG;
+  if (s_max < 1 || s_max > MV_MAX_TOPK || s_max > V) return MV_ERR_UNSUPPORTED;
+  for (int k = 0; k < K; ++k)
+    if (s_per_head[k] < 1 || s_per_head[k] > s_max) return MV_ERR_INVALID_ARG;
+  if (ld_topk == 0) ld_topk = K * s_max;
+  if (ld_topk < K * s_max) return MV_ERR_INVALID_ARG;
+  HeadsLayout need = heads_layout(nullptr, dt, B, d, V, K, s_max);
+  MV_TRY(check_ws(ws, ws_bytes, need.bytes));
+  HeadsLayout L = heads_layout(ws, dt, B, d, V, K, s_max);
+  GemvParams p{};
+  p.B = B; p.d = d; p.R = V; p.K = K; p.T = d / 32; p.nrb = ceil_div(V, kRows);
+  p.W = w_head; p.cnt = L.cnt; p.logits = logits;
+  p.pval = L.pval; p.pidx = L.pidx; p.pm = L.pm; p.pl = L.pl;
+  p.topk_ids = topk_ids; p.topk_vals = topk_vals; p.ld_topk = ld_topk; p.lse = lse;
+  p.s_max = s_max;
+  for (int k = 0; k < K; ++k) p.s[k] = s_per_head[k];
+  if (dt == MV_BF16) {
+    const int nct = nct_for(B);
+    p.bsrc = reinterpret_cast<const u32x4*>(L.bpack_hk);
+    p.bsrc_hstride = static_cast<long long>(d / 32) * nct * 64;
+  } else {
+    p.xsrc = L.hk;
+    p.x_bstride = static_cast<long long>(K) * d;
+    p.x_hstride = d;
+  }
+  return launch_gemv<1>(dt, p, K, as_stream(stream));
+}
+
+MV_API int mv_medusa_heads(int dt, int B, int d, int V, int K, const int* s_per_head, int s_max,
+                           const void* h, const void* w_res, const void* w_head, float* hk,
+                           void* logits, int32_t* topk_ids, float* topk_vals, int ld_topk,
+                           float* lse, void* ws, size_t ws_bytes, void* stream) {
+  MV_TRY(check_common(dt, B, d, K));
+  if (V < 1 || !s_per_head || !w_head || !topk_ids || !topk_vals) return MV_ERR_INVALID_ARG;
+  if (s_max < 1 || s_max > MV_MAX_TOPK || s_max > V) return MV_ERR_UNSUPPORTED;
+  for (int k = 0; k < K; ++k)
+    if (s_per_head[k] < 1 || s_per_head[k] > s_max) return MV_ERR_INVALID_ARG;
+  if (ld_topk != 0 && ld_topk < K * s_max) return MV_ERR_INVALID_ARG;
+  MV_TRY(check_ws(ws, ws_bytes, heads_layout(nullptr, dt, B, d, V, K, s_max).bytes));
+  MV_TRY(mv_medusa_residual(dt, B, d, K, h, w_res, hk, ws, ws_bytes, stream));
+  return mv_medusa_head_topk(dt, B, d, V, K, s_per_head, s_max, w_head, logits, topk_ids,
+                             topk_vals, ld_topk, lse, ws, ws_bytes, stream);
+}
+
+MV_API int mv_topk_rows(int dt, int R, int V, int s, const void* x, long long ldx, int32_t* ids,
+                        float* vals, int ld_out, void* stream) {
+  if (dt != MV_F32 && dt != MV_BF16) return MV_ERR_INVALID_ARG;
+  if (R < 1 || V < 1 || !x || !ids) return MV_ERR_INVALID_ARG;
+  if (s < 1 || s > MV_MAX_TOPK || s > V) return MV_ERR_UNSUPPORTED;
+  if (ldx < V || ld_out < s) return MV_ERR_INVALID_ARG;
+  hipStream_t st = as_stream(stream);
+  if (dt == MV_BF16) topk_rows_kernel<true><<<R, 256, 0, st>>>(V, s, x, ldx, ids, vals, ld_out);
+  else topk_rows_kernel<false><<<R, 256, 0, st>>>(V, s, x, ldx, ids, vals, ld_out);
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,271 @@
+"""PyTorch-facing wrappers of the C ABI (argument marshalling only).
+
+Tensors must live on the current HIP device; every call enqueues work on torch's current
+stream and returns.  Each function mirrors the C entry point of the same name; see
+include/medusa_verify.h for the semantics and the page sections they follow.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import torch
+
+from . import _lib as L
+
+_DT = {torch.float32: L.MV_F32, torch.bfloat16: L.MV_BF16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    return _DT[t.dtype]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+class Workspace:
+    """Grow-only device scratch buffer handed to the library (256-byte aligned by torch)."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf: Optional[torch.Tensor] = None
+
+    def get(self, nbytes: int):
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device or "cuda")
+        return self.buf.data_ptr(), self.buf.numel()
+
+
+_default_ws: Dict[str, Workspace] = {}
+
+
+def _ws(key: str, ws: Optional[Workspace]) -> Workspace:
+    if ws is not None:
+        return ws
+    if key not in _default_ws:
+        _default_ws[key] = Workspace()
+    return _default_ws[key]
+
+
+def device_check(device: int = 0) -> int:
+    return L.lib().mv_device_check(int(device))
+
+
+def validate_parents(parents: Sequence[int]) -> None:
+    """Host check of a tree spec: topological parent array with -1 roots."""
+    n = len(parents)
+    if n < 1 or n > L.MV_MAX_NODES:
+        raise ValueError(f"tree must have 1..{L.MV_MAX_NODES} nodes, got {n}")
+    for i, p in enumerate(parents):
+        if not (-1 <= int(p) < i):
+            raise ValueError(f"node {i}: parent {p} is not in [-1, {i})")
+
+
+# ------------------------------------------------------------------ Medusa heads
+def heads_workspace_bytes(dt: int, B: int, d: int, V: int, K: int, s_max: int) -> int:
+    return int(L.lib().mv_medusa_heads_workspace(dt, B, d, V, K, s_max))
+
+
+def medusa_residual(h: torch.Tensor, w_res: torch.Tensor, hk: Optional[torch.Tensor] = None,
+                    V: int = 1, s_max: int = 1, ws: Optional[Workspace] = None) -> Workspace:
+    """a1: h_k = SiLU(W_res^(k) h) + h.  Returns the workspace holding h_k for the projection."""
+    dt = _dt(h)
+    B, d = h.shape
+    K = w_res.shape[0]
+    _need(h, "h")
+    _need(w_res, "w_res", h.dtype, (K, d, d))
+    if hk is not None:
+        _need(hk, "hk", torch.float32, (B, K, d))
+    w = _ws("heads", ws)
+    ptr, n = w.get(heads_workspace_bytes(dt, B, d, V, K, s_max))
+    L.check("mv_medusa_residual", L.lib().mv_medusa_residual(
+        dt, B, d, K, _ptr(h), _ptr(w_res), _ptr(hk), ptr, n, _stream()))
+    return w
+
+
+def medusa_head_topk(w_head: torch.Tensor, B: int, s_per_head: Sequence[int],
+                     s_max: Optional[int] = None, logits: Optional[torch.Tensor] = None,
+                     topk_ids: Optional[torch.Tensor] = None,
+                     topk_vals: Optional[torch.Tensor] = None, ld_topk: int = 0,
+                     lse: Optional[torch.Tensor] = None,
+                     ws: Optional[Workspace] = None) -> Dict[str, torch.Tensor]:
+    """a2: logits_k = W_head^(k) h_k (h_k from medusa_residual's workspace), top-s_k, lse."""
+    dt = _dt(w_head)
+    K, V, d = w_head.shape
+    s_max = int(s_max or max(s_per_head))
+    _need(w_head, "w_head")
+    dev = w_head.device
+    if topk_ids is None:
+        topk_ids = torch.empty((B, K, s_max), dtype=torch.int32, device=dev)
+    if topk_vals is None:
+        topk_vals = torch.empty(topk_ids.shape, dtype=torch.float32, device=dev)
+    if logits is not None:
+        _need(logits, "logits", w_head.dtype, (B, K, V))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, K))
+    w = _ws("heads", ws)
+    ptr, n = w.get(heads_workspace_bytes(dt, B, d, V, K, s_max))
+    L.check("mv_medusa_head_topk", L.lib().mv_medusa_head_topk(
+        dt, B, d, V, K, L.int_array(s_per_head), s_max, _ptr(w_head), _ptr(logits),
+        _ptr(topk_ids), _ptr(topk_vals), int(ld_topk), _ptr(lse), ptr, n, _stream()))
+    return {"topk_ids": topk_ids, "topk_vals": topk_vals, "logits": logits, "lse": lse}
+
+
+def medusa_heads(h: torch.Tensor, w_res: torch.Tensor, w_head: torch.Tensor,
+                 s_per_head: Sequence[int], s_max: Optional[int] = None, want_hk: bool = False,
+                 want_logits: bool = False, want_lse: bool = True,
+                 ws: Optional[Workspace] = None) -> Dict[str, torch.Tensor]:
+    """a1 + a2 in one call."""
+    dt = _dt(h)
+    B, d = h.shape
+    K, V, _ = w_head.shape
+    s_max = int(s_max or max(s_per_head))
+    for t, nm in ((h, "h"), (w_res, "w_res"), (w_head, "w_head")):
+        _need(t, nm, h.dtype)
+    dev = h.device
+    hk = torch.empty((B, K, d), dtype=torch.float32, device=dev) if want_hk else None
+    logits = torch.empty((B, K, V), dtype=h.dtype, device=dev) if want_logits else None
+    lse = torch.empty((B, K), dtype=torch.float32, device=dev) if want_lse else None
+    ids = torch.empty((B, K, s_max), dtype=torch.int32, device=dev)
+    vals = torch.empty((B, K, s_max), dtype=torch.float32, device=dev)
+    w = _ws("heads", ws)
+    ptr, n = w.get(heads_workspace_bytes(dt, B, d, V, K, s_max))
+    L.check("mv_medusa_heads", L.lib().mv_medusa_heads(
+        dt, B, d, V, K, L.int_array(s_per_head), s_max, _ptr(h), _ptr(w_res), _ptr(w_head),
+        _ptr(hk), _ptr(logits), _ptr(ids), _ptr(vals), 0, _ptr(lse), ptr, n, _stream()))
+    return {"hk": hk, "logits": logits, "topk_ids": ids, "topk_vals": vals, "lse": lse}
+
+
+def topk_rows(x: torch.Tensor, s: int, R: Optional[int] = None, V: Optional[int] = None,
+              ldx: Optional[int] = None, ids: Optional[torch.Tensor] = None,
+              vals: Optional[torch.Tensor] = None, ld_out: Optional[int] = None):
+    """Top-s of R rows of x (row r at r*ldx elements).  Defaults: x is [R, V] contiguous."""
+    dt = _dt(x)
+    if R is None or V is None:
+        R, V = x.shape[-2], x.shape[-1]
+    ldx = V if ldx is None else ldx
+    if ids is None:
+        ids = torch.empty((R, s), dtype=torch.int32, device=x.device)
+        vals = torch.empty((R, s), dtype=torch.float32, device=x.device) if vals is None else vals
+        ld_out = s
+    L.check("mv_topk_rows", L.lib().mv_topk_rows(dt, R, V, s, _ptr(x), int(ldx), _ptr(ids),
+                                                 _ptr(vals), int(ld_out or s), _stream()))
+    return ids, vals
+
+
+# ------------------------------------------------------------------ tree
+def build_tree_mask(parents: torch.Tensor, cand: Optional[torch.Tensor] = None,
+                    s_per_depth: Optional[Sequence[int]] = None,
+                    status: Optional[torch.Tensor] = None,
+                    out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """a3: parents [N] int32 -> anc_mask [N, ceil(N/32)] uint32 (as int32), depth, node_tokens."""
+    _need(parents, "parents", torch.int32)
+    N = parents.numel()
+    W = (N + 31) // 32
+    dev = parents.device
+    B = D = s_max = 0
+    if cand is not None:
+        _need(cand, "cand", torch.int32)
+        B, D, s_max = cand.shape
+    if out is None:
+        out = {"anc_mask": torch.empty((N, W), dtype=torch.int32, device=dev),
+               "depth": torch.empty(N, dtype=torch.int32, device=dev),
+               "node_tokens": torch.empty((B, N), dtype=torch.int32, device=dev)
+               if cand is not None else None}
+    sp = L.int_array(s_per_depth) if s_per_depth is not None else None
+    L.check("mv_build_tree_mask", L.lib().mv_build_tree_mask(
+        N, _ptr(parents), B, D, s_max, sp, _ptr(cand), _ptr(out["anc_mask"]), _ptr(out["depth"]),
+        _ptr(out.get("node_tokens")), _ptr(status), _stream()))
+    return out
+
+
+# ------------------------------------------------------------------ attention
+def attn_workspace_bytes(dt: int, B: int, N: int, Hq: int, Hkv: int, dh: int, max_L: int) -> int:
+    return int(L.lib().mv_tree_attn_verify_workspace(dt, B, N, Hq, Hkv, dh, max_L))
+
+
+def tree_attn_verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     prefix_len: torch.Tensor, anc_mask: torch.Tensor, max_L: int,
+                     scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                     status: Optional[torch.Tensor] = None,
+                     ws: Optional[Workspace] = None):
+    """a4 + a5: tree-masked GQA attention; returns (out [B,N,Hq,dh], lse [B,Hq,N] or None)."""
+    dt = _dt(q)
+    B, N, Hq, dh = q.shape
+    _, Hkv, L_cap, _ = k_cache.shape
+    _need(q, "q")
+    _need(k_cache, "k_cache", q.dtype, (B, Hkv, L_cap, dh))
+    _need(v_cache, "v_cache", q.dtype, (B, Hkv, L_cap, dh))
+    _need(prefix_len, "prefix_len", torch.int32, (B,))
+    _need(anc_mask, "anc_mask", None, (N, (N + 31) // 32))
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    w = _ws("attn", ws)
+    ptr, n = w.get(attn_workspace_bytes(dt, B, N, Hq, Hkv, dh, max_L))
+    L.check("mv_tree_attn_verify", L.lib().mv_tree_attn_verify(
+        dt, B, N, Hq, Hkv, dh, L_cap, int(max_L), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(prefix_len), _ptr(anc_mask), float(scale), _ptr(out), _ptr(lse), _ptr(status),
+        ptr, n, _stream()))
+    return out, lse
+
+
+# ------------------------------------------------------------------ acceptance
+def accept_workspace_bytes(mode: int, B: int, N: int, V: int) -> int:
+    return int(L.lib().mv_accept_paths_workspace(mode, B, N, V))
+
+
+def accept_paths(mode: int, parents: torch.Tensor, node_tokens: torch.Tensor,
+                 target: torch.Tensor, D: int, draft: Optional[torch.Tensor] = None,
+                 uniforms: Optional[torch.Tensor] = None, want_node_accept: bool = True,
+                 want_alpha: bool = True, status: Optional[torch.Tensor] = None,
+                 out: Optional[Dict[str, torch.Tensor]] = None,
+                 ws: Optional[Workspace] = None) -> Dict[str, torch.Tensor]:
+    """a6 (greedy) / a7 (speculative): accepted length, path, committed tokens + extra token."""
+    dt = _dt(target)
+    B, R, V = target.shape
+    N = R - 1
+    _need(parents, "parents", torch.int32, (N,))
+    _need(node_tokens, "node_tokens", torch.int32, (B, N))
+    _need(target, "target")
+    spec = mode == L.MV_ACCEPT_SPECULATIVE
+    if spec:
+        _need(draft, "draft", torch.float32, (B, R, V))
+        _need(uniforms, "uniforms", torch.float32, (B, R))
+    dev = target.device
+    if out is None:
+        out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+               "path_nodes": torch.empty((B, D), dtype=torch.int32, device=dev),
+               "out_tokens": torch.empty((B, D + 1), dtype=torch.int32, device=dev),
+               "node_accept": torch.empty((B, N), dtype=torch.uint8, device=dev)
+               if want_node_accept else None,
+               "alpha": torch.empty((B, N), dtype=torch.float32, device=dev)
+               if (want_alpha and spec) else None}
+    w = _ws("accept", ws)
+    ptr, n = w.get(accept_workspace_bytes(mode, B, N, V))
+    L.check("mv_accept_paths", L.lib().mv_accept_paths(
+        mode, dt, B, N, V, D, _ptr(parents), _ptr(node_tokens), _ptr(target), _ptr(draft),
+        _ptr(uniforms), _ptr(out["accept_len"]), _ptr(out["path_nodes"]), _ptr(out["out_tokens"]),
+        _ptr(out.get("node_accept")), _ptr(out.get("alpha")), _ptr(status), ptr, n, _stream()))
+    return out

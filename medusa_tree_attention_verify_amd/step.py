@@ -1,0 +1,162 @@
+"""One Medusa tree-verification step on the GPU: heads -> tree -> attention -> acceptance.
+
+All buffers (outputs and workspaces) are allocated once in ``VerifyStep.__init__``.
+``bind(inp)`` turns one set of device inputs into five pre-marshalled C-ABI calls (heads
+residual, heads projection, tree, attention, acceptance), so a step costs five ctypes calls
+and no Python-side checks or allocation.  The candidate tokens of depth k come from Medusa
+head k; with ``lm_width > 0`` the depth-1 candidates are instead the top ``lm_width`` tokens
+of the target's first row (the base model's own head, which predicts the next token) and
+the Medusa heads supply depths 2..D.
+"""
+from __future__ import annotations
+
+from typing import Callable, Dict, List, Optional, Sequence
+
+import torch
+
+from . import _lib as L
+from . import ops
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+class VerifyStep:
+    PARTS = ("heads_residual", "heads_projection", "tree", "attention", "accept")
+
+    def __init__(self, *, parents: Sequence[int], depth_widths: Sequence[int],
+                 dtype: torch.dtype, B: int, Hq: int, Hkv: int, dh: int, max_L: int,
+                 heads: Optional[Dict[str, object]] = None, lm_width: int = 0,
+                 accept: str = "greedy", V: int = 0, tokens_given: bool = False,
+                 device="cuda"):
+        ops.validate_parents(parents)
+        self.parents_list = [int(p) for p in parents]
+        self.N = len(parents)
+        self.D = len(depth_widths)
+        self.depth_widths = [int(s) for s in depth_widths]
+        self.s_max = max(self.depth_widths)
+        self.B, self.Hq, self.Hkv, self.dh, self.max_L = B, Hq, Hkv, dh, max_L
+        self.dtype = dtype
+        self.dt = L.MV_BF16 if dtype == torch.bfloat16 else L.MV_F32
+        self.accept = accept
+        self.mode = L.MV_ACCEPT_SPECULATIVE if accept == "speculative" else L.MV_ACCEPT_GREEDY
+        self.V = V
+        self.lm_width = lm_width
+        self.heads = heads  # {"d":, "V":, "K":, "widths":}
+        self.tokens_given = tokens_given  # node tokens come with the inputs (no heads)
+        dev = torch.device(device)
+        self.device = dev
+        self.parents = torch.tensor(self.parents_list, dtype=torch.int32, device=dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        N, W = self.N, (self.N + 31) // 32
+        self.cand = torch.full((B, self.D, self.s_max), -1, dtype=torch.int32, device=dev)
+        self.cand_vals = torch.empty((B, self.D, self.s_max), dtype=torch.float32, device=dev)
+        self.tree = {"anc_mask": torch.empty((N, W), dtype=torch.int32, device=dev),
+                     "depth": torch.empty(N, dtype=torch.int32, device=dev),
+                     "node_tokens": torch.empty((B, N), dtype=torch.int32, device=dev)}
+        self.attn_out = torch.empty((B, N, Hq, dh), dtype=dtype, device=dev)
+        self.attn_lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+        self.ws_heads = ops.Workspace(dev)
+        self.ws_attn = ops.Workspace(dev)
+        self.ws_accept = ops.Workspace(dev)
+        if heads is not None:
+            d, Vh, K = heads["d"], heads["V"], heads["K"]
+            self.head_lse = torch.empty((B, K), dtype=torch.float32, device=dev)
+            self.ws_heads.get(ops.heads_workspace_bytes(self.dt, B, d, Vh, K, self.s_max))
+            self._s_heads = L.int_array(heads["widths"])
+        self.ws_attn.get(ops.attn_workspace_bytes(self.dt, B, N, Hq, Hkv, dh, max_L))
+        self._s_depth = L.int_array(self.depth_widths)
+        if accept != "none":
+            self.ws_accept.get(ops.accept_workspace_bytes(self.mode, B, N, V))
+            self.acc = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+                        "path_nodes": torch.empty((B, self.D), dtype=torch.int32, device=dev),
+                        "out_tokens": torch.empty((B, self.D + 1), dtype=torch.int32, device=dev),
+                        "node_accept": torch.empty((B, N), dtype=torch.uint8, device=dev),
+                        "alpha": torch.empty((B, N), dtype=torch.float32, device=dev)
+                        if self.mode == L.MV_ACCEPT_SPECULATIVE else None}
+
+    @staticmethod
+    def _ws(w: ops.Workspace):
+        return (None, 0) if w.buf is None else (w.buf.data_ptr(), w.buf.numel())
+
+    def bind(self, inp: Dict[str, torch.Tensor]) -> Dict[str, Callable[[], None]]:
+        """Pre-marshalled calls of one step on ``inp`` (device tensors: h, w_res, w_head when
+        the step has heads; q, k_cache, v_cache, prefix_len; target (+ draft, uniforms);
+        node_tokens when the tokens are given).  Each callable raises on a non-zero status."""
+        lib = L.lib()
+        st = torch.cuda.current_stream(self.device).cuda_stream
+        calls: Dict[str, Callable[[], None]] = {}
+        B, N, D, s_max = self.B, self.N, self.D, self.s_max
+
+        def wrap(name, fn, *args):
+            def call():
+                r = fn(*args)
+                if r != 0:
+                    raise L.MVError(name, r)
+            return call
+
+        if self.heads is not None:
+            hd = self.heads
+            d, Vh, K = hd["d"], hd["V"], hd["K"]
+            wsp, wsn = self._ws(self.ws_heads)
+            calls["heads_residual"] = wrap("mv_medusa_residual", lib.mv_medusa_residual, self.dt, B,
+                                           d, K, _p(inp["h"]), _p(inp["w_res"]), None, wsp, wsn, st)
+            off = 1 if self.lm_width else 0
+            ld = D * s_max
+            esz = 4
+            proj = wrap("mv_medusa_head_topk", lib.mv_medusa_head_topk, self.dt, B, d, Vh, K,
+                        self._s_heads, s_max, _p(inp["w_head"]), None,
+                        self.cand.data_ptr() + off * s_max * esz,
+                        self.cand_vals.data_ptr() + off * s_max * esz, ld, _p(self.head_lse),
+                        wsp, wsn, st)
+            if self.lm_width:
+                tgt = inp["target"]
+                R1, Vt = tgt.shape[1], tgt.shape[2]
+                lm = wrap("mv_topk_rows", lib.mv_topk_rows, self.dt, B, Vt, self.lm_width, _p(tgt),
+                          R1 * Vt, self.cand.data_ptr(), self.cand_vals.data_ptr(), ld, st)
+
+                def both():
+                    lm()
+                    proj()
+                calls["heads_projection"] = both
+            else:
+                calls["heads_projection"] = proj
+        if self.tokens_given:
+            calls["tree"] = wrap("mv_build_tree_mask", lib.mv_build_tree_mask, N, _p(self.parents),
+                                 0, 0, 0, None, None, _p(self.tree["anc_mask"]),
+                                 _p(self.tree["depth"]), None, _p(self.status), st)
+            tokens = inp["node_tokens"]
+        else:
+            calls["tree"] = wrap("mv_build_tree_mask", lib.mv_build_tree_mask, N, _p(self.parents),
+                                 B, D, s_max, self._s_depth, _p(self.cand),
+                                 _p(self.tree["anc_mask"]), _p(self.tree["depth"]),
+                                 _p(self.tree["node_tokens"]), _p(self.status), st)
+            tokens = self.tree["node_tokens"]
+        wsp, wsn = self._ws(self.ws_attn)
+        Lcap = inp["k_cache"].shape[2]
+        calls["attention"] = wrap("mv_tree_attn_verify", lib.mv_tree_attn_verify, self.dt, B, N,
+                                  self.Hq, self.Hkv, self.dh, Lcap, self.max_L, _p(inp["q"]),
+                                  _p(inp["k_cache"]), _p(inp["v_cache"]), _p(inp["prefix_len"]),
+                                  _p(self.tree["anc_mask"]), 0.0, _p(self.attn_out),
+                                  _p(self.attn_lse), _p(self.status), wsp, wsn, st)
+        if self.accept != "none":
+            wsp, wsn = self._ws(self.ws_accept)
+            tgt = inp["target"]
+            tdt = L.MV_BF16 if tgt.dtype == torch.bfloat16 else L.MV_F32
+            a = self.acc
+            calls["accept"] = wrap("mv_accept_paths", lib.mv_accept_paths, self.mode, tdt, B, N,
+                                   tgt.shape[2], D, _p(self.parents), _p(tokens), _p(tgt),
+                                   _p(inp.get("draft")), _p(inp.get("uniforms")),
+                                   _p(a["accept_len"]), _p(a["path_nodes"]), _p(a["out_tokens"]),
+                                   _p(a["node_accept"]), _p(a["alpha"]), _p(self.status), wsp,
+                                   wsn, st)
+        return calls
+
+    def sequence(self, calls: Dict[str, Callable[[], None]]) -> List[Callable[[], None]]:
+        return [calls[p] for p in self.PARTS if p in calls]
+
+    def run(self, inp: Dict[str, torch.Tensor]) -> None:
+        """One whole step on ``inp`` (binds, then runs the five calls in order)."""
+        for c in self.sequence(self.bind(inp)):
+            c()

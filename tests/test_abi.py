@@ -1,0 +1,102 @@
+"""The C-ABI library loads, exports every symbol its header declares, and rejects bad
+arguments on the host before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from medusa_tree_attention_verify_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "medusa_verify.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"^MV_API\s+[\w\s\*]+?\b(mv_\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert len(names) == 13, names
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    assert sorted(n for n, _, _ in L.SIGNATURES) == sorted(names)
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name in ("MV_MAX_NODES", "MV_MAX_DEPTH", "MV_MAX_TOPK", "MV_MAX_BATCH_HEADS",
+                 "MV_MAX_HEADS", "MV_DEV_BAD_PARENT", "MV_DEV_BAD_RANK", "MV_DEV_TOO_DEEP",
+                 "MV_DEV_BAD_PREFIX", "MV_DEV_BAD_TOKEN"):
+        m = re.search(rf"#define {name}\s+(0x[0-9a-fA-F]+|\d+)", text)
+        assert m and int(m.group(1), 0) == getattr(L, name), name
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert L.status_string(s) not in ("", "unknown status")
+    assert L.status_string(-99) == "unknown status"
+
+
+def test_workspace_queries():
+    lib = L.lib()
+    assert lib.mv_medusa_heads_workspace(L.MV_BF16, 1, 4096, 32000, 4, 4) > 0
+    assert lib.mv_medusa_heads_workspace(L.MV_BF16, 1, 4095, 32000, 4, 4) == 0   # d % 32
+    assert lib.mv_tree_attn_verify_workspace(L.MV_BF16, 1, 64, 32, 8, 128, 4096) > 0
+    assert lib.mv_tree_attn_verify_workspace(L.MV_BF16, 1, 64, 32, 8, 96, 4096) == 0  # dh
+    assert lib.mv_tree_attn_verify_workspace(L.MV_F32, 1, 8, 4, 4, 64, 128) == 0    # no split
+    assert lib.mv_accept_paths_workspace(L.MV_ACCEPT_GREEDY, 1, 64, 32000) > 0
+    assert lib.mv_accept_paths_workspace(L.MV_ACCEPT_SPECULATIVE, 64, 64, 128256) > 0
+
+
+def test_host_argument_checks():
+    lib = L.lib()
+    P = ctypes.c_void_p(16)   # never dereferenced: every call below fails its host checks
+    ws = lambda: (None, 0)
+    # heads
+    assert lib.mv_medusa_residual(7, 1, 64, 1, P, P, None, None, 0, None) == L.MV_ERR_INVALID_ARG
+    assert lib.mv_medusa_residual(L.MV_BF16, 1, 48, 1, P, P, None, None, 0, None) == L.MV_ERR_UNSUPPORTED
+    assert lib.mv_medusa_residual(L.MV_BF16, 33, 64, 1, P, P, None, None, 0, None) == L.MV_ERR_UNSUPPORTED
+    assert lib.mv_medusa_residual(L.MV_BF16, 1, 64, 1, P, P, None, None, 0, None) == L.MV_ERR_WORKSPACE
+    assert lib.mv_medusa_residual(L.MV_BF16, 1, 64, 1, None, P, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
+    s = L.int_array([4, 3])
+    assert lib.mv_medusa_head_topk(L.MV_BF16, 1, 64, 100, 2, s, 17, P, None, P, P, 0, None, P,
+                                   1 << 20, None) == L.MV_ERR_UNSUPPORTED
+    s_bad = L.int_array([5, 3])
+    assert lib.mv_medusa_head_topk(L.MV_BF16, 1, 64, 100, 2, s_bad, 4, P, None, P, P, 0, None, P,
+                                   1 << 20, None) == L.MV_ERR_INVALID_ARG
+    assert lib.mv_medusa_head_topk(L.MV_BF16, 1, 64, 100, 2, s, 4, P, None, P, P, 3, None, P,
+                                   1 << 20, None) == L.MV_ERR_INVALID_ARG          # ld_topk
+    # top-k rows
+    assert lib.mv_topk_rows(L.MV_F32, 1, 10, 11, P, 10, P, None, 11, None) == L.MV_ERR_UNSUPPORTED
+    assert lib.mv_topk_rows(L.MV_F32, 1, 10, 2, P, 9, P, None, 2, None) == L.MV_ERR_INVALID_ARG
+    # tree
+    assert lib.mv_build_tree_mask(0, P, 0, 0, 0, None, None, P, None, None, None, None) == L.MV_ERR_INVALID_ARG
+    assert lib.mv_build_tree_mask(257, P, 0, 0, 0, None, None, P, None, None, None, None) == L.MV_ERR_UNSUPPORTED
+    assert lib.mv_build_tree_mask(8, P, 1, 17, 2, None, P, P, None, P, None, None) == L.MV_ERR_UNSUPPORTED
+    # attention
+    args = (P, P, P, P, P, 0.0, P, None, None)
+    assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 6, 4, 128, 200, 100, *args, None, 0, None) == L.MV_ERR_INVALID_ARG
+    assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 8, 4, 96, 200, 100, *args, None, 0, None) == L.MV_ERR_UNSUPPORTED
+    assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 8, 4, 128, 100, 100, *args, None, 0, None) == L.MV_ERR_INVALID_ARG
+    assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 8, 4, 128, 10000, 8000, *args, None, 0, None) == L.MV_ERR_WORKSPACE
+    # acceptance
+    assert lib.mv_accept_paths(L.MV_ACCEPT_SPECULATIVE, L.MV_BF16, 1, 4, 10, 2, P, P, P, P, P, P, P,
+                               P, None, None, None, P, 1 << 20, None) == L.MV_ERR_UNSUPPORTED
+    assert lib.mv_accept_paths(L.MV_ACCEPT_SPECULATIVE, L.MV_F32, 1, 4, 10, 2, P, P, P, None, P, P,
+                               P, P, None, None, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
+    assert lib.mv_accept_paths(L.MV_ACCEPT_GREEDY, L.MV_F32, 1, 4, 10, 17, P, P, P, None, None, P,
+                               P, P, None, None, None, P, 1 << 20, None) == L.MV_ERR_UNSUPPORTED
+    assert lib.mv_accept_paths(L.MV_ACCEPT_GREEDY, L.MV_F32, 1, 4, 10, 2, P, P, P, None, None, P,
+                               P, P, None, None, None, None, 0, None) == L.MV_ERR_WORKSPACE
+
+
+def test_host_tree_validation():
+    from medusa_tree_attention_verify_amd.ops import validate_parents
+    validate_parents([-1, 0, 1, 1, 0, -1, 5])
+    for bad in ([0], [-1, 1], [-1, -2], [], list(range(-1, 256))):
+        with pytest.raises(ValueError):
+            validate_parents(bad)

@@ -1,0 +1,116 @@
+"""GPU parity of tree-masked GQA attention (mv_tree_attn_verify) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import medusa_oracle as O
+from medusa_tree_attention_verify_amd import _lib as L
+from medusa_tree_attention_verify_amd import ops
+from medusa_tree_attention_verify_amd import workloads as W
+from medusa_tree_attention_verify_amd.workloads import branching_tree, chain_tree
+from tests.gpu_util import assert_bf16, assert_fp32, dev, dev_i32, host, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(wl, seed, lens=None, select=None):
+    print(f"attn {wl.name} B={wl.B} N={wl.N} Hq={wl.Hq} Hkv={wl.Hkv} dh={wl.dh} "
+          f"prefix={wl.prefix} lens={lens} seed={seed}", flush=True)
+    x = W.gen_attention(wl, seed, None if lens is None else np.asarray(lens, np.int32))
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    tree = O.build_tree(list(wl.parents))
+    parents = dev_i32(wl.parents)
+    anc = ops.build_tree_mask(parents)["anc_mask"]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    max_L = int(x["prefix_len"].max())
+    out, lse = ops.tree_attn_verify(dev(x["q"], dt), dev(x["k_cache"], dt), dev(x["v_cache"], dt),
+                                    dev_i32(x["prefix_len"]), anc, max_L, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ref = O.tree_attention(x["q"], x["k_cache"], x["v_cache"], x["prefix_len"], tree["anc"],
+                           select=select)
+    got_o, got_l = host(out), host(lse)
+    if select is not None:
+        idx = tuple(np.array(select).T)          # (b, h, i)
+        b, h, i = idx
+        go, ro = got_o[b, i, h], ref["out"][b, i, h]
+        gl, rl = got_l[b, h, i], ref["lse"][b, h, i]
+    else:
+        go, ro, gl, rl = got_o, ref["out"], got_l, ref["lse"]
+    if wl.dtype == "f32":
+        assert_fp32(go, ro, what="out")
+        assert_fp32(gl, rl, what="lse")
+    else:
+        assert_bf16(go, ro, what="out")
+        assert_fp32(gl, rl, atol=1e-3, what="lse")
+
+
+def test_attention_tiny_fp32():
+    require_gpu()
+    _run(W.WORKLOADS["c1"], 1)
+
+
+def _bf16(parents, B, Hq, Hkv, dh, L):
+    return W.Workload(name="bf16-case", dtype="bf16", B=B, Hq=Hq, Hkv=Hkv, dh=dh,
+                      parents=tuple(parents), prefix=(L, L), depth_widths=(1,))
+
+
+@pytest.mark.parametrize("parents,B,Hq,Hkv,dh,lens", [
+    ([-1], 2, 8, 2, 128, [37, 300]),                        # one node: plain decode
+    (chain_tree(9), 1, 4, 1, 64, [20]),                     # chain: causal
+    (branching_tree((4, 3, 2, 1)), 1, 32, 8, 128, [0]),     # empty prefix
+    (branching_tree((4, 3, 2, 1)), 2, 32, 8, 128, [5, 130]),
+    (branching_tree((4, 3, 2, 1)), 3, 16, 8, 64, [1, 511, 1000]),
+    (branching_tree((2, 2)), 2, 8, 8, 128, [33, 64]),       # G = 1
+    (branching_tree((4, 4, 4, 2)), 1, 16, 2, 128, [77]),    # 212 nodes, 7 mask words
+    ([-1, 0, 1, 1, 0, -1, 5], 1, 8, 1, 64, [3]),            # forest (two roots)
+])
+def test_attention_bf16_shapes(parents, B, Hq, Hkv, dh, lens):
+    require_gpu()
+    wl = _bf16(parents, B, Hq, Hkv, dh, max(lens))
+    _run(wl, 21, lens)
+
+
+def test_attention_multichunk_ragged():
+    """Prefixes long enough to be split into several chunks, ragged across the batch."""
+    require_gpu()
+    wl = _bf16(branching_tree((4, 3, 2, 1)), 4, 32, 8, 128, 6000)
+    _run(wl, 22, [6000, 257, 4096, 1])
+
+
+def test_attention_llama8b_full():
+    """B=1, 32/8 heads, dh 128, prefix 4096, (4,3,2,1) tree: every output row."""
+    require_gpu()
+    _run(W.WORKLOADS["c2"], 2)
+
+
+def test_attention_long_context_sampled():
+    """Prefix 131072, 64/8 heads, 212-node tree: sampled rows incl. the deepest nodes."""
+    require_gpu()
+    wl = W.WORKLOADS["c4"]
+    rng = np.random.default_rng(4)
+    sel = [(0, int(rng.integers(64)), int(i)) for i in rng.integers(0, wl.N, size=24)]
+    sel += [(0, 63, wl.N - 1), (0, 0, 0), (0, 7, 84), (0, 8, 211)]
+    _run(wl, 4, select=sel)
+
+
+def test_attention_70b_share_sampled():
+    """Batch 8, 64/8 heads, prefixes drawn in [8192, 32768]: sampled rows of every sequence."""
+    require_gpu()
+    wl = W.WORKLOADS["c3"]
+    rng = np.random.default_rng(3)
+    sel = [(b, int(rng.integers(64)), int(rng.integers(64))) for b in range(8) for _ in range(3)]
+    _run(wl, 3, select=sel)
+
+
+def test_attention_bad_prefix_flags():
+    require_gpu()
+    wl = _bf16([-1, 0], 2, 4, 2, 64, 10)
+    x = W.gen_attention(wl, 5, np.array([10, 10], np.int32))
+    anc = ops.build_tree_mask(dev_i32(wl.parents))["anc_mask"]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pl = dev_i32([10, 50])                 # 50 > max_L and 50 + N > L_cap
+    ops.tree_attn_verify(dev(x["q"], torch.bfloat16), dev(x["k_cache"], torch.bfloat16),
+                         dev(x["v_cache"], torch.bfloat16), pl, anc, 10, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & L.MV_DEV_BAD_PREFIX

@@ -1,0 +1,78 @@
+"""One whole verify step on the GPU (heads -> tree -> attention -> acceptance) vs the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import medusa_oracle as O
+from medusa_tree_attention_verify_amd import workloads as W
+from medusa_tree_attention_verify_amd.step import VerifyStep
+from tests.gpu_util import assert_bf16, assert_fp32, check_topk, dev, dev_i32, host, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_step(wl, x, target):
+    """Oracle of one step; returns candidates, tree, attention, acceptance."""
+    parents = list(wl.parents)
+    heads = O.medusa_heads(x["h"], x["w_res"], x["w_head"], list(wl.head_widths))
+    cand = []
+    if wl.lm_width:
+        cand.append(np.stack([O.topk_rows(target[b, 0], wl.lm_width)["ids"] for b in range(wl.B)]))
+    for k in range(wl.K):
+        cand.append(heads["topk_ids"][:, k, :wl.head_widths[k]])
+    tree = O.build_tree(parents, cand, list(wl.depth_widths))
+    return heads, cand, tree
+
+
+def _check_step(wl, seed):
+    parents = list(wl.parents)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    xh = W.gen_heads(wl, seed)
+    xa = W.gen_attention(wl, seed)
+    target = W.gen_target_logits(wl, seed)
+    heads, cand, tree = _oracle_step(wl, xh, target)
+    if wl.plant_p > 0:
+        target = W.plant_greedy(target, parents, tree["tokens"], seed, wl.plant_p)
+    if wl.dtype == "bf16":
+        target = W.round_bf16(target)
+    step = VerifyStep(parents=parents, depth_widths=wl.depth_widths, dtype=dt, B=wl.B, Hq=wl.Hq,
+                      Hkv=wl.Hkv, dh=wl.dh, max_L=int(xa["prefix_len"].max()),
+                      heads={"d": wl.d, "V": wl.V, "K": wl.K, "widths": list(wl.head_widths)},
+                      lm_width=wl.lm_width, accept="greedy", V=wl.accept_V)
+    inp = {"h": dev(xh["h"], dt), "w_res": dev(xh["w_res"], dt), "w_head": dev(xh["w_head"], dt),
+           "q": dev(xa["q"], dt), "k_cache": dev(xa["k_cache"], dt),
+           "v_cache": dev(xa["v_cache"], dt), "prefix_len": dev_i32(xa["prefix_len"]),
+           "target": dev(target, dt)}
+    print(f"step {wl.name} seed={seed}", flush=True)
+    step.run(inp)
+    torch.cuda.synchronize()
+    assert int(step.status.item()) == 0
+    # heads: ids exact (near-ties counted), candidate tokens and tree exact
+    off = 1 if wl.lm_width else 0
+    ties = check_topk(host(step.cand)[:, off:, :], heads["logits"],
+                      [w for w in wl.head_widths])
+    assert ties == 0, "a near-tie changes the tree; the step comparison below would not hold"
+    np.testing.assert_array_equal(host(step.tree["node_tokens"]), tree["tokens"])
+    np.testing.assert_array_equal(host(step.tree["depth"]), tree["depth"])
+    ref_att = O.tree_attention(xa["q"], xa["k_cache"], xa["v_cache"], xa["prefix_len"], tree["anc"])
+    if wl.dtype == "f32":
+        assert_fp32(host(step.attn_out), ref_att["out"], what="attention")
+    else:
+        assert_bf16(host(step.attn_out), ref_att["out"], what="attention")
+    assert_fp32(host(step.attn_lse), ref_att["lse"], atol=1e-4 if wl.dtype == "f32" else 1e-3,
+                what="lse")
+    ref_acc = O.accept_greedy(target, tree["tokens"], parents, wl.D)
+    for k in ("accept_len", "path_nodes", "out_tokens"):
+        np.testing.assert_array_equal(host(step.acc[k]), ref_acc[k], err_msg=k)
+    return host(step.acc["accept_len"])
+
+
+def test_step_tiny_fp32():
+    require_gpu()
+    _check_step(W.WORKLOADS["c1"], 1)
+
+
+def test_step_llama8b_full():
+    require_gpu()
+    lens = _check_step(W.WORKLOADS["c2"], 2)
+    print("accepted length", lens.tolist())
