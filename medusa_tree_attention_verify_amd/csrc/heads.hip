@@ -18,8 +18,8 @@
 //
 // Each workgroup owns 32 weight rows; its NW waves split the reduction dimension and meet in
 // LDS.  The projection's epilogue keeps only a per-workgroup top-s and (max, sum-exp) pair per
-// batch row; the last workgroup of each head (completion counter) merges them, so the logits
-// never have to be written.
+// batch row; a small second kernel merges them per (head, batch row), so the logits never
+// have to be written.
 
 #include <math.h>
 
@@ -30,6 +30,17 @@ namespace mv {
 namespace {
 
 constexpr int kRows = 32;  // weight rows per workgroup
+
+// Streaming parameters (measured on MI355X; see the head-projection profile).
+#ifndef MV_GEMV_U
+#define MV_GEMV_U 2            // k-steps per load batch
+#endif
+#ifndef MV_GEMV_WAVES
+#define MV_GEMV_WAVES 12288    // waves per launch to aim for (1024 SIMDs on the chip)
+#endif
+#ifndef MV_GEMV_NT
+#define MV_GEMV_NT 0           // non-temporal weight loads (measured slower when on)
+#endif
 
 struct GemvParams {
   int B, d, R, K, T, nrb;   // R = rows per head, T = d / 32, nrb = ceil(R / kRows)
@@ -43,7 +54,6 @@ struct GemvParams {
   float* hk_ws;
   float* hk_out;
   uint16_t* bpack_out;
-  unsigned* cnt;
   // projection epilogue
   void* logits;
   float* pval;
@@ -57,6 +67,14 @@ struct GemvParams {
   int s_max;
   int s[MV_MAX_HEADS];
 };
+
+__device__ __forceinline__ u32x4 wload(const u32x4* p) {
+#if MV_GEMV_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
 
 template <bool BF16>
 __device__ __forceinline__ float load_elem(const void* base, size_t i) {
@@ -97,56 +115,91 @@ __device__ void residual_epilogue(const GemvParams& p, int k, int row0, float (*
   }
 }
 
-// ---- merge of the per-workgroup partials of head k (run by the last workgroup of head k).
-__device__ void heads_merge(const GemvParams& p, int k, float* sv, int* si) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int nrb = p.nrb, s = p.s[k], smax = p.s_max;
-  for (int b = 0; b < p.B; ++b) {
-    const size_t base = (static_cast<size_t>(k) * p.B + b) * nrb;
-    float m = -INFINITY;
-    for (int j = tid; j < nrb; j += nt) m = fmaxf(m, load_agent(p.pm + base + j));
-    m = block_max(m, sv);
-    float l = 0.f;
-    for (int j = tid; j < nrb; j += nt)
-      l += load_agent(p.pl + base + j) * expf(load_agent(p.pm + base + j) - m);
-    l = block_sum(l, sv);
-    float pv = INFINITY;
-    int pi = -1;
-    for (int r = 0; r < smax; ++r) {
-      float bv = -INFINITY;
-      int bi = INT_MAX;
-      if (r < s) {
-        for (int j = tid; j < nrb * s; j += nt) {
-          const size_t q = (base + j / s) * smax + (j % s);
-          const int ii = load_agent(p.pidx + q);
-          const float vv = load_agent(p.pval + q);
-          if (ii >= 0 && kv_after(vv, ii, pv, pi) && kv_better(vv, ii, bv, bi)) {
-            bv = vv;
-            bi = ii;
-          }
-        }
-      }
-      block_argbest(bv, bi, sv, si);
-      if (tid == 0) {
-        const size_t o = static_cast<size_t>(b) * p.ld_topk + static_cast<size_t>(k) * smax + r;
-        const bool ok = r < s && bi != INT_MAX;
-        p.topk_ids[o] = ok ? bi : -1;
-        p.topk_vals[o] = ok ? bv : -INFINITY;
-      }
-      pv = bv;
-      pi = bi;
+// ---- merge of the per-workgroup partials: one workgroup per (head k, batch row b).
+// A separate launch: a completion counter inside the projection kernel would need an
+// agent-scope release/acquire per workgroup, which on this multi-XCD part writes back and
+// invalidates the XCD's L2 for every workgroup.  One pass over the partials: every thread
+// folds its blocks into a sorted register list (top MV_MAX_TOPK) and an online (max, sum);
+// the s_k winners are then drawn from the list heads, one workgroup argmax per rank.
+constexpr int kMergeThreads = 1024;
+
+__device__ __forceinline__ void list_insert(float (&lv)[MV_MAX_TOPK], int (&li)[MV_MAX_TOPK],
+                                            float v, int i) {
+#pragma unroll
+  for (int q = 0; q < MV_MAX_TOPK; ++q) {
+    if (kv_better(v, i, lv[q], li[q])) {
+      const float tv = lv[q];
+      const int ti = li[q];
+      lv[q] = v;
+      li[q] = i;
+      v = tv;
+      i = ti;
     }
-    if (tid == 0 && p.lse) p.lse[static_cast<size_t>(b) * p.K + k] = m + logf(l);
   }
-  if (tid == 0) p.cnt[k] = 0u;  // re-arm the counter for the next launch
 }
 
-// ---- projection epilogue: optional logits, per-workgroup top-s and (max, sum exp), merge.
+__global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(const GemvParams p) {
+  __shared__ float sv[kMergeThreads / 64];
+  __shared__ int si[kMergeThreads / 64];
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int k = blockIdx.x % p.K, b = blockIdx.x / p.K;
+  const int nrb = p.nrb, s = p.s[k], smax = p.s_max;
+  const size_t base = (static_cast<size_t>(k) * p.B + b) * nrb;
+  float lv[MV_MAX_TOPK];
+  int li[MV_MAX_TOPK];
+#pragma unroll
+  for (int q = 0; q < MV_MAX_TOPK; ++q) {
+    lv[q] = -INFINITY;
+    li[q] = INT_MAX;
+  }
+  // All loads of a block's partials are issued before any is used: they come from other
+  // XCDs' writes, so each one is a trip to memory and must not sit in a dependence chain.
+  float m = -INFINITY, l = 0.f;
+  for (int j = tid; j < nrb; j += nt) {
+    const size_t q0 = (base + j) * smax;
+    float pv[MV_MAX_TOPK];
+    int pi[MV_MAX_TOPK];
+#pragma unroll
+    for (int r = 0; r < MV_MAX_TOPK; ++r) {
+      pi[r] = r < s ? p.pidx[q0 + r] : -1;
+      pv[r] = r < s ? p.pval[q0 + r] : -INFINITY;
+    }
+    const float mb = p.pm[base + j], lb = p.pl[base + j];
+    const float mn = fmaxf(m, mb);
+    l = (m == -INFINITY ? 0.f : l * expf(m - mn)) + lb * expf(mb - mn);
+    m = mn;
+#pragma unroll
+    for (int r = 0; r < MV_MAX_TOPK; ++r)
+      if (pi[r] >= 0) list_insert(lv, li, pv[r], pi[r]);
+  }
+  const float M = block_max(m, sv);
+  const float Lsum = block_sum(m == -INFINITY ? 0.f : l * expf(m - M), sv);
+  for (int r = 0; r < smax; ++r) {
+    float bv = r < s ? lv[0] : -INFINITY;
+    int bi = r < s ? li[0] : INT_MAX;
+    block_argbest(bv, bi, sv, si);
+    if (r < s && li[0] == bi && bi != INT_MAX) {  // token ids are unique: the owner pops
+#pragma unroll
+      for (int q = 0; q + 1 < MV_MAX_TOPK; ++q) {
+        lv[q] = lv[q + 1];
+        li[q] = li[q + 1];
+      }
+      lv[MV_MAX_TOPK - 1] = -INFINITY;
+      li[MV_MAX_TOPK - 1] = INT_MAX;
+    }
+    if (tid == 0) {
+      const size_t o = static_cast<size_t>(b) * p.ld_topk + static_cast<size_t>(k) * smax + r;
+      const bool ok = r < s && bi != INT_MAX;
+      p.topk_ids[o] = ok ? bi : -1;
+      p.topk_vals[o] = ok ? bv : -INFINITY;
+    }
+  }
+  if (tid == 0 && p.lse) p.lse[static_cast<size_t>(b) * p.K + k] = M + logf(Lsum);
+}
+
+// ---- projection epilogue: optional logits, per-workgroup top-s and (max, sum exp).
 template <bool BF16, int NW, int BC>
 __device__ void head_epilogue(const GemvParams& p, int k, int rb, float (*ys)[BC]) {
-  __shared__ float sv[16];
-  __shared__ int si[16];
-  __shared__ int last;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int row0 = rb * kRows;
   if (p.logits) {
@@ -178,72 +231,89 @@ __device__ void head_epilogue(const GemvParams& p, int k, int rb, float (*ys)[BC
       if (bi == j) val = -INFINITY;
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) last = (atomicAdd(&p.cnt[k], 1u) == static_cast<unsigned>(p.nrb - 1));
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  heads_merge(p, k, sv, si);
 }
 
 // ---- bf16 weights: MFMA streaming loop.
 template <int NW, int NCT, int MODE>
 __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(const GemvParams p) {
-  constexpr int RT = kRows / 16, BC = 8 * NCT, U = 4;
+  constexpr int RT = kRows / 16, BC = 8 * NCT, U = MV_GEMV_U;
   __shared__ float red[NW][kRows][16 * NCT + 1];
   __shared__ float ys[kRows][BC];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int k = blockIdx.y, rb = blockIdx.x, row0 = rb * kRows;
-  if (MODE == 0 && rb == 0 && threadIdx.x < MV_MAX_HEADS) p.cnt[threadIdx.x] = 0u;
 
+  const int t0 = (w * p.T) / NW, t1 = ((w + 1) * p.T) / NW;
+  // Weight operand: lane (row r = lane % 16, k-group g = lane / 16) of row tile rt reads the
+  // 16 bytes W[row0 + 16*rt + r][32*t + 8*g .. +8] at k-step t; rows past R are clamped.
   const uint16_t* Wk = static_cast<const uint16_t*>(p.W) + static_cast<size_t>(k) * p.R * p.d;
-  const u32x4* arow[RT];
+  const u32x4* ap[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int r = min(row0 + rt * 16 + (lane & 15), p.R - 1);
-    arow[rt] = reinterpret_cast<const u32x4*>(Wk + static_cast<size_t>(r) * p.d) + (lane >> 4);
+    ap[rt] = reinterpret_cast<const u32x4*>(Wk + static_cast<size_t>(r) * p.d) + (lane >> 4) + t0 * 4;
   }
-  const u32x4* bk = p.bsrc + k * p.bsrc_hstride + lane;
+  // Vector operand.  Projection: the packed h_k, one 16-byte load per lane and k-step.
+  // Residual: h itself (bf16, no remainder part): lane (column c, k-group g) of column tile ct
+  // reads h[8*ct + c][32*t + 8*g .. +8] for c < 8 and batch rows that exist, zero otherwise.
+  const u32x4* bp[NCT];
+  bool bvalid[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    if constexpr (MODE == 0) {
+      const int c = lane & 15, bb = ct * 8 + (c & 7);
+      bvalid[ct] = c < 8 && bb < p.B;
+      bp[ct] = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.h) +
+                                              static_cast<size_t>(bvalid[ct] ? bb : 0) * p.d) +
+               (lane >> 4) + t0 * 4;
+    } else {
+      bvalid[ct] = true;
+      bp[ct] = p.bsrc + k * p.bsrc_hstride + (static_cast<size_t>(t0) * NCT + ct) * 64 + lane;
+    }
+  }
+  constexpr int BSTEP = MODE == 0 ? 4 : NCT * 64;  // u32x4 units per k-step
 
   f32x4 acc[RT][NCT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int t0 = (w * p.T) / NW, t1 = ((w + 1) * p.T) / NW;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto step = [&](const u32x4 (&a)[RT], const u32x4 (&bv)[NCT]) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, a[rt]), __builtin_bit_cast(bf16x8, bv[ct]), acc[rt][ct], 0, 0, 0);
+  };
   int t = t0;
   for (; t + U <= t1; t += U) {
     u32x4 a[U][RT], bv[U][NCT];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) a[u][rt] = __builtin_nontemporal_load(arow[rt] + (t + u) * 4);
+      for (int rt = 0; rt < RT; ++rt) a[u][rt] = wload(ap[rt] + u * 4);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int ct = 0; ct < NCT; ++ct) bv[u][ct] = bvalid[ct] ? bp[ct][u * BSTEP] : zero;
+    }
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) bv[u][ct] = bk[((t + u) * NCT + ct) * 64];
+    for (int u = 0; u < U; ++u) step(a[u], bv[u]);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int rt = 0; rt < RT; ++rt) ap[rt] += U * 4;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, a[u][rt]), __builtin_bit_cast(bf16x8, bv[u][ct]),
-              acc[rt][ct], 0, 0, 0);
+    for (int ct = 0; ct < NCT; ++ct) bp[ct] += U * BSTEP;
   }
   for (; t < t1; ++t) {
+    u32x4 a[RT], bv[NCT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const u32x4 a = __builtin_nontemporal_load(arow[rt] + t * 4);
+    for (int rt = 0; rt < RT; ++rt) a[rt] = wload(ap[rt]);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bk[(t * NCT + ct) * 64]),
-            acc[rt][ct], 0, 0, 0);
-    }
+    for (int ct = 0; ct < NCT; ++ct) bv[ct] = bvalid[ct] ? bp[ct][0] : zero;
+    step(a, bv);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) ap[rt] += 4;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) bp[ct] += BSTEP;
   }
   // D layout of a 16x16 MFMA tile: lane holds rows 4*(lane/16) + v, column lane % 16.
 #pragma unroll
@@ -273,7 +343,6 @@ __global__ __launch_bounds__(NW * 64) void gemv_f32_kernel(const GemvParams p) {
   __shared__ float ys[kRows][BC];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int k = blockIdx.y, rb = blockIdx.x, row0 = rb * kRows;
-  if (MODE == 0 && rb == 0 && threadIdx.x < MV_MAX_HEADS) p.cnt[threadIdx.x] = 0u;
   const float* Wk = static_cast<const float*>(p.W) + static_cast<size_t>(k) * p.R * p.d;
   const float* X = p.xsrc + k * p.x_hstride;
   for (int r = w; r < kRows; r += NW) {
@@ -304,25 +373,6 @@ __global__ __launch_bounds__(NW * 64) void gemv_f32_kernel(const GemvParams p) {
   __syncthreads();
   if constexpr (MODE == 0) residual_epilogue<false, BC>(p, k, row0, ys);
   else head_epilogue<false, NW, BC>(p, k, rb, ys);
-}
-
-// ---- h -> packed B operand (remainder part is zero for bf16 inputs).
-__global__ __launch_bounds__(256) void pack_h_kernel(const uint16_t* h, int B, int d, int nct,
-                                                     uint16_t* out) {
-  const int T = d / 32;
-  const long long total = static_cast<long long>(T) * nct * 64;
-  for (long long q = blockIdx.x * 256LL + threadIdx.x; q < total; q += gridDim.x * 256LL) {
-    const int lane = static_cast<int>(q & 63);
-    const long long tc = q >> 6;
-    const int ct = static_cast<int>(tc % nct), t = static_cast<int>(tc / nct);
-    const int col = lane & 15, g = lane >> 4, b = ct * 8 + (col & 7);
-    const bool use = col < 8 && b < B;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = t * 32 + g * 8 + e;
-      out[q * 8 + e] = use ? h[static_cast<size_t>(b) * d + j] : static_cast<uint16_t>(0);
-    }
-  }
 }
 
 // ---- top-s of each row of a logit matrix (one workgroup per row).
@@ -362,9 +412,7 @@ int nct_for(int B) { return B <= 8 ? 1 : (B <= 16 ? 2 : 4); }
 
 struct HeadsLayout {
   float* hk = nullptr;
-  uint16_t* bpack_h = nullptr;
   uint16_t* bpack_hk = nullptr;
-  unsigned* cnt = nullptr;
   float* pval = nullptr;
   int* pidx = nullptr;
   float* pm = nullptr;
@@ -382,10 +430,8 @@ HeadsLayout heads_layout(void* ws, int dt, int B, int d, int V, int K, int s_max
   const size_t T = static_cast<size_t>(d) / 32;
   L.hk = c.take<float>(static_cast<size_t>(B) * K * d);
   if (dt == MV_BF16) {
-    L.bpack_h = c.take<uint16_t>(T * nct * 64 * 8);
     L.bpack_hk = c.take<uint16_t>(static_cast<size_t>(K) * T * nct * 64 * 8);
   }
-  L.cnt = c.take<unsigned>(MV_MAX_HEADS);
   L.residual_bytes = c.bytes();
   const size_t nrb = static_cast<size_t>(ceil_div(V, kRows));
   const size_t np = static_cast<size_t>(K) * B * nrb;
@@ -406,11 +452,11 @@ int check_common(int dt, int B, int d, int K) {
   return MV_OK;
 }
 
-// Waves per workgroup: enough waves in flight to cover HBM latency (about 8 per SIMD over the
-// chip's 1024 SIMDs), while each wave keeps at least 8 k-steps of streaming.
+// Waves per workgroup: the smallest power of two that gives the launch about MV_GEMV_WAVES
+// waves (12 per SIMD) to cover HBM latency, while each wave keeps at least 8 k-steps.
 int pick_nw(long long nblocks, int T, int cap) {
   int nw = 1;
-  while (nw * 2 <= cap && nblocks * nw < 8192 && T / (nw * 2) >= 8) nw *= 2;
+  while (nw * 2 <= cap && nblocks * nw < MV_GEMV_WAVES && T / (nw * 2) >= 8) nw *= 2;
   return nw;
 }
 
@@ -459,14 +505,9 @@ MV_API int mv_medusa_residual(int dt, int B, int d, int K, const void* h, const 
   hipStream_t st = as_stream(stream);
   GemvParams p{};
   p.B = B; p.d = d; p.R = d; p.K = K; p.T = d / 32; p.nrb = ceil_div(d, kRows);
-  p.W = w_res; p.h = h; p.hk_ws = L.hk; p.hk_out = hk; p.cnt = L.cnt;
+  p.W = w_res; p.h = h; p.hk_ws = L.hk; p.hk_out = hk;
   if (dt == MV_BF16) {
-    const int nct = nct_for(B);
-    const long long total = static_cast<long long>(d / 32) * nct * 64;
-    const int blocks = static_cast<int>((total + 255) / 256);
-    pack_h_kernel<<<blocks, 256, 0, st>>>(static_cast<const uint16_t*>(h), B, d, nct, L.bpack_h);
-    MV_TRY(launch_status());
-    p.bsrc = reinterpret_cast<const u32x4*>(L.bpack_h);
+    p.bsrc = nullptr;
     p.bsrc_hstride = 0;
     p.bpack_out = L.bpack_hk;
   } else {
@@ -493,7 +534,7 @@ MV_API int mv_medusa_head_topk(int dt, int B, int d, int V, int K, const int* s_
   HeadsLayout L = heads_layout(ws, dt, B, d, V, K, s_max);
   GemvParams p{};
   p.B = B; p.d = d; p.R = V; p.K = K; p.T = d / 32; p.nrb = ceil_div(V, kRows);
-  p.W = w_head; p.cnt = L.cnt; p.logits = logits;
+  p.W = w_head; p.logits = logits;
   p.pval = L.pval; p.pidx = L.pidx; p.pm = L.pm; p.pl = L.pl;
   p.topk_ids = topk_ids; p.topk_vals = topk_vals; p.ld_topk = ld_topk; p.lse = lse;
   p.s_max = s_max;
@@ -507,7 +548,10 @@ MV_API int mv_medusa_head_topk(int dt, int B, int d, int V, int K, const int* s_
     p.x_bstride = static_cast<long long>(K) * d;
     p.x_hstride = d;
   }
-  return launch_gemv<1>(dt, p, K, as_stream(stream));
+  hipStream_t st = as_stream(stream);
+  MV_TRY(launch_gemv<1>(dt, p, K, st));
+  heads_merge_kernel<<<K * B, kMergeThreads, 0, st>>>(p);
+  return launch_status();
 }
 
 MV_API int mv_medusa_heads(int dt, int B, int d, int V, int K, const int* s_per_head, int s_max,

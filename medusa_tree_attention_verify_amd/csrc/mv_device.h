@@ -120,13 +120,4 @@ __device__ __forceinline__ float4 load_nt_f4(const float* p) {
   return make_float4(v[0], v[1], v[2], v[3]);
 }
 
-// Loads that must observe stores made by other workgroups of the same kernel (after the
-// acquire fence that follows a completion counter).
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int load_agent(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 }  // namespace mv
