@@ -8,17 +8,21 @@
 //
 // bf16 path.  For one (sequence b, KV head g) the G query heads of the group and the N tree
 // nodes form M = N*G query rows that share every key, so they are packed into the MFMA tile:
-// a wave owns 32 query rows, a workgroup 32*NWV.  The prefix is split into chunks handled by
-// separate workgroups (split-KV); the chunk that ends the prefix also takes the N tree keys,
-// where the per-node ancestor bitmask replaces the dense mask.  Per 32-key tile:
-//   * K and V come from HBM with coalesced 16-byte loads (prefetched one tile ahead into
-//     registers) and land in LDS: K row-major, V transposed with its keys permuted so that
-//     the P.V operand of every lane is one 16-byte LDS read;
-//   * S^T = K Q^T is one 32x32 output tile of v_mfma_f32_32x32x16_bf16 per wave; in its
-//     output layout a lane holds 16 keys of one query, so the softmax max/sum need one
-//     cross-lane step (lanes l and l+32);
-//   * online softmax in the exp2 domain (scale * log2(e) folded into the scores);
-//   * O^T += V^T P^T, P rounded to bf16, accumulated in fp32.
+// a wave owns 32 query rows, a workgroup of 8 waves 256 rows (all of them for a 64-node tree
+// with 4 query heads per KV head, so each K/V byte crosses HBM once).  The prefix is split
+// into chunks handled by separate workgroups (split-KV); the chunk that ends the prefix also
+// takes the N tree keys, where the per-node ancestor bitmask replaces the dense mask.  Per
+// 64-key tile:
+//   * K and V arrive with coalesced 16-byte loads one tile ahead (registers) and are stored
+//     row-major in LDS with a padded pitch, so every operand read is bank-conflict free;
+//   * S^T = K Q^T: two 32x32 output tiles of v_mfma_f32_32x32x16_bf16 per wave; in that output
+//     layout a lane holds 32 keys of one query, so the softmax max/sum need one cross-lane
+//     step (lanes l and l+32);
+//   * online softmax: running max in raw score units, p = 2^(s*c - m*c) with c = scale*log2(e)
+//     as one FMA and a raw v_exp_f32 per score; the O rescale is skipped when no lane's max
+//     moved;
+//   * O^T += V^T P^T with P rounded to bf16 (v_cvt_pk_bf16_f32) and fp32 accumulation; the V^T
+//     operand is gathered from the row-major V tile with 16-bit LDS reads.
 // A second kernel merges the chunk partials with their (max, sum) pairs.
 //
 // fp32 path: a vector-ALU kernel, one wave per query row, no chunking (the fp32 configuration
@@ -60,25 +64,27 @@ __device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool re
   return Lb;
 }
 
-// Slot of key k (0..31) in a transposed V tile row: the keys that one lane feeds to one
-// P.V MFMA become 8 consecutive slots.
-__device__ __forceinline__ int v_slot(int k) {
-  const int kk = k & 15;
-  return (k >> 4) * 16 + ((kk & 7) >> 2) * 8 + ((kk >> 3) << 2) + (kk & 3);
-}
+#ifndef MV_ATTN_TARGET_WG
+#define MV_ATTN_TARGET_WG 1024  // split-KV: aim for this many workgroups
+#endif
+#ifndef MV_ATTN_MIN_CHUNK
+#define MV_ATTN_MIN_CHUNK 512   // but never chunks shorter than this many keys
+#endif
+
+constexpr int kKT = 64;  // keys per tile
 
 template <int DH, int NWV>
-__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 8))) void tree_attn_bf16_kernel(const AttnParams p) {
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void tree_attn_bf16_kernel(const AttnParams p) {
   constexpr int NT = NWV * 64;
-  constexpr int KP = DH + 8;  // K tile pitch (elements)
-  constexpr int VP = 32 + 8;  // V^T tile pitch (elements)
-  constexpr int KS = DH / 16;
-  constexpr int DB = DH / 32;
-  constexpr int DG = DH / 8;  // 16-byte pieces per key row
-  constexpr int PPT = 32 * DG / NT;
-  static_assert((32 * DG) % NT == 0, "tile pieces must split evenly");
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][32 * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DH * VP];
+  constexpr int KP = DH + 8;    // K and V tile pitch (elements): conflict-free LDS reads
+  constexpr int KS = DH / 16;   // k-steps of one S^T MFMA chain
+  constexpr int DB = DH / 32;   // 32-wide blocks of the head dimension
+  constexpr int DG = DH / 8;    // 16-byte pieces per key row
+  constexpr int PPT = kKT * DG / NT;
+  static_assert((kKT * DG) % NT == 0, "tile pieces must split evenly");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKT * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKT * KP];
 
   // XCD-aware order: consecutive logical tiles (the query tiles of one KV chunk) run on one XCD.
   const int per = (p.total + kXcds - 1) / kXcds;
@@ -97,8 +103,8 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 8))
   if (c >= ncb) return;
   const int kbeg = c * p.CK, kend = min(Lb, kbeg + p.CK);
   const bool last = c == ncb - 1;
-  const int ntp = kend > kbeg ? (kend - kbeg + 31) / 32 : 0;
-  const int ntiles = ntp + (last ? (p.N + 31) / 32 : 0);
+  const int ntp = kend > kbeg ? (kend - kbeg + kKT - 1) / kKT : 0;
+  const int ntiles = ntp + (last ? (p.N + kKT - 1) / kKT : 0);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
@@ -107,13 +113,13 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 8))
   const int node = qvalid ? m / p.G : 0;
   const int h = g * p.G + (qvalid ? m % p.G : 0);
 
-  const uint16_t* qp = static_cast<const uint16_t*>(p.q);
+  // Q is the B operand of S^T = K Q^T: lane holds query l32, dims ks*16 + 8*half .. +8.
   bf16x8 qreg[KS];
   {
-    const uint16_t* qrow = qp + (static_cast<size_t>(b * p.N + node) * p.Hq + h) * DH;
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (static_cast<size_t>(b * p.N + node) * p.Hq + h) * DH;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      uint4 t4 = qvalid ? *reinterpret_cast<const uint4*>(qrow + ks * 16 + half * 8) : make_uint4(0, 0, 0, 0);
+      const uint4 t4 = qvalid ? *reinterpret_cast<const uint4*>(qrow + ks * 16 + half * 8) : make_uint4(0, 0, 0, 0);
       qreg[ks] = as_bf16x8(t4);
     }
   }
@@ -121,55 +127,40 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 8))
   const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + kvbase;
   const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + kvbase;
 
-  uint4 kreg[PPT], vreg[PPT];
   auto tile_rows = [&](int t, int& row0, int& nv) {
     if (t < ntp) {
-      row0 = kbeg + t * 32;
-      nv = min(32, kend - row0);
+      row0 = kbeg + t * kKT;
+      nv = min(kKT, kend - row0);
     } else {
       const int tt = t - ntp;
-      row0 = Lb + tt * 32;
-      nv = min(32, p.N - tt * 32);
+      row0 = Lb + tt * kKT;
+      nv = min(kKT, p.N - tt * kKT);
     }
   };
-  auto gload = [&](int t) {
-    int row0, nv;
-    tile_rows(t, row0, nv);
+  // Two register sets of prefetched K/V pieces: tile t+2 is requested while tile t computes.
+  uint4 kr0[PPT], vr0[PPT];
+  auto gload = [&](int t, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
+    int row0 = 0, nv = 0;
+    if (t < ntiles) tile_rows(t, row0, nv);
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int pc = tid + i * NT, key = pc / DG, dg = pc % DG;
       if (key < nv) {
         const size_t o = static_cast<size_t>(row0 + key) * DH + dg * 8;
-        kreg[i] = load_nt_u4(Kg + o);
-        vreg[i] = load_nt_u4(Vg + o);
+        kr[i] = *reinterpret_cast<const uint4*>(Kg + o);
+        vr[i] = *reinterpret_cast<const uint4*>(Vg + o);
       } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
+        kr[i] = make_uint4(0, 0, 0, 0);
+        vr[i] = make_uint4(0, 0, 0, 0);
       }
     }
   };
-  auto swrite = [&](int buf) {
+  auto swrite = [&](int buf, const uint4 (&kr)[PPT], const uint4 (&vr)[PPT]) {
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int pc = tid + i * NT, key = pc / DG, dg = pc % DG;
-      *reinterpret_cast<uint4*>(&Ks[buf][key * KP + dg * 8]) = kreg[i];
-      // The lane holding key^1 (same d range) is lane ^ DG; two keys share one 32-bit word.
-      const uint32_t mine[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-      uint32_t other[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) other[q] = __shfl_xor(mine[q], DG);
-      const bool odd = key & 1;
-      const int slot = v_slot(key & ~1);
-      uint32_t* vt = reinterpret_cast<uint32_t*>(&Vt[buf][0]);
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int e = odd ? e4 + 4 : e4;
-        const uint32_t wm = mine[e >> 1], wo = other[e >> 1];
-        const uint32_t hm = (e & 1) ? (wm >> 16) : (wm & 0xffffu);
-        const uint32_t ho = (e & 1) ? (wo >> 16) : (wo & 0xffffu);
-        const uint32_t word = odd ? (ho | (hm << 16)) : (hm | (ho << 16));
-        vt[((dg * 8 + e) * VP + slot) >> 1] = word;
-      }
+      *reinterpret_cast<uint4*>(&Ks[buf][key * KP + dg * 8]) = kr[i];
+      *reinterpret_cast<uint4*>(&Vs[buf][key * KP + dg * 8]) = vr[i];
     }
   };
 
@@ -180,67 +171,123 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 8))
     for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  gload(0);
-  swrite(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  auto compute = [&](int t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
-    f32x16 sacc;
+    f32x16 sacc[2];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 a = *reinterpret_cast<const uint4*>(&Ks[buf][l32 * KP + ks * 16 + half * 8]);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qreg[ks], sacc, 0, 0, 0);
+      for (int v = 0; v < 16; ++v) sacc[st][v] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&Ks[buf][(st * 32 + l32) * KP + ks * 16 + half * 8]);
+        sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qreg[ks], sacc[st], 0, 0, 0);
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
     int row0, nv;
     tile_rows(t, row0, nv);
     const bool tree = t >= ntp;
-    const uint32_t ancw = (tree && qvalid) ? p.anc[static_cast<size_t>(node) * p.W + (t - ntp)] : 0u;
-    // 32x32 output layout: lane holds query l32 and keys 8*(v/4) + 4*half + v%4.
-    float sv[16];
-    float tmax = -INFINITY;
+    // 32x32 output layout: lane holds query l32 and keys 32*st + 8*(v/4) + 4*half + v%4.
+    f32x16 (&sv)[2] = sacc;  // scores, then probabilities, in place
+    // Visibility of the 32 scores this lane holds, bit 16*st + v: all set for a full prefix
+    // tile; the tail of a partial tile and non-ancestors of a tree tile are cleared.
+    uint32_t vis = 0xffffffffu;
+    if (tree || nv < kKT) {
+      uint32_t aw[2] = {0xffffffffu, 0xffffffffu};
+      if (tree) {
+        const int w0 = 2 * (t - ntp);
+        aw[0] = qvalid ? p.anc[static_cast<size_t>(node) * p.W + w0] : 0u;
+        aw[1] = (qvalid && w0 + 1 < p.W) ? p.anc[static_cast<size_t>(node) * p.W + w0 + 1] : 0u;
+      }
+      vis = 0u;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int kl = 8 * (v >> 2) + 4 * half + (v & 3);
-      const bool ok = kl < nv && (!tree || ((ancw >> kl) & 1u));
-      sv[v] = ok ? sacc[v] * p.scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, sv[v]);
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kl = 8 * (v >> 2) + 4 * half + (v & 3);
+          const bool ok = st * 32 + kl < nv && ((aw[st] >> kl) & 1u);
+          vis |= static_cast<uint32_t>(ok) << (16 * st + v);
+        }
+    }
+    // Online softmax; the running max is kept in raw score units and the scale is folded into
+    // the exp2 argument: p = 2^(s*c - m*c), c = scale*log2(e), one FMA per score.
+    float tmax = -INFINITY;
+    if (vis == 0xffffffffu) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sv[st][v]);
+    } else {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          sv[st][v] = ((vis >> (16 * st + v)) & 1u) ? sv[st][v] : -INFINITY;
+          tmax = fmaxf(tmax, sv[st][v]);
+        }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float c2 = p.scale_log2;
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+    const float mc = m_use * c2;
     float lsum = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      sv[v] = exp2f(sv[v] - m_use);
-      lsum += sv[v];
-    }
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        sv[st][v] = __builtin_amdgcn_exp2f(fmaf(sv[st][v], c2, -mc));
+        lsum += sv[st][v];
+      }
     lsum += __shfl_xor(lsum, 32);
     l_run = l_run * alpha + lsum;
     m_run = m_new;
+    // Keep the P.V operand reads below the softmax: hoisting them above it would keep 16
+    // operand registers per lane alive across the exp2 work.
+    __builtin_amdgcn_sched_barrier(0);
+    if (!__all(alpha == 1.0f)) {  // the running max moved for some query of this wave
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
-    const uint4 pw[2] = {
-        make_uint4(pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]), pack_bf16x2(sv[4], sv[5]),
-                   pack_bf16x2(sv[6], sv[7])),
-        make_uint4(pack_bf16x2(sv[8], sv[9]), pack_bf16x2(sv[10], sv[11]),
-                   pack_bf16x2(sv[12], sv[13]), pack_bf16x2(sv[14], sv[15]))};
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&Vt[buf][(db * 32 + l32) * VP + hf * 16 + half * 8]);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pw[hf]), oacc[db], 0, 0, 0);
-      }
+        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
     }
-    if (t + 1 < ntiles) swrite(buf ^ 1);
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int o = 8 * hf;
+        const uint4 pw = make_uint4(pack_bf16x2(sv[st][o + 0], sv[st][o + 1]),
+                                    pack_bf16x2(sv[st][o + 2], sv[st][o + 3]),
+                                    pack_bf16x2(sv[st][o + 4], sv[st][o + 5]),
+                                    pack_bf16x2(sv[st][o + 6], sv[st][o + 7]));
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          // A operand of O^T += V^T P^T: lane (dim d = 32*db + l32, group half) supplies
+          // V[key][d] for the 8 keys whose probabilities it holds in pw.
+          const uint16_t* vcol = &Vs[buf][(st * 32 + hf * 16 + 4 * half) * KP + db * 32 + l32];
+          bf16x8 a;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            a[e] = __builtin_bit_cast(__bf16, vcol[(8 * (e >> 2) + (e & 3)) * KP]);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pw), oacc[db], 0, 0, 0);
+        }
+      }
+  };
+
+  // Pipeline: LDS holds tile t (computing) and receives tile t+1 at the end of iteration t;
+  // the registers hold tile t+1, requested at the start of iteration t.
+  gload(0, kr0, vr0);
+  swrite(0, kr0, vr0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) gload(t + 1, kr0, vr0);
+    compute(t);
+    if (t + 1 < ntiles) swrite((t + 1) & 1, kr0, vr0);
     __syncthreads();
   }
+
   if (!qvalid) return;
   // Output layout of O^T: lane holds query l32, dims db*32 + 8*(v/4) + 4*half + v%4.
   if (ncb == 1) {
@@ -257,7 +304,7 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 8))
         *reinterpret_cast<uint2*>(orow + d0) = w2;
       }
     if (p.lse && half == 0)
-      p.lse[(static_cast<size_t>(b) * p.Hq + h) * p.N + node] = (m_run + log2f(l_run)) * kLn2;
+      p.lse[(static_cast<size_t>(b) * p.Hq + h) * p.N + node] = (m_run * p.scale_log2 + log2f(l_run)) * kLn2;
   } else {
     const size_t rowi = (static_cast<size_t>(b * p.Hq + h) * p.N + node) * p.nchunks + c;
     float* po = p.part_o + rowi * DH;
@@ -269,7 +316,7 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 8))
         *reinterpret_cast<float4*>(po + d0) =
             make_float4(oacc[db][vq * 4 + 0], oacc[db][vq * 4 + 1], oacc[db][vq * 4 + 2], oacc[db][vq * 4 + 3]);
       }
-    if (half == 0) p.part_ml[rowi] = make_float2(m_run, l_run);
+    if (half == 0) p.part_ml[rowi] = make_float2(m_run * p.scale_log2, l_run);
   }
 }
 
@@ -379,26 +426,28 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(const AttnParams p) 
 // ---------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------
-constexpr int kNWV = 4;  // waves per workgroup -> 128 query rows
+constexpr int kNWV = 8;  // waves per workgroup -> 256 query rows
 
 struct AttnPlan {
   int qtiles = 1, CK = 256, nchunks = 1;
   size_t ws_bytes = 0;
 };
 
-// Chunking: aim for ~2048 workgroups (8 per CU) while keeping chunks >= 256 keys, so that the
-// partial outputs stay small next to the K/V bytes of a chunk.
+// Chunking (split-KV): aim for MV_ATTN_TARGET_WG workgroups so that the chip stays busy and
+// sequences of different lengths balance, but keep chunks of at least MV_ATTN_MIN_CHUNK keys:
+// every chunk writes an fp32 partial output as large as its query block, so short chunks turn
+// a K/V-streaming kernel into a partial-output-writing one.
 AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L) {
   AttnPlan a;
   if (dt == MV_F32) return a;
   const int M = N * (Hq / Hkv);
   a.qtiles = ceil_div(M, kNWV * 32);
   const long long base = static_cast<long long>(B) * Hkv * a.qtiles;
-  int want = static_cast<int>(std::max<long long>(1, (2048 + base - 1) / base));
-  const int cap = std::max(1, ceil_div(max_L, 256));
+  int want = static_cast<int>(std::max<long long>(1, (MV_ATTN_TARGET_WG + base - 1) / base));
+  const int cap = std::max(1, ceil_div(max_L, MV_ATTN_MIN_CHUNK));
   want = std::min(want, cap);
   int ck = ceil_div(std::max(max_L, 1), want);
-  ck = std::max(256, (ck + 31) / 32 * 32);
+  ck = std::max(MV_ATTN_MIN_CHUNK, (ck + kKT - 1) / kKT * kKT);
   a.CK = ck;
   a.nchunks = std::max(1, ceil_div(max_L, ck));
   if (a.nchunks > 1) {

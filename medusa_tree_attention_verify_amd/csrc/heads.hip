@@ -118,15 +118,16 @@ __device__ void residual_epilogue(const GemvParams& p, int k, int row0, float (*
 // ---- merge of the per-workgroup partials: one workgroup per (head k, batch row b).
 // A separate launch: a completion counter inside the projection kernel would need an
 // agent-scope release/acquire per workgroup, which on this multi-XCD part writes back and
-// invalidates the XCD's L2 for every workgroup.  One pass over the partials: every thread
-// folds its blocks into a sorted register list (top MV_MAX_TOPK) and an online (max, sum);
-// the s_k winners are then drawn from the list heads, one workgroup argmax per rank.
-constexpr int kMergeThreads = 1024;
+// invalidates the XCD's L2 for every workgroup.  One pass over the partials with coalesced,
+// independent loads: every thread folds its candidates into a sorted register list of SM
+// entries (SM >= s_max) and an online (max, sum); the s_k winners are then drawn from the
+// list heads, one workgroup argmax per rank.
+constexpr int kMergeThreads = 256;
 
-__device__ __forceinline__ void list_insert(float (&lv)[MV_MAX_TOPK], int (&li)[MV_MAX_TOPK],
-                                            float v, int i) {
+template <int SM>
+__device__ __forceinline__ void list_insert(float (&lv)[SM], int (&li)[SM], float v, int i) {
 #pragma unroll
-  for (int q = 0; q < MV_MAX_TOPK; ++q) {
+  for (int q = 0; q < SM; ++q) {
     if (kv_better(v, i, lv[q], li[q])) {
       const float tv = lv[q];
       const int ti = li[q];
@@ -138,39 +139,37 @@ __device__ __forceinline__ void list_insert(float (&lv)[MV_MAX_TOPK], int (&li)[
   }
 }
 
+template <int SM>
 __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(const GemvParams p) {
   __shared__ float sv[kMergeThreads / 64];
   __shared__ int si[kMergeThreads / 64];
-  const int tid = threadIdx.x, nt = blockDim.x;
+  const int tid = threadIdx.x;
   const int k = blockIdx.x % p.K, b = blockIdx.x / p.K;
   const int nrb = p.nrb, s = p.s[k], smax = p.s_max;
   const size_t base = (static_cast<size_t>(k) * p.B + b) * nrb;
-  float lv[MV_MAX_TOPK];
-  int li[MV_MAX_TOPK];
+  float lv[SM];
+  int li[SM];
 #pragma unroll
-  for (int q = 0; q < MV_MAX_TOPK; ++q) {
+  for (int q = 0; q < SM; ++q) {
     lv[q] = -INFINITY;
     li[q] = INT_MAX;
   }
-  // All loads of a block's partials are issued before any is used: they come from other
-  // XCDs' writes, so each one is a trip to memory and must not sit in a dependence chain.
+  const int n = nrb * smax;
+  const int* pidx = p.pidx + base * smax;
+  const float* pval = p.pval + base * smax;
+#pragma unroll 4
+  for (int c = tid; c < n; c += kMergeThreads) {
+    const int ii = pidx[c];
+    const float vv = pval[c];
+    if (c % smax < s && ii >= 0) list_insert<SM>(lv, li, vv, ii);
+  }
   float m = -INFINITY, l = 0.f;
-  for (int j = tid; j < nrb; j += nt) {
-    const size_t q0 = (base + j) * smax;
-    float pv[MV_MAX_TOPK];
-    int pi[MV_MAX_TOPK];
-#pragma unroll
-    for (int r = 0; r < MV_MAX_TOPK; ++r) {
-      pi[r] = r < s ? p.pidx[q0 + r] : -1;
-      pv[r] = r < s ? p.pval[q0 + r] : -INFINITY;
-    }
+#pragma unroll 4
+  for (int j = tid; j < nrb; j += kMergeThreads) {
     const float mb = p.pm[base + j], lb = p.pl[base + j];
     const float mn = fmaxf(m, mb);
     l = (m == -INFINITY ? 0.f : l * expf(m - mn)) + lb * expf(mb - mn);
     m = mn;
-#pragma unroll
-    for (int r = 0; r < MV_MAX_TOPK; ++r)
-      if (pi[r] >= 0) list_insert(lv, li, pv[r], pi[r]);
   }
   const float M = block_max(m, sv);
   const float Lsum = block_sum(m == -INFINITY ? 0.f : l * expf(m - M), sv);
@@ -180,12 +179,12 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(const GemvPa
     block_argbest(bv, bi, sv, si);
     if (r < s && li[0] == bi && bi != INT_MAX) {  // token ids are unique: the owner pops
 #pragma unroll
-      for (int q = 0; q + 1 < MV_MAX_TOPK; ++q) {
+      for (int q = 0; q + 1 < SM; ++q) {
         lv[q] = lv[q + 1];
         li[q] = li[q + 1];
       }
-      lv[MV_MAX_TOPK - 1] = -INFINITY;
-      li[MV_MAX_TOPK - 1] = INT_MAX;
+      lv[SM - 1] = -INFINITY;
+      li[SM - 1] = INT_MAX;
     }
     if (tid == 0) {
       const size_t o = static_cast<size_t>(b) * p.ld_topk + static_cast<size_t>(k) * smax + r;
@@ -550,7 +549,9 @@ MV_API int mv_medusa_head_topk(int dt, int B, int d, int V, int K, const int* s_
   }
   hipStream_t st = as_stream(stream);
   MV_TRY(launch_gemv<1>(dt, p, K, st));
-  heads_merge_kernel<<<K * B, kMergeThreads, 0, st>>>(p);
+  if (s_max <= 4) heads_merge_kernel<4><<<K * B, kMergeThreads, 0, st>>>(p);
+  else if (s_max <= 8) heads_merge_kernel<8><<<K * B, kMergeThreads, 0, st>>>(p);
+  else heads_merge_kernel<MV_MAX_TOPK><<<K * B, kMergeThreads, 0, st>>>(p);
   return launch_status();
 }
 

@@ -126,7 +126,7 @@ class VerifyStep:
             calls["tree"] = wrap("mv_build_tree_mask", lib.mv_build_tree_mask, N, _p(self.parents),
                                  0, 0, 0, None, None, _p(self.tree["anc_mask"]),
                                  _p(self.tree["depth"]), None, _p(self.status), st)
-            tokens = inp["node_tokens"]
+            tokens = inp.get("node_tokens")
         else:
             calls["tree"] = wrap("mv_build_tree_mask", lib.mv_build_tree_mask, N, _p(self.parents),
                                  B, D, s_max, self._s_depth, _p(self.cand),
