@@ -14,7 +14,8 @@
 // takes the N tree keys, where the per-node ancestor bitmask replaces the dense mask.  Per
 // 64-key tile:
 //   * K and V arrive with coalesced 16-byte loads one tile ahead (registers) and are stored
-//     row-major in LDS with a padded pitch, so every operand read is bank-conflict free;
+//     row-major in LDS, each with a padded pitch chosen so that its operand reads are
+//     bank-conflict free;
 //   * S^T = K Q^T: two 32x32 output tiles of v_mfma_f32_32x32x16_bf16 per wave; in that output
 //     layout a lane holds 32 keys of one query, so the softmax max/sum need one cross-lane
 //     step (lanes l and l+32);
@@ -22,7 +23,8 @@
 //     as one FMA and a raw v_exp_f32 per score; the O rescale is skipped when no lane's max
 //     moved;
 //   * O^T += V^T P^T with P rounded to bf16 (v_cvt_pk_bf16_f32) and fp32 accumulation; the V^T
-//     operand is gathered from the row-major V tile with 16-bit LDS reads.
+//     operand comes from the row-major V tile through transposed LDS reads
+//     (ds_read_b64_tr_b16, two per operand).
 // A second kernel merges the chunk partials with their (max, sum) pairs.
 //
 // fp32 path: a vector-ALU kernel, one wave per query row, no chunking (the fp32 configuration
@@ -73,18 +75,23 @@ __device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool re
 
 constexpr int kKT = 64;  // keys per tile
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
 template <int DH, int NWV>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void tree_attn_bf16_kernel(const AttnParams p) {
   constexpr int NT = NWV * 64;
-  constexpr int KP = DH + 8;    // K and V tile pitch (elements): conflict-free LDS reads
+  constexpr int KP = DH + 8;    // K tile pitch (elements): conflict-free 16-byte reads
+  constexpr int VKP = DH + 32;  // V tile pitch: conflict-free transposed reads (see below)
   constexpr int KS = DH / 16;   // k-steps of one S^T MFMA chain
   constexpr int DB = DH / 32;   // 32-wide blocks of the head dimension
   constexpr int DG = DH / 8;    // 16-byte pieces per key row
   constexpr int PPT = kKT * DG / NT;
   static_assert((kKT * DG) % NT == 0, "tile pieces must split evenly");
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKT * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKT * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKT * VKP];
 
   // XCD-aware order: consecutive logical tiles (the query tiles of one KV chunk) run on one XCD.
   const int per = (p.total + kXcds - 1) / kXcds;
@@ -160,7 +167,7 @@ void tree_attn_bf16_kernel(const AttnParams p) {
     for (int i = 0; i < PPT; ++i) {
       const int pc = tid + i * NT, key = pc / DG, dg = pc % DG;
       *reinterpret_cast<uint4*>(&Ks[buf][key * KP + dg * 8]) = kr[i];
-      *reinterpret_cast<uint4*>(&Vs[buf][key * KP + dg * 8]) = vr[i];
+      *reinterpret_cast<uint4*>(&Vs[buf][key * VKP + dg * 8]) = vr[i];
     }
   };
 
@@ -264,13 +271,19 @@ void tree_attn_bf16_kernel(const AttnParams p) {
                                     pack_bf16x2(sv[st][o + 6], sv[st][o + 7]));
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          // A operand of O^T += V^T P^T: lane (dim d = 32*db + l32, group half) supplies
-          // V[key][d] for the 8 keys whose probabilities it holds in pw.
-          const uint16_t* vcol = &Vs[buf][(st * 32 + hf * 16 + 4 * half) * KP + db * 32 + l32];
-          bf16x8 a;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            a[e] = __builtin_bit_cast(__bf16, vcol[(8 * (e >> 2) + (e & 3)) * KP]);
+          // A operand of O^T += V^T P^T: lane (dim 32*db + l32, key group half) needs V[key][dim]
+          // for the 8 keys whose probabilities it holds in pw.  Two transposed LDS reads
+          // (ds_read_b64_tr_b16): in each 16-lane group, output lane j gets element j%4 of the
+          // 4-element read of group lane 4e + j/4, so group lane i reads dims
+          // 16*(G&1) + 4*(i&3) .. +3 of key row 4*half + i/4 (and that row + 8).  With the
+          // V pitch of DH+32 elements the 4 rows x 4 column chunks of two groups land on 64
+          // distinct banks.
+          const int G = lane >> 4, il = lane & 15;
+          const uint16_t* vp = &Vs[buf][(st * 32 + hf * 16 + 4 * half + (il >> 2)) * VKP + db * 32 + 16 * (G & 1) + 4 * (il & 3)];
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 8 * VKP));
+          const v8i16 a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, a16);
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pw), oacc[db], 0, 0, 0);
         }
       }
