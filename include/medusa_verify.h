@@ -117,8 +117,9 @@ MV_API int mv_version(void);
  *             logits by lower token id.  Slots r >= s_k hold id -1 and value -inf.
  *   lse       [B, K] fp32 natural-log log-sum-exp of each head's logits, or NULL.
  *   ws        workspace from mv_medusa_heads_workspace(dt, B, d, V, K, s_max).  The residual
- *             call leaves the head input there for the projection call, so the two calls of
- *             one step must get the same ws (mv_medusa_heads does both).
+ *             call leaves the head input there for the projection, the projection leaves its
+ *             per-block partials there for the selection, so the calls of one step must get
+ *             the same ws (mv_medusa_heads does all three).
  * Values are accumulated in fp32.  With bf16 weights, h_k stays fp32: the projection feeds it
  * to the bf16 matrix cores as the sum of two bf16 numbers (high part + remainder), which keeps
  * about 16 significant bits of h_k in every product.
@@ -128,9 +129,17 @@ MV_API size_t mv_medusa_heads_workspace(int dt, int B, int d, int V, int K, int 
 MV_API int mv_medusa_residual(int dt, int B, int d, int K, const void* h, const void* w_res,
                        float* hk, void* ws, size_t ws_bytes, void* stream);
 
-MV_API int mv_medusa_head_topk(int dt, int B, int d, int V, int K, const int* s_per_head, int s_max,
-                        const void* w_head, void* logits, int32_t* topk_ids, float* topk_vals,
-                        int ld_topk, float* lse, void* ws, size_t ws_bytes, void* stream);
+/* The projection (streams W_head once; per-32-row block top-s and (max, sum exp) partials go to
+ * ws; logits are written only when `logits` is not NULL) and the selection (merges those
+ * partials into topk_ids / topk_vals / lse).  They are two calls so that the weight stream can
+ * be timed on its own; both need the same ws, after mv_medusa_residual. */
+MV_API int mv_medusa_head_project(int dt, int B, int d, int V, int K, const int* s_per_head,
+                                  int s_max, const void* w_head, void* logits, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+MV_API int mv_medusa_head_select(int dt, int B, int d, int V, int K, const int* s_per_head,
+                                 int s_max, int32_t* topk_ids, float* topk_vals, int ld_topk,
+                                 float* lse, void* ws, size_t ws_bytes, void* stream);
 
 MV_API int mv_medusa_heads(int dt, int B, int d, int V, int K, const int* s_per_head, int s_max,
                     const void* h, const void* w_res, const void* w_head, float* hk,

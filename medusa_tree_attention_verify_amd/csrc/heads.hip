@@ -122,7 +122,7 @@ __device__ void residual_epilogue(const GemvParams& p, int k, int row0, float (*
 // independent loads: every thread folds its candidates into a sorted register list of SM
 // entries (SM >= s_max) and an online (max, sum); the s_k winners are then drawn from the
 // list heads, one workgroup argmax per rank.
-constexpr int kMergeThreads = 256;
+constexpr int kMergeThreads = 1024;
 
 template <int SM>
 __device__ __forceinline__ void list_insert(float (&lv)[SM], int (&li)[SM], float v, int i) {
@@ -157,19 +157,38 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(const GemvPa
   const int n = nrb * smax;
   const int* pidx = p.pidx + base * smax;
   const float* pval = p.pval + base * smax;
-#pragma unroll 4
-  for (int c = tid; c < n; c += kMergeThreads) {
-    const int ii = pidx[c];
-    const float vv = pval[c];
-    if (c % smax < s && ii >= 0) list_insert<SM>(lv, li, vv, ii);
+  // Eight candidates per thread are requested before any is used: the partials were written
+  // from every XCD, so each load is a trip to memory and must not wait for the previous one.
+  constexpr int BATCH = 8;
+  for (int c0 = tid; c0 < n; c0 += kMergeThreads * BATCH) {
+    int ii[BATCH];
+    float vv[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int c = c0 + u * kMergeThreads;
+      ii[u] = c < n ? pidx[c] : -1;
+      vv[u] = c < n ? pval[c] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u)
+      if (ii[u] >= 0 && (c0 + u * kMergeThreads) % smax < s) list_insert<SM>(lv, li, vv[u], ii[u]);
   }
   float m = -INFINITY, l = 0.f;
-#pragma unroll 4
-  for (int j = tid; j < nrb; j += kMergeThreads) {
-    const float mb = p.pm[base + j], lb = p.pl[base + j];
-    const float mn = fmaxf(m, mb);
-    l = (m == -INFINITY ? 0.f : l * expf(m - mn)) + lb * expf(mb - mn);
-    m = mn;
+  for (int j0 = tid; j0 < nrb; j0 += kMergeThreads * BATCH) {
+    float mb[BATCH], lb[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int j = j0 + u * kMergeThreads;
+      mb[u] = j < nrb ? p.pm[base + j] : -INFINITY;
+      lb[u] = j < nrb ? p.pl[base + j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      if (mb[u] == -INFINITY) continue;
+      const float mn = fmaxf(m, mb[u]);
+      l = (m == -INFINITY ? 0.f : l * expf(m - mn)) + lb[u] * expf(mb[u] - mn);
+      m = mn;
+    }
   }
   const float M = block_max(m, sv);
   const float Lsum = block_sum(m == -INFINITY ? 0.f : l * expf(m - M), sv);
@@ -517,25 +536,19 @@ MV_API int mv_medusa_residual(int dt, int B, int d, int K, const void* h, const 
   return launch_gemv<0>(dt, p, K, st);
 }
 
-MV_API int mv_medusa_head_topk(int dt, int B, int d, int V, int K, const int* s_per_head,
-                               int s_max, const void* w_head, void* logits, int32_t* topk_ids,
-                               float* topk_vals, int ld_topk, float* lse, void* ws,
-                               size_t ws_bytes, void* stream) {
-  MV_TRY(check_common(dt, B, d, K));
-  if (V < 1 || !s_per_head || !w_head || !topk_ids || !topk_vals) return MV_ERR_INVALID_ARG;
+static int check_select(int V, int K, const int* s_per_head, int s_max) {
+  if (V < 1 || !s_per_head) return MV_ERR_INVALID_ARG;
   if (s_max < 1 || s_max > MV_MAX_TOPK || s_max > V) return MV_ERR_UNSUPPORTED;
   for (int k = 0; k < K; ++k)
     if (s_per_head[k] < 1 || s_per_head[k] > s_max) return MV_ERR_INVALID_ARG;
-  if (ld_topk == 0) ld_topk = K * s_max;
-  if (ld_topk < K * s_max) return MV_ERR_INVALID_ARG;
-  HeadsLayout need = heads_layout(nullptr, dt, B, d, V, K, s_max);
-  MV_TRY(check_ws(ws, ws_bytes, need.bytes));
-  HeadsLayout L = heads_layout(ws, dt, B, d, V, K, s_max);
+  return MV_OK;
+}
+
+static GemvParams head_params(int dt, int B, int d, int V, int K, const int* s_per_head,
+                              int s_max, const HeadsLayout& L) {
   GemvParams p{};
   p.B = B; p.d = d; p.R = V; p.K = K; p.T = d / 32; p.nrb = ceil_div(V, kRows);
-  p.W = w_head; p.logits = logits;
   p.pval = L.pval; p.pidx = L.pidx; p.pm = L.pm; p.pl = L.pl;
-  p.topk_ids = topk_ids; p.topk_vals = topk_vals; p.ld_topk = ld_topk; p.lse = lse;
   p.s_max = s_max;
   for (int k = 0; k < K; ++k) p.s[k] = s_per_head[k];
   if (dt == MV_BF16) {
@@ -547,8 +560,39 @@ MV_API int mv_medusa_head_topk(int dt, int B, int d, int V, int K, const int* s_
     p.x_bstride = static_cast<long long>(K) * d;
     p.x_hstride = d;
   }
+  return p;
+}
+
+MV_API int mv_medusa_head_project(int dt, int B, int d, int V, int K, const int* s_per_head,
+                                  int s_max, const void* w_head, void* logits, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  MV_TRY(check_common(dt, B, d, K));
+  MV_TRY(check_select(V, K, s_per_head, s_max));
+  if (!w_head) return MV_ERR_INVALID_ARG;
+  MV_TRY(check_ws(ws, ws_bytes, heads_layout(nullptr, dt, B, d, V, K, s_max).bytes));
+  const HeadsLayout L = heads_layout(ws, dt, B, d, V, K, s_max);
+  GemvParams p = head_params(dt, B, d, V, K, s_per_head, s_max, L);
+  p.W = w_head;
+  p.logits = logits;
+  return launch_gemv<1>(dt, p, K, as_stream(stream));
+}
+
+MV_API int mv_medusa_head_select(int dt, int B, int d, int V, int K, const int* s_per_head,
+                                 int s_max, int32_t* topk_ids, float* topk_vals, int ld_topk,
+                                 float* lse, void* ws, size_t ws_bytes, void* stream) {
+  MV_TRY(check_common(dt, B, d, K));
+  MV_TRY(check_select(V, K, s_per_head, s_max));
+  if (!topk_ids || !topk_vals) return MV_ERR_INVALID_ARG;
+  if (ld_topk == 0) ld_topk = K * s_max;
+  if (ld_topk < K * s_max) return MV_ERR_INVALID_ARG;
+  MV_TRY(check_ws(ws, ws_bytes, heads_layout(nullptr, dt, B, d, V, K, s_max).bytes));
+  const HeadsLayout L = heads_layout(ws, dt, B, d, V, K, s_max);
+  GemvParams p = head_params(dt, B, d, V, K, s_per_head, s_max, L);
+  p.topk_ids = topk_ids;
+  p.topk_vals = topk_vals;
+  p.ld_topk = ld_topk;
+  p.lse = lse;
   hipStream_t st = as_stream(stream);
-  MV_TRY(launch_gemv<1>(dt, p, K, st));
   if (s_max <= 4) heads_merge_kernel<4><<<K * B, kMergeThreads, 0, st>>>(p);
   else if (s_max <= 8) heads_merge_kernel<8><<<K * B, kMergeThreads, 0, st>>>(p);
   else heads_merge_kernel<MV_MAX_TOPK><<<K * B, kMergeThreads, 0, st>>>(p);
@@ -567,8 +611,10 @@ MV_API int mv_medusa_heads(int dt, int B, int d, int V, int K, const int* s_per_
   if (ld_topk != 0 && ld_topk < K * s_max) return MV_ERR_INVALID_ARG;
   MV_TRY(check_ws(ws, ws_bytes, heads_layout(nullptr, dt, B, d, V, K, s_max).bytes));
   MV_TRY(mv_medusa_residual(dt, B, d, K, h, w_res, hk, ws, ws_bytes, stream));
-  return mv_medusa_head_topk(dt, B, d, V, K, s_per_head, s_max, w_head, logits, topk_ids,
-                             topk_vals, ld_topk, lse, ws, ws_bytes, stream);
+  MV_TRY(mv_medusa_head_project(dt, B, d, V, K, s_per_head, s_max, w_head, logits, ws, ws_bytes,
+                                stream));
+  return mv_medusa_head_select(dt, B, d, V, K, s_per_head, s_max, topk_ids, topk_vals, ld_topk,
+                               lse, ws, ws_bytes, stream);
 }
 
 MV_API int mv_topk_rows(int dt, int R, int V, int s, const void* x, long long ldx, int32_t* ids,

@@ -1,9 +1,9 @@
 """One Medusa tree-verification step on the GPU: heads -> tree -> attention -> acceptance.
 
 All buffers (outputs and workspaces) are allocated once in ``VerifyStep.__init__``.
-``bind(inp)`` turns one set of device inputs into five pre-marshalled C-ABI calls (heads
-residual, heads projection, tree, attention, acceptance), so a step costs five ctypes calls
-and no Python-side checks or allocation.  The candidate tokens of depth k come from Medusa
+``bind(inp)`` turns one set of device inputs into six pre-marshalled C-ABI calls (heads
+residual, heads projection, heads selection, tree, attention, acceptance), so a step costs
+six ctypes calls and no Python-side checks or allocation.  The candidate tokens of depth k come from Medusa
 head k; with ``lm_width > 0`` the depth-1 candidates are instead the top ``lm_width`` tokens
 of the target's first row (the base model's own head, which predicts the next token) and
 the Medusa heads supply depths 2..D.
@@ -23,7 +23,7 @@ def _p(t: Optional[torch.Tensor]):
 
 
 class VerifyStep:
-    PARTS = ("heads_residual", "heads_projection", "tree", "attention", "accept")
+    PARTS = ("heads_residual", "heads_projection", "heads_select", "tree", "attention", "accept")
 
     def __init__(self, *, parents: Sequence[int], depth_widths: Sequence[int],
                  dtype: torch.dtype, B: int, Hq: int, Hkv: int, dh: int, max_L: int,
@@ -105,11 +105,13 @@ class VerifyStep:
             off = 1 if self.lm_width else 0
             ld = D * s_max
             esz = 4
-            proj = wrap("mv_medusa_head_topk", lib.mv_medusa_head_topk, self.dt, B, d, Vh, K,
-                        self._s_heads, s_max, _p(inp["w_head"]), None,
-                        self.cand.data_ptr() + off * s_max * esz,
-                        self.cand_vals.data_ptr() + off * s_max * esz, ld, _p(self.head_lse),
-                        wsp, wsn, st)
+            proj = wrap("mv_medusa_head_project", lib.mv_medusa_head_project, self.dt, B, d, Vh,
+                        K, self._s_heads, s_max, _p(inp["w_head"]), None, wsp, wsn, st)
+            calls["heads_select"] = wrap("mv_medusa_head_select", lib.mv_medusa_head_select,
+                                         self.dt, B, d, Vh, K, self._s_heads, s_max,
+                                         self.cand.data_ptr() + off * s_max * esz,
+                                         self.cand_vals.data_ptr() + off * s_max * esz, ld,
+                                         _p(self.head_lse), wsp, wsn, st)
             if self.lm_width:
                 tgt = inp["target"]
                 R1, Vt = tgt.shape[1], tgt.shape[2]
@@ -160,3 +162,24 @@ class VerifyStep:
         """One whole step on ``inp`` (binds, then runs the five calls in order)."""
         for c in self.sequence(self.bind(inp)):
             c()
+
+    def capture(self, inp: Dict[str, torch.Tensor]) -> "torch.cuda.CUDAGraph":
+        """A HIP graph of one whole step on ``inp`` (replay with ``graph.replay()``).
+
+        The calls are bound inside the capture so that they are enqueued on the capture
+        stream; the step allocates nothing and issues no memset, so every replay repeats
+        exactly the kernels of an eager step on the same buffers."""
+        calls = None
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream(device=self.device)
+        s.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(s):
+            calls = self.sequence(self.bind(inp))   # warm-up on the side stream
+            for c in calls:
+                c()
+        torch.cuda.current_stream(self.device).wait_stream(s)
+        torch.cuda.synchronize(self.device)
+        with torch.cuda.graph(g):
+            for c in self.sequence(self.bind(inp)):
+                c()
+        return g

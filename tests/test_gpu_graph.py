@@ -1,0 +1,54 @@
+"""A whole verify step captured as one HIP graph: every replay equals the eager step.
+
+Replays are interleaved with eager work on the same buffers and with synchronizations, and
+each replay's outputs are compared with the eager result (bit-exact: same kernels, same
+inputs)."""
+import numpy as np
+import pytest
+import torch
+
+from medusa_tree_attention_verify_amd import workloads as W
+from medusa_tree_attention_verify_amd.step import VerifyStep
+from tests.gpu_util import dev, dev_i32, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _outputs(step):
+    return [t.clone() for t in (step.cand, step.tree["node_tokens"], step.attn_out, step.attn_lse,
+                                step.acc["accept_len"], step.acc["out_tokens"])]
+
+
+def test_graph_replays_match_eager():
+    require_gpu()
+    wl = W.WORKLOADS["c2"].scaled(d=512, V=3000, prefix=(700, 700))
+    dt = torch.bfloat16
+    xh = W.gen_heads(wl, 9)
+    xa = W.gen_attention(wl, 9)
+    target = W.round_bf16(W.gen_target_logits(wl, 9))
+    step = VerifyStep(parents=wl.parents, depth_widths=wl.depth_widths, dtype=dt, B=wl.B,
+                      Hq=wl.Hq, Hkv=wl.Hkv, dh=wl.dh, max_L=int(xa["prefix_len"].max()),
+                      heads={"d": wl.d, "V": wl.V, "K": wl.K, "widths": list(wl.head_widths)},
+                      accept="greedy", V=wl.accept_V)
+    inp = {"h": dev(xh["h"], dt), "w_res": dev(xh["w_res"], dt), "w_head": dev(xh["w_head"], dt),
+           "q": dev(xa["q"], dt), "k_cache": dev(xa["k_cache"], dt),
+           "v_cache": dev(xa["v_cache"], dt), "prefix_len": dev_i32(xa["prefix_len"]),
+           "target": dev(target, dt)}
+    step.run(inp)
+    torch.cuda.synchronize()
+    ref = _outputs(step)
+    g = step.capture(inp)
+    for rep in range(4):
+        # eager work in between: clobber the outputs, then replay the graph
+        for t in (step.cand, step.tree["node_tokens"], step.acc["accept_len"]):
+            t.fill_(-7)
+        step.attn_out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(_outputs(step), ref):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
+        if rep == 1:
+            step.run(inp)           # an eager step between replays
+            torch.cuda.synchronize()
+    assert int(step.status.item()) == 0

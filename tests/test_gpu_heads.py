@@ -79,7 +79,8 @@ def test_heads_70b_width_batch8():
 
 
 def test_split_calls_match_fused_and_repeat():
-    """mv_medusa_residual + mv_medusa_head_topk (twice) equal mv_medusa_heads."""
+    """mv_medusa_residual + (mv_medusa_head_project + mv_medusa_head_select) twice equal
+    mv_medusa_heads."""
     require_gpu()
     wl = W.WORKLOADS["c2"].scaled(B=2, d=512, V=3000, K=4, head_widths=(4, 3, 2, 1))
     x = W.gen_heads(wl, 11)
