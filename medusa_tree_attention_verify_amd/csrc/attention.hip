@@ -145,7 +145,7 @@ void tree_attn_bf16_kernel(const AttnParams p) {
     }
   };
   // Two register sets of prefetched K/V pieces: tile t+2 is requested while tile t computes.
-  uint4 kr0[PPT], vr0[PPT];
+  uint4 kr0[PPT], vr0[PPT], kr1[PPT], vr1[PPT];
   auto gload = [&](int t, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
     int row0 = 0, nv = 0;
     if (t < ntiles) tile_rows(t, row0, nv);
@@ -289,17 +289,25 @@ void tree_attn_bf16_kernel(const AttnParams p) {
       }
   };
 
-  // Pipeline: LDS holds tile t (computing) and receives tile t+1 at the end of iteration t;
-  // the registers hold tile t+1, requested at the start of iteration t.
+  // Pipeline: LDS holds tile t (computing) and tile t+1 (written at the end of iteration t);
+  // the registers hold tile t+1 (arrived) and tile t+2 (requested at the start of
+  // iteration t), so every load has two tiles of compute to arrive.
   gload(0, kr0, vr0);
+  gload(1, kr1, vr1);
   swrite(0, kr0, vr0);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) gload(t + 1, kr0, vr0);
+  int t = 0;
+  for (; t + 2 <= ntiles; t += 2) {
+    gload(t + 2, kr0, vr0);
     compute(t);
-    if (t + 1 < ntiles) swrite((t + 1) & 1, kr0, vr0);
+    swrite((t + 1) & 1, kr1, vr1);
+    __syncthreads();
+    gload(t + 3, kr1, vr1);
+    compute(t + 1);
+    swrite(t & 1, kr0, vr0);
     __syncthreads();
   }
+  if (t < ntiles) compute(t);
 
   if (!qvalid) return;
   // Output layout of O^T: lane holds query l32, dims db*32 + 8*(v/4) + 4*half + v%4.
