@@ -231,9 +231,7 @@ __global__ __launch_bounds__(256) void residual_segsum_kernel(const AcceptParams
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     double v = wave_sum_f64(vals[q]);
-    int mi = idx[q];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mi = max(mi, __shfl_xor(mi, o));
+    const int mi = wave_max_i(idx[q]);
     __syncthreads();
     if (lane == 0) { sd[w] = v; smx[w] = mi; }
     __syncthreads();
@@ -312,9 +310,7 @@ __global__ __launch_bounds__(256) void residual_sample_kernel(const AcceptParams
     const double start = sub[tid];
     const bool cross = a0 < a1 && start + mine > t;
     // the first thread whose range crosses t scans it
-    int first = cross ? tid : INT_MAX;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o));
+    const int first = wave_min_i(cross ? tid : INT_MAX);
     __syncthreads();
     if ((tid & 63) == 0) sh[tid >> 6] = first;
     __syncthreads();

@@ -234,7 +234,10 @@ void tree_attn_bf16_kernel(const AttnParams p) {
           tmax = fmaxf(tmax, sv[st][v]);
         }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    {  // lanes l and l^32 hold the two key halves of one query
+      const LanePair t2 = swap32(__float_as_uint(tmax));
+      tmax = fmaxf(__uint_as_float(t2.a), __uint_as_float(t2.b));
+    }
     const float c2 = p.scale_log2;
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -248,7 +251,10 @@ void tree_attn_bf16_kernel(const AttnParams p) {
         sv[st][v] = __builtin_amdgcn_exp2f(fmaf(sv[st][v], c2, -mc));
         lsum += sv[st][v];
       }
-    lsum += __shfl_xor(lsum, 32);
+    {
+      const LanePair t2 = swap32(__float_as_uint(lsum));
+      lsum = __uint_as_float(t2.a) + __uint_as_float(t2.b);
+    }
     l_run = l_run * alpha + lsum;
     m_run = m_new;
     // Keep the P.V operand reads below the softmax: hoisting them above it would keep 16

@@ -120,9 +120,11 @@ __device__ void residual_epilogue(const GemvParams& p, int k, int row0, float (*
 // agent-scope release/acquire per workgroup, which on this multi-XCD part writes back and
 // invalidates the XCD's L2 for every workgroup.  One pass over the partials with coalesced,
 // independent loads: every thread folds its candidates into a sorted register list of SM
-// entries (SM >= s_max) and an online (max, sum); the s_k winners are then drawn from the
-// list heads, one workgroup argmax per rank.
-constexpr int kMergeThreads = 1024;
+// entries (SM >= s_max) and an online (max, sum); each wave then draws its top s_k from the
+// list heads and merges its (max, sum) pairs with register butterflies, and after a single
+// barrier wave 0 draws the final s_k from the waves' winners.
+constexpr int kMergeThreads = 512;
+constexpr int kMergeWaves = kMergeThreads / 64;
 
 template <int SM>
 __device__ __forceinline__ void list_insert(float (&lv)[SM], int (&li)[SM], float v, int i) {
@@ -140,10 +142,56 @@ __device__ __forceinline__ void list_insert(float (&lv)[SM], int (&li)[SM], floa
 }
 
 template <int SM>
+__device__ __forceinline__ void list_pop(float (&lv)[SM], int (&li)[SM]) {
+#pragma unroll
+  for (int q = 0; q + 1 < SM; ++q) {
+    lv[q] = lv[q + 1];
+    li[q] = li[q + 1];
+  }
+  lv[SM - 1] = -INFINITY;
+  li[SM - 1] = INT_MAX;
+}
+
+// Log-sum-exp merge of two partial (max, sum of exp(x - max)) pairs; symmetric in its operands,
+// so the butterfly below leaves the same bits in every lane.
+__device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    l = l2;
+    return;
+  }
+  const float mn = fmaxf(m, m2);
+  l = l * expf(m - mn) + l2 * expf(m2 - mn);
+  m = mn;
+}
+
+__device__ __forceinline__ void wave_ml_merge(float& m, float& l) {
+  auto step = [&](uint32_t om, uint32_t ol) { ml_merge(m, l, __uint_as_float(om), __uint_as_float(ol)); };
+  step(dpp_u32<kDppXor1>(__float_as_uint(m)), dpp_u32<kDppXor1>(__float_as_uint(l)));
+  step(dpp_u32<kDppXor2>(__float_as_uint(m)), dpp_u32<kDppXor2>(__float_as_uint(l)));
+  step(dpp_u32<kDppHalfMirror>(__float_as_uint(m)), dpp_u32<kDppHalfMirror>(__float_as_uint(l)));
+  step(dpp_u32<kDppMirror>(__float_as_uint(m)), dpp_u32<kDppMirror>(__float_as_uint(l)));
+  {
+    const LanePair tm = swap16(__float_as_uint(m)), tl = swap16(__float_as_uint(l));
+    m = __uint_as_float(tm.a);
+    l = __uint_as_float(tl.a);
+    step(tm.b, tl.b);
+  }
+  {
+    const LanePair tm = swap32(__float_as_uint(m)), tl = swap32(__float_as_uint(l));
+    m = __uint_as_float(tm.a);
+    l = __uint_as_float(tl.a);
+    step(tm.b, tl.b);
+  }
+}
+
+template <int SM>
 __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(const GemvParams p) {
-  __shared__ float sv[kMergeThreads / 64];
-  __shared__ int si[kMergeThreads / 64];
-  const int tid = threadIdx.x;
+  __shared__ float wtv[kMergeWaves][MV_MAX_TOPK];
+  __shared__ int wti[kMergeWaves][MV_MAX_TOPK];
+  __shared__ float wm[kMergeWaves], wl[kMergeWaves];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int k = blockIdx.x % p.K, b = blockIdx.x / p.K;
   const int nrb = p.nrb, s = p.s[k], smax = p.s_max;
   const size_t base = (static_cast<size_t>(k) * p.B + b) * nrb;
@@ -157,12 +205,14 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(const GemvPa
   const int n = nrb * smax;
   const int* pidx = p.pidx + base * smax;
   const float* pval = p.pval + base * smax;
-  // Eight candidates per thread are requested before any is used: the partials were written
-  // from every XCD, so each load is a trip to memory and must not wait for the previous one.
-  constexpr int BATCH = 8;
-  for (int c0 = tid; c0 < n; c0 += kMergeThreads * BATCH) {
+  // Every candidate and (max, sum) pair a thread merges is requested before any is used: the
+  // partials were written from every XCD, so each load is a trip to memory and must not wait
+  // for the previous one (with V = 32000 and s_max = 4 one pass of 8 + 2 loads covers all).
+  constexpr int BATCH = 8, MBATCH = 2;
+  float m = -INFINITY, l = 0.f;
+  for (int c0 = tid, j0 = tid; c0 < n || j0 < nrb; c0 += kMergeThreads * BATCH, j0 += kMergeThreads * MBATCH) {
     int ii[BATCH];
-    float vv[BATCH];
+    float vv[BATCH], mb[MBATCH], lb[MBATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int c = c0 + u * kMergeThreads;
@@ -170,49 +220,74 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(const GemvPa
       vv[u] = c < n ? pval[c] : -INFINITY;
     }
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u)
-      if (ii[u] >= 0 && (c0 + u * kMergeThreads) % smax < s) list_insert<SM>(lv, li, vv[u], ii[u]);
-  }
-  float m = -INFINITY, l = 0.f;
-  for (int j0 = tid; j0 < nrb; j0 += kMergeThreads * BATCH) {
-    float mb[BATCH], lb[BATCH];
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
+    for (int u = 0; u < MBATCH; ++u) {
       const int j = j0 + u * kMergeThreads;
       mb[u] = j < nrb ? p.pm[base + j] : -INFINITY;
       lb[u] = j < nrb ? p.pl[base + j] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      if (mb[u] == -INFINITY) continue;
-      const float mn = fmaxf(m, mb[u]);
-      l = (m == -INFINITY ? 0.f : l * expf(m - mn)) + lb[u] * expf(mb[u] - mn);
-      m = mn;
+    for (int u = 0; u < BATCH; ++u)
+      if (ii[u] >= 0 && (c0 + u * kMergeThreads) % smax < s) list_insert<SM>(lv, li, vv[u], ii[u]);
+#pragma unroll
+    for (int u = 0; u < MBATCH; ++u) ml_merge(m, l, mb[u], lb[u]);
+  }
+  // per wave: top s (token ids are unique, so exactly one lane owns each winner and pops it)
+  for (int r = 0; r < s; ++r) {
+    float bv = lv[0];
+    int bi = li[0];
+    wave_argbest(bv, bi);
+    if (bi != INT_MAX && li[0] == bi) list_pop<SM>(lv, li);
+    if (lane == 0) {
+      wtv[w][r] = bv;
+      wti[w][r] = bi;
     }
   }
-  const float M = block_max(m, sv);
-  const float Lsum = block_sum(m == -INFINITY ? 0.f : l * expf(m - M), sv);
-  for (int r = 0; r < smax; ++r) {
-    float bv = r < s ? lv[0] : -INFINITY;
-    int bi = r < s ? li[0] : INT_MAX;
-    block_argbest(bv, bi, sv, si);
-    if (r < s && li[0] == bi && bi != INT_MAX) {  // token ids are unique: the owner pops
+  wave_ml_merge(m, l);
+  if (lane == 0) {
+    wm[w] = m;
+    wl[w] = l;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  // wave 0: at most kMergeWaves * s <= 128 candidates, two per lane, sorted
+  float cv[2];
+  int ci[2];
 #pragma unroll
-      for (int q = 0; q + 1 < SM; ++q) {
-        lv[q] = lv[q + 1];
-        li[q] = li[q + 1];
-      }
-      lv[SM - 1] = -INFINITY;
-      li[SM - 1] = INT_MAX;
+  for (int q = 0; q < 2; ++q) {
+    const int c = lane + 64 * q;
+    const bool ok = c < kMergeWaves * s;
+    cv[q] = ok ? wtv[c / max(s, 1)][c % max(s, 1)] : -INFINITY;
+    ci[q] = ok ? wti[c / max(s, 1)][c % max(s, 1)] : INT_MAX;
+  }
+  if (kv_better(cv[1], ci[1], cv[0], ci[0])) {
+    const float tv = cv[0];
+    const int ti = ci[0];
+    cv[0] = cv[1];
+    ci[0] = ci[1];
+    cv[1] = tv;
+    ci[1] = ti;
+  }
+  for (int r = 0; r < smax; ++r) {
+    float bv = r < s ? cv[0] : -INFINITY;
+    int bi = r < s ? ci[0] : INT_MAX;
+    wave_argbest(bv, bi);
+    if (r < s && bi != INT_MAX && ci[0] == bi) {
+      cv[0] = cv[1];
+      ci[0] = ci[1];
+      cv[1] = -INFINITY;
+      ci[1] = INT_MAX;
     }
-    if (tid == 0) {
+    if (lane == 0) {
       const size_t o = static_cast<size_t>(b) * p.ld_topk + static_cast<size_t>(k) * smax + r;
       const bool ok = r < s && bi != INT_MAX;
       p.topk_ids[o] = ok ? bi : -1;
       p.topk_vals[o] = ok ? bv : -INFINITY;
     }
   }
-  if (tid == 0 && p.lse) p.lse[static_cast<size_t>(b) * p.K + k] = M + logf(Lsum);
+  float M = lane < kMergeWaves ? wm[lane] : -INFINITY;
+  float Ls = lane < kMergeWaves ? wl[lane] : 0.f;
+  wave_ml_merge(M, Ls);
+  if (lane == 0 && p.lse) p.lse[static_cast<size_t>(b) * p.K + k] = M + logf(Ls);
 }
 
 // ---- projection epilogue: optional logits, per-workgroup top-s and (max, sum exp).

@@ -38,22 +38,84 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// ---- wave64 butterfly reductions with vector-ALU cross-lane moves.  The six exchange steps
+// pair lanes 1 and 2 apart (DPP quad permutations), then mirror 8- and 16-lane rows (DPP row
+// mirrors: after the quad steps every lane of a quad holds the same value, so a mirror pairs
+// distinct quads), then swap 16-lane rows and 32-lane halves (v_permlane16_swap /
+// v_permlane32_swap, which hand each lane its own value and its partner's).  No LDS round
+// trips; every lane ends with the same bits for a commutative operation.  All 64 lanes must be
+// active.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x), CTRL, 0xF, 0xF, false));
+}
+struct LanePair {
+  uint32_t a, b;  // this lane's value and its partner's, in either order
+};
+__device__ __forceinline__ LanePair swap16(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return {r[0], r[1]};
+}
+__device__ __forceinline__ LanePair swap32(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return {r[0], r[1]};
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_allreduce_u32(uint32_t v, Op op) {
+  v = op(v, dpp_u32<kDppXor1>(v));
+  v = op(v, dpp_u32<kDppXor2>(v));
+  v = op(v, dpp_u32<kDppHalfMirror>(v));
+  v = op(v, dpp_u32<kDppMirror>(v));
+  LanePair t = swap16(v);
+  v = op(t.a, t.b);
+  t = swap32(v);
+  return op(t.a, t.b);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return __uint_as_float(wave_allreduce_u32(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+    return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y)));
+  }));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return __uint_as_float(wave_allreduce_u32(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+    return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
+  }));
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+  return static_cast<int>(wave_allreduce_u32(static_cast<uint32_t>(v), [](uint32_t x, uint32_t y) {
+    return static_cast<uint32_t>(max(static_cast<int>(x), static_cast<int>(y)));
+  }));
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+  return static_cast<int>(wave_allreduce_u32(static_cast<uint32_t>(v), [](uint32_t x, uint32_t y) {
+    return static_cast<uint32_t>(min(static_cast<int>(x), static_cast<int>(y)));
+  }));
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  auto step = [](double x, uint32_t lo, uint32_t hi) {
+    return x + __hiloint2double(static_cast<int>(hi), static_cast<int>(lo));
+  };
+  auto lo = [](double x) { return static_cast<uint32_t>(__double2loint(x)); };
+  auto hi = [](double x) { return static_cast<uint32_t>(__double2hiint(x)); };
+  v = step(v, dpp_u32<kDppXor1>(lo(v)), dpp_u32<kDppXor1>(hi(v)));
+  v = step(v, dpp_u32<kDppXor2>(lo(v)), dpp_u32<kDppXor2>(hi(v)));
+  v = step(v, dpp_u32<kDppHalfMirror>(lo(v)), dpp_u32<kDppHalfMirror>(hi(v)));
+  v = step(v, dpp_u32<kDppMirror>(lo(v)), dpp_u32<kDppMirror>(hi(v)));
+  LanePair l = swap16(lo(v)), h = swap16(hi(v));
+  v = __hiloint2double(static_cast<int>(h.a), static_cast<int>(l.a)) + __hiloint2double(static_cast<int>(h.b), static_cast<int>(l.b));
+  l = swap32(lo(v));
+  h = swap32(hi(v));
+  return __hiloint2double(static_cast<int>(h.a), static_cast<int>(l.a)) + __hiloint2double(static_cast<int>(h.b), static_cast<int>(l.b));
 }
 
 // Ordering used by every top-k / argmax of the library: larger value first, equal values by
@@ -68,11 +130,27 @@ __device__ __forceinline__ bool kv_after(float v, int i, float pv, int pi) {
 }
 
 __device__ __forceinline__ void wave_argbest(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float ov = __shfl_xor(v, o);
-    int oi = __shfl_xor(i, o);
-    if (kv_better(ov, oi, v, i)) { v = ov; i = oi; }
+  auto take = [&](uint32_t ov, uint32_t oi) {
+    if (kv_better(__uint_as_float(ov), static_cast<int>(oi), v, i)) {
+      v = __uint_as_float(ov);
+      i = static_cast<int>(oi);
+    }
+  };
+  take(dpp_u32<kDppXor1>(__float_as_uint(v)), dpp_u32<kDppXor1>(static_cast<uint32_t>(i)));
+  take(dpp_u32<kDppXor2>(__float_as_uint(v)), dpp_u32<kDppXor2>(static_cast<uint32_t>(i)));
+  take(dpp_u32<kDppHalfMirror>(__float_as_uint(v)), dpp_u32<kDppHalfMirror>(static_cast<uint32_t>(i)));
+  take(dpp_u32<kDppMirror>(__float_as_uint(v)), dpp_u32<kDppMirror>(static_cast<uint32_t>(i)));
+  {
+    const LanePair tv = swap16(__float_as_uint(v)), ti = swap16(static_cast<uint32_t>(i));
+    v = __uint_as_float(tv.a);
+    i = static_cast<int>(ti.a);
+    take(tv.b, ti.b);
+  }
+  {
+    const LanePair tv = swap32(__float_as_uint(v)), ti = swap32(static_cast<uint32_t>(i));
+    v = __uint_as_float(tv.a);
+    i = static_cast<int>(ti.a);
+    take(tv.b, ti.b);
   }
 }
 
