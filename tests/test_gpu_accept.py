@@ -127,6 +127,34 @@ def test_speculative_serving_shape_full_vocab():
     print("accept lengths", lens.tolist())
 
 
+def test_speculative_serving_full_sampled():
+    """The full batched-serving acceptance shape (64 sequences, vocabulary 128256): the GPU
+    decides every sequence; the oracle recomputes 8 sampled sequences from their own slices of
+    the same inputs (acceptance is independent per sequence)."""
+    require_gpu()
+    wl = W.WORKLOADS["c5"]
+    x = W.gen_speculative(wl, 17)
+    D, parents = wl.D, list(wl.parents)
+    print(f"spec full B={wl.B} V={wl.accept_V}", flush=True)
+    got = ops.accept_paths(L.MV_ACCEPT_SPECULATIVE, dev_i32(parents), dev_i32(x["node_tokens"]),
+                           dev(x["p_target"]), D, draft=dev(x["p_draft"]),
+                           uniforms=dev(x["uniforms"]))
+    torch.cuda.synchronize()
+    g = {k: host(v) for k, v in got.items() if v is not None}
+    for b in (0, 9, 17, 26, 35, 44, 53, 63):
+        sl = slice(b, b + 1)
+        ref = O.accept_speculative(x["p_target"][sl], x["p_draft"][sl], x["node_tokens"][sl], parents,
+                                   x["uniforms"][sl], D)
+        u = x["uniforms"][b, :wl.N].astype(np.float64)
+        assert np.all(np.abs(g["alpha"][b] - ref["alpha"][0]) <= 1e-6)
+        if np.any(np.abs(u - ref["alpha"][0]) < 1e-6):
+            print(f"sequence {b}: near-tie decision, skipped")
+            continue
+        for key in ("accept_len", "path_nodes", "out_tokens"):
+            np.testing.assert_array_equal(g[key][b], ref[key][0], err_msg=f"{key} b={b}")
+        np.testing.assert_array_equal(g["node_accept"][b].astype(bool), ref["node_accept"][0])
+
+
 def test_speculative_batch64_small_vocab():
     require_gpu()
     wl = W.WORKLOADS["c5"].scaled(accept_V=4096)

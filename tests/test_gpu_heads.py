@@ -78,6 +78,29 @@ def test_heads_70b_width_batch8():
     assert ties <= 2
 
 
+def test_heads_70b_full_sampled():
+    """The full 70B-share head shape (d=8192, V=32000, 4 heads, batch 8): the GPU computes every
+    (batch row, head); the oracle recomputes four sampled pairs in fp64, each from its own slice
+    of the same inputs, and their h_k, top-k ids/values and LSE must match."""
+    require_gpu()
+    wl = W.WORKLOADS["c3"]
+    widths = list(wl.head_widths)
+    x = W.gen_heads(wl, 13)
+    print(f"heads full B={wl.B} d={wl.d} V={wl.V} K={wl.K}", flush=True)
+    got = ops.medusa_heads(dev(x["h"], torch.bfloat16), dev(x["w_res"], torch.bfloat16),
+                           dev(x["w_head"], torch.bfloat16), widths, want_hk=True)
+    torch.cuda.synchronize()
+    hk, ids, vals, lse = (host(got[n]) for n in ("hk", "topk_ids", "topk_vals", "lse"))
+    for b, k in ((0, 0), (3, 1), (5, 2), (7, 3)):
+        ref = O.medusa_heads(x["h"][b:b + 1], x["w_res"][k:k + 1], x["w_head"][k:k + 1], [widths[k]])
+        s = widths[k]
+        assert_fp32(hk[b, k], ref["hk"][0, 0], what=f"hk b={b} k={k}")
+        assert_fp32(lse[b, k], ref["lse"][0, 0], atol=1e-3, what=f"lse b={b} k={k}")
+        ties = check_topk(ids[b:b + 1, k:k + 1], ref["logits"], [s])
+        assert ties <= 1
+        assert_fp32(vals[b, k, :s], ref["logits"][0, 0][ids[b, k, :s]], what=f"topk_vals b={b} k={k}")
+
+
 def test_split_calls_match_fused_and_repeat():
     """mv_medusa_residual + (mv_medusa_head_project + mv_medusa_head_select) twice equal
     mv_medusa_heads."""
