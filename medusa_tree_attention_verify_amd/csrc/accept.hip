@@ -29,8 +29,11 @@
 namespace mv {
 namespace {
 
+__device__ __forceinline__ int ceil_div_dev(int a, int b) { return (a + b - 1) / b; }
+
 struct AcceptParams {
   int B, N, V, D, R, S, segLen;
+  int vec4;  // speculative rows may be read as float4 (V, segLen multiples of 4; 16-byte bases)
   const int32_t* parents;
   const int32_t* tokens;
   const void* target;
@@ -201,36 +204,69 @@ __global__ __launch_bounds__(256) void accept_path_kernel(const AcceptParams p) 
   if (flags && p.status) atomicOr(p.status, flags);
 }
 
-// ---- speculative: fp64 segment sums of the terminal row (residual and target).
-__global__ __launch_bounds__(256) void residual_segsum_kernel(const AcceptParams p) {
-  __shared__ double sd[4];
-  __shared__ int smx[4];
-  const int s = blockIdx.x % p.S, b = blockIdx.x / p.S;
-  const int row = p.term[b * 4 + 0], resid = p.term[b * 4 + 1];
-  const size_t off = (static_cast<size_t>(b) * p.R + row) * p.V;
-  const float* pt = static_cast<const float*>(p.target) + off;
-  const float* pd = p.draft + off;
-  const int j0 = s * p.segLen, j1 = min(p.V, j0 + p.segLen);
+// One element of the terminal row: the target probability and the residual max(0, P_t - P_d),
+// folded into fp64 segment sums and last-positive indices.
+struct SegAcc {
   double sr = 0.0, st = 0.0;
   int lr = -1, lt = -1;
-  for (int j = j0 + threadIdx.x; j < j1; j += 256) {
-    const double t = pt[j];
+  __device__ __forceinline__ void add(float x, float y, int j, bool resid) {
+    const double t = x;
     st += t;
     if (t > 0.0) lt = j;
     if (resid) {
-      const double r = fmax(0.0, t - static_cast<double>(pd[j]));
+      const double r = fmax(0.0, t - static_cast<double>(y));
       sr += r;
       if (r > 0.0) lr = j;
     }
   }
+};
+
+// ---- speculative: fp64 segment sums of the terminal row (residual and target).  Each thread
+// walks its elements in increasing index order, so its last positive index is the largest.
+__global__ __launch_bounds__(256) void residual_segsum_kernel(const AcceptParams p) {
+  __shared__ double sd[4];
+  __shared__ int smx[4];
+  const int s = blockIdx.x % p.S, b = blockIdx.x / p.S;
+  const int row = p.term[b * 4 + 0];
+  const bool resid = p.term[b * 4 + 1] != 0;
+  const size_t off = (static_cast<size_t>(b) * p.R + row) * p.V;
+  const float* pt = static_cast<const float*>(p.target) + off;
+  const float* pd = p.draft + off;
+  const int j0 = s * p.segLen, j1 = min(p.V, j0 + p.segLen);
+  SegAcc a;
+  if (p.vec4) {
+    // 16-byte pieces, two per thread in flight (j0 and j1 are multiples of 4)
+    constexpr int U = 2;
+    for (int j = j0 + 4 * static_cast<int>(threadIdx.x); j < j1; j += 4 * 256 * U) {
+      float4 t4[U], d4[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int jj = j + 4 * 256 * u;
+        t4[u] = jj < j1 ? *reinterpret_cast<const float4*>(pt + jj) : make_float4(0.f, 0.f, 0.f, 0.f);
+        d4[u] = (resid && jj < j1) ? *reinterpret_cast<const float4*>(pd + jj) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int jj = j + 4 * 256 * u;
+        if (jj < j1) {
+          a.add(t4[u].x, d4[u].x, jj + 0, resid);
+          a.add(t4[u].y, d4[u].y, jj + 1, resid);
+          a.add(t4[u].z, d4[u].z, jj + 2, resid);
+          a.add(t4[u].w, d4[u].w, jj + 3, resid);
+        }
+      }
+    }
+  } else {
+    for (int j = j0 + static_cast<int>(threadIdx.x); j < j1; j += 256) a.add(pt[j], resid ? pd[j] : 0.f, j, resid);
+  }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  double vals[2] = {sr, st};
-  int idx[2] = {lr, lt};
+  double vals[2] = {a.sr, a.st};
+  int idx[2] = {a.lr, a.lt};
   double outv[2];
   int outi[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    double v = wave_sum_f64(vals[q]);
+    const double v = wave_sum_f64(vals[q]);
     const int mi = wave_max_i(idx[q]);
     __syncthreads();
     if (lane == 0) { sd[w] = v; smx[w] = mi; }
@@ -247,11 +283,19 @@ __global__ __launch_bounds__(256) void residual_segsum_kernel(const AcceptParams
   }
 }
 
-// ---- speculative: inverse-CDF position of u * Z in the chosen distribution.
+// ---- speculative: inverse-CDF position of u * Z in the chosen distribution.  The segment
+// records are staged in LDS by as many threads, thread 0 picks the segment; the 256 threads
+// split that segment into contiguous ranges of up to kSampleChunk elements each fetched in one
+// batch, an LDS scan gives each range its starting cumulative mass, and the one thread t with
+// incl(t-1) <= u*Z < incl(t) walks its range element by element in registers.
+constexpr int kSampleChunk = 32;
+
 __global__ __launch_bounds__(256) void residual_sample_kernel(const AcceptParams p) {
-  __shared__ double pref[257];
-  __shared__ double sub[257];
-  __shared__ int sh[4];
+  __shared__ double sc[256];
+  __shared__ double segm[2][256];
+  __shared__ int segl[2][256];
+  __shared__ double tval;
+  __shared__ int sh[3];
   __shared__ int found;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int row = p.term[b * 4 + 0], resid = p.term[b * 4 + 1], len = p.term[b * 4 + 2];
@@ -259,74 +303,103 @@ __global__ __launch_bounds__(256) void residual_sample_kernel(const AcceptParams
   const float* pt = static_cast<const float*>(p.target) + off;
   const float* pd = p.draft + off;
   const size_t sq = static_cast<size_t>(b) * p.S;
+  if (tid < p.S) {  // S <= 256
+    segm[0][tid] = p.seg_r[sq + tid];
+    segm[1][tid] = p.seg_t[sq + tid];
+    segl[0][tid] = p.seg_lr[sq + tid];
+    segl[1][tid] = p.seg_lt[sq + tid];
+  }
+  __syncthreads();
   if (tid == 0) {
     double zr = 0.0;
-    for (int s = 0; s < p.S; ++s) zr += p.seg_r[sq + s];
+    for (int s = 0; s < p.S; ++s) zr += segm[0][s];
     const int use_r = resid && zr > 0.0;
-    double acc = 0.0;
+    const int q = use_r ? 0 : 1;
+    double tot = 0.0;
+    for (int s = 0; s < p.S; ++s) tot += segm[q][s];
+    const double t = static_cast<double>(p.uniforms[static_cast<size_t>(b) * p.R + p.N]) * tot;
+    int sstar = -1, last = -1;
+    double acc = 0.0, base = 0.0;
     for (int s = 0; s < p.S; ++s) {
-      pref[s] = acc;
-      acc += use_r ? p.seg_r[sq + s] : p.seg_t[sq + s];
+      const double nx = acc + segm[q][s];
+      if (sstar < 0 && nx > t) {
+        sstar = s;
+        base = acc;
+      }
+      acc = nx;
+      last = max(last, segl[q][s]);
     }
-    pref[p.S] = acc;
-    const double t = static_cast<double>(p.uniforms[static_cast<size_t>(b) * p.R + p.N]) * acc;
-    int sstar = -1;
-    for (int s = 0; s < p.S; ++s)
-      if (pref[s + 1] > t) { sstar = s; break; }
-    int last = -1;
-    for (int s = 0; s < p.S; ++s) last = max(last, use_r ? p.seg_lr[sq + s] : p.seg_lt[sq + s]);
     sh[0] = use_r;
     sh[1] = sstar;
     sh[2] = last;
-    sub[256] = t;
+    tval = t - base;  // mass still to cover inside the chosen segment
     found = -1;
   }
   __syncthreads();
-  const int use_r = sh[0], sstar = sh[1];
-  const double t = sub[256];
+  const bool use_r = sh[0] != 0;
+  const int sstar = sh[1];
   int token = sh[2];
   if (sstar >= 0) {
+    const double t = tval;
     const int j0 = sstar * p.segLen, j1 = min(p.V, j0 + p.segLen);
-    const int per = (j1 - j0 + 255) / 256;
+    const int per = (ceil_div_dev(j1 - j0, 256) + 3) / 4 * 4;  // a multiple of 4: aligned pieces
     const int a0 = min(j1, j0 + tid * per), a1 = min(j1, a0 + per);
-    auto rv = [&](int j) -> double {
-      const double x = pt[j];
-      return use_r ? fmax(0.0, x - static_cast<double>(pd[j])) : x;
+    auto rv = [&](float x, float y) -> double {
+      return use_r ? fmax(0.0, static_cast<double>(x) - static_cast<double>(y)) : static_cast<double>(x);
+    };
+    float xv[kSampleChunk], yv[kSampleChunk];
+    auto fetch = [&](int j) {  // elements j .. j+kSampleChunk-1 of this range (zeros past a1)
+      if (p.vec4 && j + kSampleChunk <= a1) {
+#pragma unroll
+        for (int u = 0; u < kSampleChunk; u += 4) {
+          const float4 x4 = *reinterpret_cast<const float4*>(pt + j + u);
+          const float4 y4 = use_r ? *reinterpret_cast<const float4*>(pd + j + u) : make_float4(0.f, 0.f, 0.f, 0.f);
+          xv[u] = x4.x; xv[u + 1] = x4.y; xv[u + 2] = x4.z; xv[u + 3] = x4.w;
+          yv[u] = y4.x; yv[u + 1] = y4.y; yv[u + 2] = y4.z; yv[u + 3] = y4.w;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kSampleChunk; ++u) {
+          xv[u] = j + u < a1 ? pt[j + u] : 0.f;
+          yv[u] = (use_r && j + u < a1) ? pd[j + u] : 0.f;
+        }
+      }
     };
     double mine = 0.0;
-    for (int j = a0; j < a1; ++j) mine += rv(j);
-    __syncthreads();
-    sub[tid] = mine;
-    __syncthreads();
-    if (tid == 0) {
-      double acc = pref[sstar];
-      for (int q = 0; q < 256; ++q) {
-        const double nx = acc + sub[q];
-        sub[q] = acc;  // exclusive prefix
-        acc = nx;
-      }
+    for (int j = a0; j < a1; j += kSampleChunk) {
+      fetch(j);
+#pragma unroll
+      for (int u = 0; u < kSampleChunk; ++u) mine += rv(xv[u], yv[u]);
     }
+    // inclusive scan of the 256 range masses (Hillis-Steele in LDS)
+    sc[tid] = mine;
     __syncthreads();
-    const double start = sub[tid];
-    const bool cross = a0 < a1 && start + mine > t;
-    // the first thread whose range crosses t scans it
-    const int first = wave_min_i(cross ? tid : INT_MAX);
-    __syncthreads();
-    if ((tid & 63) == 0) sh[tid >> 6] = first;
-    __syncthreads();
-    const int ft = min(min(sh[0], sh[1]), min(sh[2], sh[3]));
-    if (tid == ft) {
-      double acc = start;
+    for (int o = 1; o < 256; o <<= 1) {
+      const double v = tid >= o ? sc[tid - o] : 0.0;
+      __syncthreads();
+      sc[tid] += v;
+      __syncthreads();
+    }
+    const double incl = sc[tid];
+    const double excl = tid > 0 ? sc[tid - 1] : 0.0;
+    if (a0 < a1 && excl <= t && t < incl) {
+      double acc = excl;
       int hit = -1;
-      for (int j = a0; j < a1; ++j) {
-        acc += rv(j);
-        if (acc > t) { hit = j; break; }
+      for (int j = a0; j < a1 && hit < 0; j += kSampleChunk) {
+        if (a1 - a0 > kSampleChunk) fetch(j);  // a single-chunk range is still in registers
+#pragma unroll
+        for (int u = 0; u < kSampleChunk; ++u) {
+          if (hit < 0 && j + u < a1) {
+            acc += rv(xv[u], yv[u]);
+            if (acc > t) hit = j + u;
+          }
+        }
       }
       found = hit;
     }
     __syncthreads();
     if (found >= 0) token = found;
-    else token = use_r ? p.seg_lr[sq + sstar] : p.seg_lt[sq + sstar];
+    else token = use_r ? segl[0][sstar] : segl[1][sstar];
   }
   if (tid == 0) p.out_tokens[static_cast<size_t>(b) * (p.D + 1) + len] = token;
 }
@@ -406,6 +479,8 @@ MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D,
   const AcceptPlan a = plan_accept(mode, B, N, V, ws, &p);
   p.S = a.S;
   p.segLen = a.segLen;
+  p.vec4 = (V % 4 == 0 && a.segLen % 4 == 0 &&
+            ((reinterpret_cast<uintptr_t>(target) | reinterpret_cast<uintptr_t>(draft)) & 15) == 0) ? 1 : 0;
   hipStream_t st = as_stream(stream);
   if (mode == MV_ACCEPT_GREEDY) {
     const long long blocks = static_cast<long long>(B) * p.R * a.S;

@@ -347,35 +347,56 @@ void tree_attn_bf16_kernel(const AttnParams p) {
   }
 }
 
-// Merge of the chunk partials: O = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c.
+// Merge of the chunk partials: O = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c, as an online
+// log-sum-exp over the chunks.  DH/4 lanes per output row, each with one 16-byte piece of every
+// partial; the partials of up to kCombineBatch chunks are requested before any is used.
+constexpr int kCombineBatch = 4;
+
 template <int DH>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
-  const int rowid = blockIdx.x * 4 + (threadIdx.x >> 6);  // ((b*Hq + h)*N + i)
+  constexpr int LPR = DH / 4;       // lanes per row
+  constexpr int RPB = 256 / LPR;    // rows per workgroup
+  const int rowid = blockIdx.x * RPB + static_cast<int>(threadIdx.x) / LPR;  // ((b*Hq + h)*N + i)
   if (rowid >= p.B * p.Hq * p.N) return;
-  const int lane = threadIdx.x & 63;
+  const int e = static_cast<int>(threadIdx.x) % LPR;
   const int i = rowid % p.N, h = (rowid / p.N) % p.Hq, b = rowid / (p.N * p.Hq);
   const int Lb = clamp_prefix(p, p.prefix_len[b], false);
   const int ncb = max(1, (Lb + p.CK - 1) / p.CK);
-  if (ncb == 1) return;
+  if (ncb == 1) return;  // the attention kernel wrote this row itself
   const size_t base = static_cast<size_t>(rowid) * p.nchunks;
-  float M = -INFINITY;
-  for (int c = 0; c < ncb; ++c) M = fmaxf(M, p.part_ml[base + c].x);
-  float L = 0.f, acc[DH / 64];
+  float M = -INFINITY, L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < ncb; c0 += kCombineBatch) {
+    float2 ml[kCombineBatch];
+    float4 po[kCombineBatch];
 #pragma unroll
-  for (int e = 0; e < DH / 64; ++e) acc[e] = 0.f;
-  for (int c = 0; c < ncb; ++c) {
-    const float2 ml = p.part_ml[base + c];
-    const float w = exp2f(ml.x - M);
-    L += w * ml.y;
-    const float* po = p.part_o + (base + c) * DH;
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const int c = c0 + u;
+      ml[u] = c < ncb ? p.part_ml[base + c] : make_float2(-INFINITY, 0.f);
+      po[u] = c < ncb ? *reinterpret_cast<const float4*>(p.part_o + (base + c) * DH + 4 * e)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
-    for (int e = 0; e < DH / 64; ++e) acc[e] += w * po[lane + 64 * e];
+    for (int u = 0; u < kCombineBatch; ++u) {
+      if (ml[u].x == -INFINITY) continue;
+      const float mn = fmaxf(M, ml[u].x);
+      const float a = exp2f(M - mn);  // 0 while M is -inf
+      const float w = exp2f(ml[u].x - mn);
+      acc.x = acc.x * a + w * po[u].x;
+      acc.y = acc.y * a + w * po[u].y;
+      acc.z = acc.z * a + w * po[u].z;
+      acc.w = acc.w * a + w * po[u].w;
+      L = L * a + w * ml[u].y;
+      M = mn;
+    }
   }
   const float inv = 1.f / L;
   uint16_t* orow = static_cast<uint16_t*>(p.out) + (static_cast<size_t>(b * p.N + i) * p.Hq + h) * DH;
-#pragma unroll
-  for (int e = 0; e < DH / 64; ++e) orow[lane + 64 * e] = f32_to_bf16(acc[e] * inv);
-  if (p.lse && lane == 0) p.lse[(static_cast<size_t>(b) * p.Hq + h) * p.N + i] = (M + log2f(L)) * kLn2;
+  uint2 w2;
+  w2.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+  w2.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+  *reinterpret_cast<uint2*>(orow + 4 * e) = w2;
+  if (p.lse && e == 0) p.lse[(static_cast<size_t>(b) * p.Hq + h) * p.N + i] = (M + log2f(L)) * kLn2;
 }
 
 // fp32: one wave per query row (b, node i, head h); lanes run over keys for the scores and
@@ -544,9 +565,8 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
   MV_TRY(launch_status());
   if (a.nchunks > 1) {
     const int rows = B * Hq * N;
-    const int blocks = (rows + 3) / 4;
-    if (dh == 64) attn_combine_kernel<64><<<blocks, 256, 0, st>>>(p);
-    else attn_combine_kernel<128><<<blocks, 256, 0, st>>>(p);
+    if (dh == 64) attn_combine_kernel<64><<<ceil_div(rows, 256 / 16), 256, 0, st>>>(p);
+    else attn_combine_kernel<128><<<ceil_div(rows, 256 / 32), 256, 0, st>>>(p);
     MV_TRY(launch_status());
   }
   return MV_OK;
