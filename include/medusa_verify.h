@@ -72,6 +72,9 @@ typedef enum {
 typedef enum { MV_F32 = 0, MV_BF16 = 1 } mv_dtype;
 typedef enum { MV_ACCEPT_GREEDY = 0, MV_ACCEPT_SPECULATIVE = 1 } mv_accept_mode;
 
+/* target_dt of greedy mv_accept_paths when the target rows arrive as argmax ids. */
+#define MV_TARGET_IDS 2
+
 /* Device-side error flags (OR-ed into *dev_status). */
 #define MV_DEV_BAD_PARENT   0x1  /* parents[i] outside [-1, i) (parents must be topological) */
 #define MV_DEV_BAD_RANK     0x2  /* a node's sibling rank is >= the candidate width of its depth */
@@ -206,6 +209,29 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
                         void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Target LM head over the verification rows (the row before acceptance).  [MX] "2. Single-Pass
+ * Tree Attention Verification", step 2: the target model outputs a distribution for every
+ * candidate node; step 3 compares each node with the target's greedy prediction.  [SD] "The
+ * Acceptance Sampling Rule": P_target is the softmax of the target's logits.
+ *
+ * logits[t][v] = sum_j W[v][j] x[t][j] for T rows of final hidden states (B*(N+1) per verify
+ * step: per sequence the last prefix position, then node 0..N-1).  Per row the call returns
+ * the greedy token (argmax over v, lowest id on ties) and optionally its logit and
+ * LSE = log sum_v exp(logits[t][v]); the [T, V] logits are never written.  The argmax ids feed
+ * mv_accept_paths with target_dt = MV_TARGET_IDS; P_target(v) = exp(logit - LSE).
+ *
+ *   dt         MV_BF16 only (MV_F32 -> MV_ERR_UNSUPPORTED).  d % 32 == 0.
+ *   x [T, d], w_lm [V, d] (the LM head weight, one row per vocabulary entry), bf16.
+ *   argmax_ids [T] int32; max_logit [T] fp32 or NULL; lse [T] fp32 or NULL.
+ *   Accumulation in fp32.  No device flags.
+ * ------------------------------------------------------------------------------------- */
+MV_API size_t mv_lm_head_workspace(int dt, int T, int d, int V);
+
+MV_API int mv_lm_head_argmax(int dt, int T, int d, int V, const void* x, const void* w_lm,
+                             int32_t* argmax_ids, float* max_logit, float* lse, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * (a6)+(a7) Acceptance and the extra token.  Row 0 of target/draft is the distribution after
  * the last prefix token; row i+1 the one after node i.  Node i (index order) is tested
  * against the row of its parent and is accepted iff it passes and its parent is -1 or
@@ -224,7 +250,9 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
  *   has children (all of them rejected), from P_t when that residual is all zero, and from
  *   P_t of the terminal's row when the terminal is a leaf.  Decisions and sums are in fp64.
  *
- *   target_dt MV_BF16 or MV_F32 for greedy; must be MV_F32 for speculative.
+ *   target_dt MV_BF16 or MV_F32 for greedy; must be MV_F32 for speculative.  Greedy also
+ *            takes MV_TARGET_IDS: target then holds the target's greedy token per row,
+ *            int32 [B, N+1] (e.g. from mv_lm_head_argmax), and needs no workspace.
  *   parents [N], node_tokens [B, N] int32; target [B, N+1, V]; draft [B, N+1, V] fp32 and
  *   uniforms [B, N+1] fp32 in [0, 1) (speculative only, else NULL).
  *   D        max tree depth (size of the outputs), 1..MV_MAX_DEPTH.

@@ -20,6 +20,7 @@ MV_ERR_HIP = -5
 
 MV_F32 = 0
 MV_BF16 = 1
+MV_TARGET_IDS = 2
 MV_ACCEPT_GREEDY = 0
 MV_ACCEPT_SPECULATIVE = 1
 
@@ -58,6 +59,8 @@ SIGNATURES = [
     ("mv_tree_attn_verify_workspace", _Z, [_I, _I, _I, _I, _I, _I, _I]),
     ("mv_tree_attn_verify", _I, [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _F, _P, _P,
                                  _P, _P, _Z, _P]),
+    ("mv_lm_head_workspace", _Z, [_I, _I, _I, _I]),
+    ("mv_lm_head_argmax", _I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     ("mv_accept_paths_workspace", _Z, [_I, _I, _I, _I]),
     ("mv_accept_paths", _I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                              _P, _Z, _P]),

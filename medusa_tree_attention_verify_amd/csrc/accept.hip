@@ -34,6 +34,7 @@ __device__ __forceinline__ int ceil_div_dev(int a, int b) { return (a + b - 1) /
 struct AcceptParams {
   int B, N, V, D, R, S, segLen;
   int vec4;  // speculative rows may be read as float4 (V, segLen multiples of 4; 16-byte bases)
+  const int32_t* pred_ids;  // greedy with precomputed target argmax ids [B][N+1], or null
   const int32_t* parents;
   const int32_t* tokens;
   const void* target;
@@ -118,7 +119,8 @@ __global__ __launch_bounds__(256) void accept_path_kernel(const AcceptParams p) 
   const int b = blockIdx.x, tid = threadIdx.x, N = p.N, R = p.R;
   if (tid < N) par[tid] = p.parents[tid];
   if constexpr (!SPEC) {
-    for (int r = tid; r < R; r += 256) {
+    for (int r = tid; r < R && p.pred_ids; r += 256) pred[r] = p.pred_ids[static_cast<size_t>(b) * R + r];
+    for (int r = tid; r < R && !p.pred_ids; r += 256) {
       float bv = -INFINITY;
       int bi = INT_MAX;
       const size_t q = (static_cast<size_t>(b) * R + r) * p.S;
@@ -460,7 +462,8 @@ MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D,
                            float* alpha, int32_t* dev_status, void* ws, size_t ws_bytes,
                            void* stream) {
   if (mode != MV_ACCEPT_GREEDY && mode != MV_ACCEPT_SPECULATIVE) return MV_ERR_INVALID_ARG;
-  if (target_dt != MV_F32 && target_dt != MV_BF16) return MV_ERR_INVALID_ARG;
+  if (target_dt != MV_F32 && target_dt != MV_BF16 && target_dt != MV_TARGET_IDS) return MV_ERR_INVALID_ARG;
+  if (target_dt == MV_TARGET_IDS && mode != MV_ACCEPT_GREEDY) return MV_ERR_INVALID_ARG;
   if (B < 1 || N < 1 || V < 1 || D < 1) return MV_ERR_INVALID_ARG;
   if (N > MV_MAX_NODES || D > MV_MAX_DEPTH) return MV_ERR_UNSUPPORTED;
   if (!parents || !node_tokens || !target || !accept_len || !path_nodes || !out_tokens)
@@ -469,19 +472,25 @@ MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D,
     if (target_dt != MV_F32) return MV_ERR_UNSUPPORTED;
     if (!draft || !uniforms) return MV_ERR_INVALID_ARG;
   }
+  const bool ids = target_dt == MV_TARGET_IDS;
   const AcceptPlan need = plan_accept(mode, B, N, V, nullptr, nullptr);
-  MV_TRY(check_ws(ws, ws_bytes, need.ws_bytes));
+  if (!ids) MV_TRY(check_ws(ws, ws_bytes, need.ws_bytes));
   AcceptParams p{};
   p.B = B; p.N = N; p.V = V; p.D = D; p.R = N + 1;
   p.parents = parents; p.tokens = node_tokens; p.target = target; p.draft = draft;
   p.uniforms = uniforms; p.accept_len = accept_len; p.path_nodes = path_nodes;
   p.out_tokens = out_tokens; p.node_accept = node_accept; p.alpha = alpha; p.status = dev_status;
-  const AcceptPlan a = plan_accept(mode, B, N, V, ws, &p);
+  const AcceptPlan a = plan_accept(mode, B, N, V, ids ? nullptr : ws, ids ? nullptr : &p);
+  if (ids) p.pred_ids = static_cast<const int32_t*>(target);
   p.S = a.S;
   p.segLen = a.segLen;
   p.vec4 = (V % 4 == 0 && a.segLen % 4 == 0 &&
             ((reinterpret_cast<uintptr_t>(target) | reinterpret_cast<uintptr_t>(draft)) & 15) == 0) ? 1 : 0;
   hipStream_t st = as_stream(stream);
+  if (ids) {
+    accept_path_kernel<false><<<B, 256, 0, st>>>(p);
+    return launch_status();
+  }
   if (mode == MV_ACCEPT_GREEDY) {
     const long long blocks = static_cast<long long>(B) * p.R * a.S;
     if (blocks > (1LL << 31) - 1) return MV_ERR_UNSUPPORTED;

@@ -152,40 +152,6 @@ __device__ __forceinline__ void list_pop(float (&lv)[SM], int (&li)[SM]) {
   li[SM - 1] = INT_MAX;
 }
 
-// Log-sum-exp merge of two partial (max, sum of exp(x - max)) pairs; symmetric in its operands,
-// so the butterfly below leaves the same bits in every lane.
-__device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2) {
-  if (m2 == -INFINITY) return;
-  if (m == -INFINITY) {
-    m = m2;
-    l = l2;
-    return;
-  }
-  const float mn = fmaxf(m, m2);
-  l = l * expf(m - mn) + l2 * expf(m2 - mn);
-  m = mn;
-}
-
-__device__ __forceinline__ void wave_ml_merge(float& m, float& l) {
-  auto step = [&](uint32_t om, uint32_t ol) { ml_merge(m, l, __uint_as_float(om), __uint_as_float(ol)); };
-  step(dpp_u32<kDppXor1>(__float_as_uint(m)), dpp_u32<kDppXor1>(__float_as_uint(l)));
-  step(dpp_u32<kDppXor2>(__float_as_uint(m)), dpp_u32<kDppXor2>(__float_as_uint(l)));
-  step(dpp_u32<kDppHalfMirror>(__float_as_uint(m)), dpp_u32<kDppHalfMirror>(__float_as_uint(l)));
-  step(dpp_u32<kDppMirror>(__float_as_uint(m)), dpp_u32<kDppMirror>(__float_as_uint(l)));
-  {
-    const LanePair tm = swap16(__float_as_uint(m)), tl = swap16(__float_as_uint(l));
-    m = __uint_as_float(tm.a);
-    l = __uint_as_float(tl.a);
-    step(tm.b, tl.b);
-  }
-  {
-    const LanePair tm = swap32(__float_as_uint(m)), tl = swap32(__float_as_uint(l));
-    m = __uint_as_float(tm.a);
-    l = __uint_as_float(tl.a);
-    step(tm.b, tl.b);
-  }
-}
-
 template <int SM>
 __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(const GemvParams p) {
   __shared__ float wtv[kMergeWaves][MV_MAX_TOPK];

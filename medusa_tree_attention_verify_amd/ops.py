@@ -241,15 +241,53 @@ def accept_workspace_bytes(mode: int, B: int, N: int, V: int) -> int:
     return int(L.lib().mv_accept_paths_workspace(mode, B, N, V))
 
 
+def lm_head_workspace_bytes(T: int, d: int, V: int) -> int:
+    return int(L.lib().mv_lm_head_workspace(L.MV_BF16, T, d, V))
+
+
+def lm_head_argmax(x: torch.Tensor, w_lm: torch.Tensor, want_max: bool = True,
+                   want_lse: bool = True, out: Optional[Dict[str, torch.Tensor]] = None,
+                   ws: Optional[Workspace] = None) -> Dict[str, torch.Tensor]:
+    """Target LM head over T rows of hidden states x [T, d] (bf16) with W [V, d] (bf16): the
+    greedy token per row (int32), and optionally its logit and the row's LSE (fp32)."""
+    _need(x, "x", torch.bfloat16)
+    _need(w_lm, "w_lm", torch.bfloat16)
+    T, d = x.shape
+    V, d2 = w_lm.shape
+    if d2 != d:
+        raise ValueError(f"w_lm is [V, {d2}] but x has d = {d}")
+    dev = x.device
+    if out is None:
+        out = {"ids": torch.empty(T, dtype=torch.int32, device=dev),
+               "max": torch.empty(T, dtype=torch.float32, device=dev) if want_max else None,
+               "lse": torch.empty(T, dtype=torch.float32, device=dev) if want_lse else None}
+    w = _ws("lm_head", ws)
+    ptr, n = w.get(lm_head_workspace_bytes(T, d, V))
+    L.check("mv_lm_head_argmax", L.lib().mv_lm_head_argmax(
+        L.MV_BF16, T, d, V, _ptr(x), _ptr(w_lm), _ptr(out["ids"]), _ptr(out.get("max")),
+        _ptr(out.get("lse")), ptr, n, _stream()))
+    return out
+
+
 def accept_paths(mode: int, parents: torch.Tensor, node_tokens: torch.Tensor,
                  target: torch.Tensor, D: int, draft: Optional[torch.Tensor] = None,
                  uniforms: Optional[torch.Tensor] = None, want_node_accept: bool = True,
                  want_alpha: bool = True, status: Optional[torch.Tensor] = None,
                  out: Optional[Dict[str, torch.Tensor]] = None,
-                 ws: Optional[Workspace] = None) -> Dict[str, torch.Tensor]:
-    """a6 (greedy) / a7 (speculative): accepted length, path, committed tokens + extra token."""
-    dt = _dt(target)
-    B, R, V = target.shape
+                 ws: Optional[Workspace] = None, vocab: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """a6 (greedy) / a7 (speculative): accepted length, path, committed tokens + extra token.
+
+    Greedy also takes the target rows as argmax ids: target int32 [B, N+1] (then V = vocab
+    size must be given, used only to range-check node tokens)."""
+    if target.dtype == torch.int32:
+        if mode != L.MV_ACCEPT_GREEDY or vocab is None:
+            raise ValueError("argmax-id targets need greedy mode and vocab=")
+        dt = L.MV_TARGET_IDS
+        B, R = target.shape
+        V = int(vocab)
+    else:
+        dt = _dt(target)
+        B, R, V = target.shape
     N = R - 1
     _need(parents, "parents", torch.int32, (N,))
     _need(node_tokens, "node_tokens", torch.int32, (B, N))
@@ -268,7 +306,7 @@ def accept_paths(mode: int, parents: torch.Tensor, node_tokens: torch.Tensor,
                "alpha": torch.empty((B, N), dtype=torch.float32, device=dev)
                if (want_alpha and spec) else None}
     w = _ws("accept", ws)
-    ptr, n = w.get(accept_workspace_bytes(mode, B, N, V))
+    ptr, n = (None, 0) if dt == L.MV_TARGET_IDS else w.get(accept_workspace_bytes(mode, B, N, V))
     L.check("mv_accept_paths", L.lib().mv_accept_paths(
         mode, dt, B, N, V, D, _ptr(parents), _ptr(node_tokens), _ptr(target), _ptr(draft),
         _ptr(uniforms), _ptr(out["accept_len"]), _ptr(out["path_nodes"]), _ptr(out["out_tokens"]),

@@ -21,7 +21,8 @@ verification):
   Figure-1 text box (longest valid path plus one bonus token).
 * "Speculative Decoding & Medusa Tree Attention" (akmalkhaniub blog):
   section 2, "The Acceptance Sampling Rule" (alpha = min(1, P_t/P_d) and the
-  residual distribution normalize(max(0, P_t - P_d))).
+  residual distribution normalize(max(0, P_t - P_d)); P_target is the softmax of
+  the target model's logits).
 
 Readings where the pages are silent (scale 1/sqrt(dh), contiguous GQA groups,
 tree K/V appended after the prefix, ties, the speculative rule applied node by
@@ -39,7 +40,7 @@ import numpy as np
 
 __all__ = [
     "silu", "medusa_heads", "topk_rows", "build_tree", "tree_attention",
-    "accept_greedy", "accept_speculative", "paths_to_parents",
+    "accept_greedy", "accept_speculative", "paths_to_parents", "lm_head_argmax",
 ]
 
 
@@ -360,3 +361,22 @@ def accept_speculative(p_target, p_draft, node_tokens, parents, uniforms,
     acc_len, path_nodes, out_tokens = _pack(res, B, D)
     return {"accept_len": acc_len, "path_nodes": path_nodes, "out_tokens": out_tokens,
             "node_accept": accepted, "alpha": alpha}
+
+
+# --------------------------------------------------------------------------
+# 6. Target LM head over the verification rows ("2. Single-Pass Tree Attention
+#    Verification", step 2: the target model outputs a distribution for every
+#    candidate node, step 3 compares each node with its greedy prediction;
+#    "The Acceptance Sampling Rule": P_target = softmax of the logits)
+# --------------------------------------------------------------------------
+def lm_head_argmax(x, w) -> Dict[str, np.ndarray]:
+    """Target logits z[t] = W x[t] for hidden-state rows x [T, d] and the LM-head weight
+    W [V, d] (one row per vocabulary entry).  Per row: the greedy token (the first, i.e.
+    lowest, index of the maximum), that logit, and LSE = log sum_v exp(z[t][v]), so that
+    P_target(v) = exp(z[t][v] - LSE).  Also returns the logits."""
+    x, w = _f64(x), _f64(w)
+    z = x @ w.T
+    ids = np.argmax(z, axis=1)
+    mx = z[np.arange(z.shape[0]), ids]
+    lse = mx + np.log(np.exp(z - mx[:, None]).sum(axis=1))
+    return {"ids": ids.astype(np.int64), "max": mx, "lse": lse, "logits": z}
