@@ -129,12 +129,15 @@ __global__ __launch_bounds__(NW * 64) void lm_head_kernel(const LmParams p) {
     for (int cc = w; cc < 16; cc += NW) {
       const int tok = col0 + ct * 16 + cc;
       if (tok >= p.T || ct * 16 + cc >= p.ncols) continue;  // wave-uniform
-      float val = 0.f;
+      const bool live = row < p.V;
+      float val = -INFINITY;
+      if (live) {
+        val = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) val += red[ww][lane][cc];
-      if (row >= p.V) val = -INFINITY;
+        for (int ww = 0; ww < NW; ++ww) val += red[ww][lane][cc];
+      }
       float bv = val;
-      int bi = row < p.V ? row : INT_MAX;
+      int bi = live ? row : INT_MAX;
       wave_argbest(bv, bi);
       const float l = wave_sum(val == -INFINITY ? 0.f : expf(val - bv));
       if (lane == 0) {
@@ -262,13 +265,15 @@ MV_API int mv_lm_head_argmax(int dt, int T, int d, int V, const void* x, const v
   p.lse = lse;
   hipStream_t st = as_stream(stream);
   const dim3 grid(a.nrb, a.ngrp);
+  bool launched = false;
 #define MV_LM_CASE(NW_, NCT_) \
-  if (a.nw == NW_ && a.nct == NCT_) lm_head_kernel<NW_, NCT_><<<grid, NW_ * 64, 0, st>>>(p);
+  if (a.nw == NW_ && a.nct == NCT_) { lm_head_kernel<NW_, NCT_><<<grid, NW_ * 64, 0, st>>>(p); launched = true; }
   MV_LM_CASE(4, 1) MV_LM_CASE(4, 2) MV_LM_CASE(4, 3) MV_LM_CASE(4, 4)
   MV_LM_CASE(4, 5) MV_LM_CASE(4, 6) MV_LM_CASE(4, 7) MV_LM_CASE(4, 8)
   MV_LM_CASE(8, 1) MV_LM_CASE(8, 2) MV_LM_CASE(8, 3) MV_LM_CASE(8, 4)
   MV_LM_CASE(8, 5) MV_LM_CASE(8, 6) MV_LM_CASE(8, 7) MV_LM_CASE(8, 8)
 #undef MV_LM_CASE
+  if (!launched) return MV_ERR_UNSUPPORTED;  // no kernel instance for this shape
   MV_TRY(launch_status());
   lm_head_merge_kernel<<<T, kLmMergeThreads, 0, st>>>(p);
   return launch_status();
