@@ -45,6 +45,8 @@ DESCR = {
           "attention only, bf16",
     "c5": "spec-serving-b64: B=64, Hq=32, Hkv=8, dh=128, prefix U[512,8192], 64-node (4,3,2,1) "
           "tree, speculative acceptance over V=128256 (fp32 probabilities)",
+    "c6": "llama3-8b-layer-lmhead: the llama3-8b-layer step with the greedy target computed by "
+          "the target LM head (W_lm 32000 x 4096 bf16 over the 65 verify rows, argmax fused)",
 }
 
 
@@ -72,7 +74,9 @@ def make_inputs(wl, seed):
     if wl.has_heads:
         x.update(W.gen_heads(wl, seed))
     x.update(W.gen_attention(wl, seed))
-    if wl.accept == "greedy":
+    if wl.target_head:
+        x.update(W.gen_target_head(wl, seed))
+    elif wl.accept == "greedy":
         x["target"] = W.gen_target_logits(wl, seed)
     elif wl.accept == "speculative":
         x.update(W.gen_speculative(wl, seed))
@@ -97,7 +101,11 @@ def step_bytes(wl, x):
         depth.append(1 if p < 0 else depth[p] + 1)
     flops = float(np.sum(4.0 * wl.dh * wl.Hq * (N * L + sum(depth))))
     parts["attention"] = (kv + qo, flops)
-    if wl.accept == "greedy":
+    if wl.target_head:
+        T = wl.B * (N + 1)
+        parts["target_head"] = (wl.accept_V * wl.d * 2 + T * wl.d * 2, 2.0 * T * wl.accept_V * wl.d)
+        parts["accept"] = (T * 4, 0.0)
+    elif wl.accept == "greedy":
         parts["accept"] = (wl.B * (N + 1) * wl.accept_V * esz, 0.0)
     elif wl.accept == "speculative":
         parts["accept"] = (wl.B * (2 * N * 4 + 2 * wl.accept_V * 4), 0.0)
@@ -131,7 +139,12 @@ def cpu_baseline(wl, x, seed, budget_s):
         tree = O.build_tree(parents, cand, list(wl.depth_widths)) if cand else O.build_tree(parents)
         t1 = time.perf_counter()
         target = None
-        if wl.accept == "greedy":    # input generation (planting) is not timed
+        x_t = None
+        if wl.target_head:           # input generation (planting) is not timed
+            x_t = x["x_t"].copy()
+            if wl.plant_p > 0:
+                x_t = W.plant_target_head(x_t, x["w_lm"], parents, tree["tokens"], seed, wl.plant_p)
+        elif wl.accept == "greedy":  # input generation (planting) is not timed
             target = x["target"].copy()
             if wl.plant_p > 0:
                 target = W.plant_greedy(target, parents, tree["tokens"], seed, wl.plant_p)
@@ -142,6 +155,9 @@ def cpu_baseline(wl, x, seed, budget_s):
         if sample is None:
             sample = "1 full step"
         O.tree_attention(x["q"], x["k_cache"], x["v_cache"], x["prefix_len"], tree["anc"])
+        if wl.target_head:
+            z = O.lm_head_argmax(x_t.reshape(-1, wl.d), x["w_lm"])["logits"]
+            target = z.reshape(wl.B, wl.N + 1, wl.accept_V)
         if wl.accept == "greedy":
             O.accept_greedy(target, tree["tokens"], parents, wl.D)
         elif wl.accept == "speculative":
@@ -217,11 +233,13 @@ def main():
                       heads={"d": wl.d, "V": wl.V, "K": wl.K, "widths": list(wl.head_widths)}
                       if wl.has_heads else None,
                       lm_width=wl.lm_width, accept=wl.accept, V=wl.accept_V,
-                      tokens_given=not wl.has_heads)
+                      tokens_given=not wl.has_heads, target_head=wl.d if wl.target_head else None)
     d = lambda a, t=dt: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
     static = {}
     if wl.has_heads:
         static.update(h=d(x["h"]), w_res=d(x["w_res"]), w_head=d(x["w_head"]))
+    if wl.target_head:
+        static["w_lm"] = d(x["w_lm"], torch.bfloat16)
     # Rotating copies of the per-step activations so that the 256 MB Infinity Cache cannot
     # serve them as "HBM" reads: only needed when one step moves less than 2x the cache.
     rot_bytes = parts["attention"][0] + (parts["accept"][0] if "accept" in parts else 0)
@@ -233,13 +251,26 @@ def main():
         base.update(target=d(x["p_target"], torch.float32), draft=d(x["p_draft"], torch.float32),
                     uniforms=d(x["uniforms"], torch.float32),
                     node_tokens=d(x["node_tokens"], torch.int32))
+    elif wl.target_head:
+        # the target rows' hidden states are planted against the node tokens this step
+        # produces (the heads and the tree run once, untimed, to get them)
+        base["x_t"] = d(x["x_t"], torch.bfloat16)
+        if wl.plant_p > 0:
+            c = step.bind(dict(static, **base))
+            for part in ("heads_residual", "heads_projection", "heads_select", "tree"):
+                c[part]()
+            torch.cuda.synchronize()
+            toks = step.tree["node_tokens"].cpu().numpy()
+            xt = W.plant_target_head(x["x_t"].copy(), x["w_lm"], list(wl.parents), toks, seed,
+                                     wl.plant_p)
+            base["x_t"] = d(xt, torch.bfloat16)
     elif wl.accept == "greedy":
         # the greedy target is planted against the node tokens this step produces: run the
         # heads and the tree once (untimed) to get them
         base["target"] = d(W.round_bf16(x["target"]) if wl.dtype == "bf16" else x["target"])
         if wl.plant_p > 0:
             c = step.bind(dict(static, **base))
-            for part in ("heads_residual", "heads_projection", "tree"):
+            for part in ("heads_residual", "heads_projection", "heads_select", "tree"):
                 c[part]()
             torch.cuda.synchronize()
             toks = step.tree["node_tokens"].cpu().numpy()
@@ -332,6 +363,8 @@ def main():
         "config": {"workload": DESCR[args.workload], "global_batch": wl.B, "tree_nodes": wl.N,
                    "seq_len": max_L, "rotating_input_sets": R},
         "verified_tree_tokens_per_s": round(steps_per_s * wl.B * wl.N, 1),
+        "mean_accept_len": (round(float(step.acc["accept_len"].float().mean().item()), 3)
+                            if wl.accept != "none" else None),
         "step_roofline_frac": round(t_roof / (ms / 1000.0), 4),
         "step_algorithmic_bytes": int(step_total),
         "parts_ms": parts_ms,

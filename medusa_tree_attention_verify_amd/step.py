@@ -23,13 +23,14 @@ def _p(t: Optional[torch.Tensor]):
 
 
 class VerifyStep:
-    PARTS = ("heads_residual", "heads_projection", "heads_select", "tree", "attention", "accept")
+    PARTS = ("heads_residual", "heads_projection", "heads_select", "tree", "attention",
+             "target_head", "accept")
 
     def __init__(self, *, parents: Sequence[int], depth_widths: Sequence[int],
                  dtype: torch.dtype, B: int, Hq: int, Hkv: int, dh: int, max_L: int,
                  heads: Optional[Dict[str, object]] = None, lm_width: int = 0,
                  accept: str = "greedy", V: int = 0, tokens_given: bool = False,
-                 device="cuda"):
+                 target_head: Optional[int] = None, device="cuda"):
         ops.validate_parents(parents)
         self.parents_list = [int(p) for p in parents]
         self.N = len(parents)
@@ -45,6 +46,9 @@ class VerifyStep:
         self.lm_width = lm_width
         self.heads = heads  # {"d":, "V":, "K":, "widths":}
         self.tokens_given = tokens_given  # node tokens come with the inputs (no heads)
+        # greedy target from the LM head (hidden width target_head): inputs x_t [B, N+1, d]
+        # and w_lm [V, d]; its argmax ids feed greedy acceptance (no logits materialised)
+        self.target_head = target_head
         dev = torch.device(device)
         self.device = dev
         self.parents = torch.tensor(self.parents_list, dtype=torch.int32, device=dev)
@@ -67,6 +71,12 @@ class VerifyStep:
             self._s_heads = L.int_array(heads["widths"])
         self.ws_attn.get(ops.attn_workspace_bytes(self.dt, B, N, Hq, Hkv, dh, max_L))
         self._s_depth = L.int_array(self.depth_widths)
+        if target_head:
+            if accept != "greedy" or dtype != torch.bfloat16:
+                raise ValueError("the target LM head feeds bf16 greedy acceptance")
+            self.ws_lm = ops.Workspace(dev)
+            self.ws_lm.get(ops.lm_head_workspace_bytes(B * (N + 1), target_head, V))
+            self.target_ids = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
         if accept != "none":
             self.ws_accept.get(ops.accept_workspace_bytes(self.mode, B, N, V))
             self.acc = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
@@ -83,7 +93,8 @@ class VerifyStep:
     def bind(self, inp: Dict[str, torch.Tensor]) -> Dict[str, Callable[[], None]]:
         """Pre-marshalled calls of one step on ``inp`` (device tensors: h, w_res, w_head when
         the step has heads; q, k_cache, v_cache, prefix_len; target (+ draft, uniforms);
-        node_tokens when the tokens are given).  Each callable raises on a non-zero status."""
+        node_tokens when the tokens are given; x_t, w_lm with the target LM head).  Each callable
+        raises on a non-zero status."""
         lib = L.lib()
         st = torch.cuda.current_stream(self.device).cuda_stream
         calls: Dict[str, Callable[[], None]] = {}
@@ -142,13 +153,23 @@ class VerifyStep:
                                   _p(inp["k_cache"]), _p(inp["v_cache"]), _p(inp["prefix_len"]),
                                   _p(self.tree["anc_mask"]), 0.0, _p(self.attn_out),
                                   _p(self.attn_lse), _p(self.status), wsp, wsn, st)
+        if self.target_head:
+            wsp, wsn = self._ws(self.ws_lm)
+            calls["target_head"] = wrap("mv_lm_head_argmax", lib.mv_lm_head_argmax, L.MV_BF16,
+                                        B * (N + 1), self.target_head, self.V, _p(inp["x_t"]),
+                                        _p(inp["w_lm"]), self.target_ids.data_ptr(), None, None,
+                                        wsp, wsn, st)
         if self.accept != "none":
             wsp, wsn = self._ws(self.ws_accept)
-            tgt = inp["target"]
-            tdt = L.MV_BF16 if tgt.dtype == torch.bfloat16 else L.MV_F32
+            if self.target_head:
+                tgt, tdt, Vt = self.target_ids, L.MV_TARGET_IDS, self.V
+            else:
+                tgt = inp["target"]
+                tdt = L.MV_BF16 if tgt.dtype == torch.bfloat16 else L.MV_F32
+                Vt = tgt.shape[2]
             a = self.acc
             calls["accept"] = wrap("mv_accept_paths", lib.mv_accept_paths, self.mode, tdt, B, N,
-                                   tgt.shape[2], D, _p(self.parents), _p(tokens), _p(tgt),
+                                   Vt, D, _p(self.parents), _p(tokens), _p(tgt),
                                    _p(inp.get("draft")), _p(inp.get("uniforms")),
                                    _p(a["accept_len"]), _p(a["path_nodes"]), _p(a["out_tokens"]),
                                    _p(a["node_accept"]), _p(a["alpha"]), _p(self.status), wsp,

@@ -93,6 +93,8 @@ class Workload:
     plant_p: float = 0.0             # probability that a parent row's argmax is one of its children
     draft_noise_std: float = 1.0
     qkv_scaled: bool = False         # Q,K,V divided by sqrt(dh)
+    target_head: bool = False        # greedy target from the LM head: W_lm [accept_V, d] times
+                                     # the verify rows' hidden states x_t [B, N+1, d]
 
     @property
     def N(self) -> int:
@@ -144,6 +146,10 @@ WORKLOADS: Dict[str, Workload] = {
                    parents=_T4321, prefix=(512, 8192), depth_widths=(4, 3, 2, 1),
                    accept="speculative", accept_V=128256, target_std=3.0,
                    draft_noise_std=1.0),
+    "c6": Workload(name="llama3-8b-layer-lmhead", dtype="bf16", B=1, Hq=32, Hkv=8, dh=128,
+                   parents=_T4321, prefix=(4096, 4096), depth_widths=(4, 3, 2, 1),
+                   d=4096, V=32000, K=4, head_widths=(4, 3, 2, 1), weight_std=0.02,
+                   accept="greedy", accept_V=32000, plant_p=0.6, target_head=True),
 }
 
 
@@ -251,6 +257,30 @@ def gen_attention(w: Workload, seed: int, prefix_len: Optional[np.ndarray] = Non
     v = normal(seed, "v_cache", (w.B, w.Hkv, L_cap, w.dh), s, bf)
     return {"q": q, "k_cache": k, "v_cache": v, "prefix_len": prefix_len.astype(np.int32),
             "L_cap": L_cap}
+
+
+def gen_target_head(w: Workload, seed: int) -> Dict[str, np.ndarray]:
+    """Hidden states of the verify rows x_t [B, N+1, d] ~ N(0,1) and the LM-head weight
+    W_lm [accept_V, d] ~ N(0, 1/d) (rows of norm ~1), both rounded to bf16."""
+    return {"x_t": normal(seed, "x_t", (w.B, w.N + 1, w.d), 1.0, True),
+            "w_lm": normal(seed, "w_lm", (w.accept_V, w.d), 1.0 / np.sqrt(w.d), True)}
+
+
+def plant_target_head(x_t: np.ndarray, w_lm: np.ndarray, parents: Sequence[int],
+                      node_tokens: np.ndarray, seed: int, p: float) -> np.ndarray:
+    """Make each parent row's greedy token one of its children with probability p, through the
+    hidden state: the row becomes 8 x the chosen token's W_lm row (rounded to bf16), whose
+    logit (~8) then clears every other one (~N(0, (8/sqrt(d))^2)).  Other rows keep their
+    random state.  Works in place and returns x_t."""
+    rng = rng_for(seed, "plant_lm")
+    ch = children_of(parents)
+    for b in range(x_t.shape[0]):
+        for par in sorted(ch):
+            if rng.random() < p:
+                kids = ch[par]
+                t = int(node_tokens[b, kids[int(rng.integers(len(kids)))]])
+                x_t[b, par + 1] = round_bf16(np.float32(8.0) * w_lm[t])
+    return x_t
 
 
 def gen_target_logits(w: Workload, seed: int) -> np.ndarray:

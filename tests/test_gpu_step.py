@@ -29,20 +29,37 @@ def _check_step(wl, seed):
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     xh = W.gen_heads(wl, seed)
     xa = W.gen_attention(wl, seed)
-    target = W.gen_target_logits(wl, seed)
-    heads, cand, tree = _oracle_step(wl, xh, target)
-    if wl.plant_p > 0:
-        target = W.plant_greedy(target, parents, tree["tokens"], seed, wl.plant_p)
-    if wl.dtype == "bf16":
-        target = W.round_bf16(target)
+    if wl.target_head:
+        xt = W.gen_target_head(wl, seed)
+        heads, cand, tree = _oracle_step(wl, xh, None)
+        x_t = xt["x_t"].copy()
+        if wl.plant_p > 0:
+            x_t = W.plant_target_head(x_t, xt["w_lm"], parents, tree["tokens"], seed, wl.plant_p)
+        lm = O.lm_head_argmax(x_t.reshape(-1, wl.d), xt["w_lm"])
+        target = lm["logits"].reshape(wl.B, wl.N + 1, wl.accept_V)
+    else:
+        target = W.gen_target_logits(wl, seed)
+        heads, cand, tree = _oracle_step(wl, xh, target)
+        if wl.plant_p > 0:
+            target = W.plant_greedy(target, parents, tree["tokens"], seed, wl.plant_p)
+        if wl.dtype == "bf16":
+            target = W.round_bf16(target)
     step = VerifyStep(parents=parents, depth_widths=wl.depth_widths, dtype=dt, B=wl.B, Hq=wl.Hq,
                       Hkv=wl.Hkv, dh=wl.dh, max_L=int(xa["prefix_len"].max()),
                       heads={"d": wl.d, "V": wl.V, "K": wl.K, "widths": list(wl.head_widths)},
-                      lm_width=wl.lm_width, accept="greedy", V=wl.accept_V)
+                      lm_width=wl.lm_width, accept="greedy", V=wl.accept_V,
+                      target_head=wl.d if wl.target_head else None)
     inp = {"h": dev(xh["h"], dt), "w_res": dev(xh["w_res"], dt), "w_head": dev(xh["w_head"], dt),
            "q": dev(xa["q"], dt), "k_cache": dev(xa["k_cache"], dt),
-           "v_cache": dev(xa["v_cache"], dt), "prefix_len": dev_i32(xa["prefix_len"]),
-           "target": dev(target, dt)}
+           "v_cache": dev(xa["v_cache"], dt), "prefix_len": dev_i32(xa["prefix_len"])}
+    if wl.target_head:
+        inp.update(x_t=dev(x_t.reshape(wl.B, wl.N + 1, wl.d), torch.bfloat16),
+                   w_lm=dev(xt["w_lm"], torch.bfloat16))
+        # the greedy tokens must not hinge on a near-tie between the two largest logits
+        srt = np.sort(target, axis=-1)
+        assert np.all(srt[..., -1] - srt[..., -2] > 1e-4 * np.maximum(1.0, np.abs(srt[..., -1])))
+    else:
+        inp["target"] = dev(target, dt)
     print(f"step {wl.name} seed={seed}", flush=True)
     step.run(inp)
     torch.cuda.synchronize()
@@ -76,3 +93,18 @@ def test_step_llama8b_full():
     require_gpu()
     lens = _check_step(W.WORKLOADS["c2"], 2)
     print("accepted length", lens.tolist())
+
+
+def test_step_target_head_small():
+    """A whole step whose greedy target comes from the LM head over the verify rows."""
+    require_gpu()
+    wl = W.WORKLOADS["c6"].scaled(d=512, V=3000, accept_V=3000, prefix=(700, 700))
+    lens = _check_step(wl, 31)
+    print("accept lengths", lens.tolist())
+
+
+def test_step_target_head_llama8b_full():
+    """The Llama-3-8B-shaped step with the target LM head (W_lm 32000 x 4096)."""
+    require_gpu()
+    lens = _check_step(W.WORKLOADS["c6"], 6)
+    print("accept lengths", lens.tolist())
