@@ -81,6 +81,7 @@ typedef enum { MV_ACCEPT_GREEDY = 0, MV_ACCEPT_SPECULATIVE = 1 } mv_accept_mode;
 #define MV_DEV_TOO_DEEP     0x4  /* a node's depth exceeds D */
 #define MV_DEV_BAD_PREFIX   0x8  /* prefix_len[b] < 0, > max_L, or prefix_len[b] + N > L_cap */
 #define MV_DEV_BAD_TOKEN    0x10 /* a node token is outside [0, V) */
+#define MV_DEV_BAD_PATH     0x20 /* a committed path node outside [j, N), or a length outside [0, D] */
 
 /* Limits of this build. */
 #define MV_MAX_NODES 256   /* N: tree nodes */
@@ -268,6 +269,28 @@ MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D, 
                     const float* uniforms, int32_t* accept_len, int32_t* path_nodes,
                     int32_t* out_tokens, uint8_t* node_accept, float* alpha,
                     int32_t* dev_status, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Commit of the accepted path (the step after acceptance).  [MTP] "The 2D Tree Attention
+ * Mask": the engine commits the longest accepted path, and a node sees exactly its ancestors,
+ * so the kept path is an ordinary causal continuation of the prefix; [MTP] "Production
+ * Deployment Guidelines": the KV entries of unselected branches are culled.
+ *
+ * For every sequence b with L = prefix_len[b] and len = accept_len[b]: cache rows
+ * L + path_nodes[b][j] move to rows L + j (j < len) in k_cache and v_cache for every KV head,
+ * then prefix_len[b] += len.  The next step's attention then sees prefix + accepted tokens as
+ * one contiguous prefix.  In place (sources are staged before any write); rows L + len ..
+ * L + N - 1 keep stale tree entries and are overwritten by the next step's tree.
+ *
+ *   dt         MV_BF16 or MV_F32 (the caches' element type).  dh in {64, 128}.
+ *   k_cache, v_cache [B, Hkv, L_cap, dh] (modified); prefix_len [B] int32 (advanced);
+ *   path_nodes [B, D], accept_len [B] int32 as written by mv_accept_paths.
+ *   dev_status MV_DEV_BAD_PREFIX (L + N > L_cap) / MV_DEV_BAD_PATH; such a sequence is left
+ *            unchanged.  No workspace.
+ * ------------------------------------------------------------------------------------- */
+MV_API int mv_kv_commit(int dt, int B, int Hkv, int dh, int L_cap, int N, int D, void* k_cache,
+                        void* v_cache, int32_t* prefix_len, const int32_t* path_nodes,
+                        const int32_t* accept_len, int32_t* dev_status, void* stream);
 
 #ifdef __cplusplus
 }

@@ -29,6 +29,7 @@ MV_DEV_BAD_RANK = 0x2
 MV_DEV_TOO_DEEP = 0x4
 MV_DEV_BAD_PREFIX = 0x8
 MV_DEV_BAD_TOKEN = 0x10
+MV_DEV_BAD_PATH = 0x20
 
 MV_MAX_NODES = 256
 MV_MAX_DEPTH = 16
@@ -62,6 +63,7 @@ SIGNATURES = [
     ("mv_lm_head_workspace", _Z, [_I, _I, _I, _I]),
     ("mv_lm_head_argmax", _I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     ("mv_accept_paths_workspace", _Z, [_I, _I, _I, _I]),
+    ("mv_kv_commit", _I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     ("mv_accept_paths", _I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                              _P, _Z, _P]),
 ]

@@ -312,3 +312,21 @@ def accept_paths(mode: int, parents: torch.Tensor, node_tokens: torch.Tensor,
         _ptr(uniforms), _ptr(out["accept_len"]), _ptr(out["path_nodes"]), _ptr(out["out_tokens"]),
         _ptr(out.get("node_accept")), _ptr(out.get("alpha")), _ptr(status), ptr, n, _stream()))
     return out
+
+
+def kv_commit(k_cache: torch.Tensor, v_cache: torch.Tensor, prefix_len: torch.Tensor, N: int,
+              path_nodes: torch.Tensor, accept_len: torch.Tensor,
+              status: Optional[torch.Tensor] = None) -> None:
+    """Move the accepted path's K/V rows L+path[j] -> L+j (all KV heads) and advance
+    prefix_len by the accepted length, in place."""
+    dt = _dt(k_cache)
+    B, Hkv, L_cap, dh = k_cache.shape
+    _need(k_cache, "k_cache")
+    _need(v_cache, "v_cache", k_cache.dtype, tuple(k_cache.shape))
+    _need(prefix_len, "prefix_len", torch.int32, (B,))
+    D = path_nodes.shape[1]
+    _need(path_nodes, "path_nodes", torch.int32, (B, D))
+    _need(accept_len, "accept_len", torch.int32, (B,))
+    L.check("mv_kv_commit", L.lib().mv_kv_commit(
+        dt, B, Hkv, dh, L_cap, N, D, _ptr(k_cache), _ptr(v_cache), _ptr(prefix_len),
+        _ptr(path_nodes), _ptr(accept_len), _ptr(status), _stream()))

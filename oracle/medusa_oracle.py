@@ -18,7 +18,9 @@ verification):
   (globaltechdigest blog): "The 2D Tree Attention Mask" (boolean mask,
   ancestor-or-self), the verification-engine code (parent array with -1
   roots, index-order acceptance, longest path with first-wins ties) and the
-  Figure-1 text box (longest valid path plus one bonus token).
+  Figure-1 text box (longest valid path plus one bonus token), and
+  "Production Deployment Guidelines" (unselected branches culled from the KV
+  cache after verification).
 * "Speculative Decoding & Medusa Tree Attention" (akmalkhaniub blog):
   section 2, "The Acceptance Sampling Rule" (alpha = min(1, P_t/P_d) and the
   residual distribution normalize(max(0, P_t - P_d)); P_target is the softmax of
@@ -40,7 +42,7 @@ import numpy as np
 
 __all__ = [
     "silu", "medusa_heads", "topk_rows", "build_tree", "tree_attention",
-    "accept_greedy", "accept_speculative", "paths_to_parents", "lm_head_argmax",
+    "accept_greedy", "accept_speculative", "paths_to_parents", "lm_head_argmax", "kv_commit",
 ]
 
 
@@ -380,3 +382,39 @@ def lm_head_argmax(x, w) -> Dict[str, np.ndarray]:
     mx = z[np.arange(z.shape[0]), ids]
     lse = mx + np.log(np.exp(z - mx[:, None]).sum(axis=1))
     return {"ids": ids.astype(np.int64), "max": mx, "lse": lse, "logits": z}
+
+
+# --------------------------------------------------------------------------
+# 7. Commit of the accepted path ("Multi-Token Prediction: Draft-Model-Free
+#    Speculative Decoding", "The 2D Tree Attention Mask": the engine commits
+#    the longest accepted path, and each node sees exactly its ancestors, so
+#    the kept path continues the prefix causally; "Production Deployment
+#    Guidelines": the KV entries of unselected branches are culled).
+#    Reading: the tree's K/V rows sit after the prefix in node order; keeping
+#    the path means moving its rows to the front of that block and growing the
+#    prefix by its length.
+# --------------------------------------------------------------------------
+def kv_commit(k_cache, v_cache, prefix_len, path_nodes, accept_len, N: int):
+    """New (k_cache, v_cache, prefix_len) after keeping each sequence's accepted path.
+
+    k_cache/v_cache [B, Hkv, L_cap, dh]; row L_b + i holds tree node i.  For sequence b with
+    len = accept_len[b] and path = path_nodes[b][:len], row L_b + j of the result is row
+    L_b + path[j] of the input (every KV head), other rows are unchanged, and the prefix
+    becomes L_b + len.  Raises ValueError for a path that is not a valid accepted path
+    (len outside [0, D], a node outside [j, N), or L_b + N beyond L_cap)."""
+    k_new, v_new = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    L_cap = k_new.shape[2]
+    D = np.asarray(path_nodes).shape[1]
+    prefix_new = np.array(prefix_len, dtype=np.int64, copy=True)
+    for b in range(k_new.shape[0]):
+        L, n = int(prefix_len[b]), int(accept_len[b])
+        if L < 0 or L + N > L_cap or n < 0 or n > D:
+            raise ValueError(f"sequence {b}: prefix {L} / length {n} out of range")
+        for j in range(n):
+            node = int(path_nodes[b][j])
+            if node < j or node >= N:
+                raise ValueError(f"sequence {b}: path node {node} at level {j}")
+            k_new[b, :, L + j] = k_cache[b, :, L + node]
+            v_new[b, :, L + j] = v_cache[b, :, L + node]
+        prefix_new[b] = L + n
+    return k_new, v_new, prefix_new

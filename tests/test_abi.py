@@ -19,7 +19,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -30,7 +30,7 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ("MV_MAX_NODES", "MV_MAX_DEPTH", "MV_MAX_TOPK", "MV_MAX_BATCH_HEADS",
                  "MV_MAX_HEADS", "MV_DEV_BAD_PARENT", "MV_DEV_BAD_RANK", "MV_DEV_TOO_DEEP",
-                 "MV_DEV_BAD_PREFIX", "MV_DEV_BAD_TOKEN", "MV_TARGET_IDS"):
+                 "MV_DEV_BAD_PREFIX", "MV_DEV_BAD_TOKEN", "MV_DEV_BAD_PATH", "MV_TARGET_IDS"):
         m = re.search(rf"#define {name}\s+(0x[0-9a-fA-F]+|\d+)", text)
         assert m and int(m.group(1), 0) == getattr(L, name), name
 
@@ -102,6 +102,11 @@ def test_host_argument_checks():
     # argmax-id targets: greedy only
     assert lib.mv_accept_paths(L.MV_ACCEPT_SPECULATIVE, L.MV_TARGET_IDS, 1, 4, 10, 2, P, P, P, P, P,
                                P, P, P, None, None, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
+    # KV commit
+    assert lib.mv_kv_commit(L.MV_BF16, 1, 8, 96, 200, 8, 4, P, P, P, P, P, None, None) == L.MV_ERR_UNSUPPORTED
+    assert lib.mv_kv_commit(L.MV_BF16, 1, 8, 128, 7, 8, 4, P, P, P, P, P, None, None) == L.MV_ERR_INVALID_ARG
+    assert lib.mv_kv_commit(L.MV_BF16, 1, 8, 128, 200, 8, 17, P, P, P, P, P, None, None) == L.MV_ERR_UNSUPPORTED
+    assert lib.mv_kv_commit(L.MV_BF16, 1, 8, 128, 200, 8, 4, P, P, None, P, P, None, None) == L.MV_ERR_INVALID_ARG
     # LM head
     args = (P, P, P, None, None, P, 1 << 30, None)
     assert lib.mv_lm_head_argmax(L.MV_F32, 65, 4096, 32000, *args) == L.MV_ERR_UNSUPPORTED
