@@ -2,10 +2,11 @@
 
 One step = the whole hot path on one batch of synthetic input, already resident in HBM:
 Medusa heads (residual block + vocabulary projection with top-k) -> candidate-tree assembly
--> tree-masked GQA attention -> acceptance.  The default workload is the Llama-3-8B-shaped
-layer: batch 1, 32 query / 8 KV heads of 128 dims, a 4096-token prefix, the 64-node
-(4,3,2,1) tree, 4 Medusa heads over d=4096 and a 32000-token vocabulary, bf16, greedy
-acceptance against target logits whose argmax matches a child token with probability 0.6.
+-> tree-masked GQA attention -> acceptance -> commit of the accepted path into the KV cache.
+The default workload is the Llama-3-8B-shaped layer: batch 1, 32 query / 8 KV heads of 128
+dims, a 4096-token prefix, the 64-node (4,3,2,1) tree, 4 Medusa heads over d=4096 and a
+32000-token vocabulary, bf16, greedy acceptance against target logits whose argmax matches a
+child token with probability 0.6.
 
 Prints one JSON line: steps/s (and verified tree tokens/s), the roofline of the dominant
 kernel (the vocabulary-streaming head projection) timed with HIP events on the stream it
@@ -159,10 +160,17 @@ def cpu_baseline(wl, x, seed, budget_s):
             z = O.lm_head_argmax(x_t.reshape(-1, wl.d), x["w_lm"])["logits"]
             target = z.reshape(wl.B, wl.N + 1, wl.accept_V)
         if wl.accept == "greedy":
-            O.accept_greedy(target, tree["tokens"], parents, wl.D)
+            acc = O.accept_greedy(target, tree["tokens"], parents, wl.D)
         elif wl.accept == "speculative":
-            O.accept_speculative(x["p_target"], x["p_draft"], x["node_tokens"], parents,
-                                 x["uniforms"], wl.D)
+            acc = O.accept_speculative(x["p_target"], x["p_draft"], x["node_tokens"], parents,
+                                       x["uniforms"], wl.D)
+        if wl.accept != "none":     # commit, on each sequence's tree block
+            for b in range(wl.B):
+                Lb = int(x["prefix_len"][b])
+                blk = slice(Lb, Lb + wl.N)
+                O.kv_commit(x["k_cache"][b:b + 1, :, blk], x["v_cache"][b:b + 1, :, blk],
+                            np.zeros(1, np.int64), acc["path_nodes"][b:b + 1],
+                            acc["accept_len"][b:b + 1], wl.N)
         t3 = time.perf_counter()
         t_total += (t1 - t0) + (t3 - t2)
         steps += 1
@@ -233,7 +241,8 @@ def main():
                       heads={"d": wl.d, "V": wl.V, "K": wl.K, "widths": list(wl.head_widths)}
                       if wl.has_heads else None,
                       lm_width=wl.lm_width, accept=wl.accept, V=wl.accept_V,
-                      tokens_given=not wl.has_heads, target_head=wl.d if wl.target_head else None)
+                      tokens_given=not wl.has_heads, target_head=wl.d if wl.target_head else None,
+                      commit=wl.accept != "none")
     d = lambda a, t=dt: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
     static = {}
     if wl.has_heads:
@@ -288,9 +297,16 @@ def main():
         if ev is not None:
             ev[len(present)].record()
 
-    for i in range(args.warmup):
+    for i in range(max(args.warmup, 1)):
         one_step(i)
     torch.cuda.synchronize()
+    if step.commit:
+        # the commit moves 2 (K, V) x Hkv x dh elements per accepted token, read and written,
+        # and reads the path, its length and the prefix, and writes the next prefix
+        esz = 2 if wl.dtype == "bf16" else 4
+        n_acc = int(step.acc["accept_len"].sum().item())
+        parts["commit"] = (4 * wl.Hkv * wl.dh * esz * n_acc + 4 * wl.B * (wl.D + 3), 0.0)
+        step_total = sum(b for b, _ in parts.values())
     K = args.steps
     # Pass 1 (eager, per-part HIP events on the launch stream): per-kernel durations.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(present) + 1)]
@@ -365,6 +381,10 @@ def main():
         "verified_tree_tokens_per_s": round(steps_per_s * wl.B * wl.N, 1),
         "mean_accept_len": (round(float(step.acc["accept_len"].float().mean().item()), 3)
                             if wl.accept != "none" else None),
+        # accepted tokens + one bonus token per sequence, per second of replayed steps
+        "emitted_tokens_per_s": (round(steps_per_s * float((step.acc["accept_len"] + 1).sum()
+                                                             .item()), 1)
+                                 if wl.accept != "none" else None),
         "step_roofline_frac": round(t_roof / (ms / 1000.0), 4),
         "step_algorithmic_bytes": int(step_total),
         "parts_ms": parts_ms,

@@ -278,19 +278,22 @@ MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D, 
  *
  * For every sequence b with L = prefix_len[b] and len = accept_len[b]: cache rows
  * L + path_nodes[b][j] move to rows L + j (j < len) in k_cache and v_cache for every KV head,
- * then prefix_len[b] += len.  The next step's attention then sees prefix + accepted tokens as
+ * then prefix_out[b] = L + len.  The next step's attention then sees prefix + accepted tokens as
  * one contiguous prefix.  In place (sources are staged before any write); rows L + len ..
  * L + N - 1 keep stale tree entries and are overwritten by the next step's tree.
  *
  *   dt         MV_BF16 or MV_F32 (the caches' element type).  dh in {64, 128}.
- *   k_cache, v_cache [B, Hkv, L_cap, dh] (modified); prefix_len [B] int32 (advanced);
+ *   k_cache, v_cache [B, Hkv, L_cap, dh] (modified); prefix_len [B] int32 (read);
+ *   prefix_out [B] int32 (written; may be prefix_len itself, for an in-place advance, or a
+ *            second buffer so that a replayed step keeps its input prefix);
  *   path_nodes [B, D], accept_len [B] int32 as written by mv_accept_paths.
- *   dev_status MV_DEV_BAD_PREFIX (L + N > L_cap) / MV_DEV_BAD_PATH; such a sequence is left
- *            unchanged.  No workspace.
+ *   dev_status MV_DEV_BAD_PREFIX (L + N > L_cap) / MV_DEV_BAD_PATH; such a sequence keeps its
+ *            cache rows and prefix_out[b] = prefix_len[b].  No workspace.
  * ------------------------------------------------------------------------------------- */
 MV_API int mv_kv_commit(int dt, int B, int Hkv, int dh, int L_cap, int N, int D, void* k_cache,
-                        void* v_cache, int32_t* prefix_len, const int32_t* path_nodes,
-                        const int32_t* accept_len, int32_t* dev_status, void* stream);
+                        void* v_cache, const int32_t* prefix_len, int32_t* prefix_out,
+                        const int32_t* path_nodes, const int32_t* accept_len,
+                        int32_t* dev_status, void* stream);
 
 #ifdef __cplusplus
 }

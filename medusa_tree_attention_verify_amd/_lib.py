@@ -63,7 +63,7 @@ SIGNATURES = [
     ("mv_lm_head_workspace", _Z, [_I, _I, _I, _I]),
     ("mv_lm_head_argmax", _I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     ("mv_accept_paths_workspace", _Z, [_I, _I, _I, _I]),
-    ("mv_kv_commit", _I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
+    ("mv_kv_commit", _I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     ("mv_accept_paths", _I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                              _P, _Z, _P]),
 ]

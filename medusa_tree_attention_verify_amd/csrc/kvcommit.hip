@@ -9,11 +9,12 @@
 //
 // The tree's K/V rows sit at cache rows [L_b, L_b + N) in node order.  Committing the accepted
 // path path_nodes[b][0..len) moves row L_b + path_nodes[b][j] to row L_b + j for every KV head
-// and then advances prefix_len[b] by len, so the next step sees prefix + accepted tokens as one
-// contiguous causal prefix.  The copy is in place: a destination row can be a later source
+// and then writes prefix_len[b] + len to prefix_out[b], so the next step sees prefix + accepted
+// tokens as one contiguous causal prefix.  The copy is in place: a destination row can be a later source
 // (path [1, 3] writes row L_b + 1 and reads it), so each workgroup stages all of its source
-// rows in LDS before it writes any.  prefix_len is advanced by a second launch, after every
-// workgroup has read it.
+// rows in LDS before it writes any.  The new prefix lengths go to a separate buffer from the
+// copy kernel itself; written in place they need a second launch, after every workgroup has
+// read the old ones.
 
 #include "mv_device.h"
 #include "mv_host.h"
@@ -25,7 +26,8 @@ struct CommitParams {
   int B, Hkv, dh, L_cap, N, D, esz;  // esz: bytes per element
   char* k;
   char* v;
-  int32_t* prefix_len;
+  const int32_t* prefix_len;
+  int32_t* prefix_out;        // may equal prefix_len
   const int32_t* path_nodes;  // [B][D]
   const int32_t* accept_len;  // [B]
   int32_t* status;
@@ -67,7 +69,11 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(const CommitP
   if (tid == 0) {
     int flags = 0;
     nrows = commit_len(p, b, &flags, src);
-    if (flags && p.status && g == 0) atomicOr(p.status, flags);
+    if (g == 0) {
+      if (flags && p.status) atomicOr(p.status, flags);
+      // a separate output buffer takes the new prefix here; in place it needs a second launch
+      if (p.prefix_out != p.prefix_len) p.prefix_out[b] = p.prefix_len[b] + nrows;
+    }
   }
   __syncthreads();
   const int n = nrows;
@@ -93,14 +99,14 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(const CommitP
   }
 }
 
-// prefix_len[b] += accept_len[b] for valid sequences (after the copies, which read the old
-// value; the same validation, so an invalid sequence keeps its prefix).
+// prefix_out[b] = prefix_len[b] + accept_len[b] for a valid sequence, prefix_len[b] otherwise
+// (after the copies, which read prefix_len; a separate launch, so prefix_out may alias it).
 __global__ void advance_prefix_kernel(const CommitParams p) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= p.B) return;
   int flags = 0;
   const int len = commit_len(p, b, &flags, nullptr);
-  if (flags == 0) p.prefix_len[b] += len;
+  p.prefix_out[b] = p.prefix_len[b] + (flags == 0 ? len : 0);
 }
 
 }  // namespace
@@ -111,11 +117,13 @@ using namespace mv;
 extern "C" {
 
 MV_API int mv_kv_commit(int dt, int B, int Hkv, int dh, int L_cap, int N, int D, void* k_cache,
-                        void* v_cache, int32_t* prefix_len, const int32_t* path_nodes,
-                        const int32_t* accept_len, int32_t* dev_status, void* stream) {
+                        void* v_cache, const int32_t* prefix_len, int32_t* prefix_out,
+                        const int32_t* path_nodes, const int32_t* accept_len,
+                        int32_t* dev_status, void* stream) {
   if (dt != MV_F32 && dt != MV_BF16) return MV_ERR_INVALID_ARG;
   if (B < 1 || Hkv < 1 || N < 1 || D < 1 || L_cap < N) return MV_ERR_INVALID_ARG;
-  if (!k_cache || !v_cache || !prefix_len || !path_nodes || !accept_len) return MV_ERR_INVALID_ARG;
+  if (!k_cache || !v_cache || !prefix_len || !prefix_out || !path_nodes || !accept_len)
+    return MV_ERR_INVALID_ARG;
   if (dh != 64 && dh != 128) return MV_ERR_UNSUPPORTED;
   if (N > MV_MAX_NODES || D > MV_MAX_DEPTH) return MV_ERR_UNSUPPORTED;
   CommitParams p{};
@@ -124,6 +132,7 @@ MV_API int mv_kv_commit(int dt, int B, int Hkv, int dh, int L_cap, int N, int D,
   p.k = static_cast<char*>(k_cache);
   p.v = static_cast<char*>(v_cache);
   p.prefix_len = prefix_len;
+  p.prefix_out = prefix_out;
   p.path_nodes = path_nodes;
   p.accept_len = accept_len;
   p.status = dev_status;
@@ -131,6 +140,7 @@ MV_API int mv_kv_commit(int dt, int B, int Hkv, int dh, int L_cap, int N, int D,
   if (blocks > (1LL << 31) - 1) return MV_ERR_UNSUPPORTED;
   hipStream_t st = as_stream(stream);
   kv_commit_kernel<<<static_cast<int>(blocks), kCommitThreads, 0, st>>>(p);
+  if (prefix_out != prefix_len) return launch_status();
   MV_TRY(launch_status());
   advance_prefix_kernel<<<ceil_div(B, 256), 256, 0, st>>>(p);
   return launch_status();

@@ -316,9 +316,10 @@ def accept_paths(mode: int, parents: torch.Tensor, node_tokens: torch.Tensor,
 
 def kv_commit(k_cache: torch.Tensor, v_cache: torch.Tensor, prefix_len: torch.Tensor, N: int,
               path_nodes: torch.Tensor, accept_len: torch.Tensor,
-              status: Optional[torch.Tensor] = None) -> None:
-    """Move the accepted path's K/V rows L+path[j] -> L+j (all KV heads) and advance
-    prefix_len by the accepted length, in place."""
+              status: Optional[torch.Tensor] = None,
+              prefix_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Move the accepted path's K/V rows L+path[j] -> L+j (all KV heads, in place) and write
+    prefix_len + accept_len to prefix_out (default: prefix_len itself).  Returns prefix_out."""
     dt = _dt(k_cache)
     B, Hkv, L_cap, dh = k_cache.shape
     _need(k_cache, "k_cache")
@@ -327,6 +328,10 @@ def kv_commit(k_cache: torch.Tensor, v_cache: torch.Tensor, prefix_len: torch.Te
     D = path_nodes.shape[1]
     _need(path_nodes, "path_nodes", torch.int32, (B, D))
     _need(accept_len, "accept_len", torch.int32, (B,))
+    if prefix_out is None:
+        prefix_out = prefix_len
+    _need(prefix_out, "prefix_out", torch.int32, (B,))
     L.check("mv_kv_commit", L.lib().mv_kv_commit(
         dt, B, Hkv, dh, L_cap, N, D, _ptr(k_cache), _ptr(v_cache), _ptr(prefix_len),
-        _ptr(path_nodes), _ptr(accept_len), _ptr(status), _stream()))
+        _ptr(prefix_out), _ptr(path_nodes), _ptr(accept_len), _ptr(status), _stream()))
+    return prefix_out

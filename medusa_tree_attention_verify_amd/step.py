@@ -1,12 +1,17 @@
-"""One Medusa tree-verification step on the GPU: heads -> tree -> attention -> acceptance.
+"""One Medusa tree-verification step on the GPU: heads -> tree -> attention -> acceptance
+(-> commit of the accepted path into the KV cache, with ``commit=True``).
 
 All buffers (outputs and workspaces) are allocated once in ``VerifyStep.__init__``.
-``bind(inp)`` turns one set of device inputs into six pre-marshalled C-ABI calls (heads
-residual, heads projection, heads selection, tree, attention, acceptance), so a step costs
-six ctypes calls and no Python-side checks or allocation.  The candidate tokens of depth k come from Medusa
-head k; with ``lm_width > 0`` the depth-1 candidates are instead the top ``lm_width`` tokens
+``bind(inp)`` turns one set of device inputs into one pre-marshalled C-ABI call per part
+(heads residual, heads projection, heads selection, tree, attention, target LM head,
+acceptance, commit; those the step has), so a step costs a few ctypes calls and no Python-side
+checks or allocation.  The candidate tokens of depth k come from Medusa head k; with ``lm_width > 0`` the depth-1 candidates are instead the top ``lm_width`` tokens
 of the target's first row (the base model's own head, which predicts the next token) and
 the Medusa heads supply depths 2..D.
+
+With ``commit=True`` the step ends by moving the accepted path's K/V rows to the front of the
+tree block (in the caller's ``k_cache`` / ``v_cache``) and writing the grown prefix lengths to
+``prefix_next``; ``prefix_len`` itself is left alone, so a replayed step sees the same prefix.
 """
 from __future__ import annotations
 
@@ -24,13 +29,13 @@ def _p(t: Optional[torch.Tensor]):
 
 class VerifyStep:
     PARTS = ("heads_residual", "heads_projection", "heads_select", "tree", "attention",
-             "target_head", "accept")
+             "target_head", "accept", "commit")
 
     def __init__(self, *, parents: Sequence[int], depth_widths: Sequence[int],
                  dtype: torch.dtype, B: int, Hq: int, Hkv: int, dh: int, max_L: int,
                  heads: Optional[Dict[str, object]] = None, lm_width: int = 0,
                  accept: str = "greedy", V: int = 0, tokens_given: bool = False,
-                 target_head: Optional[int] = None, device="cuda"):
+                 target_head: Optional[int] = None, commit: bool = False, device="cuda"):
         ops.validate_parents(parents)
         self.parents_list = [int(p) for p in parents]
         self.N = len(parents)
@@ -77,6 +82,10 @@ class VerifyStep:
             self.ws_lm = ops.Workspace(dev)
             self.ws_lm.get(ops.lm_head_workspace_bytes(B * (N + 1), target_head, V))
             self.target_ids = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
+        if commit and accept == "none":
+            raise ValueError("the commit needs an acceptance rule")
+        self.commit = commit
+        self.prefix_next = torch.empty(B, dtype=torch.int32, device=dev) if commit else None
         if accept != "none":
             self.ws_accept.get(ops.accept_workspace_bytes(self.mode, B, N, V))
             self.acc = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
@@ -174,13 +183,19 @@ class VerifyStep:
                                    _p(a["accept_len"]), _p(a["path_nodes"]), _p(a["out_tokens"]),
                                    _p(a["node_accept"]), _p(a["alpha"]), _p(self.status), wsp,
                                    wsn, st)
+        if self.commit:
+            a = self.acc
+            calls["commit"] = wrap("mv_kv_commit", lib.mv_kv_commit, self.dt, B, self.Hkv,
+                                   self.dh, Lcap, N, D, _p(inp["k_cache"]), _p(inp["v_cache"]),
+                                   _p(inp["prefix_len"]), _p(self.prefix_next),
+                                   _p(a["path_nodes"]), _p(a["accept_len"]), _p(self.status), st)
         return calls
 
     def sequence(self, calls: Dict[str, Callable[[], None]]) -> List[Callable[[], None]]:
         return [calls[p] for p in self.PARTS if p in calls]
 
     def run(self, inp: Dict[str, torch.Tensor]) -> None:
-        """One whole step on ``inp`` (binds, then runs the five calls in order)."""
+        """One whole step on ``inp`` (binds, then runs its calls in order)."""
         for c in self.sequence(self.bind(inp)):
             c()
 

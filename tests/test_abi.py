@@ -103,10 +103,13 @@ def test_host_argument_checks():
     assert lib.mv_accept_paths(L.MV_ACCEPT_SPECULATIVE, L.MV_TARGET_IDS, 1, 4, 10, 2, P, P, P, P, P,
                                P, P, P, None, None, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
     # KV commit
-    assert lib.mv_kv_commit(L.MV_BF16, 1, 8, 96, 200, 8, 4, P, P, P, P, P, None, None) == L.MV_ERR_UNSUPPORTED
-    assert lib.mv_kv_commit(L.MV_BF16, 1, 8, 128, 7, 8, 4, P, P, P, P, P, None, None) == L.MV_ERR_INVALID_ARG
-    assert lib.mv_kv_commit(L.MV_BF16, 1, 8, 128, 200, 8, 17, P, P, P, P, P, None, None) == L.MV_ERR_UNSUPPORTED
-    assert lib.mv_kv_commit(L.MV_BF16, 1, 8, 128, 200, 8, 4, P, P, None, P, P, None, None) == L.MV_ERR_INVALID_ARG
+    kv = lambda dh, L_cap, D, pre=P, out=P: lib.mv_kv_commit(
+        L.MV_BF16, 1, 8, dh, L_cap, 8, D, P, P, pre, out, P, P, None, None)
+    assert kv(96, 200, 4) == L.MV_ERR_UNSUPPORTED
+    assert kv(128, 7, 4) == L.MV_ERR_INVALID_ARG
+    assert kv(128, 200, 17) == L.MV_ERR_UNSUPPORTED
+    assert kv(128, 200, 4, pre=None) == L.MV_ERR_INVALID_ARG
+    assert kv(128, 200, 4, out=None) == L.MV_ERR_INVALID_ARG
     # LM head
     args = (P, P, P, None, None, P, 1 << 30, None)
     assert lib.mv_lm_head_argmax(L.MV_F32, 65, 4096, 32000, *args) == L.MV_ERR_UNSUPPORTED

@@ -78,14 +78,16 @@ def test_commit_invalid_paths_leave_sequence_unchanged():
     alen = np.array([2, 3, 2, 1], dtype=np.int32)         # seq 0: node 0 on level 1
     kd, vd, pd = dev(k, torch.bfloat16), dev(-k, torch.bfloat16), dev_i32(prefix)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    ops.kv_commit(kd, vd, pd, N, dev_i32(path_nodes), dev_i32(alen), status)
+    pout = torch.full((B,), -7, dtype=torch.int32, device="cuda")    # a separate output
+    ops.kv_commit(kd, vd, pd, N, dev_i32(path_nodes), dev_i32(alen), status, prefix_out=pout)
     torch.cuda.synchronize()
     assert int(status.item()) == L.MV_DEV_BAD_PATH | L.MV_DEV_BAD_PREFIX
+    np.testing.assert_array_equal(host(pd), prefix)                     # input kept
     # only sequence 1 is valid
     ok = np.array([1])
     k2, v2, p2 = O.kv_commit(k[ok], -k[ok], prefix[ok], path_nodes[ok], alen[ok], N)
     got_k = host(kd)
-    np.testing.assert_array_equal(host(pd), [3, 6, 3, 15])
+    np.testing.assert_array_equal(host(pout), [3, 6, 3, 15])
     np.testing.assert_array_equal(got_k[1], k2[0])
     np.testing.assert_array_equal(host(vd)[1], v2[0])
     for b in (0, 2, 3):
@@ -164,3 +166,58 @@ def test_verify_commit_verify():
         assert_fp32(o1[b, nodes], ref["out"][b, nodes], what="first pass")
         assert_fp32(o2[b, :alen[b]], ref["out"][b, nodes], what="after commit")
         assert_fp32(host(lse2)[b, :, :alen[b]], ref["lse"][b][:, nodes], what="lse after commit")
+
+
+def test_decode_loop_three_steps():
+    """Three verify steps in a row (fp32), each ending with the commit: every step writes a
+    fresh tree's K/V after the current prefix, verifies it, accepts greedily and commits, and
+    the next step starts from the grown prefix.  The oracle runs the same loop on the host;
+    attention, acceptance, the cache and the prefix lengths are compared at every step."""
+    require_gpu()
+    from medusa_tree_attention_verify_amd.step import VerifyStep
+    parents = branching_tree((3, 2, 1))
+    N, B, Hq, Hkv, dh, V = len(parents), 4, 8, 2, 64, 50
+    D = 3
+    anc = O.build_tree(parents)["anc"]
+    prefix = np.array([5, 17, 30, 0], dtype=np.int64)
+    L_cap = int(prefix.max()) + 3 * D + N
+    kh = W.normal(40, "loop_k", (B, Hkv, L_cap, dh))
+    vh = W.normal(40, "loop_v", (B, Hkv, L_cap, dh))
+    kd, vd = dev(kh), dev(vh)
+    pd = dev_i32(prefix)
+    step = VerifyStep(parents=parents, depth_widths=(3, 2, 1), dtype=torch.float32, B=B, Hq=Hq,
+                      Hkv=Hkv, dh=dh, max_L=L_cap - N, accept="greedy", V=V,
+                      tokens_given=True, commit=True)
+    total = 0
+    for s in range(3):
+        print(f"decode loop step {s} prefix {prefix.tolist()}", flush=True)
+        q = W.normal(41 + s, "loop_q", (B, N, Hq, dh))
+        newk = W.normal(41 + s, "loop_tree_k", (B, Hkv, N, dh))
+        newv = W.normal(41 + s, "loop_tree_v", (B, Hkv, N, dh))
+        for b in range(B):
+            Lb = int(prefix[b])
+            kh[b, :, Lb:Lb + N] = newk[b]
+            vh[b, :, Lb:Lb + N] = newv[b]
+            kd[b, :, Lb:Lb + N] = dev(newk[b])
+            vd[b, :, Lb:Lb + N] = dev(newv[b])
+        toks = W.rng_for(41 + s, "loop_tokens").integers(0, V, (B, N)).astype(np.int32)
+        target = W.plant_greedy(W.normal(41 + s, "loop_target", (B, N + 1, V), 2.0),
+                                parents, toks, 41 + s, 0.7)
+        inp = {"q": dev(q), "k_cache": kd, "v_cache": vd, "prefix_len": pd,
+               "target": dev(target), "node_tokens": dev_i32(toks)}
+        step.run(inp)
+        torch.cuda.synchronize()
+        assert int(step.status.item()) == 0
+        ref = O.tree_attention(q, kh, vh, prefix, anc)
+        assert_fp32(host(step.attn_out), ref["out"], what=f"attention, step {s}")
+        acc = O.accept_greedy(target, toks, parents, D)
+        for k in ("accept_len", "path_nodes", "out_tokens"):
+            np.testing.assert_array_equal(host(step.acc[k]), acc[k], err_msg=f"{k}, step {s}")
+        kh, vh, prefix = O.kv_commit(kh, vh, prefix, acc["path_nodes"], acc["accept_len"], N)
+        np.testing.assert_array_equal(host(step.prefix_next), prefix)
+        np.testing.assert_array_equal(host(kd), kh)
+        np.testing.assert_array_equal(host(vd), vh)
+        pd.copy_(step.prefix_next)
+        total += int(acc["accept_len"].sum())
+    print("accepted tokens over 3 steps:", total)
+    assert total > 0

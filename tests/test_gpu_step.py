@@ -1,4 +1,5 @@
-"""One whole verify step on the GPU (heads -> tree -> attention -> acceptance) vs the oracle."""
+"""One whole verify step on the GPU (heads -> tree -> attention -> acceptance -> commit of
+the accepted path) vs the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -48,7 +49,7 @@ def _check_step(wl, seed):
                       Hkv=wl.Hkv, dh=wl.dh, max_L=int(xa["prefix_len"].max()),
                       heads={"d": wl.d, "V": wl.V, "K": wl.K, "widths": list(wl.head_widths)},
                       lm_width=wl.lm_width, accept="greedy", V=wl.accept_V,
-                      target_head=wl.d if wl.target_head else None)
+                      target_head=wl.d if wl.target_head else None, commit=True)
     inp = {"h": dev(xh["h"], dt), "w_res": dev(xh["w_res"], dt), "w_head": dev(xh["w_head"], dt),
            "q": dev(xa["q"], dt), "k_cache": dev(xa["k_cache"], dt),
            "v_cache": dev(xa["v_cache"], dt), "prefix_len": dev_i32(xa["prefix_len"])}
@@ -81,6 +82,13 @@ def _check_step(wl, seed):
     ref_acc = O.accept_greedy(target, tree["tokens"], parents, wl.D)
     for k in ("accept_len", "path_nodes", "out_tokens"):
         np.testing.assert_array_equal(host(step.acc[k]), ref_acc[k], err_msg=k)
+    # the step ends with the commit of the accepted path (a copy: bit-exact)
+    k2, v2, p2 = O.kv_commit(xa["k_cache"], xa["v_cache"], xa["prefix_len"],
+                             ref_acc["path_nodes"], ref_acc["accept_len"], wl.N)
+    np.testing.assert_array_equal(host(step.prefix_next), p2)
+    np.testing.assert_array_equal(host(inp["prefix_len"]), xa["prefix_len"])
+    np.testing.assert_array_equal(host(inp["k_cache"]), k2)
+    np.testing.assert_array_equal(host(inp["v_cache"]), v2)
     return host(step.acc["accept_len"])
 
 
