@@ -43,6 +43,7 @@ import numpy as np
 __all__ = [
     "silu", "medusa_heads", "topk_rows", "build_tree", "tree_attention",
     "accept_greedy", "accept_speculative", "paths_to_parents", "lm_head_argmax", "kv_commit",
+    "accept_multicandidate",
 ]
 
 
@@ -418,3 +419,67 @@ def kv_commit(k_cache, v_cache, prefix_len, path_nodes, accept_len, N: int):
             v_new[b, :, L + j] = v_cache[b, :, L + node]
         prefix_new[b] = L + n
     return k_new, v_new, prefix_new
+
+
+# --------------------------------------------------------------------------
+# 8. Multi-candidate speculative acceptance ("Speculative Decoding & Medusa
+#    Tree Attention", section 2, "The Acceptance Sampling Rule": accept x with
+#    probability min(1, P_t(x)/P_d(x)), otherwise draw from
+#    normalize(max(0, P_t - P_d)); "Multi-Token Prediction: Draft-Model-Free
+#    Speculative Decoding", "The 2D Tree Attention Mask": the tree is evaluated
+#    by rejection sampling and the longest accepted path is committed).
+#    Reading for several candidates under one node: the siblings are tested in
+#    index order, and after each rejection the residual distribution takes the
+#    place of the target for the next sibling (the replacement draw of the
+#    single-candidate rule is made from a further draft sample instead).  When
+#    the candidates are independent draws from the parent row's P_d, every
+#    emitted token follows P_t (the recursive form of the rule, published as
+#    multi-step speculative sampling in SpecInfer).
+# --------------------------------------------------------------------------
+def accept_multicandidate(p_target, p_draft, node_tokens, parents, uniforms,
+                          D: int) -> Dict[str, np.ndarray]:
+    """Lossless acceptance over a candidate tree with several candidates per node.
+
+    p_target/p_draft [B, N+1, V] (row 0 = after the prefix, row i+1 = after node i);
+    uniforms [B, N+1] in [0, 1).  Starting at the prefix with P = P_t[row], the children
+    of the current node are tested in index order: child i with token x has
+    alpha_i = min(1, P(x) / P_d[row](x)) (1 when P_d(x) = 0) and is accepted iff
+    u[b, i] < alpha_i; the walk then moves to it (P = P_t of its row).  After a rejection
+    P = normalize(max(0, P - P_d[row])) (P_t[row] when that is all zero) and the next
+    sibling is tested.  When a node has no children left, the extra token is drawn from
+    the current P with u[b, N] by inverse CDF.  alpha is -1 for nodes never tested;
+    node_accept marks the path."""
+    p_t, p_d = _f64(p_target), _f64(p_draft)
+    u = _f64(uniforms)
+    B = p_t.shape[0]
+    N = len(parents)
+    kids: Dict[int, List[int]] = {}
+    for i in range(N):
+        kids.setdefault(int(parents[i]), []).append(i)
+    alpha = np.full((B, N), -1.0)
+    accepted = np.zeros((B, N), dtype=bool)
+    res = []
+    for b in range(B):
+        node, path = -1, []
+        P = p_t[b, 0]
+        moved = True
+        while moved:
+            moved = False
+            Q = p_d[b, node + 1]
+            for c in kids.get(node, []):
+                x = int(node_tokens[b, c])
+                alpha[b, c] = 1.0 if Q[x] == 0.0 else min(1.0, P[x] / Q[x])
+                if u[b, c] < alpha[b, c]:
+                    accepted[b, c] = True
+                    path.append(c)
+                    node = c
+                    P = p_t[b, c + 1]
+                    moved = True
+                    break
+                r = np.maximum(0.0, P - Q)
+                P = r / r.sum() if r.sum() > 0.0 else p_t[b, node + 1]
+        tok = _inverse_cdf(P, u[b, N])
+        res.append((path, [int(node_tokens[b, n]) for n in path], tok))
+    acc_len, path_nodes, out_tokens = _pack(res, B, D)
+    return {"accept_len": acc_len, "path_nodes": path_nodes, "out_tokens": out_tokens,
+            "node_accept": accepted, "alpha": alpha}
