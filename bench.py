@@ -46,6 +46,8 @@ DESCR = {
           "attention only, bf16",
     "c5": "spec-serving-b64: B=64, Hq=32, Hkv=8, dh=128, prefix U[512,8192], 64-node (4,3,2,1) "
           "tree, speculative acceptance over V=128256 (fp32 probabilities)",
+    "c7": "spec-serving-b64-multicand: the spec-serving-b64 attention with 4/3/2/1 independent "
+          "draft samples per node and sibling-recursive (lossless) acceptance over V=128256",
     "c6": "llama3-8b-layer-lmhead: the llama3-8b-layer step with the greedy target computed by "
           "the target LM head (W_lm 32000 x 4096 bf16 over the 65 verify rows, argmax fused)",
 }
@@ -79,7 +81,7 @@ def make_inputs(wl, seed):
         x.update(W.gen_target_head(wl, seed))
     elif wl.accept == "greedy":
         x["target"] = W.gen_target_logits(wl, seed)
-    elif wl.accept == "speculative":
+    elif wl.accept in ("speculative", "multicand"):
         x.update(W.gen_speculative(wl, seed))
     return x
 
@@ -108,7 +110,9 @@ def step_bytes(wl, x):
         parts["accept"] = (T * 4, 0.0)
     elif wl.accept == "greedy":
         parts["accept"] = (wl.B * (N + 1) * wl.accept_V * esz, 0.0)
-    elif wl.accept == "speculative":
+    elif wl.accept in ("speculative", "multicand"):
+        # the extra token's pass over the terminal rows (P_t, P_d) and the 2N gathers; the
+        # multi-candidate walk adds one such row pass per rejection followed by a sibling
         parts["accept"] = (wl.B * (2 * N * 4 + 2 * wl.accept_V * 4), 0.0)
     return parts
 
@@ -161,6 +165,9 @@ def cpu_baseline(wl, x, seed, budget_s):
             target = z.reshape(wl.B, wl.N + 1, wl.accept_V)
         if wl.accept == "greedy":
             acc = O.accept_greedy(target, tree["tokens"], parents, wl.D)
+        elif wl.accept == "multicand":
+            acc = O.accept_multicandidate(x["p_target"], x["p_draft"], x["node_tokens"], parents,
+                                          x["uniforms"], wl.D)
         elif wl.accept == "speculative":
             acc = O.accept_speculative(x["p_target"], x["p_draft"], x["node_tokens"], parents,
                                        x["uniforms"], wl.D)
@@ -235,7 +242,7 @@ def main():
     step_total = sum(b for b, _ in parts.values())
 
     max_L = int(x["prefix_len"].max())
-    spec = wl.accept == "speculative"
+    spec = wl.accept in ("speculative", "multicand")
     step = VerifyStep(parents=wl.parents, depth_widths=wl.depth_widths, dtype=dt, B=wl.B,
                       Hq=wl.Hq, Hkv=wl.Hkv, dh=wl.dh, max_L=max_L,
                       heads={"d": wl.d, "V": wl.V, "K": wl.K, "widths": list(wl.head_widths)}

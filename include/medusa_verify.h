@@ -70,7 +70,11 @@ typedef enum {
 } mv_status;
 
 typedef enum { MV_F32 = 0, MV_BF16 = 1 } mv_dtype;
-typedef enum { MV_ACCEPT_GREEDY = 0, MV_ACCEPT_SPECULATIVE = 1 } mv_accept_mode;
+typedef enum {
+  MV_ACCEPT_GREEDY = 0,
+  MV_ACCEPT_SPECULATIVE = 1,
+  MV_ACCEPT_MULTICAND = 2
+} mv_accept_mode;
 
 /* target_dt of greedy mv_accept_paths when the target rows arrive as argmax ids. */
 #define MV_TARGET_IDS 2
@@ -250,16 +254,28 @@ MV_API int mv_lm_head_argmax(int dt, int T, int d, int V, const void* x, const v
  *   token order) from normalize(max(0, P_t - P_d)) of the terminal's row when the terminal
  *   has children (all of them rejected), from P_t when that residual is all zero, and from
  *   P_t of the terminal's row when the terminal is a leaf.  Decisions and sums are in fp64.
+ * MV_ACCEPT_MULTICAND ([SD] "The Acceptance Sampling Rule" applied to the siblings in turn;
+ *   [MTP] "The 2D Tree Attention Mask": the tree is evaluated by rejection sampling): same
+ *   inputs as speculative.  Walking from the prefix with P = P_t of the current row, the
+ *   children of the current node are tested in index order: alpha_i = min(1, P(x_i)/P_d(x_i))
+ *   at the current (parent) row, accepted iff uniforms[b][i] < alpha_i, and the walk moves to
+ *   the first accepted child (P = P_t of its row).  A rejection replaces P by
+ *   normalize(max(0, P - P_d)) (P_t when that is all zero) before the next sibling.  The
+ *   extra token is drawn with uniforms[b][N] from P where the walk stops.  Lossless when
+ *   the siblings are independent draws from the parent row's P_d.  alpha is -1 for nodes
+ *   that were never tested; node_accept marks the path.  Each rejection followed by a
+ *   further sibling costs one pass over the vocabulary row.
  *
- *   target_dt MV_BF16 or MV_F32 for greedy; must be MV_F32 for speculative.  Greedy also
+ *   target_dt MV_BF16 or MV_F32 for greedy; must be MV_F32 for the two sampling modes.  Greedy also
  *            takes MV_TARGET_IDS: target then holds the target's greedy token per row,
  *            int32 [B, N+1] (e.g. from mv_lm_head_argmax), and needs no workspace.
  *   parents [N], node_tokens [B, N] int32; target [B, N+1, V]; draft [B, N+1, V] fp32 and
- *   uniforms [B, N+1] fp32 in [0, 1) (speculative only, else NULL).
+ *   uniforms [B, N+1] fp32 in [0, 1) (sampling modes only, else NULL).
  *   D        max tree depth (size of the outputs), 1..MV_MAX_DEPTH.
  *   accept_len [B] int32; path_nodes [B, D] int32 (-1 padded); out_tokens [B, D+1] int32
  *            (accepted tokens, then the extra token, then -1).
- *   node_accept [B, N] uint8 (1 = accepted) or NULL; alpha [B, N] fp32 (speculative) or NULL.
+ *   node_accept [B, N] uint8 (1 = accepted) or NULL; alpha [B, N] fp32 (sampling modes) or
+ *            NULL.
  *   dev_status MV_DEV_BAD_PARENT / MV_DEV_TOO_DEEP / MV_DEV_BAD_TOKEN flags, or NULL.
  * ------------------------------------------------------------------------------------- */
 MV_API size_t mv_accept_paths_workspace(int mode, int B, int N, int V);

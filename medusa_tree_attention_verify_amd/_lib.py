@@ -23,6 +23,7 @@ MV_BF16 = 1
 MV_TARGET_IDS = 2
 MV_ACCEPT_GREEDY = 0
 MV_ACCEPT_SPECULATIVE = 1
+MV_ACCEPT_MULTICAND = 2
 
 MV_DEV_BAD_PARENT = 0x1
 MV_DEV_BAD_RANK = 0x2

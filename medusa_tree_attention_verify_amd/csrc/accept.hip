@@ -15,6 +15,9 @@
 // Speculative: one workgroup per sequence gathers the 2N probabilities it needs, decides,
 // walks and picks the terminal row; the terminal row is then summed in segments by many
 // workgroups (fp64) and a last pass per sequence locates the inverse-CDF position.
+// Multi-candidate (siblings tested in turn against the running residual): one workgroup per
+// sequence walks the tree; each rejection that is followed by another sibling costs one fp64
+// reduction over the vocabulary, and the extra token reuses the segment-sum and sample passes.
 //
 // Decision exactness: u < P_t/P_d is evaluated as u*P_d < P_t in fp64; the product of two
 // fp32 numbers is exact in fp64, so the decision is the exact real-number comparison.
@@ -48,7 +51,9 @@ struct AcceptParams {
   int32_t* status;
   float* amax_v;  // greedy partials [B*R][S]
   int* amax_i;
-  int* term;      // speculative: [B][4] = {terminal row, residual?, accepted length, -}
+  int* term;      // speculative: [B][4] = {terminal row, -, accepted length, -}
+  double* term_c; // speculative: [B] residual coefficient c of the terminal row: the extra
+                  // token is drawn from max(0, P_t - c P_d) (c = 0: from P_t itself)
   double* seg_r;  // speculative: [B][S] segment sums of the residual / of P_t
   double* seg_t;
   int* seg_lr;    // last index with a positive entry in the segment (-1 if none)
@@ -197,8 +202,8 @@ __global__ __launch_bounds__(256) void accept_path_kernel(const AcceptParams p) 
     p.accept_len[b] = lc;
     if constexpr (SPEC) {
       p.term[b * 4 + 0] = term + 1;
-      p.term[b * 4 + 1] = has_child;
       p.term[b * 4 + 2] = lc;
+      p.term_c[b] = has_child ? 1.0 : 0.0;  // all children of the terminal were rejected
     } else {
       tk_out[lc] = pred[term + 1];
     }
@@ -211,12 +216,12 @@ __global__ __launch_bounds__(256) void accept_path_kernel(const AcceptParams p) 
 struct SegAcc {
   double sr = 0.0, st = 0.0;
   int lr = -1, lt = -1;
-  __device__ __forceinline__ void add(float x, float y, int j, bool resid) {
+  __device__ __forceinline__ void add(float x, float y, int j, bool resid, double c) {
     const double t = x;
     st += t;
     if (t > 0.0) lt = j;
     if (resid) {
-      const double r = fmax(0.0, t - static_cast<double>(y));
+      const double r = fmax(0.0, t - c * static_cast<double>(y));
       sr += r;
       if (r > 0.0) lr = j;
     }
@@ -230,7 +235,8 @@ __global__ __launch_bounds__(256) void residual_segsum_kernel(const AcceptParams
   __shared__ int smx[4];
   const int s = blockIdx.x % p.S, b = blockIdx.x / p.S;
   const int row = p.term[b * 4 + 0];
-  const bool resid = p.term[b * 4 + 1] != 0;
+  const double cres = p.term_c[b];
+  const bool resid = cres > 0.0;
   const size_t off = (static_cast<size_t>(b) * p.R + row) * p.V;
   const float* pt = static_cast<const float*>(p.target) + off;
   const float* pd = p.draft + off;
@@ -251,15 +257,16 @@ __global__ __launch_bounds__(256) void residual_segsum_kernel(const AcceptParams
       for (int u = 0; u < U; ++u) {
         const int jj = j + 4 * 256 * u;
         if (jj < j1) {
-          a.add(t4[u].x, d4[u].x, jj + 0, resid);
-          a.add(t4[u].y, d4[u].y, jj + 1, resid);
-          a.add(t4[u].z, d4[u].z, jj + 2, resid);
-          a.add(t4[u].w, d4[u].w, jj + 3, resid);
+          a.add(t4[u].x, d4[u].x, jj + 0, resid, cres);
+          a.add(t4[u].y, d4[u].y, jj + 1, resid, cres);
+          a.add(t4[u].z, d4[u].z, jj + 2, resid, cres);
+          a.add(t4[u].w, d4[u].w, jj + 3, resid, cres);
         }
       }
     }
   } else {
-    for (int j = j0 + static_cast<int>(threadIdx.x); j < j1; j += 256) a.add(pt[j], resid ? pd[j] : 0.f, j, resid);
+    for (int j = j0 + static_cast<int>(threadIdx.x); j < j1; j += 256)
+      a.add(pt[j], resid ? pd[j] : 0.f, j, resid, cres);
   }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   double vals[2] = {a.sr, a.st};
@@ -300,7 +307,9 @@ __global__ __launch_bounds__(256) void residual_sample_kernel(const AcceptParams
   __shared__ int sh[3];
   __shared__ int found;
   const int b = blockIdx.x, tid = threadIdx.x;
-  const int row = p.term[b * 4 + 0], resid = p.term[b * 4 + 1], len = p.term[b * 4 + 2];
+  const int row = p.term[b * 4 + 0], len = p.term[b * 4 + 2];
+  const double cres = p.term_c[b];
+  const int resid = cres > 0.0;
   const size_t off = (static_cast<size_t>(b) * p.R + row) * p.V;
   const float* pt = static_cast<const float*>(p.target) + off;
   const float* pd = p.draft + off;
@@ -347,7 +356,8 @@ __global__ __launch_bounds__(256) void residual_sample_kernel(const AcceptParams
     const int per = (ceil_div_dev(j1 - j0, 256) + 3) / 4 * 4;  // a multiple of 4: aligned pieces
     const int a0 = min(j1, j0 + tid * per), a1 = min(j1, a0 + per);
     auto rv = [&](float x, float y) -> double {
-      return use_r ? fmax(0.0, static_cast<double>(x) - static_cast<double>(y)) : static_cast<double>(x);
+      return use_r ? fmax(0.0, static_cast<double>(x) - cres * static_cast<double>(y))
+                   : static_cast<double>(x);
     };
     float xv[kSampleChunk], yv[kSampleChunk];
     auto fetch = [&](int j) {  // elements j .. j+kSampleChunk-1 of this range (zeros past a1)
@@ -406,6 +416,204 @@ __global__ __launch_bounds__(256) void residual_sample_kernel(const AcceptParams
   if (tid == 0) p.out_tokens[static_cast<size_t>(b) * (p.D + 1) + len] = token;
 }
 
+// ---- multi-candidate: the sibling-recursive rule.  At a node with target row P_t and draft
+// row Q, the r-th rejection among its children turns the running distribution into
+// normalize(max(0, P_r-1 - Q)).  Unrolled, P_r = max(0, P_t - c_r Q) / Z(c_r) with
+// Z(c) = sum_v max(0, P_t(v) - c Q(v)), c_1 = 1 and c_r+1 = c_r + Z(c_r), so the walk only
+// carries (c, Z(c)) and needs one reduction over the vocabulary per rejection that is
+// followed by another sibling.  A zero residual falls back to P_t (c = 0, Z = 1).
+constexpr int kWalkThreads = 1024;
+#ifndef MV_WALK_U
+#define MV_WALK_U 2
+#endif
+
+// Z(c) over one row pair, fp64, by the whole workgroup; the same reduction order every time.
+__device__ double residual_mass(const AcceptParams& p, const float* pt, const float* pd, double c,
+                                double* red) {
+  const int tid = threadIdx.x;
+  double acc = 0.0;
+  if (p.vec4) {
+    constexpr int U = MV_WALK_U;  // float4 pieces per row in flight per thread
+    for (int j = 4 * tid; j < p.V; j += 4 * kWalkThreads * U) {
+      float4 t4[U], d4[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int jj = j + 4 * kWalkThreads * u;
+        t4[u] = jj < p.V ? *reinterpret_cast<const float4*>(pt + jj) : make_float4(0.f, 0.f, 0.f, 0.f);
+        d4[u] = jj < p.V ? *reinterpret_cast<const float4*>(pd + jj) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        acc += fmax(0.0, static_cast<double>(t4[u].x) - c * static_cast<double>(d4[u].x));
+        acc += fmax(0.0, static_cast<double>(t4[u].y) - c * static_cast<double>(d4[u].y));
+        acc += fmax(0.0, static_cast<double>(t4[u].z) - c * static_cast<double>(d4[u].z));
+        acc += fmax(0.0, static_cast<double>(t4[u].w) - c * static_cast<double>(d4[u].w));
+      }
+    }
+  } else {
+    for (int j = tid; j < p.V; j += kWalkThreads)
+      acc += fmax(0.0, static_cast<double>(pt[j]) - c * static_cast<double>(pd[j]));
+  }
+  const double w = wave_sum_f64(acc);
+  if ((tid & 63) == 0) red[tid >> 6] = w;
+  __syncthreads();
+  double z = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWalkThreads / 64; ++i) z += red[i];
+  __syncthreads();  // red is free again
+  return z;
+}
+
+__global__ __launch_bounds__(kWalkThreads) void multicand_walk_kernel(const AcceptParams p) {
+  __shared__ int par[MV_MAX_NODES];
+  __shared__ int first[MV_MAX_NODES + 1];  // first child of node r - 1 (r = 0: the prefix)
+  __shared__ int nsib[MV_MAX_NODES];       // next sibling in index order
+  __shared__ int path[MV_MAX_NODES];
+  __shared__ float alph[MV_MAX_NODES];
+  __shared__ float gpt[MV_MAX_NODES], gpd[MV_MAX_NODES], gu[MV_MAX_NODES];  // per-node gathers
+  __shared__ int gtok[MV_MAX_NODES];  // node token, -1 if outside [0, V)
+  __shared__ uint8_t onpath[MV_MAX_NODES];
+  __shared__ double red[kWalkThreads / 64];
+  __shared__ int st_child, st_node, st_len, st_reduce;
+  __shared__ double st_c, st_z, st_cn;
+  const int b = blockIdx.x, tid = threadIdx.x, N = p.N;
+  const size_t rb = static_cast<size_t>(b) * p.R;
+  const float* PT = static_cast<const float*>(p.target);
+  int flags = 0;
+  if (tid <= N) first[tid] = N;
+  if (tid < N) {
+    par[tid] = p.parents[tid];
+    alph[tid] = -1.f;
+    onpath[tid] = 0;
+  }
+  __syncthreads();
+  bool valid = false;
+  if (tid < N) {  // a node with a malformed parent entry takes no part in the walk
+    const int pn = par[tid];
+    valid = pn >= -1 && pn < tid;
+    if (valid) atomicMin(&first[pn + 1], tid);
+    else flags |= MV_DEV_BAD_PARENT;
+    // whatever the running residual, node i's test reads P_t and P_d at its parent's row and
+    // its own token, and its uniform: gather them all now, in parallel
+    const int x = p.tokens[static_cast<size_t>(b) * N + tid];
+    const bool ok = valid && x >= 0 && x < p.V;
+    if (valid && !ok) flags |= MV_DEV_BAD_TOKEN;
+    gtok[tid] = ok ? x : -1;
+    if (ok) {
+      const size_t o = (rb + pn + 1) * p.V + x;
+      gpt[tid] = PT[o];
+      gpd[tid] = p.draft[o];
+      gu[tid] = p.uniforms[rb + tid];
+    }
+  }
+  __syncthreads();
+  if (tid < N) {
+    int nx = -1;
+    if (valid) {
+      const int pn = par[tid];
+      for (int j = tid + 1; j < N; ++j) {
+        if (par[j] == pn) {
+          nx = j;
+          break;
+        }
+      }
+    }
+    nsib[tid] = nx;
+  }
+  if (tid <= N && first[tid] >= N) first[tid] = -1;
+  __syncthreads();
+  if (tid == 0) {
+    st_child = first[0];
+    st_node = -1;
+    st_len = 0;
+    st_c = 0.0;
+    st_z = 1.0;
+  }
+  __syncthreads();
+  for (;;) {
+    const int child = st_child;
+    __syncthreads();  // every thread has the state before thread 0 changes it
+    if (child < 0) break;
+    if (tid == 0) {
+      const double c = st_c, z = st_z;
+      int reduce = 0;
+      if (gtok[child] < 0) {  // not a candidate: rejected, the distribution is unchanged
+        alph[child] = 0.f;
+        st_child = nsib[child];
+      } else {
+        const double p0 = gpt[child], q = gpd[child], u = gu[child];
+        const double numer = c == 0.0 ? p0 : fmax(0.0, p0 - c * q);  // Z(c) P_r(x)
+        const double den = q * z;                                     // Z(c) Q(x)
+        int acc;
+        double a;
+        if (q == 0.0) {
+          a = 1.0;
+          acc = u < 1.0;
+        } else {
+          a = fmin(1.0, numer / den);
+          acc = u < 1.0 && u * den < numer;
+        }
+        alph[child] = static_cast<float>(a);
+        if (acc) {
+          path[st_len] = child;
+          onpath[child] = 1;
+          st_len = st_len + 1;
+          st_node = child;
+          st_c = 0.0;
+          st_z = 1.0;
+          st_child = first[child + 1];
+        } else {
+          const double cn = c == 0.0 ? 1.0 : c + z;
+          const int sib = nsib[child];
+          if (sib >= 0) {
+            st_cn = cn;
+            reduce = 1;
+          } else {
+            st_c = cn;  // the extra token's pass normalises this last residual
+          }
+          st_child = sib;
+        }
+      }
+      st_reduce = reduce;
+    }
+    __syncthreads();
+    if (st_reduce) {
+      const size_t off = (rb + st_node + 1) * p.V;
+      const double zz = residual_mass(p, PT + off, p.draft + off, st_cn, red);
+      if (tid == 0) {
+        if (zz > 0.0) {
+          st_c = st_cn;
+          st_z = zz;
+        } else {
+          st_c = 0.0;
+          st_z = 1.0;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const int len = st_len, D = p.D;
+    if (len > D) flags |= MV_DEV_TOO_DEEP;
+    const int lc = min(len, D);
+    int32_t* pn_out = p.path_nodes + static_cast<size_t>(b) * D;
+    int32_t* tk_out = p.out_tokens + static_cast<size_t>(b) * (D + 1);
+    for (int k = 0; k < D; ++k) pn_out[k] = k < lc ? path[k] : -1;
+    for (int k = 0; k <= D; ++k)
+      tk_out[k] = k < lc ? p.tokens[static_cast<size_t>(b) * N + path[k]] : -1;
+    p.accept_len[b] = lc;
+    p.term[b * 4 + 0] = st_node + 1;
+    p.term[b * 4 + 2] = lc;
+    p.term_c[b] = st_c;
+  }
+  __syncthreads();
+  if (tid < N) {
+    if (p.node_accept) p.node_accept[static_cast<size_t>(b) * N + tid] = onpath[tid];
+    if (p.alpha) p.alpha[static_cast<size_t>(b) * N + tid] = alph[tid];
+  }
+  if (flags && p.status) atomicOr(p.status, flags);
+}
+
 struct AcceptPlan {
   int S = 1, segLen = 1;
   size_t ws_bytes = 0;
@@ -432,11 +640,15 @@ AcceptPlan plan_accept(int mode, int B, int N, int V, void* ws, AcceptParams* p)
     if (p) { p->amax_v = av; p->amax_i = ai; }
   } else {
     int* tm = c.take<int>(static_cast<size_t>(B) * 4);
+    double* tc = c.take<double>(static_cast<size_t>(B));
     double* sr = c.take<double>(static_cast<size_t>(B) * a.S);
     double* st = c.take<double>(static_cast<size_t>(B) * a.S);
     int* lr = c.take<int>(static_cast<size_t>(B) * a.S);
     int* lt = c.take<int>(static_cast<size_t>(B) * a.S);
-    if (p) { p->term = tm; p->seg_r = sr; p->seg_t = st; p->seg_lr = lr; p->seg_lt = lt; }
+    if (p) {
+      p->term = tm; p->term_c = tc;
+      p->seg_r = sr; p->seg_t = st; p->seg_lr = lr; p->seg_lt = lt;
+    }
   }
   a.ws_bytes = c.bytes();
   return a;
@@ -450,7 +662,9 @@ using namespace mv;
 extern "C" {
 
 MV_API size_t mv_accept_paths_workspace(int mode, int B, int N, int V) {
-  if ((mode != MV_ACCEPT_GREEDY && mode != MV_ACCEPT_SPECULATIVE) || B < 1 || N < 1 || V < 1) return 0;
+  if ((mode != MV_ACCEPT_GREEDY && mode != MV_ACCEPT_SPECULATIVE && mode != MV_ACCEPT_MULTICAND) ||
+      B < 1 || N < 1 || V < 1)
+    return 0;
   if (N > MV_MAX_NODES) return 0;
   return plan_accept(mode, B, N, V, nullptr, nullptr).ws_bytes;
 }
@@ -461,14 +675,15 @@ MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D,
                            int32_t* path_nodes, int32_t* out_tokens, uint8_t* node_accept,
                            float* alpha, int32_t* dev_status, void* ws, size_t ws_bytes,
                            void* stream) {
-  if (mode != MV_ACCEPT_GREEDY && mode != MV_ACCEPT_SPECULATIVE) return MV_ERR_INVALID_ARG;
+  if (mode != MV_ACCEPT_GREEDY && mode != MV_ACCEPT_SPECULATIVE && mode != MV_ACCEPT_MULTICAND)
+    return MV_ERR_INVALID_ARG;
   if (target_dt != MV_F32 && target_dt != MV_BF16 && target_dt != MV_TARGET_IDS) return MV_ERR_INVALID_ARG;
   if (target_dt == MV_TARGET_IDS && mode != MV_ACCEPT_GREEDY) return MV_ERR_INVALID_ARG;
   if (B < 1 || N < 1 || V < 1 || D < 1) return MV_ERR_INVALID_ARG;
   if (N > MV_MAX_NODES || D > MV_MAX_DEPTH) return MV_ERR_UNSUPPORTED;
   if (!parents || !node_tokens || !target || !accept_len || !path_nodes || !out_tokens)
     return MV_ERR_INVALID_ARG;
-  if (mode == MV_ACCEPT_SPECULATIVE) {
+  if (mode != MV_ACCEPT_GREEDY) {
     if (target_dt != MV_F32) return MV_ERR_UNSUPPORTED;
     if (!draft || !uniforms) return MV_ERR_INVALID_ARG;
   }
@@ -500,7 +715,8 @@ MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D,
     accept_path_kernel<false><<<B, 256, 0, st>>>(p);
     return launch_status();
   }
-  accept_path_kernel<true><<<B, 256, 0, st>>>(p);
+  if (mode == MV_ACCEPT_MULTICAND) multicand_walk_kernel<<<B, kWalkThreads, 0, st>>>(p);
+  else accept_path_kernel<true><<<B, 256, 0, st>>>(p);
   MV_TRY(launch_status());
   residual_segsum_kernel<<<B * a.S, 256, 0, st>>>(p);
   MV_TRY(launch_status());

@@ -275,7 +275,8 @@ def accept_paths(mode: int, parents: torch.Tensor, node_tokens: torch.Tensor,
                  want_alpha: bool = True, status: Optional[torch.Tensor] = None,
                  out: Optional[Dict[str, torch.Tensor]] = None,
                  ws: Optional[Workspace] = None, vocab: Optional[int] = None) -> Dict[str, torch.Tensor]:
-    """a6 (greedy) / a7 (speculative): accepted length, path, committed tokens + extra token.
+    """a6 (greedy) / a7 (speculative) / multi-candidate (siblings tested in turn against the
+    running residual): accepted length, path, committed tokens + extra token.
 
     Greedy also takes the target rows as argmax ids: target int32 [B, N+1] (then V = vocab
     size must be given, used only to range-check node tokens)."""
@@ -292,7 +293,7 @@ def accept_paths(mode: int, parents: torch.Tensor, node_tokens: torch.Tensor,
     _need(parents, "parents", torch.int32, (N,))
     _need(node_tokens, "node_tokens", torch.int32, (B, N))
     _need(target, "target")
-    spec = mode == L.MV_ACCEPT_SPECULATIVE
+    spec = mode in (L.MV_ACCEPT_SPECULATIVE, L.MV_ACCEPT_MULTICAND)
     if spec:
         _need(draft, "draft", torch.float32, (B, R, V))
         _need(uniforms, "uniforms", torch.float32, (B, R))

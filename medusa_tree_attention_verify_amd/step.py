@@ -46,7 +46,8 @@ class VerifyStep:
         self.dtype = dtype
         self.dt = L.MV_BF16 if dtype == torch.bfloat16 else L.MV_F32
         self.accept = accept
-        self.mode = L.MV_ACCEPT_SPECULATIVE if accept == "speculative" else L.MV_ACCEPT_GREEDY
+        self.mode = {"speculative": L.MV_ACCEPT_SPECULATIVE,
+                     "multicand": L.MV_ACCEPT_MULTICAND}.get(accept, L.MV_ACCEPT_GREEDY)
         self.V = V
         self.lm_width = lm_width
         self.heads = heads  # {"d":, "V":, "K":, "widths":}
@@ -93,7 +94,7 @@ class VerifyStep:
                         "out_tokens": torch.empty((B, self.D + 1), dtype=torch.int32, device=dev),
                         "node_accept": torch.empty((B, N), dtype=torch.uint8, device=dev),
                         "alpha": torch.empty((B, N), dtype=torch.float32, device=dev)
-                        if self.mode == L.MV_ACCEPT_SPECULATIVE else None}
+                        if self.mode != L.MV_ACCEPT_GREEDY else None}
 
     @staticmethod
     def _ws(w: ops.Workspace):

@@ -87,11 +87,13 @@ class Workload:
     lm_width: int = 0                # depth-1 candidates taken from the target's own row 0
     weight_std: float = 0.0          # 0 -> N(0,1)/sqrt(fan_in)
     # acceptance
-    accept: str = "greedy"           # "greedy", "speculative" or "none"
+    accept: str = "greedy"           # "greedy", "speculative", "multicand" or "none"
     accept_V: int = 0
     target_std: float = 2.0
     plant_p: float = 0.0             # probability that a parent row's argmax is one of its children
     draft_noise_std: float = 1.0
+    draft_tokens: str = "top"        # sampling modes: children's tokens are the draft row's
+                                     # top tokens ("top") or independent draws from it ("sampled")
     qkv_scaled: bool = False         # Q,K,V divided by sqrt(dh)
     target_head: bool = False        # greedy target from the LM head: W_lm [accept_V, d] times
                                      # the verify rows' hidden states x_t [B, N+1, d]
@@ -146,6 +148,12 @@ WORKLOADS: Dict[str, Workload] = {
                    parents=_T4321, prefix=(512, 8192), depth_widths=(4, 3, 2, 1),
                    accept="speculative", accept_V=128256, target_std=3.0,
                    draft_noise_std=1.0),
+    # batched serving with several independent draft samples per node and the
+    # sibling-recursive (lossless) acceptance rule
+    "c7": Workload(name="spec-serving-b64-multicand", dtype="bf16", B=64, Hq=32, Hkv=8, dh=128,
+                   parents=_T4321, prefix=(512, 8192), depth_widths=(4, 3, 2, 1),
+                   accept="multicand", accept_V=128256, target_std=3.0,
+                   draft_noise_std=1.0, draft_tokens="sampled"),
     "c6": Workload(name="llama3-8b-layer-lmhead", dtype="bf16", B=1, Hq=32, Hkv=8, dh=128,
                    parents=_T4321, prefix=(4096, 4096), depth_widths=(4, 3, 2, 1),
                    d=4096, V=32000, K=4, head_widths=(4, 3, 2, 1), weight_std=0.02,
@@ -321,7 +329,8 @@ def gen_speculative(w: Workload, seed: int, rows: Optional[Sequence[int]] = None
 
     P_target = softmax(N(0, target_std) logits); P_draft = softmax(the same logits
     + N(0, draft_noise_std) noise).  Children of a row get, in index order, the
-    draft's highest-probability tokens of that row (the draft's own proposals).
+    draft's highest-probability tokens of that row (the draft's own proposals), or with
+    ``draft_tokens == "sampled"`` independent draws from that row (repeats allowed).
     ``rows`` restricts generation to a subset of sequences (others are left 0).
     """
     B, R, V = w.B, w.N + 1, w.accept_V
@@ -342,6 +351,15 @@ def gen_speculative(w: Workload, seed: int, rows: Optional[Sequence[int]] = None
         list(ex.map(seq, rows))
     ch = children_of(w.parents)
     node_tokens = np.zeros((B, w.N), dtype=np.int32)
+    if w.draft_tokens == "sampled":
+        g = rng_for(seed, "draft_draws")
+        for b in rows:
+            for par, kids_ in ch.items():
+                cdf = np.cumsum(p_d[b, par + 1].astype(np.float64))
+                u = g.random(len(kids_)) * cdf[-1]
+                node_tokens[b, kids_] = np.minimum(np.searchsorted(cdf, u, side="right"), V - 1)
+        uniforms = rng_for(seed, "uniforms").random((B, R), dtype=np.float32)
+        return {"p_target": p_t, "p_draft": p_d, "node_tokens": node_tokens, "uniforms": uniforms}
     for b in rows:
         for par, kids_ in ch.items():
             row = p_d[b, par + 1]

@@ -33,6 +33,10 @@ def test_header_constants_match_binding():
                  "MV_DEV_BAD_PREFIX", "MV_DEV_BAD_TOKEN", "MV_DEV_BAD_PATH", "MV_TARGET_IDS"):
         m = re.search(rf"#define {name}\s+(0x[0-9a-fA-F]+|\d+)", text)
         assert m and int(m.group(1), 0) == getattr(L, name), name
+    for name in ("MV_F32", "MV_BF16", "MV_ACCEPT_GREEDY", "MV_ACCEPT_SPECULATIVE",
+                 "MV_ACCEPT_MULTICAND"):
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
+        assert m and int(m.group(1)) == getattr(L, name), name
 
 
 def test_status_strings():
@@ -50,6 +54,9 @@ def test_workspace_queries():
     assert lib.mv_tree_attn_verify_workspace(L.MV_F32, 1, 8, 4, 4, 64, 128) == 0    # no split
     assert lib.mv_accept_paths_workspace(L.MV_ACCEPT_GREEDY, 1, 64, 32000) > 0
     assert lib.mv_accept_paths_workspace(L.MV_ACCEPT_SPECULATIVE, 64, 64, 128256) > 0
+    assert (lib.mv_accept_paths_workspace(L.MV_ACCEPT_MULTICAND, 64, 64, 128256)
+            == lib.mv_accept_paths_workspace(L.MV_ACCEPT_SPECULATIVE, 64, 64, 128256))
+    assert lib.mv_accept_paths_workspace(3, 64, 64, 128256) == 0
     assert lib.mv_lm_head_workspace(L.MV_BF16, 65, 4096, 32000) >= 65 * 500 * 12  # 3 x [T][V/64]
     assert lib.mv_lm_head_workspace(L.MV_F32, 65, 4096, 32000) == 0               # bf16 only
     assert lib.mv_lm_head_workspace(L.MV_BF16, 65, 4080, 32000) == 0              # d % 32
@@ -99,6 +106,12 @@ def test_host_argument_checks():
                                P, P, None, None, None, P, 1 << 20, None) == L.MV_ERR_UNSUPPORTED
     assert lib.mv_accept_paths(L.MV_ACCEPT_GREEDY, L.MV_F32, 1, 4, 10, 2, P, P, P, None, None, P,
                                P, P, None, None, None, None, 0, None) == L.MV_ERR_WORKSPACE
+    assert lib.mv_accept_paths(L.MV_ACCEPT_MULTICAND, L.MV_BF16, 1, 4, 10, 2, P, P, P, P, P, P, P,
+                               P, None, None, None, P, 1 << 20, None) == L.MV_ERR_UNSUPPORTED
+    assert lib.mv_accept_paths(L.MV_ACCEPT_MULTICAND, L.MV_F32, 1, 4, 10, 2, P, P, P, P, None, P,
+                               P, P, None, None, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
+    assert lib.mv_accept_paths(3, L.MV_F32, 1, 4, 10, 2, P, P, P, P, P, P,
+                               P, P, None, None, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
     # argmax-id targets: greedy only
     assert lib.mv_accept_paths(L.MV_ACCEPT_SPECULATIVE, L.MV_TARGET_IDS, 1, 4, 10, 2, P, P, P, P, P,
                                P, P, P, None, None, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
