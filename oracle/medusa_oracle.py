@@ -43,7 +43,7 @@ import numpy as np
 __all__ = [
     "silu", "medusa_heads", "topk_rows", "build_tree", "tree_attention",
     "accept_greedy", "accept_speculative", "paths_to_parents", "lm_head_argmax", "kv_commit",
-    "accept_multicandidate",
+    "accept_multicandidate", "dynamic_tree",
 ]
 
 
@@ -483,3 +483,68 @@ def accept_multicandidate(p_target, p_draft, node_tokens, parents, uniforms,
     acc_len, path_nodes, out_tokens = _pack(res, B, D)
     return {"accept_len": acc_len, "path_nodes": path_nodes, "out_tokens": out_tokens,
             "node_accept": accepted, "alpha": alpha}
+
+
+# --------------------------------------------------------------------------
+# 9. Dynamic (confidence-ranked) tree ("Multi-Token Prediction: Draft-Model-Free
+#    Speculative Decoding", section "2. EAGLE & EAGLE-2: Feature-Level
+#    Autoregression": the tree is shaped by the candidates' confidence, deeper
+#    where the predictions are sure and wider where they are not; "Production
+#    Deployment Guidelines", "Dynamic Tree Depth Tuning": depth and the number
+#    of candidate paths are tuned per workload).  Reading: a node is a
+#    path of candidate ranks (r_1 .. r_d), one per Medusa head, scored by the
+#    log of its joint probability sum_k log p_k(r_k); the tree is the N
+#    best-scoring paths.  A path never scores above its prefix, so the set is
+#    a tree.  Ties: higher score first, then smaller depth, then smaller ranks
+#    in order from the first head.  Nodes are laid out breadth first, children
+#    of a node in rank order.
+# --------------------------------------------------------------------------
+def dynamic_tree(cand_ids, cand_vals, cand_lse, s_per_depth: Sequence[int],
+                 N: int) -> Dict[str, object]:
+    """The N most probable candidate paths of each sequence, as a tree.
+
+    cand_ids / cand_vals [B, D, s_max]: head k's candidates, best first (ids and logits);
+    cand_lse [B, D] (log-sum-exp of head k's logits) or None when cand_vals already hold
+    log-probabilities; log-probabilities above 0 count as 0.  Only the first s_per_depth[k]
+    candidates of head k are used.
+    Returns per sequence lists: parents, depth (1-based), tokens, score (fp64 joint
+    log-probability, summed from the first head on), ranks, and the ancestor sets."""
+    ids = np.asarray(cand_ids)
+    vals = _f64(cand_vals)
+    B, D, _ = vals.shape
+    # log-probabilities, clamped at 0 (a dominant token's val - lse can round above 0), so
+    # that no path scores above its prefix
+    logp = np.minimum(0.0, vals - (_f64(cand_lse)[:, :, None] if cand_lse is not None else 0.0))
+    out = {"parents": [], "depth": [], "tokens": [], "score": [], "ranks": [], "anc": []}
+    for b in range(B):
+        paths = []
+        stack = [((), 0.0)]
+        while stack:
+            ranks, sc = stack.pop()
+            d = len(ranks)
+            if d == D:
+                continue
+            for r in range(int(s_per_depth[d])):
+                s2 = sc + logp[b, d, r]
+                paths.append((ranks + (r,), s2))
+                stack.append((ranks + (r,), s2))
+        if len(paths) < N:
+            raise ValueError("fewer candidate paths than tree nodes")
+        paths.sort(key=lambda t: (-t[1], len(t[0]), t[0]))
+        chosen = {rk: sc for rk, sc in paths[:N]}
+        order = []                      # breadth first; children in rank order
+        pos = {(): -1}
+        for d in range(1, D + 1):
+            level = [rk for rk in chosen if len(rk) == d]
+            level.sort(key=lambda rk: (pos[rk[:-1]], rk[-1]))
+            for rk in level:
+                pos[rk] = len(order)
+                order.append(rk)
+        parents = [pos[rk[:-1]] for rk in order]
+        out["parents"].append(parents)
+        out["depth"].append([len(rk) for rk in order])
+        out["tokens"].append([int(ids[b, len(rk) - 1, rk[-1]]) for rk in order])
+        out["score"].append([chosen[rk] for rk in order])
+        out["ranks"].append(order)
+        out["anc"].append(build_tree(parents)["anc"])
+    return out
