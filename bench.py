@@ -48,6 +48,8 @@ DESCR = {
           "tree, speculative acceptance over V=128256 (fp32 probabilities)",
     "c7": "spec-serving-b64-multicand: the spec-serving-b64 attention with 4/3/2/1 independent "
           "draft samples per node and sibling-recursive (lossless) acceptance over V=128256",
+    "c8": "llama3-8b-layer-dyntree: the llama3-8b-layer step with 10 candidates per head and a "
+          "per-sequence dynamic tree of the 64 most probable candidate paths",
     "c6": "llama3-8b-layer-lmhead: the llama3-8b-layer step with the greedy target computed by "
           "the target LM head (W_lm 32000 x 4096 bf16 over the 65 verify rows, argmax fused)",
 }
@@ -141,7 +143,17 @@ def cpu_baseline(wl, x, seed, budget_s):
             cand += [heads["topk_ids"][:, k, :wl.head_widths[k]] for k in range(wl.K)]
         elif wl.accept == "speculative":
             cand = None
-        tree = O.build_tree(parents, cand, list(wl.depth_widths)) if cand else O.build_tree(parents)
+        if wl.dynamic_nodes:         # one tree per sequence: its most probable head paths
+            dyn = O.dynamic_tree(heads["topk_ids"], heads["topk_vals"], heads["lse"],
+                                 list(wl.head_widths), wl.dynamic_nodes)
+            trees = [{"parents": dyn["parents"][b], "anc": dyn["anc"][b],
+                      "tokens": np.array([dyn["tokens"][b]])} for b in range(wl.B)]
+        else:
+            tree = (O.build_tree(parents, cand, list(wl.depth_widths)) if cand
+                    else O.build_tree(parents))
+            trees = [{"parents": parents, "anc": tree["anc"],
+                      "tokens": tree["tokens"][b:b + 1] if "tokens" in tree else None}
+                     for b in range(wl.B)]
         t1 = time.perf_counter()
         target = None
         x_t = None
@@ -151,7 +163,11 @@ def cpu_baseline(wl, x, seed, budget_s):
                 x_t = W.plant_target_head(x_t, x["w_lm"], parents, tree["tokens"], seed, wl.plant_p)
         elif wl.accept == "greedy":  # input generation (planting) is not timed
             target = x["target"].copy()
-            if wl.plant_p > 0:
+            if wl.plant_p > 0 and wl.dynamic_nodes:
+                for b, t in enumerate(trees):
+                    target[b:b + 1] = W.plant_greedy(target[b:b + 1], t["parents"], t["tokens"],
+                                                     seed + b, wl.plant_p)
+            elif wl.plant_p > 0:
                 target = W.plant_greedy(target, parents, tree["tokens"], seed, wl.plant_p)
             if wl.dtype == "bf16":
                 target = W.round_bf16(target)
@@ -159,11 +175,21 @@ def cpu_baseline(wl, x, seed, budget_s):
         # attention: whole batch when it fits the budget, else a slice of the query rows
         if sample is None:
             sample = "1 full step"
-        O.tree_attention(x["q"], x["k_cache"], x["v_cache"], x["prefix_len"], tree["anc"])
+        if wl.dynamic_nodes:
+            for b, t in enumerate(trees):
+                sl = slice(b, b + 1)
+                O.tree_attention(x["q"][sl], x["k_cache"][sl], x["v_cache"][sl],
+                                 x["prefix_len"][sl], t["anc"])
+        else:
+            O.tree_attention(x["q"], x["k_cache"], x["v_cache"], x["prefix_len"], tree["anc"])
         if wl.target_head:
             z = O.lm_head_argmax(x_t.reshape(-1, wl.d), x["w_lm"])["logits"]
             target = z.reshape(wl.B, wl.N + 1, wl.accept_V)
-        if wl.accept == "greedy":
+        if wl.accept == "greedy" and wl.dynamic_nodes:
+            per = [O.accept_greedy(target[b:b + 1], t["tokens"], t["parents"], wl.D)
+                   for b, t in enumerate(trees)]
+            acc = {k: np.concatenate([a[k] for a in per]) for k in ("accept_len", "path_nodes")}
+        elif wl.accept == "greedy":
             acc = O.accept_greedy(target, tree["tokens"], parents, wl.D)
         elif wl.accept == "multicand":
             acc = O.accept_multicandidate(x["p_target"], x["p_draft"], x["node_tokens"], parents,
@@ -249,7 +275,7 @@ def main():
                       if wl.has_heads else None,
                       lm_width=wl.lm_width, accept=wl.accept, V=wl.accept_V,
                       tokens_given=not wl.has_heads, target_head=wl.d if wl.target_head else None,
-                      commit=wl.accept != "none")
+                      commit=wl.accept != "none", dynamic_nodes=wl.dynamic_nodes or None)
     d = lambda a, t=dt: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
     static = {}
     if wl.has_heads:
@@ -290,7 +316,14 @@ def main():
                 c[part]()
             torch.cuda.synchronize()
             toks = step.tree["node_tokens"].cpu().numpy()
-            tgt = W.plant_greedy(x["target"].copy(), list(wl.parents), toks, seed, wl.plant_p)
+            if step.dynamic:         # each sequence planted against its own tree
+                par = step.parents.cpu().numpy()
+                tgt = x["target"].copy()
+                for b in range(wl.B):
+                    tgt[b:b + 1] = W.plant_greedy(tgt[b:b + 1], par[b].tolist(), toks[b:b + 1],
+                                                  seed + b, wl.plant_p)
+            else:
+                tgt = W.plant_greedy(x["target"].copy(), list(wl.parents), toks, seed, wl.plant_p)
             base["target"] = d(W.round_bf16(tgt) if wl.dtype == "bf16" else tgt)
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
     seqs = [step.sequence(step.bind(dict(static, **s))) for s in sets]

@@ -188,6 +188,39 @@ MV_API int mv_build_tree_mask(int N, const int32_t* parents, int B, int D, int s
                        void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Dynamic (confidence-ranked) tree: an alternative to (a3) for per-sequence trees.
+ * [MTP] "2. EAGLE & EAGLE-2: Feature-Level Autoregression": the tree follows the candidates'
+ * confidence (deeper where the predictions are sure, wider where they are not); [MTP]
+ * "Production Deployment Guidelines", "Dynamic Tree Depth Tuning"; [MX] "1. Combinatorial
+ * Tree Construction": head k proposes the candidates of depth k.
+ *
+ * A node is a path of candidate ranks (r_1 .. r_d), scored by sum_k log p_k(r_k) with
+ * log p = min(0, cand_vals - cand_lse) summed in fp64 from the first head on.  Each
+ * sequence's tree is its N best paths: higher score first, then smaller depth, then smaller
+ * ranks from the first head on.  Nodes are laid out breadth first, children of a node in rank
+ * order (parents[i] < i).  The outputs feed mv_tree_attn_verify (mask_stride = N *
+ * ceil(N/32)) and mv_accept_paths (parents_stride = N).
+ *
+ *   cand_ids, cand_vals [B, D, s_max]: head k's candidates best first (int32 token ids, fp32
+ *            logits), e.g. from mv_medusa_head_select with ld = D * s_max.
+ *   cand_lse [B, D] fp32 (each head's log-sum-exp) or NULL when cand_vals are
+ *            log-probabilities.
+ *   s_per_depth host [D] (1 <= s_k <= s_max) or NULL for s_max everywhere; D <= 15,
+ *            s_max <= MV_MAX_TOPK, N <= MV_MAX_NODES, and the number of paths
+ *            sum_d prod_{k<=d} s_k must be >= N (else MV_ERR_INVALID_ARG).
+ *   parents, depth (1-based), node_tokens [B, N] int32; anc_mask [B, N, ceil(N/32)] uint32
+ *            (ancestor-or-self bits, as mv_build_tree_mask); node_logp [B, N] fp32 (the
+ *            path's score) or NULL.
+ *   dev_status MV_DEV_BAD_RANK when a chosen candidate's id is negative (an empty slot).
+ * One 64-lane workgroup per sequence; no workspace.
+ * ------------------------------------------------------------------------------------- */
+MV_API int mv_build_dynamic_tree(int B, int D, int s_max, const int* s_per_depth, int N,
+                                 const int32_t* cand_ids, const float* cand_vals,
+                                 const float* cand_lse, int32_t* parents, int32_t* depth,
+                                 int32_t* node_tokens, uint32_t* anc_mask, float* node_logp,
+                                 int32_t* dev_status, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * (a4)+(a5) Tree-masked GQA attention.  [MX] "2. Single-Pass Tree Attention Verification":
  * the tree is flattened into one packed sequence after the prefix and each node attends to
  * the whole prefix plus its ancestors (additive mask 0 / -inf); [MTP] "The 2D Tree Attention
@@ -198,7 +231,10 @@ MV_API int mv_build_tree_mask(int N, const int32_t* parents, int B, int D, int s
  *   k_cache, v_cache [B, Hkv, L_cap, dh]: rows [0, L_b) of sequence b are the prefix and rows
  *            [L_b, L_b + N) hold the tree's own keys/values in node order; L_b =
  *            prefix_len[b] (device int32 [B]), 0 <= L_b <= max_L, L_b + N <= L_cap.
- *   anc_mask [N, ceil(N/32)] uint32 from mv_build_tree_mask.
+ *   anc_mask [N, ceil(N/32)] uint32 from mv_build_tree_mask (one tree for the batch,
+ *            mask_stride = 0), or one mask per sequence, sequence b's at
+ *            anc_mask + b * mask_stride (mask_stride >= N * ceil(N/32) words; e.g. from
+ *            mv_build_dynamic_tree).
  *   scale    softmax scale; <= 0 selects 1/sqrt(dh).
  *   out      [B, N, Hq, dh] dt output.  lse [B, Hq, N] fp32 natural-log output, or NULL.
  *   ws       workspace from mv_tree_attn_verify_workspace() with the same sizes: the prefix
@@ -209,9 +245,9 @@ MV_API size_t mv_tree_attn_verify_workspace(int dt, int B, int N, int Hq, int Hk
 
 MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, int L_cap, int max_L,
                         const void* q, const void* k_cache, const void* v_cache,
-                        const int32_t* prefix_len, const uint32_t* anc_mask, float scale,
-                        void* out, float* lse, int32_t* dev_status, void* ws, size_t ws_bytes,
-                        void* stream);
+                        const int32_t* prefix_len, const uint32_t* anc_mask, int mask_stride,
+                        float scale, void* out, float* lse, int32_t* dev_status, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * Target LM head over the verification rows (the row before acceptance).  [MX] "2. Single-Pass
@@ -266,10 +302,12 @@ MV_API int mv_lm_head_argmax(int dt, int T, int d, int V, const void* x, const v
  *   that were never tested; node_accept marks the path.  Each rejection followed by a
  *   further sibling costs one pass over the vocabulary row.
  *
- *   target_dt MV_BF16 or MV_F32 for greedy; must be MV_F32 for the two sampling modes.  Greedy also
- *            takes MV_TARGET_IDS: target then holds the target's greedy token per row,
- *            int32 [B, N+1] (e.g. from mv_lm_head_argmax), and needs no workspace.
- *   parents [N], node_tokens [B, N] int32; target [B, N+1, V]; draft [B, N+1, V] fp32 and
+ *   target_dt MV_BF16 or MV_F32 for greedy; must be MV_F32 for the two sampling modes.
+ *            Greedy also takes MV_TARGET_IDS: target then holds the target's greedy token per
+ *            row, int32 [B, N+1] (e.g. from mv_lm_head_argmax), and needs no workspace.
+ *   parents [N] int32 (one tree for the batch, parents_stride = 0) or one parent array per
+ *            sequence at parents + b * parents_stride (parents_stride >= N).
+ *   node_tokens [B, N] int32; target [B, N+1, V]; draft [B, N+1, V] fp32 and
  *   uniforms [B, N+1] fp32 in [0, 1) (sampling modes only, else NULL).
  *   D        max tree depth (size of the outputs), 1..MV_MAX_DEPTH.
  *   accept_len [B] int32; path_nodes [B, D] int32 (-1 padded); out_tokens [B, D+1] int32
@@ -280,7 +318,8 @@ MV_API int mv_lm_head_argmax(int dt, int T, int d, int V, const void* x, const v
  * ------------------------------------------------------------------------------------- */
 MV_API size_t mv_accept_paths_workspace(int mode, int B, int N, int V);
 
-MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D, const int32_t* parents,
+MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D,
+                    const int32_t* parents, int parents_stride,
                     const int32_t* node_tokens, const void* target, const float* draft,
                     const float* uniforms, int32_t* accept_len, int32_t* path_nodes,
                     int32_t* out_tokens, uint8_t* node_accept, float* alpha,

@@ -59,14 +59,15 @@ SIGNATURES = [
     ("mv_topk_rows", _I, [_I, _I, _I, _I, _P, _LL, _P, _P, _I, _P]),
     ("mv_build_tree_mask", _I, [_I, _P, _I, _I, _I, _IP, _P, _P, _P, _P, _P, _P]),
     ("mv_tree_attn_verify_workspace", _Z, [_I, _I, _I, _I, _I, _I, _I]),
-    ("mv_tree_attn_verify", _I, [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _F, _P, _P,
-                                 _P, _P, _Z, _P]),
+    ("mv_tree_attn_verify", _I, [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _F, _P,
+                                 _P, _P, _P, _Z, _P]),
     ("mv_lm_head_workspace", _Z, [_I, _I, _I, _I]),
     ("mv_lm_head_argmax", _I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     ("mv_accept_paths_workspace", _Z, [_I, _I, _I, _I]),
+    ("mv_build_dynamic_tree", _I, [_I, _I, _I, _IP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     ("mv_kv_commit", _I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
-    ("mv_accept_paths", _I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                             _P, _Z, _P]),
+    ("mv_accept_paths", _I, [_I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                             _P, _P, _Z, _P]),
 ]
 
 _lib = None

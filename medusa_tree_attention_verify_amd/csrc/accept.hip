@@ -39,6 +39,7 @@ struct AcceptParams {
   int vec4;  // speculative rows may be read as float4 (V, segLen multiples of 4; 16-byte bases)
   const int32_t* pred_ids;  // greedy with precomputed target argmax ids [B][N+1], or null
   const int32_t* parents;
+  int pstride;  // entries between two sequences' parent arrays (0: one tree for the batch)
   const int32_t* tokens;
   const void* target;
   const float* draft;
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(256) void accept_path_kernel(const AcceptParams p) 
   __shared__ float sv[4];
   __shared__ int si[4];
   const int b = blockIdx.x, tid = threadIdx.x, N = p.N, R = p.R;
-  if (tid < N) par[tid] = p.parents[tid];
+  if (tid < N) par[tid] = p.parents[static_cast<size_t>(b) * p.pstride + tid];
   if constexpr (!SPEC) {
     for (int r = tid; r < R && p.pred_ids; r += 256) pred[r] = p.pred_ids[static_cast<size_t>(b) * R + r];
     for (int r = tid; r < R && !p.pred_ids; r += 256) {
@@ -482,7 +483,7 @@ __global__ __launch_bounds__(kWalkThreads) void multicand_walk_kernel(const Acce
   int flags = 0;
   if (tid <= N) first[tid] = N;
   if (tid < N) {
-    par[tid] = p.parents[tid];
+    par[tid] = p.parents[static_cast<size_t>(b) * p.pstride + tid];
     alph[tid] = -1.f;
     onpath[tid] = 0;
   }
@@ -670,7 +671,8 @@ MV_API size_t mv_accept_paths_workspace(int mode, int B, int N, int V) {
 }
 
 MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D,
-                           const int32_t* parents, const int32_t* node_tokens, const void* target,
+                           const int32_t* parents, int parents_stride,
+                           const int32_t* node_tokens, const void* target,
                            const float* draft, const float* uniforms, int32_t* accept_len,
                            int32_t* path_nodes, int32_t* out_tokens, uint8_t* node_accept,
                            float* alpha, int32_t* dev_status, void* ws, size_t ws_bytes,
@@ -680,6 +682,7 @@ MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D,
   if (target_dt != MV_F32 && target_dt != MV_BF16 && target_dt != MV_TARGET_IDS) return MV_ERR_INVALID_ARG;
   if (target_dt == MV_TARGET_IDS && mode != MV_ACCEPT_GREEDY) return MV_ERR_INVALID_ARG;
   if (B < 1 || N < 1 || V < 1 || D < 1) return MV_ERR_INVALID_ARG;
+  if (parents_stride != 0 && parents_stride < N) return MV_ERR_INVALID_ARG;
   if (N > MV_MAX_NODES || D > MV_MAX_DEPTH) return MV_ERR_UNSUPPORTED;
   if (!parents || !node_tokens || !target || !accept_len || !path_nodes || !out_tokens)
     return MV_ERR_INVALID_ARG;
@@ -692,7 +695,7 @@ MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D,
   if (!ids) MV_TRY(check_ws(ws, ws_bytes, need.ws_bytes));
   AcceptParams p{};
   p.B = B; p.N = N; p.V = V; p.D = D; p.R = N + 1;
-  p.parents = parents; p.tokens = node_tokens; p.target = target; p.draft = draft;
+  p.parents = parents; p.pstride = parents_stride; p.tokens = node_tokens; p.target = target; p.draft = draft;
   p.uniforms = uniforms; p.accept_len = accept_len; p.path_nodes = path_nodes;
   p.out_tokens = out_tokens; p.node_accept = node_accept; p.alpha = alpha; p.status = dev_status;
   const AcceptPlan a = plan_accept(mode, B, N, V, ids ? nullptr : ws, ids ? nullptr : &p);

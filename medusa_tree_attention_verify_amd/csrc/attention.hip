@@ -48,6 +48,7 @@ struct AttnParams {
   const void* v;
   const int32_t* prefix_len;
   const uint32_t* anc;
+  int mask_stride;  // words between two sequences' masks (0: one mask for the whole batch)
   void* out;
   float* lse;
   float* part_o;
@@ -204,8 +205,10 @@ void tree_attn_bf16_kernel(const AttnParams p) {
       uint32_t aw[2] = {0xffffffffu, 0xffffffffu};
       if (tree) {
         const int w0 = 2 * (t - ntp);
-        aw[0] = qvalid ? p.anc[static_cast<size_t>(node) * p.W + w0] : 0u;
-        aw[1] = (qvalid && w0 + 1 < p.W) ? p.anc[static_cast<size_t>(node) * p.W + w0 + 1] : 0u;
+        const uint32_t* arow = p.anc + static_cast<size_t>(b) * p.mask_stride +
+                               static_cast<size_t>(node) * p.W;
+        aw[0] = qvalid ? arow[w0] : 0u;
+        aw[1] = (qvalid && w0 + 1 < p.W) ? arow[w0 + 1] : 0u;
       }
       vis = 0u;
 #pragma unroll
@@ -419,7 +422,8 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(const AttnParams p) 
   const size_t kvbase = (static_cast<size_t>(b) * p.Hkv + g) * p.L_cap * DH;
   const float* Kg = static_cast<const float*>(p.k) + kvbase;
   const float* Vg = static_cast<const float*>(p.v) + kvbase;
-  const uint32_t* ancrow = p.anc + static_cast<size_t>(i) * p.W;
+  const uint32_t* ancrow =
+      p.anc + static_cast<size_t>(b) * p.mask_stride + static_cast<size_t>(i) * p.W;
   const int nkeys = Lb + p.N;
   float m_run = -INFINITY, l_run = 0.f, acc[DH / 64];
 #pragma unroll
@@ -523,7 +527,8 @@ MV_API size_t mv_tree_attn_verify_workspace(int dt, int B, int N, int Hq, int Hk
 
 MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, int L_cap, int max_L,
                                const void* q, const void* k_cache, const void* v_cache,
-                               const int32_t* prefix_len, const uint32_t* anc_mask, float scale,
+                               const int32_t* prefix_len, const uint32_t* anc_mask,
+                               int mask_stride, float scale,
                                void* out, float* lse, int32_t* dev_status, void* ws,
                                size_t ws_bytes, void* stream) {
   if (dt != MV_F32 && dt != MV_BF16) return MV_ERR_INVALID_ARG;
@@ -533,6 +538,7 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
   if (dh != 64 && dh != 128) return MV_ERR_UNSUPPORTED;
   if (N > MV_MAX_NODES) return MV_ERR_UNSUPPORTED;
   if (max_L > L_cap - N) return MV_ERR_INVALID_ARG;
+  if (mask_stride != 0 && mask_stride < N * ((N + 31) / 32)) return MV_ERR_INVALID_ARG;
   const AttnPlan a = plan_attn(dt, B, N, Hq, Hkv, dh, max_L);
   MV_TRY(check_ws(ws, ws_bytes, a.ws_bytes));
   AttnParams p{};
@@ -541,6 +547,7 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
   p.W = (N + 31) / 32;
   p.scale_log2 = (scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(dh))) * kLog2e;
   p.q = q; p.k = k_cache; p.v = v_cache; p.prefix_len = prefix_len; p.anc = anc_mask;
+  p.mask_stride = mask_stride;
   p.out = out; p.lse = lse; p.status = dev_status;
   hipStream_t st = as_stream(stream);
   if (dt == MV_F32) {

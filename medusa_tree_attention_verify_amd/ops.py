@@ -203,6 +203,36 @@ def build_tree_mask(parents: torch.Tensor, cand: Optional[torch.Tensor] = None,
     return out
 
 
+def build_dynamic_tree(cand_ids: torch.Tensor, cand_vals: torch.Tensor,
+                       cand_lse: Optional[torch.Tensor], N: int,
+                       s_per_depth: Optional[Sequence[int]] = None,
+                       status: Optional[torch.Tensor] = None,
+                       out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """Per-sequence tree of the N most probable candidate paths.  cand_ids int32 and
+    cand_vals fp32 [B, D, s_max] (best first), cand_lse fp32 [B, D] or None (values are
+    log-probabilities).  Returns parents, depth, node_tokens [B, N], anc_mask [B, N, W] (as
+    int32), node_logp [B, N]."""
+    B, D, s_max = cand_ids.shape
+    _need(cand_ids, "cand_ids", torch.int32)
+    _need(cand_vals, "cand_vals", torch.float32, (B, D, s_max))
+    if cand_lse is not None:
+        _need(cand_lse, "cand_lse", torch.float32, (B, D))
+    W = (N + 31) // 32
+    dev = cand_ids.device
+    if out is None:
+        out = {"parents": torch.empty((B, N), dtype=torch.int32, device=dev),
+               "depth": torch.empty((B, N), dtype=torch.int32, device=dev),
+               "node_tokens": torch.empty((B, N), dtype=torch.int32, device=dev),
+               "anc_mask": torch.empty((B, N, W), dtype=torch.int32, device=dev),
+               "node_logp": torch.empty((B, N), dtype=torch.float32, device=dev)}
+    sp = L.int_array(s_per_depth) if s_per_depth is not None else None
+    L.check("mv_build_dynamic_tree", L.lib().mv_build_dynamic_tree(
+        B, D, s_max, sp, N, _ptr(cand_ids), _ptr(cand_vals), _ptr(cand_lse),
+        _ptr(out["parents"]), _ptr(out["depth"]), _ptr(out["node_tokens"]), _ptr(out["anc_mask"]),
+        _ptr(out.get("node_logp")), _ptr(status), _stream()))
+    return out
+
+
 # ------------------------------------------------------------------ attention
 def attn_workspace_bytes(dt: int, B: int, N: int, Hq: int, Hkv: int, dh: int, max_L: int) -> int:
     return int(L.lib().mv_tree_attn_verify_workspace(dt, B, N, Hq, Hkv, dh, max_L))
@@ -214,7 +244,9 @@ def tree_attn_verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
                      lse: Optional[torch.Tensor] = None, want_lse: bool = True,
                      status: Optional[torch.Tensor] = None,
                      ws: Optional[Workspace] = None):
-    """a4 + a5: tree-masked GQA attention; returns (out [B,N,Hq,dh], lse [B,Hq,N] or None)."""
+    """a4 + a5: tree-masked GQA attention; returns (out [B,N,Hq,dh], lse [B,Hq,N] or None).
+
+    anc_mask [N, W] (one tree for the batch) or [B, N, W] (one tree per sequence)."""
     dt = _dt(q)
     B, N, Hq, dh = q.shape
     _, Hkv, L_cap, _ = k_cache.shape
@@ -222,7 +254,13 @@ def tree_attn_verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     _need(k_cache, "k_cache", q.dtype, (B, Hkv, L_cap, dh))
     _need(v_cache, "v_cache", q.dtype, (B, Hkv, L_cap, dh))
     _need(prefix_len, "prefix_len", torch.int32, (B,))
-    _need(anc_mask, "anc_mask", None, (N, (N + 31) // 32))
+    W = (N + 31) // 32
+    if anc_mask.dim() == 3:
+        _need(anc_mask, "anc_mask", None, (B, N, W))
+        mstride = N * W
+    else:
+        _need(anc_mask, "anc_mask", None, (N, W))
+        mstride = 0
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -231,7 +269,8 @@ def tree_attn_verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     ptr, n = w.get(attn_workspace_bytes(dt, B, N, Hq, Hkv, dh, max_L))
     L.check("mv_tree_attn_verify", L.lib().mv_tree_attn_verify(
         dt, B, N, Hq, Hkv, dh, L_cap, int(max_L), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-        _ptr(prefix_len), _ptr(anc_mask), float(scale), _ptr(out), _ptr(lse), _ptr(status),
+        _ptr(prefix_len), _ptr(anc_mask), mstride, float(scale), _ptr(out), _ptr(lse),
+        _ptr(status),
         ptr, n, _stream()))
     return out, lse
 
@@ -279,7 +318,8 @@ def accept_paths(mode: int, parents: torch.Tensor, node_tokens: torch.Tensor,
     running residual): accepted length, path, committed tokens + extra token.
 
     Greedy also takes the target rows as argmax ids: target int32 [B, N+1] (then V = vocab
-    size must be given, used only to range-check node tokens)."""
+    size must be given, used only to range-check node tokens).  parents [N] (one tree for the
+    batch) or [B, N] (one tree per sequence)."""
     if target.dtype == torch.int32:
         if mode != L.MV_ACCEPT_GREEDY or vocab is None:
             raise ValueError("argmax-id targets need greedy mode and vocab=")
@@ -290,7 +330,12 @@ def accept_paths(mode: int, parents: torch.Tensor, node_tokens: torch.Tensor,
         dt = _dt(target)
         B, R, V = target.shape
     N = R - 1
-    _need(parents, "parents", torch.int32, (N,))
+    if parents.dim() == 2:
+        _need(parents, "parents", torch.int32, (B, N))
+        pstride = N
+    else:
+        _need(parents, "parents", torch.int32, (N,))
+        pstride = 0
     _need(node_tokens, "node_tokens", torch.int32, (B, N))
     _need(target, "target")
     spec = mode in (L.MV_ACCEPT_SPECULATIVE, L.MV_ACCEPT_MULTICAND)
@@ -309,7 +354,7 @@ def accept_paths(mode: int, parents: torch.Tensor, node_tokens: torch.Tensor,
     w = _ws("accept", ws)
     ptr, n = (None, 0) if dt == L.MV_TARGET_IDS else w.get(accept_workspace_bytes(mode, B, N, V))
     L.check("mv_accept_paths", L.lib().mv_accept_paths(
-        mode, dt, B, N, V, D, _ptr(parents), _ptr(node_tokens), _ptr(target), _ptr(draft),
+        mode, dt, B, N, V, D, _ptr(parents), pstride, _ptr(node_tokens), _ptr(target), _ptr(draft),
         _ptr(uniforms), _ptr(out["accept_len"]), _ptr(out["path_nodes"]), _ptr(out["out_tokens"]),
         _ptr(out.get("node_accept")), _ptr(out.get("alpha")), _ptr(status), ptr, n, _stream()))
     return out

@@ -31,14 +31,25 @@ class VerifyStep:
     PARTS = ("heads_residual", "heads_projection", "heads_select", "tree", "attention",
              "target_head", "accept", "commit")
 
-    def __init__(self, *, parents: Sequence[int], depth_widths: Sequence[int],
+    def __init__(self, *, parents: Optional[Sequence[int]], depth_widths: Sequence[int],
                  dtype: torch.dtype, B: int, Hq: int, Hkv: int, dh: int, max_L: int,
                  heads: Optional[Dict[str, object]] = None, lm_width: int = 0,
                  accept: str = "greedy", V: int = 0, tokens_given: bool = False,
-                 target_head: Optional[int] = None, commit: bool = False, device="cuda"):
-        ops.validate_parents(parents)
-        self.parents_list = [int(p) for p in parents]
-        self.N = len(parents)
+                 target_head: Optional[int] = None, commit: bool = False,
+                 dynamic_nodes: Optional[int] = None, device="cuda"):
+        # dynamic_nodes = N: each sequence's tree is its N most probable head-candidate paths
+        # (built every step from the heads' candidates); parents is then unused
+        self.dynamic = dynamic_nodes
+        if dynamic_nodes:
+            if heads is None or lm_width or tokens_given or heads["K"] != len(depth_widths):
+                raise ValueError("a dynamic tree is built from the Medusa heads' candidates "
+                                 "(one head per depth)")
+            self.parents_list = None
+            self.N = int(dynamic_nodes)
+        else:
+            ops.validate_parents(parents)
+            self.parents_list = [int(p) for p in parents]
+            self.N = len(parents)
         self.D = len(depth_widths)
         self.depth_widths = [int(s) for s in depth_widths]
         self.s_max = max(self.depth_widths)
@@ -57,14 +68,23 @@ class VerifyStep:
         self.target_head = target_head
         dev = torch.device(device)
         self.device = dev
-        self.parents = torch.tensor(self.parents_list, dtype=torch.int32, device=dev)
+        if self.dynamic:
+            self.parents = torch.empty((B, self.N), dtype=torch.int32, device=dev)
+        else:
+            self.parents = torch.tensor(self.parents_list, dtype=torch.int32, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         N, W = self.N, (self.N + 31) // 32
         self.cand = torch.full((B, self.D, self.s_max), -1, dtype=torch.int32, device=dev)
         self.cand_vals = torch.empty((B, self.D, self.s_max), dtype=torch.float32, device=dev)
-        self.tree = {"anc_mask": torch.empty((N, W), dtype=torch.int32, device=dev),
-                     "depth": torch.empty(N, dtype=torch.int32, device=dev),
-                     "node_tokens": torch.empty((B, N), dtype=torch.int32, device=dev)}
+        if self.dynamic:
+            self.tree = {"anc_mask": torch.empty((B, N, W), dtype=torch.int32, device=dev),
+                         "depth": torch.empty((B, N), dtype=torch.int32, device=dev),
+                         "node_tokens": torch.empty((B, N), dtype=torch.int32, device=dev),
+                         "node_logp": torch.empty((B, N), dtype=torch.float32, device=dev)}
+        else:
+            self.tree = {"anc_mask": torch.empty((N, W), dtype=torch.int32, device=dev),
+                         "depth": torch.empty(N, dtype=torch.int32, device=dev),
+                         "node_tokens": torch.empty((B, N), dtype=torch.int32, device=dev)}
         self.attn_out = torch.empty((B, N, Hq, dh), dtype=dtype, device=dev)
         self.attn_lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
         self.ws_heads = ops.Workspace(dev)
@@ -150,6 +170,13 @@ class VerifyStep:
                                  0, 0, 0, None, None, _p(self.tree["anc_mask"]),
                                  _p(self.tree["depth"]), None, _p(self.status), st)
             tokens = inp.get("node_tokens")
+        elif self.dynamic:
+            calls["tree"] = wrap("mv_build_dynamic_tree", lib.mv_build_dynamic_tree, B, D, s_max,
+                                 self._s_depth, N, _p(self.cand), _p(self.cand_vals),
+                                 _p(self.head_lse), _p(self.parents), _p(self.tree["depth"]),
+                                 _p(self.tree["node_tokens"]), _p(self.tree["anc_mask"]),
+                                 _p(self.tree["node_logp"]), _p(self.status), st)
+            tokens = self.tree["node_tokens"]
         else:
             calls["tree"] = wrap("mv_build_tree_mask", lib.mv_build_tree_mask, N, _p(self.parents),
                                  B, D, s_max, self._s_depth, _p(self.cand),
@@ -161,7 +188,9 @@ class VerifyStep:
         calls["attention"] = wrap("mv_tree_attn_verify", lib.mv_tree_attn_verify, self.dt, B, N,
                                   self.Hq, self.Hkv, self.dh, Lcap, self.max_L, _p(inp["q"]),
                                   _p(inp["k_cache"]), _p(inp["v_cache"]), _p(inp["prefix_len"]),
-                                  _p(self.tree["anc_mask"]), 0.0, _p(self.attn_out),
+                                  _p(self.tree["anc_mask"]),
+                                  N * ((N + 31) // 32) if self.dynamic else 0, 0.0,
+                                  _p(self.attn_out),
                                   _p(self.attn_lse), _p(self.status), wsp, wsn, st)
         if self.target_head:
             wsp, wsn = self._ws(self.ws_lm)
@@ -179,7 +208,8 @@ class VerifyStep:
                 Vt = tgt.shape[2]
             a = self.acc
             calls["accept"] = wrap("mv_accept_paths", lib.mv_accept_paths, self.mode, tdt, B, N,
-                                   Vt, D, _p(self.parents), _p(tokens), _p(tgt),
+                                   Vt, D, _p(self.parents), N if self.dynamic else 0, _p(tokens),
+                                   _p(tgt),
                                    _p(inp.get("draft")), _p(inp.get("uniforms")),
                                    _p(a["accept_len"]), _p(a["path_nodes"]), _p(a["out_tokens"]),
                                    _p(a["node_accept"]), _p(a["alpha"]), _p(self.status), wsp,

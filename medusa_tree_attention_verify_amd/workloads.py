@@ -92,6 +92,7 @@ class Workload:
     target_std: float = 2.0
     plant_p: float = 0.0             # probability that a parent row's argmax is one of its children
     draft_noise_std: float = 1.0
+    dynamic_nodes: int = 0           # > 0: per-sequence tree of the N most probable head paths
     draft_tokens: str = "top"        # sampling modes: children's tokens are the draft row's
                                      # top tokens ("top") or independent draws from it ("sampled")
     qkv_scaled: bool = False         # Q,K,V divided by sqrt(dh)
@@ -154,6 +155,13 @@ WORKLOADS: Dict[str, Workload] = {
                    parents=_T4321, prefix=(512, 8192), depth_widths=(4, 3, 2, 1),
                    accept="multicand", accept_V=128256, target_std=3.0,
                    draft_noise_std=1.0, draft_tokens="sampled"),
+    # the Llama-3-8B-shaped step with a dynamic tree: each head proposes 10 candidates and the
+    # tree is the 64 most probable paths (parents below only fix N = 64 for the shapes)
+    "c8": Workload(name="llama3-8b-layer-dyntree", dtype="bf16", B=1, Hq=32, Hkv=8, dh=128,
+                   parents=_T4321, prefix=(4096, 4096), depth_widths=(10, 10, 10, 10),
+                   d=4096, V=32000, K=4, head_widths=(10, 10, 10, 10), weight_std=0.02,
+                   accept="greedy", accept_V=32000, target_std=2.0, plant_p=0.6,
+                   dynamic_nodes=64),
     "c6": Workload(name="llama3-8b-layer-lmhead", dtype="bf16", B=1, Hq=32, Hkv=8, dh=128,
                    parents=_T4321, prefix=(4096, 4096), depth_widths=(4, 3, 2, 1),
                    d=4096, V=32000, K=4, head_widths=(4, 3, 2, 1), weight_std=0.02,

@@ -19,7 +19,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -92,29 +92,41 @@ def test_host_argument_checks():
     assert lib.mv_build_tree_mask(257, P, 0, 0, 0, None, None, P, None, None, None, None) == L.MV_ERR_UNSUPPORTED
     assert lib.mv_build_tree_mask(8, P, 1, 17, 2, None, P, P, None, P, None, None) == L.MV_ERR_UNSUPPORTED
     # attention
-    args = (P, P, P, P, P, 0.0, P, None, None)
+    args = (P, P, P, P, P, 0, 0.0, P, None, None)
     assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 6, 4, 128, 200, 100, *args, None, 0, None) == L.MV_ERR_INVALID_ARG
     assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 8, 4, 96, 200, 100, *args, None, 0, None) == L.MV_ERR_UNSUPPORTED
     assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 8, 4, 128, 100, 100, *args, None, 0, None) == L.MV_ERR_INVALID_ARG
     assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 8, 4, 128, 10000, 8000, *args, None, 0, None) == L.MV_ERR_WORKSPACE
+    bad_stride = (P, P, P, P, P, 7, 0.0, P, None, None)     # N * W = 8 words per sequence
+    assert lib.mv_tree_attn_verify(L.MV_BF16, 2, 8, 8, 4, 128, 200, 100, *bad_stride, None, 0, None) == L.MV_ERR_INVALID_ARG
     # acceptance
-    assert lib.mv_accept_paths(L.MV_ACCEPT_SPECULATIVE, L.MV_BF16, 1, 4, 10, 2, P, P, P, P, P, P, P,
+    assert lib.mv_accept_paths(L.MV_ACCEPT_SPECULATIVE, L.MV_BF16, 1, 4, 10, 2, P, 0, P, P, P, P, P, P,
                                P, None, None, None, P, 1 << 20, None) == L.MV_ERR_UNSUPPORTED
-    assert lib.mv_accept_paths(L.MV_ACCEPT_SPECULATIVE, L.MV_F32, 1, 4, 10, 2, P, P, P, None, P, P,
+    assert lib.mv_accept_paths(L.MV_ACCEPT_SPECULATIVE, L.MV_F32, 1, 4, 10, 2, P, 0, P, P, None, P, P,
                                P, P, None, None, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
-    assert lib.mv_accept_paths(L.MV_ACCEPT_GREEDY, L.MV_F32, 1, 4, 10, 17, P, P, P, None, None, P,
+    assert lib.mv_accept_paths(L.MV_ACCEPT_GREEDY, L.MV_F32, 1, 4, 10, 17, P, 0, P, P, None, None, P,
                                P, P, None, None, None, P, 1 << 20, None) == L.MV_ERR_UNSUPPORTED
-    assert lib.mv_accept_paths(L.MV_ACCEPT_GREEDY, L.MV_F32, 1, 4, 10, 2, P, P, P, None, None, P,
+    assert lib.mv_accept_paths(L.MV_ACCEPT_GREEDY, L.MV_F32, 1, 4, 10, 2, P, 0, P, P, None, None, P,
                                P, P, None, None, None, None, 0, None) == L.MV_ERR_WORKSPACE
-    assert lib.mv_accept_paths(L.MV_ACCEPT_MULTICAND, L.MV_BF16, 1, 4, 10, 2, P, P, P, P, P, P, P,
+    assert lib.mv_accept_paths(L.MV_ACCEPT_MULTICAND, L.MV_BF16, 1, 4, 10, 2, P, 0, P, P, P, P, P, P,
                                P, None, None, None, P, 1 << 20, None) == L.MV_ERR_UNSUPPORTED
-    assert lib.mv_accept_paths(L.MV_ACCEPT_MULTICAND, L.MV_F32, 1, 4, 10, 2, P, P, P, P, None, P,
+    assert lib.mv_accept_paths(L.MV_ACCEPT_MULTICAND, L.MV_F32, 1, 4, 10, 2, P, 0, P, P, P, None, P,
                                P, P, None, None, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
-    assert lib.mv_accept_paths(3, L.MV_F32, 1, 4, 10, 2, P, P, P, P, P, P,
+    assert lib.mv_accept_paths(3, L.MV_F32, 1, 4, 10, 2, P, 0, P, P, P, P, P,
+                               P, P, None, None, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
+    # a per-sequence parents stride shorter than N
+    assert lib.mv_accept_paths(L.MV_ACCEPT_GREEDY, L.MV_F32, 2, 4, 10, 2, P, 3, P, P, None, None, P,
                                P, P, None, None, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
     # argmax-id targets: greedy only
-    assert lib.mv_accept_paths(L.MV_ACCEPT_SPECULATIVE, L.MV_TARGET_IDS, 1, 4, 10, 2, P, P, P, P, P,
+    assert lib.mv_accept_paths(L.MV_ACCEPT_SPECULATIVE, L.MV_TARGET_IDS, 1, 4, 10, 2, P, 0, P, P, P, P,
                                P, P, P, None, None, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
+    # dynamic tree
+    dyn = lambda D, smax, s, N: lib.mv_build_dynamic_tree(
+        1, D, smax, L.int_array(s) if s else None, N, P, P, None, P, P, P, P, None, None, None)
+    assert dyn(16, 4, None, 8) == L.MV_ERR_UNSUPPORTED          # depth above 15
+    assert dyn(2, 17, None, 8) == L.MV_ERR_UNSUPPORTED          # more than 16 candidates
+    assert dyn(2, 4, [2, 2], 7) == L.MV_ERR_INVALID_ARG         # 2 + 4 = 6 paths < 7 nodes
+    assert dyn(2, 4, [5, 2], 8) == L.MV_ERR_INVALID_ARG         # width above s_max
     # KV commit
     kv = lambda dh, L_cap, D, pre=P, out=P: lib.mv_kv_commit(
         L.MV_BF16, 1, 8, dh, L_cap, 8, D, P, P, pre, out, P, P, None, None)
