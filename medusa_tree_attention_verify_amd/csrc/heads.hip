@@ -130,7 +130,17 @@ template <int SM>
 __device__ __forceinline__ void list_insert(float (&lv)[SM], int (&li)[SM], float v, int i) {
 #pragma unroll
   for (int q = 0; q < SM; ++q) {
-    if (kv_better(v, i, lv[q], li[q])) {
+    if constexpr (SM > 8) {
+      // long lists: a compare-exchange chain of selects (as branches, lanes that disagree
+      // run both sides of every step); short ones are faster with the branches
+      const bool c = kv_better(v, i, lv[q], li[q]);
+      const float tv = lv[q];
+      const int ti = li[q];
+      lv[q] = c ? v : tv;
+      li[q] = c ? i : ti;
+      v = c ? tv : v;
+      i = c ? ti : i;
+    } else if (kv_better(v, i, lv[q], li[q])) {
       const float tv = lv[q];
       const int ti = li[q];
       lv[q] = v;
