@@ -71,7 +71,7 @@ __device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool re
 #define MV_ATTN_TARGET_WG 1024  // split-KV: aim for this many workgroups
 #endif
 #ifndef MV_ATTN_MIN_CHUNK
-#define MV_ATTN_MIN_CHUNK 512   // but never chunks shorter than this many keys
+#define MV_ATTN_MIN_CHUNK 256   // but never chunks shorter than this many keys
 #endif
 
 constexpr int kKT = 64;  // keys per tile

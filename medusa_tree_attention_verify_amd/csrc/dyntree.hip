@@ -59,7 +59,10 @@ struct SelKey {
 };
 
 __device__ __forceinline__ void take_if_less(SelKey& x, uint64_t oa, uint64_t ok, uint32_t oj) {
-  if (oa < x.a || (oa == x.a && ok < x.k)) x = {oa, ok, oj};
+  const bool c = (oa < x.a) | ((oa == x.a) & (ok < x.k));  // selects, not a branch per lane
+  x.a = c ? oa : x.a;
+  x.k = c ? ok : x.k;
+  x.j = c ? oj : x.j;
 }
 
 template <int CTRL>
