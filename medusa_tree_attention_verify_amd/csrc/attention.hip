@@ -68,7 +68,10 @@ __device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool re
 }
 
 #ifndef MV_ATTN_TARGET_WG
-#define MV_ATTN_TARGET_WG 1024  // split-KV: aim for this many workgroups
+#define MV_ATTN_TARGET_WG 1024  // split-KV: aim for this many workgroups (one sequence)
+#endif
+#ifndef MV_ATTN_TARGET_WG_BATCH
+#define MV_ATTN_TARGET_WG_BATCH 512  // ... and with several sequences
 #endif
 #ifndef MV_ATTN_MIN_CHUNK
 #define MV_ATTN_MIN_CHUNK 256   // but never chunks shorter than this many keys
@@ -485,8 +488,8 @@ struct AttnPlan {
   size_t ws_bytes = 0;
 };
 
-// Chunking (split-KV): aim for MV_ATTN_TARGET_WG workgroups so that the chip stays busy and
-// sequences of different lengths balance, but keep chunks of at least MV_ATTN_MIN_CHUNK keys:
+// Chunking (split-KV): aim for MV_ATTN_TARGET_WG workgroups (MV_ATTN_TARGET_WG_BATCH for a
+// batch) so that the chip stays busy, but keep chunks of at least MV_ATTN_MIN_CHUNK keys:
 // every chunk writes an fp32 partial output as large as its query block, so short chunks turn
 // a K/V-streaming kernel into a partial-output-writing one.
 AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L) {
@@ -495,7 +498,10 @@ AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L) {
   const int M = N * (Hq / Hkv);
   a.qtiles = ceil_div(M, kNWV * 32);
   const long long base = static_cast<long long>(B) * Hkv * a.qtiles;
-  int want = static_cast<int>(std::max<long long>(1, (MV_ATTN_TARGET_WG + base - 1) / base));
+  // Several sequences of different lengths already balance across the chip, and every extra
+  // chunk writes M x dh partials that the combine reads back: aim lower for batches.
+  const long long target = B > 1 ? MV_ATTN_TARGET_WG_BATCH : MV_ATTN_TARGET_WG;
+  int want = static_cast<int>(std::max<long long>(1, (target + base - 1) / base));
   const int cap = std::max(1, ceil_div(max_L, MV_ATTN_MIN_CHUNK));
   want = std::min(want, cap);
   int ck = ceil_div(std::max(max_L, 1), want);
