@@ -41,7 +41,7 @@ namespace mv {
 namespace {
 
 struct AttnParams {
-  int B, N, Hq, Hkv, G, M, L_cap, max_L, CK, nchunks, qtiles, W, total;
+  int B, N, Hq, Hkv, G, M, L_cap, max_L, CK, nchunks, qtiles, W, jobs;
   float scale_log2;
   const void* q;
   const void* k;
@@ -54,6 +54,7 @@ struct AttnParams {
   float* part_o;
   float2* part_ml;
   int32_t* status;
+  const int32_t* order;  // sequences by decreasing prefix length (null: batch order)
 };
 
 constexpr int kXcds = 8;  // MI355X: workgroups are handed to the 8 XCDs round-robin
@@ -97,17 +98,17 @@ void tree_attn_bf16_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKT * KP];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKT * VKP];
 
-  // XCD-aware order: consecutive logical tiles (the query tiles of one KV chunk) run on one XCD.
-  const int per = (p.total + kXcds - 1) / kXcds;
-  const int lid = static_cast<int>(blockIdx.x % kXcds) * per + static_cast<int>(blockIdx.x / kXcds);
-  if (lid >= p.total) return;
-  int r = lid;
-  const int qt = r % p.qtiles;
-  r /= p.qtiles;
-  const int c = r % p.nchunks;
-  r /= p.nchunks;
-  const int g = r % p.Hkv;
-  const int b = r / p.Hkv;
+  // Job j = (sequence rank, chunk, KV head), longest sequences first (workgroups are dispatched
+  // in index order, so the long jobs do not end up in the tail); jobs are dealt round-robin
+  // over the XCDs, and the query tiles of one job stay on one XCD, where they share its K/V.
+  const int xcd = static_cast<int>(blockIdx.x % kXcds), pos = static_cast<int>(blockIdx.x / kXcds);
+  const int qt = pos % p.qtiles;
+  const int job = (pos / p.qtiles) * kXcds + xcd;
+  if (job >= p.jobs) return;
+  const int g = job % p.Hkv;
+  const int c = (job / p.Hkv) % p.nchunks;
+  const int rank = job / (p.Hkv * p.nchunks);
+  const int b = p.order ? p.order[rank] : rank;
 
   const int Lb = clamp_prefix(p, p.prefix_len[b], threadIdx.x == 0 && qt == 0 && c == 0 && g == 0);
   const int ncb = max(1, (Lb + p.CK - 1) / p.CK);
@@ -483,8 +484,24 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(const AttnParams p) 
 // ---------------------------------------------------------------------------------------
 constexpr int kNWV = 8;  // waves per workgroup -> 256 query rows
 
+// Sequences ranked by decreasing (clamped) prefix length, ties by index: order[rank] = b.
+constexpr int kOrderMaxB = 1024;
+
+__global__ __launch_bounds__(kOrderMaxB) void seq_order_kernel(const AttnParams p, int32_t* order) {
+  __shared__ int Ls[kOrderMaxB];
+  const int b = threadIdx.x;
+  if (b < p.B) Ls[b] = clamp_prefix(p, p.prefix_len[b], false);
+  __syncthreads();
+  if (b >= p.B) return;
+  const int Lb = Ls[b];
+  int rank = 0;
+  for (int j = 0; j < p.B; ++j) rank += Ls[j] > Lb || (Ls[j] == Lb && j < b);
+  order[rank] = b;
+}
+
 struct AttnPlan {
   int qtiles = 1, CK = 256, nchunks = 1;
+  bool ordered = false;  // a length ordering of the sequences in the workspace
   size_t ws_bytes = 0;
 };
 
@@ -508,13 +525,15 @@ AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L) {
   ck = std::max(MV_ATTN_MIN_CHUNK, (ck + kKT - 1) / kKT * kKT);
   a.CK = ck;
   a.nchunks = std::max(1, ceil_div(max_L, ck));
+  a.ordered = B > 1 && B <= kOrderMaxB;
+  Carver c(nullptr);
+  if (a.ordered) c.take<int32_t>(B);
   if (a.nchunks > 1) {
-    Carver c(nullptr);
     const size_t rows = static_cast<size_t>(B) * Hq * N * a.nchunks;
     c.take<float>(rows * dh);
     c.take<float2>(rows);
-    a.ws_bytes = c.bytes();
   }
+  a.ws_bytes = c.bytes();
   return a;
 }
 
@@ -563,18 +582,24 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
     else tree_attn_f32_kernel<128><<<blocks, 256, 0, st>>>(p);
     return launch_status();
   }
+  Carver c(ws);
+  int32_t* order = a.ordered ? c.take<int32_t>(B) : nullptr;
   if (a.nchunks > 1) {
-    Carver c(ws);
     const size_t rows = static_cast<size_t>(B) * Hq * N * a.nchunks;
     p.part_o = c.take<float>(rows * dh);
     p.part_ml = c.take<float2>(rows);
   }
-  const long long total = static_cast<long long>(B) * Hkv * a.nchunks * a.qtiles;
-  if (total > (1LL << 30)) return MV_ERR_UNSUPPORTED;
-  p.total = static_cast<int>(total);
-  const int grid = ceil_div(total, kXcds) * kXcds;
-  if (dh == 64) tree_attn_bf16_kernel<64, kNWV><<<grid, kNWV * 64, 0, st>>>(p);
-  else tree_attn_bf16_kernel<128, kNWV><<<grid, kNWV * 64, 0, st>>>(p);
+  const long long jobs = static_cast<long long>(B) * Hkv * a.nchunks;
+  const long long grid = (jobs + kXcds - 1) / kXcds * kXcds * a.qtiles;
+  if (grid > (1LL << 30)) return MV_ERR_UNSUPPORTED;
+  p.jobs = static_cast<int>(jobs);
+  if (order) {
+    seq_order_kernel<<<1, kOrderMaxB, 0, st>>>(p, order);
+    MV_TRY(launch_status());
+    p.order = order;
+  }
+  if (dh == 64) tree_attn_bf16_kernel<64, kNWV><<<static_cast<int>(grid), kNWV * 64, 0, st>>>(p);
+  else tree_attn_bf16_kernel<128, kNWV><<<static_cast<int>(grid), kNWV * 64, 0, st>>>(p);
   MV_TRY(launch_status());
   if (a.nchunks > 1) {
     const int rows = B * Hq * N;
