@@ -72,7 +72,7 @@ __device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool re
 #define MV_ATTN_TARGET_WG 1024  // split-KV: aim for this many workgroups (one sequence)
 #endif
 #ifndef MV_ATTN_TARGET_WG_BATCH
-#define MV_ATTN_TARGET_WG_BATCH 512  // ... and with several sequences
+#define MV_ATTN_TARGET_WG_BATCH 256  // ... and with several sequences
 #endif
 #ifndef MV_ATTN_MIN_CHUNK
 #define MV_ATTN_MIN_CHUNK 256   // but never chunks shorter than this many keys
