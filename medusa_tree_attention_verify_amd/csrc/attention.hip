@@ -80,6 +80,11 @@ __device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool re
 
 constexpr int kKT = 64;  // keys per tile
 
+// Raw buffer resource (gfx950): dword 3 selects 32-bit data format for untyped loads; an
+// offset at or past the record count reads as zero.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kBufferOutOfRange = 0x7fffffff;
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -150,6 +155,14 @@ void tree_attn_bf16_kernel(const AttnParams p) {
     }
   };
   // Two register sets of prefetched K/V pieces: tile t+2 is requested while tile t computes.
+  // Buffer loads over this (sequence, KV head)'s slice of the cache: rows past a partial tile
+  // and requests past the last tile get an offset beyond the slice, which the hardware's range
+  // check turns into zeros.  No load sits under a branch, so the wait before each LDS store
+  // leaves the other register set in flight.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Kg), 0, p.L_cap * DH * 2, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Vg), 0, p.L_cap * DH * 2, kBufferRsrcWord3);
   uint4 kr0[PPT], vr0[PPT], kr1[PPT], vr1[PPT];
   auto gload = [&](int t, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
     int row0 = 0, nv = 0;
@@ -157,14 +170,9 @@ void tree_attn_bf16_kernel(const AttnParams p) {
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int pc = tid + i * NT, key = pc / DG, dg = pc % DG;
-      if (key < nv) {
-        const size_t o = static_cast<size_t>(row0 + key) * DH + dg * 8;
-        kr[i] = *reinterpret_cast<const uint4*>(Kg + o);
-        vr[i] = *reinterpret_cast<const uint4*>(Vg + o);
-      } else {
-        kr[i] = make_uint4(0, 0, 0, 0);
-        vr[i] = make_uint4(0, 0, 0, 0);
-      }
+      const int off = key < nv ? ((row0 + key) * DH + dg * 8) * 2 : kBufferOutOfRange;
+      kr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+      vr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
     }
   };
   auto swrite = [&](int buf, const uint4 (&kr)[PPT], const uint4 (&vr)[PPT]) {
