@@ -364,10 +364,9 @@ void tree_attn_bf16_kernel(const AttnParams p) {
 
 // Merge of the chunk partials: O = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c, as an online
 // log-sum-exp over the chunks.  DH/4 lanes per output row, each with one 16-byte piece of every
-// partial; the partials of up to kCombineBatch chunks are requested before any is used.
-constexpr int kCombineBatch = 4;
-
-template <int DH>
+// partial; the partials of up to CB chunks are requested before any is used (CB covers every
+// chunk of the one-sequence launches, so their combine is a single round trip to memory).
+template <int DH, int CB>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   constexpr int LPR = DH / 4;       // lanes per row
   constexpr int RPB = 256 / LPR;    // rows per workgroup
@@ -381,18 +380,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   const size_t base = static_cast<size_t>(rowid) * p.nchunks;
   float M = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c0 = 0; c0 < ncb; c0 += kCombineBatch) {
-    float2 ml[kCombineBatch];
-    float4 po[kCombineBatch];
+  for (int c0 = 0; c0 < ncb; c0 += CB) {
+    float2 ml[CB];
+    float4 po[CB];
 #pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u) {
+    for (int u = 0; u < CB; ++u) {
       const int c = c0 + u;
       ml[u] = c < ncb ? p.part_ml[base + c] : make_float2(-INFINITY, 0.f);
       po[u] = c < ncb ? *reinterpret_cast<const float4*>(p.part_o + (base + c) * DH + 4 * e)
                       : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u) {
+    for (int u = 0; u < CB; ++u) {
       if (ml[u].x == -INFINITY) continue;
       const float mn = fmaxf(M, ml[u].x);
       const float a = exp2f(M - mn);  // 0 while M is -inf
@@ -611,8 +610,17 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
   MV_TRY(launch_status());
   if (a.nchunks > 1) {
     const int rows = B * Hq * N;
-    if (dh == 64) attn_combine_kernel<64><<<ceil_div(rows, 256 / 16), 256, 0, st>>>(p);
-    else attn_combine_kernel<128><<<ceil_div(rows, 256 / 32), 256, 0, st>>>(p);
+    const dim3 g64(ceil_div(rows, 256 / 16)), g128(ceil_div(rows, 256 / 32));
+    if (a.nchunks <= 4) {
+      if (dh == 64) attn_combine_kernel<64, 4><<<g64, 256, 0, st>>>(p);
+      else attn_combine_kernel<128, 4><<<g128, 256, 0, st>>>(p);
+    } else if (a.nchunks <= 8) {
+      if (dh == 64) attn_combine_kernel<64, 8><<<g64, 256, 0, st>>>(p);
+      else attn_combine_kernel<128, 8><<<g128, 256, 0, st>>>(p);
+    } else {
+      if (dh == 64) attn_combine_kernel<64, 16><<<g64, 256, 0, st>>>(p);
+      else attn_combine_kernel<128, 16><<<g128, 256, 0, st>>>(p);
+    }
     MV_TRY(launch_status());
   }
   return MV_OK;
