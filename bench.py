@@ -60,16 +60,17 @@ def _kernel_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic(kernel_key, src_path, launches_bytes=None):
-    """HBM traffic per launch from the committed counter summary, if it is still current."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{kernel_key}.json")
-    if not os.path.exists(p):
-        return None
-    with open(p) as f:
-        t = json.load(f)
-    if t.get("kernel_src_sha") != _kernel_sha(src_path):
-        return None
-    return t.get("hbm_bytes_per_launch")
+def _traffic(kernel_key, workload, src_path):
+    """HBM traffic per launch from the committed counter record of this kernel on this
+    workload, if there is one and the kernel's source is still the one it was taken on."""
+    for name in sorted(os.listdir(os.path.join(ROOT, "profiles"))):
+        if not (name.startswith(f"traffic_{kernel_key}_") and name.endswith(".json")):
+            continue
+        with open(os.path.join(ROOT, "profiles", name)) as f:
+            t = json.load(f)
+        if t.get("workload") == workload and t.get("kernel_src_sha") == _kernel_sha(src_path):
+            return t.get("hbm_bytes_per_launch")
+    return None
 
 
 # --------------------------------------------------------------------------- inputs
@@ -207,7 +208,7 @@ def cpu_baseline(wl, x, seed, budget_s):
         t3 = time.perf_counter()
         t_total += (t1 - t0) + (t3 - t2)
         steps += 1
-        if t_total >= budget_s or steps >= 5:
+        if t_total >= budget_s or steps >= 100:
             break
     return {"value": steps / t_total, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{steps} full step(s) of the same workload (seed {seed}), "
@@ -234,7 +235,8 @@ def main():
     ap.add_argument("--workload", default="c2", choices=sorted(DESCR))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work timed for cpu_baseline (whole steps, at least one)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="time the step replayed as one HIP graph (default) or as eager launches")
@@ -393,7 +395,8 @@ def main():
         src = os.path.join(ROOT, "medusa_tree_attention_verify_amd", "csrc", "heads.hip")
         roof = {"kernel": "gemv_bf16_kernel<head projection>", "bound": "hbm",
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": _traffic("head_projection_llama8b", src),
+                "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": _traffic("head_projection", DESCR[args.workload].split(":")[0], src),
                 "algorithmic_bytes": int(b_head), "avg_launch_us": round(seg_mean["heads_projection"] * 1000, 2)}
     else:
         b_att, f_att = parts["attention"]
