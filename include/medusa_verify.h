@@ -231,6 +231,8 @@ MV_API int mv_build_dynamic_tree(int B, int D, int s_max, const int* s_per_depth
  *   k_cache, v_cache [B, Hkv, L_cap, dh]: rows [0, L_b) of sequence b are the prefix and rows
  *            [L_b, L_b + N) hold the tree's own keys/values in node order; L_b =
  *            prefix_len[b] (device int32 [B]), 0 <= L_b <= max_L, L_b + N <= L_cap.
+ *            bf16: one (sequence, KV head) slice must stay below 2 GiB (L_cap * dh * 2 <
+ *            2^31, i.e. L_cap < 8388608 at dh = 128), else MV_ERR_UNSUPPORTED.
  *   anc_mask [N, ceil(N/32)] uint32 from mv_build_tree_mask (one tree for the batch,
  *            mask_stride = 0), or one mask per sequence, sequence b's at
  *            anc_mask + b * mask_stride (mask_stride >= N * ceil(N/32) words; e.g. from

@@ -571,6 +571,9 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
   if (N > MV_MAX_NODES) return MV_ERR_UNSUPPORTED;
   if (max_L > L_cap - N) return MV_ERR_INVALID_ARG;
   if (mask_stride != 0 && mask_stride < N * ((N + 31) / 32)) return MV_ERR_INVALID_ARG;
+  // bf16 K/V are read through buffer resources over one (sequence, KV head) slice, whose
+  // byte size must fit the 31-bit offsets.
+  if (dt == MV_BF16 && static_cast<long long>(L_cap) * dh * 2 > 0x7fffffffLL) return MV_ERR_UNSUPPORTED;
   const AttnPlan a = plan_attn(dt, B, N, Hq, Hkv, dh, max_L);
   MV_TRY(check_ws(ws, ws_bytes, a.ws_bytes));
   AttnParams p{};

@@ -97,6 +97,8 @@ def test_host_argument_checks():
     assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 8, 4, 96, 200, 100, *args, None, 0, None) == L.MV_ERR_UNSUPPORTED
     assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 8, 4, 128, 100, 100, *args, None, 0, None) == L.MV_ERR_INVALID_ARG
     assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 8, 4, 128, 10000, 8000, *args, None, 0, None) == L.MV_ERR_WORKSPACE
+    # a (sequence, KV head) slice of 2 GiB or more does not fit the bf16 path's buffer offsets
+    assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 8, 4, 128, 1 << 23, 100, *args, None, 0, None) == L.MV_ERR_UNSUPPORTED
     bad_stride = (P, P, P, P, P, 7, 0.0, P, None, None)     # N * W = 8 words per sequence
     assert lib.mv_tree_attn_verify(L.MV_BF16, 2, 8, 8, 4, 128, 200, 100, *bad_stride, None, 0, None) == L.MV_ERR_INVALID_ARG
     # acceptance
