@@ -79,6 +79,7 @@ __device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool re
 #endif
 
 constexpr int kKT = 64;  // keys per tile
+constexpr float kLazyLog2 = 8.f;  // running-max slack of the online softmax (log2 units)
 
 // Raw buffer resource (gfx950): dword 3 selects 32-bit data format for untyped loads; an
 // offset at or past the record count reads as zero.
@@ -190,6 +191,7 @@ void tree_attn_bf16_kernel(const AttnParams p) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  const float lazy = kLazyLog2 / p.scale_log2;  // in raw score units
 
   auto compute = [&](int t) {
     const int buf = t & 1;
@@ -254,7 +256,11 @@ void tree_attn_bf16_kernel(const AttnParams p) {
       tmax = fmaxf(__uint_as_float(t2.a), __uint_as_float(t2.b));
     }
     const float c2 = p.scale_log2;
-    const float m_new = fmaxf(m_run, tmax);
+    // Lazy rescaling: the running max moves only when a score passes it by more than
+    // kLazyLog2 in log2 units.  Until then the stale max keeps every p <= 2^kLazyLog2, well
+    // inside fp32 and bf16 range, and the O rescale below is skipped; (m, l, O) stay an exact
+    // log-sum-exp triple for whatever reference max they carry.
+    const float m_new = tmax > m_run + lazy ? tmax : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
     const float mc = m_use * c2;
