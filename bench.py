@@ -216,6 +216,25 @@ def cpu_baseline(wl, x, seed, budget_s):
 
 
 # --------------------------------------------------------------------------- main
+def hbm_copy_probe(nbytes=1 << 30, reps=5):
+    """GB/s of a plain device-to-device copy (read + write bytes), best of `reps`."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    best = 0.0
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * nbytes / (e0.elapsed_time(e1) / 1000.0) / 1e9)
+    del a, b
+    torch.cuda.empty_cache()
+    return best
+
+
 def copy_calibration(nbytes=1 << 30, reps=5):
     import torch
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -231,7 +250,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c2", choices=sorted(DESCR))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -382,6 +401,19 @@ def main():
         raise RuntimeError(f"device status flags {int(step.status.item())}")
     ms = start.elapsed_time(stop) / K
     steps_per_s = 1000.0 / ms
+    # Spread: four more regions of the same K steps after the timed one (not part of `value`).
+    repeats = [steps_per_s]
+    for _ in range(4):
+        start.record()
+        for i in range(K):
+            if args.launch == "graph":
+                graphs[i % R].replay()
+            else:
+                one_step(i)
+        stop.record()
+        torch.cuda.synchronize()
+        repeats.append(1000.0 * K / start.elapsed_time(stop))
+    probe = hbm_copy_probe()
     seg = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(len(present))] for e in evs])
     seg_mean = dict(zip(present, seg.mean(axis=0)))  # ms per part
     parts_ms = {n: round(float(v), 4) for n, v in seg_mean.items()}
@@ -435,6 +467,11 @@ def main():
         "launch": args.launch,
         "eager_steps_per_s": round(1000.0 / ms_eager, 2),
         "wall_s_timed_region": None if t_wall is None else round(t_wall, 4),
+        "repeats_steps_per_s": [round(v, 1) for v in repeats],
+        "repeats_p10_p50_p90": [round(float(np.percentile(repeats, q)), 1) for q in (10, 50, 90)],
+        # context for the 8 TB/s denominator: a plain 1 GiB device copy on this GPU (bytes read
+        # + written per second, best of 5)
+        "hbm_copy_probe_GBs": round(probe, 1),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
