@@ -36,7 +36,8 @@ def _check_ids(got, z, rows=None):
 
 
 @pytest.mark.parametrize("T,d,V", [(1, 256, 1000), (5, 256, 999), (33, 512, 777),
-                                   (130, 256, 1500), (65, 1024, 5000)])
+                                   (128, 256, 1500), (129, 512, 999), (130, 256, 1500),
+                                   (300, 256, 1500), (65, 1024, 5000)])
 def test_lm_head_small_shapes(T, d, V):
     require_gpu()
     print(f"lm head T={T} d={d} V={V}", flush=True)
@@ -62,6 +63,26 @@ def test_lm_head_llama8b_shape():
     assert ties <= 1
     assert_fp32(host(got["max"]), ref["max"], atol=1e-3, what="max logit")
     assert_fp32(host(got["lse"]), ref["lse"], atol=1e-3, what="lse")
+
+
+@pytest.mark.parametrize("B", [8, 64])
+def test_lm_head_batched_verify_rows_sampled(B):
+    """A batch of verify steps (B x 65 rows: T = 520 and 4160 take the tiled-GEMM kernel),
+    d = 4096, V = 32000: the GPU computes every row, the oracle recomputes 16 sampled rows
+    spread over the 128-row tiles, including the last (ragged) one."""
+    require_gpu()
+    T = B * 65
+    print(f"lm head batched T={T}", flush=True)
+    x, w = _inputs(T, 4096, 32000, 10 + B)
+    got = ops.lm_head_argmax(dev(x, torch.bfloat16), dev(w, torch.bfloat16))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(B)
+    rows = sorted(set([0, 127, 128, T - 1] + rng.choice(T, 12, replace=False).tolist()))
+    ref = O.lm_head_argmax(x[rows], w)
+    ids, mx, lse = host(got["ids"]), host(got["max"]), host(got["lse"])
+    assert _check_ids(ids, ref["logits"], rows) <= 1
+    assert_fp32(mx[rows], ref["max"], atol=1e-3, what="max logit")
+    assert_fp32(lse[rows], ref["lse"], atol=1e-3, what="lse")
 
 
 def test_lm_head_full_vocab_sampled():
