@@ -35,16 +35,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile and link the library; returns its path.  Always rebuilds."""
+def build(verbose: bool = False, jobs: int = 8, out_path: str = LIB_PATH,
+          extra_flags=(), objdir: str = os.path.join(PKG, "_build")) -> str:
+    """Compile and link the library; returns its path.  Always rebuilds.
+
+    ``out_path``, ``extra_flags`` and ``objdir`` build a variant elsewhere (the host-sanitizer
+    test builds one with host-only UBSan flags); the default is the in-tree library."""
     cc = hipcc()
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
+    extra = list(extra_flags)
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [cc, *FLAGS, "-c", src, "-o", obj]
+        cmd = [cc, *FLAGS, *extra, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                         if "packed-fp32-ops" not in l)
@@ -56,13 +60,13 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     with ThreadPoolExecutor(max(1, min(jobs, len(srcs)))) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [cc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp]
+    tmp = out_path + ".tmp"
+    cmd = [cc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_path)
+    return out_path
 
 
 if __name__ == "__main__":
