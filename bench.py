@@ -249,7 +249,7 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c2", choices=sorted(DESCR))
     ap.add_argument("--seed", type=int, default=0)
