@@ -79,6 +79,7 @@ __device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool re
 #endif
 
 constexpr int kKT = 64;  // keys per tile
+constexpr int kNWVCombine = 8;  // waves per attention workgroup (the partial blocks' layout)
 constexpr float kLazyLog2 = 8.f;  // running-max slack of the online softmax (log2 units)
 
 // Raw buffer resource (gfx950): dword 3 selects 32-bit data format for untyped loads; an
@@ -354,36 +355,52 @@ void tree_attn_bf16_kernel(const AttnParams p) {
     if (p.lse && half == 0)
       p.lse[(static_cast<size_t>(b) * p.Hq + h) * p.N + node] = (m_run * p.scale_log2 + log2f(l_run)) * kLn2;
   } else {
+    // The partial output goes out in the MFMA register order: one 16 KB block per (job, query
+    // tile, wave), float4 (db, vq) of lane l at [(db*4 + vq)*64 + l], so every store
+    // instruction writes 1 KB of consecutive bytes (the combine reads it in the same order).
     const size_t rowi = (static_cast<size_t>(b * p.Hq + h) * p.N + node) * p.nchunks + c;
-    float* po = p.part_o + rowi * DH;
+    const size_t slot = ((static_cast<size_t>(b * p.Hkv + g) * p.nchunks + c) * p.qtiles + qt) * NWV + wv;
+    float4* po = reinterpret_cast<float4*>(p.part_o) + slot * (DB * 4 * 64) + lane;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int vq = 0; vq < 4; ++vq) {
-        const int d0 = db * 32 + 8 * vq + 4 * half;
-        *reinterpret_cast<float4*>(po + d0) =
+      for (int vq = 0; vq < 4; ++vq)
+        po[(db * 4 + vq) * 64] =
             make_float4(oacc[db][vq * 4 + 0], oacc[db][vq * 4 + 1], oacc[db][vq * 4 + 2], oacc[db][vq * 4 + 3]);
-      }
     if (half == 0) p.part_ml[rowi] = make_float2(m_run * p.scale_log2, l_run);
   }
 }
 
 // Merge of the chunk partials: O = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c, as an online
-// log-sum-exp over the chunks.  DH/4 lanes per output row, each with one 16-byte piece of every
-// partial; the partials of up to CB chunks are requested before any is used (CB covers every
-// chunk of the one-sequence launches, so their combine is a single round trip to memory).
+// log-sum-exp over the chunks.  One thread per float4 of the attention kernel's register-order
+// partial blocks (the same position in every chunk's block), so each wave reads 1 KB of
+// consecutive bytes per chunk; the partials of up to CB chunks are requested before any is
+// used (CB covers every chunk of the one-sequence launches: one round trip to memory).
 template <int DH, int CB>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
-  constexpr int LPR = DH / 4;       // lanes per row
-  constexpr int RPB = 256 / LPR;    // rows per workgroup
-  const int rowid = blockIdx.x * RPB + static_cast<int>(threadIdx.x) / LPR;  // ((b*Hq + h)*N + i)
-  if (rowid >= p.B * p.Hq * p.N) return;
-  const int e = static_cast<int>(threadIdx.x) % LPR;
-  const int i = rowid % p.N, h = (rowid / p.N) % p.Hq, b = rowid / (p.N * p.Hq);
+  constexpr int DB = DH / 32, SLOT = DB * 4 * 64;  // float4 per (job, query tile, wave) block
+  constexpr int NWV = kNWVCombine;
+  const size_t gid = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int pos = static_cast<int>(gid % SLOT);
+  const size_t slot = gid / SLOT;                   // ((b*Hkv + g)*qtiles + qt)*NWV + wv
+  const int wv = static_cast<int>(slot % NWV);
+  const int qt = static_cast<int>((slot / NWV) % p.qtiles);
+  const size_t bg = slot / (static_cast<size_t>(NWV) * p.qtiles);
+  if (bg >= static_cast<size_t>(p.B) * p.Hkv) return;
+  const int g = static_cast<int>(bg % p.Hkv), b = static_cast<int>(bg / p.Hkv);
+  const int lane = pos % 64, dbvq = pos / 64, l32 = lane & 31, half = lane >> 5;
+  const int m = qt * (NWV * 32) + wv * 32 + l32;
+  if (m >= p.M) return;
+  const int i = m / p.G, h = g * p.G + m % p.G;
+  const int d0 = (dbvq / 4) * 32 + 8 * (dbvq % 4) + 4 * half;
   const int Lb = clamp_prefix(p, p.prefix_len[b], false);
   const int ncb = max(1, (Lb + p.CK - 1) / p.CK);
   if (ncb == 1) return;  // the attention kernel wrote this row itself
-  const size_t base = static_cast<size_t>(rowid) * p.nchunks;
+  const size_t mlbase = (static_cast<size_t>(b * p.Hq + h) * p.N + i) * p.nchunks;
+  const float4* pbase = reinterpret_cast<const float4*>(p.part_o) +
+                        ((bg * p.nchunks) * p.qtiles + qt) * (static_cast<size_t>(NWV) * SLOT) +
+                        static_cast<size_t>(wv) * SLOT + pos;
+  const size_t cstride = static_cast<size_t>(p.qtiles) * NWV * SLOT;  // float4 per chunk
   float M = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c0 = 0; c0 < ncb; c0 += CB) {
@@ -392,9 +409,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
       const int c = c0 + u;
-      ml[u] = c < ncb ? p.part_ml[base + c] : make_float2(-INFINITY, 0.f);
-      po[u] = c < ncb ? *reinterpret_cast<const float4*>(p.part_o + (base + c) * DH + 4 * e)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      ml[u] = c < ncb ? p.part_ml[mlbase + c] : make_float2(-INFINITY, 0.f);
+      po[u] = c < ncb ? pbase[c * cstride] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
@@ -415,8 +431,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   uint2 w2;
   w2.x = pack_bf16x2(acc.x * inv, acc.y * inv);
   w2.y = pack_bf16x2(acc.z * inv, acc.w * inv);
-  *reinterpret_cast<uint2*>(orow + 4 * e) = w2;
-  if (p.lse && e == 0) p.lse[(static_cast<size_t>(b) * p.Hq + h) * p.N + i] = (M + log2f(L)) * kLn2;
+  *reinterpret_cast<uint2*>(orow + d0) = w2;
+  if (p.lse && d0 == 0) p.lse[(static_cast<size_t>(b) * p.Hq + h) * p.N + i] = (M + log2f(L)) * kLn2;
 }
 
 // fp32: one wave per query row (b, node i, head h); lanes run over keys for the scores and
@@ -495,7 +511,7 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(const AttnParams p) 
 // ---------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------
-constexpr int kNWV = 8;  // waves per workgroup -> 256 query rows
+constexpr int kNWV = kNWVCombine;  // waves per workgroup -> 256 query rows
 
 // Sequences ranked by decreasing (clamped) prefix length, ties by index: order[rank] = b.
 constexpr int kOrderMaxB = 1024;
@@ -543,7 +559,8 @@ AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L) {
   if (a.ordered) c.take<int32_t>(B);
   if (a.nchunks > 1) {
     const size_t rows = static_cast<size_t>(B) * Hq * N * a.nchunks;
-    c.take<float>(rows * dh);
+    const size_t tile_rows = static_cast<size_t>(B) * Hkv * a.nchunks * a.qtiles * kNWV * 32;
+    c.take<float>(tile_rows * dh);  // register-order blocks, padded to whole query tiles
     c.take<float2>(rows);
   }
   a.ws_bytes = c.bytes();
@@ -602,7 +619,8 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
   int32_t* order = a.ordered ? c.take<int32_t>(B) : nullptr;
   if (a.nchunks > 1) {
     const size_t rows = static_cast<size_t>(B) * Hq * N * a.nchunks;
-    p.part_o = c.take<float>(rows * dh);
+    const size_t tile_rows = static_cast<size_t>(B) * Hkv * a.nchunks * a.qtiles * kNWV * 32;
+    p.part_o = c.take<float>(tile_rows * dh);
     p.part_ml = c.take<float2>(rows);
   }
   const long long jobs = static_cast<long long>(B) * Hkv * a.nchunks;
@@ -618,8 +636,9 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
   else tree_attn_bf16_kernel<128, kNWV><<<static_cast<int>(grid), kNWV * 64, 0, st>>>(p);
   MV_TRY(launch_status());
   if (a.nchunks > 1) {
-    const int rows = B * Hq * N;
-    const dim3 g64(ceil_div(rows, 256 / 16)), g128(ceil_div(rows, 256 / 32));
+    const long long slots = static_cast<long long>(B) * Hkv * a.qtiles * kNWV;
+    const dim3 g64(static_cast<unsigned>(ceil_div(slots * (2 * 4 * 64), 256LL))),
+        g128(static_cast<unsigned>(ceil_div(slots * (4 * 4 * 64), 256LL)));
     if (a.nchunks <= 4) {
       if (dh == 64) attn_combine_kernel<64, 4><<<g64, 256, 0, st>>>(p);
       else attn_combine_kernel<128, 4><<<g128, 256, 0, st>>>(p);
