@@ -12,14 +12,8 @@
 // per row the greedy token argmax_v logits[t][v] (ties: lowest id), optionally that logit and
 // LSE[t] = log sum_v exp(logits[t][v]), and never writes the [T][V] logits.
 //
-// One streaming pass over W: a workgroup owns 64 vocabulary rows and a group of up to 128
-// target rows, and its NW waves split d.  Per k-step a lane loads one 16-byte piece of each of
-// the 4 row tiles (the A operand of v_mfma_f32_16x16x32_bf16: 16 rows x 32 columns of W) and of
-// each of the NCT column tiles of x (the B operand: 16 target rows), so every weight byte
-// crosses HBM once and the x pieces come from L2.  The waves reduce one 16-row column tile at a
-// time through LDS; for those 16 target rows the epilogue writes per 64-row vocabulary block
-// the partial (max, its id, sum exp(logit - max)).  A second kernel merges the ceil(V/64)
-// partials of each row.
+// One streaming pass over W per group of up to 128 target rows (the kernel below), then a
+// second kernel merges each row's ceil(V/64) block partials into the greedy id and the LSE.
 
 #include <math.h>
 
@@ -32,7 +26,6 @@ namespace mv {
 namespace {
 
 constexpr int kLmRows = 64;        // vocabulary rows per workgroup
-constexpr int kLmMaxCols = 128;    // target rows per workgroup (8 column tiles)
 constexpr int kLmMergeThreads = 256;
 
 struct LmParams {
@@ -47,107 +40,170 @@ struct LmParams {
   float* lse;                   // [T] or null
 };
 
-template <int NW, int NCT>
-__global__ __launch_bounds__(NW * 64) void lm_head_kernel(const LmParams p) {
-  constexpr int RT = kLmRows / 16, U = 2;
-  __shared__ float red[NW][kLmRows][17];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int rb = blockIdx.x, row0 = rb * kLmRows;
-  const int col0 = blockIdx.y * p.ncols;
-  const int t0 = (w * p.KT) / NW, t1 = ((w + 1) * p.KT) / NW;
+// Streaming kernel.  A workgroup owns 64 vocabulary rows, one 16-row MFMA tile per wave, and a
+// group of up to 128 target rows (NCT column tiles of 16).  Each wave streams its 16 weight rows
+// over the whole of d as the A operand of v_mfma_f32_16x16x32_bf16 (one 16-byte load per lane
+// and k-step, U k-steps per batch, the next batch in registers), so every weight byte crosses
+// HBM once per target-row group.  The target rows' slice of x for a batch is staged in LDS once
+// for the four waves (double-buffered, the next batch in registers) and read back as the B
+// operand; an 80-byte row pitch makes those 16-byte reads conflict-free.  Epilogue per column
+// tile: each wave reduces its 16 rows for every target row in registers (lane swaps between the
+// four 16-lane groups), the four waves meet in LDS, and the workgroup writes per target row the
+// partial (max, its id, sum exp(logit - max)) of its 64-row vocabulary block.
+constexpr int kLmThreads = 256;
+constexpr int kLmXPitch = 40;  // bf16 elements per staged target row (32 + 8 padding)
 
-  // A operand: lane (row r = lane % 16, k-group g = lane / 16) of row tile rt reads the 16 bytes
-  // W[row0 + 16*rt + r][32*t + 8*g .. +8]; rows past V are clamped (their logits are not used).
-  const u32x4* ap[RT];
+template <int NCT, int U>
+__global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const LmParams p) {
+  constexpr int NCOL = 16 * NCT;
+  constexpr int XP = NCOL * 4 * U;                           // 16-byte pieces of one x batch
+  constexpr int XPT = (XP + kLmThreads - 1) / kLmThreads;    // per thread
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][U][NCOL * kLmXPitch];
+  __shared__ float em[4][NCOL], es[4][NCOL];
+  __shared__ int ei[4][NCOL];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rb = blockIdx.x, row0 = rb * kLmRows, col0 = blockIdx.y * NCOL;
+  const int nb = p.KT / U;
+  // A operand: lane (row r = lane % 16, k-group g = lane / 16) of wave w reads the 16 bytes
+  // W[row0 + 16w + r][32t + 8g .. +8] at k-step t; rows past V are clamped (not used).
+  const uint16_t* wp = p.w + static_cast<size_t>(min(row0 + 16 * w + (lane & 15), p.V - 1)) * p.d + 8 * (lane >> 4);
+  auto wload = [&](int bt, u32x4 (&a)[U]) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = min(row0 + rt * 16 + (lane & 15), p.V - 1);
-    ap[rt] = reinterpret_cast<const u32x4*>(p.w + static_cast<size_t>(r) * p.d) + (lane >> 4) + t0 * 4;
-  }
-  // B operand: lane (column c = lane % 16, k-group g) of column tile ct reads
-  // x[col0 + 16*ct + c][32*t + 8*g .. +8]; columns past T read row T-1 (results not used).
-  const u32x4* bp[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int c = min(col0 + ct * 16 + (lane & 15), p.T - 1);
-    bp[ct] = reinterpret_cast<const u32x4*>(p.x + static_cast<size_t>(c) * p.d) + (lane >> 4) + t0 * 4;
-  }
-  f32x4 acc[RT][NCT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto step = [&](const u32x4 (&a)[RT], const u32x4 (&b)[NCT]) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, a[rt]), __builtin_bit_cast(bf16x8, b[ct]), acc[rt][ct], 0, 0, 0);
+    for (int u = 0; u < U; ++u) a[u] = *reinterpret_cast<const u32x4*>(wp + static_cast<size_t>(bt * U + u) * 32);
   };
-  int t = t0;
-  for (; t + U <= t1; t += U) {
-    u32x4 a[U][RT], b[U][NCT];
+  // x batch bt: piece q = (u, target row c, quarter qq) is x[col0 + c][32*(bt*U + u) + 8*qq .. +8];
+  // target rows past T read row T-1 (their results are not written).
+  auto xload = [&](int bt, u32x4 (&xr)[XPT]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) a[u][rt] = ap[rt][u * 4];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) b[u][ct] = bp[ct][u * 4];
+    for (int i = 0; i < XPT; ++i) {
+      const int q = tid + i * kLmThreads;
+      if (XP % kLmThreads == 0 || q < XP) {
+        const int u = q / (NCOL * 4), c = (q / 4) % NCOL, qq = q % 4;
+        xr[i] = *reinterpret_cast<const u32x4*>(p.x + static_cast<size_t>(min(col0 + c, p.T - 1)) * p.d +
+                                                32 * (bt * U + u) + 8 * qq);
+      }
     }
+  };
+  auto xstore = [&](int buf, const u32x4 (&xr)[XPT]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) step(a[u], b[u]);
+    for (int i = 0; i < XPT; ++i) {
+      const int q = tid + i * kLmThreads;
+      if (XP % kLmThreads == 0 || q < XP) {
+        const int u = q / (NCOL * 4), c = (q / 4) % NCOL, qq = q % 4;
+        *reinterpret_cast<u32x4*>(&Xs[buf][u][c * kLmXPitch + 8 * qq]) = xr[i];
+      }
+    }
+  };
+  f32x4 acc[NCT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) ap[rt] += U * 4;
+  for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf, const u32x4 (&a)[U]) {
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) bp[ct] += U * 4;
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        // B operand: lane (target row c = lane % 16, k-group g) reads x[16ct + c][8g .. +8]
+        const u32x4 bop = *reinterpret_cast<const u32x4*>(&Xs[buf][u][(16 * ct + (lane & 15)) * kLmXPitch + 8 * (lane >> 4)]);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
+                                                          __builtin_bit_cast(bf16x8, bop), acc[ct], 0, 0, 0);
+      }
+  };
+  // Batch bt computes from LDS buffer bt & 1 with weights in register set bt & 1; the x batch
+  // bt+1 (already in registers) is stored to the other buffer after the compute, then batch
+  // bt+2 is requested into the registers just freed.
+  u32x4 xr[XPT], wa0[U], wa1[U];
+  xload(0, xr);
+  wload(0, wa0);
+  xstore(0, xr);
+  if (nb > 1) {
+    xload(1, xr);
+    wload(1, wa1);
   }
-  for (; t < t1; ++t) {
-    u32x4 a[RT], b[NCT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) a[rt] = ap[rt][0];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) b[ct] = bp[ct][0];
-    step(a, b);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) ap[rt] += 4;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) bp[ct] += 4;
+  __syncthreads();
+  for (int bt = 0; bt < nb; bt += 2) {
+    compute(0, wa0);
+    if (bt + 1 < nb) xstore(1, xr);
+    if (bt + 2 < nb) {
+      xload(bt + 2, xr);
+      wload(bt + 2, wa0);
+    }
+    __syncthreads();
+    if (bt + 1 < nb) {
+      compute(1, wa1);
+      if (bt + 2 < nb) xstore(0, xr);
+      if (bt + 3 < nb) {
+        xload(bt + 3, xr);
+        wload(bt + 3, wa1);
+      }
+    }
+    __syncthreads();
   }
 
-  // Per column tile: the waves' partial sums meet in LDS (16x16 D layout: lane holds rows
-  // 4*(lane/16) + v, column lane % 16), then each wave takes 16/NW of the tile's target rows;
-  // lane = vocabulary row for the (max, id, sum exp) of its 64-row block.
-  const int row = row0 + lane;
+  // Epilogue.  acc[ct][v]: vocabulary row row0 + 16w + 4*(lane/16) + v, target row
+  // col0 + 16ct + lane%16; the four 16-lane groups hold the other rows of the same target rows.
+  const int c16 = lane & 15;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) red[w][rt * 16 + (lane >> 4) * 4 + v][lane & 15] = acc[rt][ct][v];
-    __syncthreads();
-    for (int cc = w; cc < 16; cc += NW) {
-      const int tok = col0 + ct * 16 + cc;
-      if (tok >= p.T || ct * 16 + cc >= p.ncols) continue;  // wave-uniform
-      const bool live = row < p.V;
-      float val = -INFINITY;
-      if (live) {
-        val = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) val += red[ww][lane][cc];
-      }
-      float bv = val;
-      int bi = live ? row : INT_MAX;
-      wave_argbest(bv, bi);
-      const float l = wave_sum(val == -INFINITY ? 0.f : expf(val - bv));
-      if (lane == 0) {
-        const size_t q = static_cast<size_t>(tok) * p.nrb + rb;
-        p.pm[q] = bv;
-        p.pl[q] = l;
-        p.pidx[q] = bi;
+    for (int v = 0; v < 4; ++v) {
+      const int r = row0 + 16 * w + 4 * (lane >> 4) + v;
+      const float val = r < p.V ? acc[ct][v] : -INFINITY;
+      if (kv_better(val, r, bv, bi)) {
+        bv = val;
+        bi = r;
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+      const LanePair tv = step == 0 ? swap16(__float_as_uint(bv)) : swap32(__float_as_uint(bv));
+      const LanePair ti = step == 0 ? swap16(static_cast<uint32_t>(bi)) : swap32(static_cast<uint32_t>(bi));
+      bv = __uint_as_float(tv.a);
+      bi = static_cast<int>(ti.a);
+      if (kv_better(__uint_as_float(tv.b), static_cast<int>(ti.b), bv, bi)) {
+        bv = __uint_as_float(tv.b);
+        bi = static_cast<int>(ti.b);
+      }
+    }
+    float sm = 0.f;
+    if (bv != -INFINITY) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = row0 + 16 * w + 4 * (lane >> 4) + v;
+        sm += r < p.V ? expf(acc[ct][v] - bv) : 0.f;
+      }
+    }
+    {
+      LanePair t2 = swap16(__float_as_uint(sm));
+      sm = __uint_as_float(t2.a) + __uint_as_float(t2.b);
+      t2 = swap32(__float_as_uint(sm));
+      sm = __uint_as_float(t2.a) + __uint_as_float(t2.b);
+    }
+    if (lane < 16) {
+      em[w][16 * ct + c16] = bv;
+      ei[w][16 * ct + c16] = bi;
+      es[w][16 * ct + c16] = sm;
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < NCOL; c += kLmThreads) {
+    const int tok = col0 + c;
+    if (tok >= p.T) break;
+    float m = em[0][c], l = es[0][c], bv = em[0][c];
+    int bi = ei[0][c];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) {
+      if (kv_better(em[q][c], ei[q][c], bv, bi)) {
+        bv = em[q][c];
+        bi = ei[q][c];
+      }
+      ml_merge(m, l, em[q][c], es[q][c]);
+    }
+    const size_t o = static_cast<size_t>(tok) * p.nrb + rb;
+    p.pm[o] = m;
+    p.pl[o] = l;
+    p.pidx[o] = bi;
   }
 }
 
@@ -204,18 +260,32 @@ __global__ __launch_bounds__(kLmMergeThreads) void lm_head_merge_kernel(const Lm
 }
 
 struct LmPlan {
-  int nrb = 1, ncols = 16, nct = 1, ngrp = 1, nw = 4;
+  int nrb = 1, nct = 1, ncols = 16, ngrp = 1, u = 1;
   size_t ws_bytes = 0;
 };
+
+// Column tiles per workgroup: the smallest instantiated count that covers T, at most 8 (128
+// target rows; more rows run as several groups, each streaming W again).  Wider groups were
+// measured slower: 32 tiles at 520 target rows took 613 us against 506 us for groups of 128 rows
+// with the previous kernel, because every workgroup restages the whole x tile (its 64 weight
+// rows reuse it only 64-fold) and the 32-tile kernel runs one wave per SIMD.  k-steps per
+// batch: 4 (2 or 1 when d/32 is not a multiple).
+constexpr int kLmNct[] = {1, 2, 3, 4, 5, 6, 7, 8};
+constexpr int kLmMaxNct = 8;
 
 LmPlan plan_lm(int T, int d, int V) {
   LmPlan a;
   a.nrb = ceil_div(V, kLmRows);
-  const int cols = std::min(T, kLmMaxCols);
-  a.nct = ceil_div(cols, 16);
+  const int need = ceil_div(std::min(T, 16 * kLmMaxNct), 16);
+  for (int n : kLmNct)
+    if (n >= need) {
+      a.nct = n;
+      break;
+    }
   a.ncols = 16 * a.nct;
   a.ngrp = ceil_div(T, a.ncols);
-  a.nw = d / 32 >= 64 ? 8 : 4;
+  const int KT = d / 32;
+  a.u = KT % 4 == 0 ? 4 : (KT % 2 == 0 ? 2 : 1);
   Carver c(nullptr);
   const size_t np = static_cast<size_t>(T) * a.nrb;
   c.take<float>(np);
@@ -266,12 +336,14 @@ MV_API int mv_lm_head_argmax(int dt, int T, int d, int V, const void* x, const v
   hipStream_t st = as_stream(stream);
   const dim3 grid(a.nrb, a.ngrp);
   bool launched = false;
-#define MV_LM_CASE(NW_, NCT_) \
-  if (a.nw == NW_ && a.nct == NCT_) { lm_head_kernel<NW_, NCT_><<<grid, NW_ * 64, 0, st>>>(p); launched = true; }
-  MV_LM_CASE(4, 1) MV_LM_CASE(4, 2) MV_LM_CASE(4, 3) MV_LM_CASE(4, 4)
-  MV_LM_CASE(4, 5) MV_LM_CASE(4, 6) MV_LM_CASE(4, 7) MV_LM_CASE(4, 8)
-  MV_LM_CASE(8, 1) MV_LM_CASE(8, 2) MV_LM_CASE(8, 3) MV_LM_CASE(8, 4)
-  MV_LM_CASE(8, 5) MV_LM_CASE(8, 6) MV_LM_CASE(8, 7) MV_LM_CASE(8, 8)
+#define MV_LM_CASE(NCT_, U_) \
+  if (!launched && a.nct == NCT_ && a.u == U_) { lm_head_kernel<NCT_, U_><<<grid, kLmThreads, 0, st>>>(p); launched = true; }
+  MV_LM_CASE(1, 4) MV_LM_CASE(2, 4) MV_LM_CASE(3, 4) MV_LM_CASE(4, 4)
+  MV_LM_CASE(5, 4) MV_LM_CASE(6, 4) MV_LM_CASE(7, 4) MV_LM_CASE(8, 4)
+  MV_LM_CASE(1, 2) MV_LM_CASE(2, 2) MV_LM_CASE(3, 2) MV_LM_CASE(4, 2)
+  MV_LM_CASE(5, 2) MV_LM_CASE(6, 2) MV_LM_CASE(7, 2) MV_LM_CASE(8, 2)
+  MV_LM_CASE(1, 1) MV_LM_CASE(2, 1) MV_LM_CASE(3, 1) MV_LM_CASE(4, 1)
+  MV_LM_CASE(5, 1) MV_LM_CASE(6, 1) MV_LM_CASE(7, 1) MV_LM_CASE(8, 1)
 #undef MV_LM_CASE
   if (!launched) return MV_ERR_UNSUPPORTED;  // no kernel instance for this shape
   MV_TRY(launch_status());
