@@ -29,7 +29,7 @@ constexpr int kLmRows = 64;        // vocabulary rows per workgroup
 constexpr int kLmMergeThreads = 256;
 
 struct LmParams {
-  int T, d, V, KT, nrb, ncols;  // KT = d / 32, nrb = ceil(V / 64), ncols = target rows per group
+  int T, d, V, KT, nrb;         // KT = d / 32, nrb = ceil(V / 64)
   const uint16_t* x;            // [T][d] bf16
   const uint16_t* w;            // [V][d] bf16
   float* pm;                    // [T][nrb] partial max
@@ -322,7 +322,7 @@ MV_API int mv_lm_head_argmax(int dt, int T, int d, int V, const void* x, const v
   const LmPlan a = plan_lm(T, d, V);
   MV_TRY(check_ws(ws, ws_bytes, a.ws_bytes));
   LmParams p{};
-  p.T = T; p.d = d; p.V = V; p.KT = d / 32; p.nrb = a.nrb; p.ncols = a.ncols;
+  p.T = T; p.d = d; p.V = V; p.KT = d / 32; p.nrb = a.nrb;
   p.x = static_cast<const uint16_t*>(x);
   p.w = static_cast<const uint16_t*>(w_lm);
   Carver c(ws);
