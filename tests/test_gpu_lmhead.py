@@ -37,7 +37,8 @@ def _check_ids(got, z, rows=None):
 
 @pytest.mark.parametrize("T,d,V", [(1, 256, 1000), (5, 256, 999), (33, 512, 777),
                                    (128, 256, 1500), (129, 512, 999), (130, 256, 1500),
-                                   (300, 256, 1500), (65, 1024, 5000)])
+                                   (300, 256, 1500), (65, 1024, 5000),
+                                   (17, 96, 500), (40, 192, 777)])   # 3 and 6 k-steps: batches of 1 and 2
 def test_lm_head_small_shapes(T, d, V):
     require_gpu()
     print(f"lm head T={T} d={d} V={V}", flush=True)
