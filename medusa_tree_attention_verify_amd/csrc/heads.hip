@@ -266,6 +266,98 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(const GemvPa
   if (lane == 0 && p.lse) p.lse[static_cast<size_t>(b) * p.K + k] = M + logf(Ls);
 }
 
+// ---- merge as a tournament, for lists longer than 8 (up to kMergeThreads * CPT candidates
+// per (head, batch row)).  Every candidate stays in registers, unsorted (CPT per thread).  Each
+// of the s_k rounds takes the workgroup's best (value, then lower id) with one wave arg-best and
+// one LDS exchange between the waves, and the thread holding the winning id drops it.  The LDS
+// slots alternate between rounds, so one barrier per round suffices: a wave can only overwrite
+// a slot after every wave has passed the barrier that follows its last reader.  At 10
+// candidates per head this replaces the 16-slot sorted lists' insertion chains.
+template <int CPT>
+__global__ __launch_bounds__(kMergeThreads) void heads_tournament_kernel(const GemvParams p) {
+  __shared__ float rv[2][kMergeWaves];
+  __shared__ int ri[2][kMergeWaves];
+  __shared__ float wm[kMergeWaves], wl[kMergeWaves];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int k = blockIdx.x % p.K, b = blockIdx.x / p.K;
+  const int nrb = p.nrb, s = p.s[k], smax = p.s_max;
+  const size_t base = (static_cast<size_t>(k) * p.B + b) * nrb;
+  const int n = nrb * smax;
+  const int* pidx = p.pidx + base * smax;
+  const float* pval = p.pval + base * smax;
+  float cv[CPT];
+  int ci[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {  // all requested before any is used
+    const int c = tid + u * kMergeThreads;
+    ci[u] = c < n ? pidx[c] : -1;
+    cv[u] = c < n ? pval[c] : -INFINITY;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int j = tid; j < nrb; j += kMergeThreads) ml_merge(m, l, p.pm[base + j], p.pl[base + j]);
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const bool ok = ci[u] >= 0 && (tid + u * kMergeThreads) % smax < s;
+    cv[u] = ok ? cv[u] : -INFINITY;
+    ci[u] = ok ? ci[u] : INT_MAX;
+  }
+  wave_ml_merge(m, l);
+  if (lane == 0) {
+    wm[w] = m;
+    wl[w] = l;
+  }
+  const size_t o = static_cast<size_t>(b) * p.ld_topk + static_cast<size_t>(k) * smax;
+  for (int r = 0; r < s; ++r) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const bool c = kv_better(cv[u], ci[u], bv, bi);
+      bv = c ? cv[u] : bv;
+      bi = c ? ci[u] : bi;
+    }
+    wave_argbest(bv, bi);
+    if (lane == 0) {
+      rv[r & 1][w] = bv;
+      ri[r & 1][w] = bi;
+    }
+    __syncthreads();
+    float gv = rv[r & 1][0];
+    int gi = ri[r & 1][0];
+#pragma unroll
+    for (int q = 1; q < kMergeWaves; ++q) {
+      const float ov = rv[r & 1][q];
+      const int oi = ri[r & 1][q];
+      const bool c = kv_better(ov, oi, gv, gi);
+      gv = c ? ov : gv;
+      gi = c ? oi : gi;
+    }
+    if (gi != INT_MAX) {  // token ids are unique: exactly one slot of one thread holds it
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const bool hit = ci[u] == gi;
+        cv[u] = hit ? -INFINITY : cv[u];
+        ci[u] = hit ? INT_MAX : ci[u];
+      }
+    }
+    if (tid == 0) {
+      p.topk_ids[o + r] = gi != INT_MAX ? gi : -1;
+      p.topk_vals[o + r] = gi != INT_MAX ? gv : -INFINITY;
+    }
+  }
+  if (tid == 0)
+    for (int r = s; r < smax; ++r) {
+      p.topk_ids[o + r] = -1;
+      p.topk_vals[o + r] = -INFINITY;
+    }
+  __syncthreads();
+  if (w != 0) return;
+  float M = lane < kMergeWaves ? wm[lane] : -INFINITY;
+  float Ls = lane < kMergeWaves ? wl[lane] : 0.f;
+  wave_ml_merge(M, Ls);
+  if (lane == 0 && p.lse) p.lse[static_cast<size_t>(b) * p.K + k] = M + logf(Ls);
+}
+
 // ---- projection epilogue: optional logits, per-workgroup top-s and (max, sum exp).
 template <bool BF16, int NW, int BC>
 __device__ void head_epilogue(const GemvParams& p, int k, int rb, float (*ys)[BC]) {
@@ -644,8 +736,13 @@ MV_API int mv_medusa_head_select(int dt, int B, int d, int V, int K, const int* 
   p.ld_topk = ld_topk;
   p.lse = lse;
   hipStream_t st = as_stream(stream);
+  // Lists of up to 8 slots: per-thread sorted lists.  Longer (up to 16): a tournament over the
+  // candidates held in registers when they fit (up to 32 per thread), else the 16-slot lists.
+  const long long n = static_cast<long long>(p.nrb) * s_max;
   if (s_max <= 4) heads_merge_kernel<4><<<K * B, kMergeThreads, 0, st>>>(p);
   else if (s_max <= 8) heads_merge_kernel<8><<<K * B, kMergeThreads, 0, st>>>(p);
+  else if (n <= 16LL * kMergeThreads) heads_tournament_kernel<16><<<K * B, kMergeThreads, 0, st>>>(p);
+  else if (n <= 32LL * kMergeThreads) heads_tournament_kernel<32><<<K * B, kMergeThreads, 0, st>>>(p);
   else heads_merge_kernel<MV_MAX_TOPK><<<K * B, kMergeThreads, 0, st>>>(p);
   return launch_status();
 }

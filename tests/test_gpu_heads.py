@@ -54,6 +54,17 @@ def test_heads_bf16_small(B):
     assert ties <= 1
 
 
+@pytest.mark.parametrize("B,V,widths", [(3, 3000, (12, 9)),          # tournament, 16 per thread
+                                         (1, 32000, (16, 10, 5)),     # tournament, 32 per thread
+                                         (2, 64000, (16, 11))])       # 16-slot sorted lists
+def test_heads_wide_candidate_lists(B, V, widths):
+    """More than 8 candidates per head: the selection paths for long lists (d = 256)."""
+    require_gpu()
+    wl = W.WORKLOADS["c2"].scaled(B=B, d=256, V=V, K=len(widths), head_widths=widths)
+    ties = _run_and_check(wl, 40 + B, list(widths), check_logits=False)
+    assert ties <= 1
+
+
 def test_heads_fp32_batched():
     require_gpu()
     wl = W.WORKLOADS["c1"].scaled(B=5, d=128, V=777, K=2, head_widths=(3, 2))
