@@ -71,6 +71,26 @@ def test_attention_bf16_shapes(parents, B, Hq, Hkv, dh, lens):
     _run(wl, 21, lens)
 
 
+def _random_forest(n, seed):
+    """Parent array of n nodes in topological order, roots (-1) allowed anywhere."""
+    rng = np.random.default_rng(seed)
+    return [-1] + [int(rng.integers(-1, i)) for i in range(1, n)]
+
+
+def test_attention_max_nodes():
+    """256 nodes (the largest tree: 8 mask words, 4 tree tiles), a random forest, G = 4."""
+    require_gpu()
+    wl = _bf16(_random_forest(256, 7), 2, 8, 2, 64, 700)
+    _run(wl, 23, [100, 700])
+
+
+def test_attention_multichunk_with_empty_prefix():
+    """A split batch in which one sequence has no prefix (its rows skip the combine)."""
+    require_gpu()
+    wl = _bf16(branching_tree((4, 3, 2, 1)), 3, 32, 8, 128, 5000)
+    _run(wl, 24, [0, 5000, 2049])
+
+
 def test_attention_multichunk_ragged():
     """Prefixes long enough to be split into several chunks, ragged across the batch."""
     require_gpu()
