@@ -69,7 +69,7 @@ __device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool re
 }
 
 #ifndef MV_ATTN_TARGET_WG
-#define MV_ATTN_TARGET_WG 1024  // split-KV: aim for this many workgroups (one sequence)
+#define MV_ATTN_TARGET_WG 2048  // split-KV: aim for this many workgroups (one sequence)
 #endif
 #ifndef MV_ATTN_TARGET_WG_BATCH
 #define MV_ATTN_TARGET_WG_BATCH 256  // ... and with several sequences
