@@ -427,21 +427,41 @@ constexpr int kWalkThreads = 1024;
 #ifndef MV_WALK_U
 #define MV_WALK_U 2
 #endif
+constexpr int kWalkMaxVec4V = 1 << 28;  // the row's byte offsets stay far inside 31 bits
 
 // Z(c) over one row pair, fp64, by the whole workgroup; the same reduction order every time.
+// The float4 path reads both rows through buffer resources: a piece past the row reads as
+// zeros, whose term max(0, 0 - c * 0) is zero, so no load sits under a branch and the next
+// sweep's loads are in flight while this sweep's terms are summed.
 __device__ double residual_mass(const AcceptParams& p, const float* pt, const float* pd, double c,
                                 double* red) {
   const int tid = threadIdx.x;
   double acc = 0.0;
-  if (p.vec4) {
-    constexpr int U = MV_WALK_U;  // float4 pieces per row in flight per thread
-    for (int j = 4 * tid; j < p.V; j += 4 * kWalkThreads * U) {
-      float4 t4[U], d4[U];
+  if (p.vec4 && p.V <= kWalkMaxVec4V) {
+    constexpr int U = MV_WALK_U;                    // 16-byte pieces per row and sweep
+    constexpr int kSweep = 16 * kWalkThreads;       // bytes of a row one sweep covers
+    const int bytes = 4 * p.V;
+    const __amdgpu_buffer_rsrc_t rt =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(pt), 0, bytes, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rd =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(pd), 0, bytes, kBufferRsrcWord3);
+    auto ld = [](__amdgpu_buffer_rsrc_t rs, int off) {
+      return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    };
+    float4 t4[U], d4[U];
+    int off = 16 * tid;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      t4[u] = ld(rt, off + u * kSweep);
+      d4[u] = ld(rd, off + u * kSweep);
+    }
+    for (int base = 0; base < bytes; base += U * kSweep) {
+      off += U * kSweep;
+      float4 tn[U], dn[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int jj = j + 4 * kWalkThreads * u;
-        t4[u] = jj < p.V ? *reinterpret_cast<const float4*>(pt + jj) : make_float4(0.f, 0.f, 0.f, 0.f);
-        d4[u] = jj < p.V ? *reinterpret_cast<const float4*>(pd + jj) : make_float4(0.f, 0.f, 0.f, 0.f);
+        tn[u] = ld(rt, off + u * kSweep);
+        dn[u] = ld(rd, off + u * kSweep);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -449,6 +469,8 @@ __device__ double residual_mass(const AcceptParams& p, const float* pt, const fl
         acc += fmax(0.0, static_cast<double>(t4[u].y) - c * static_cast<double>(d4[u].y));
         acc += fmax(0.0, static_cast<double>(t4[u].z) - c * static_cast<double>(d4[u].z));
         acc += fmax(0.0, static_cast<double>(t4[u].w) - c * static_cast<double>(d4[u].w));
+        t4[u] = tn[u];
+        d4[u] = dn[u];
       }
     }
   } else {

@@ -82,10 +82,6 @@ constexpr int kKT = 64;  // keys per tile
 constexpr int kNWVCombine = 8;  // waves per attention workgroup (the partial blocks' layout)
 constexpr float kLazyLog2 = 8.f;  // running-max slack of the online softmax (log2 units)
 
-// Raw buffer resource (gfx950): dword 3 selects 32-bit data format for untyped loads; an
-// offset at or past the record count reads as zero.
-constexpr int kBufferRsrcWord3 = 0x00020000;
-constexpr int kBufferOutOfRange = 0x7fffffff;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));

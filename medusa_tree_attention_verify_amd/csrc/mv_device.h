@@ -15,6 +15,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Raw buffer resource (gfx950): dword 3 selects 32-bit data format for untyped loads; an
+// offset at or past the record count reads as zero.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kBufferOutOfRange = 0x7fffffff;
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
