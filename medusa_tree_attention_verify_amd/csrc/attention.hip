@@ -487,13 +487,32 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(const AttnParams p) 
     m_run = m_new;
 #pragma unroll
     for (int e = 0; e < DH / 64; ++e) acc[e] *= alpha;
+    // P.V: the V rows of kF keys are requested before any is used, and each key's weight is
+    // read from its lane with readlane (the key index is uniform).  A key with weight zero
+    // (masked or underflowed) adds nothing, whatever its V row holds.
     const int cnt = min(64, nkeys - k0);
-    for (int j = 0; j < cnt; ++j) {
-      const float pb = __shfl(pj, j);
-      if (pb != 0.f) {
-        const float* vr = Vg + static_cast<size_t>(k0 + j) * DH;
+    const float* vb = Vg + static_cast<size_t>(k0) * DH + lane;
+    constexpr int kF = 2048 / DH;  // 32 V values per lane in flight
+    int j = 0;
+    for (; j + kF <= cnt; j += kF) {
+      float vv[kF][DH / 64];
 #pragma unroll
-        for (int e = 0; e < DH / 64; ++e) acc[e] = fmaf(pb, vr[lane + 64 * e], acc[e]);
+      for (int u = 0; u < kF; ++u)
+#pragma unroll
+        for (int e = 0; e < DH / 64; ++e) vv[u][e] = vb[static_cast<size_t>(j + u) * DH + 64 * e];
+#pragma unroll
+      for (int u = 0; u < kF; ++u) {
+        const float pb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), j + u));
+#pragma unroll
+        for (int e = 0; e < DH / 64; ++e) acc[e] = pb != 0.f ? fmaf(pb, vv[u][e], acc[e]) : acc[e];
+      }
+    }
+    for (; j < cnt; ++j) {
+      const float pb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), j));
+#pragma unroll
+      for (int e = 0; e < DH / 64; ++e) {
+        const float v = vb[static_cast<size_t>(j) * DH + 64 * e];
+        acc[e] = pb != 0.f ? fmaf(pb, v, acc[e]) : acc[e];
       }
     }
   }

@@ -506,28 +506,43 @@ __global__ __launch_bounds__(NW * 64) void gemv_f32_kernel(const GemvParams p) {
   const int k = blockIdx.y, rb = blockIdx.x, row0 = rb * kRows;
   const float* Wk = static_cast<const float*>(p.W) + static_cast<size_t>(k) * p.R * p.d;
   const float* X = p.xsrc + k * p.x_hstride;
-  for (int r = w; r < kRows; r += NW) {
-    const int row = row0 + r;
-    if (row >= p.R) continue;  // wave-uniform
-    float acc[BC];
+  // The wave's rows go in groups of kRG: one 256-column step of every row of a group is
+  // requested at once, so the wave waits one round trip per group and step, not per row.
+  // Rows past R read row R-1 and are not stored.
+  constexpr int kRG = 4;
+  for (int r0 = w; r0 < kRows; r0 += NW * kRG) {
+    float acc[kRG][BC];
 #pragma unroll
-    for (int b = 0; b < BC; ++b) acc[b] = 0.f;
-    const float* wr = Wk + static_cast<size_t>(row) * p.d;
+    for (int g = 0; g < kRG; ++g)
+#pragma unroll
+      for (int b = 0; b < BC; ++b) acc[g][b] = 0.f;
+    const float* wr[kRG];
+#pragma unroll
+    for (int g = 0; g < kRG; ++g)
+      wr[g] = Wk + static_cast<size_t>(min(row0 + r0 + g * NW, p.R - 1)) * p.d;
     for (int c = lane * 4; c < p.d; c += 256) {
-      const float4 wv = *reinterpret_cast<const float4*>(wr + c);
+      float4 wv[kRG];
+#pragma unroll
+      for (int g = 0; g < kRG; ++g) wv[g] = *reinterpret_cast<const float4*>(wr[g] + c);
 #pragma unroll
       for (int b = 0; b < BC; ++b) {
         if (b < p.B) {
           const float4 xv = *reinterpret_cast<const float4*>(X + b * p.x_bstride + c);
-          acc[b] = fmaf(wv.x, xv.x, fmaf(wv.y, xv.y, fmaf(wv.z, xv.z, fmaf(wv.w, xv.w, acc[b]))));
+#pragma unroll
+          for (int g = 0; g < kRG; ++g)
+            acc[g][b] = fmaf(wv[g].x, xv.x, fmaf(wv[g].y, xv.y, fmaf(wv[g].z, xv.z, fmaf(wv[g].w, xv.w, acc[g][b]))));
         }
       }
     }
 #pragma unroll
-    for (int b = 0; b < BC; ++b) {
-      if (b < p.B) {
-        const float s = wave_sum(acc[b]);
-        if (lane == 0) ys[r][b] = s;
+    for (int g = 0; g < kRG; ++g) {
+      const int r = r0 + g * NW;
+#pragma unroll
+      for (int b = 0; b < BC; ++b) {
+        if (b < p.B) {
+          const float s = wave_sum(acc[g][b]);
+          if (lane == 0 && r < kRows && row0 + r < p.R) ys[r][b] = s;
+        }
       }
     }
   }
@@ -625,11 +640,12 @@ template <int MODE>
 int launch_gemv(int dt, const GemvParams& p, int K, hipStream_t st) {
   const dim3 grid(p.nrb, K);
   if (dt == MV_F32) {
-    const int nw = pick_nw(static_cast<long long>(p.nrb) * K, 1 << 30, 4);
+    const int nw = pick_nw(static_cast<long long>(p.nrb) * K, 1 << 30, 8);
     switch (nw) {
       case 1: gemv_f32_kernel<1, MODE><<<grid, 64, 0, st>>>(p); break;
       case 2: gemv_f32_kernel<2, MODE><<<grid, 128, 0, st>>>(p); break;
-      default: gemv_f32_kernel<4, MODE><<<grid, 256, 0, st>>>(p); break;
+      case 4: gemv_f32_kernel<4, MODE><<<grid, 256, 0, st>>>(p); break;
+      default: gemv_f32_kernel<8, MODE><<<grid, 512, 0, st>>>(p); break;
     }
     return launch_status();
   }
