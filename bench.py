@@ -250,7 +250,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps before each timed pass (the clocks settle after ~600)")
     ap.add_argument("--workload", default="c2", choices=sorted(DESCR))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
