@@ -457,7 +457,21 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(const AttnParams p) 
   float m_run = -INFINITY, l_run = 0.f, acc[DH / 64];
 #pragma unroll
   for (int e = 0; e < DH / 64; ++e) acc[e] = 0.f;
+  // P.V takes every chunk as 64 keys in batches of kF whose V rows are requested before any is
+  // used; each key's weight is read from its lane with readlane (the key index is uniform).
+  // Keys past the last one read its V row (in bounds) and, like masked or underflowed keys,
+  // carry weight zero, which adds nothing whatever the row holds.  With dh = 64 the chunk's
+  // V rows go out together with its K rows.
+  constexpr int kF = DH == 64 ? 64 : 16;
+  auto vload = [&](int key, int e) {
+    return Vg[static_cast<size_t>(min(key, nkeys - 1)) * DH + lane + 64 * e];
+  };
   for (int k0 = 0; k0 < nkeys; k0 += 64) {
+    float vv[kF][DH / 64];
+    if constexpr (DH == 64) {
+#pragma unroll
+      for (int u = 0; u < kF; ++u) vv[u][0] = vload(k0 + u, 0);
+    }
     const int kk = k0 + lane;
     bool ok = kk < nkeys;
     if (ok && kk >= Lb) {
@@ -487,32 +501,19 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(const AttnParams p) 
     m_run = m_new;
 #pragma unroll
     for (int e = 0; e < DH / 64; ++e) acc[e] *= alpha;
-    // P.V: the V rows of kF keys are requested before any is used, and each key's weight is
-    // read from its lane with readlane (the key index is uniform).  A key with weight zero
-    // (masked or underflowed) adds nothing, whatever its V row holds.
-    const int cnt = min(64, nkeys - k0);
-    const float* vb = Vg + static_cast<size_t>(k0) * DH + lane;
-    constexpr int kF = 2048 / DH;  // 32 V values per lane in flight
-    int j = 0;
-    for (; j + kF <= cnt; j += kF) {
-      float vv[kF][DH / 64];
 #pragma unroll
-      for (int u = 0; u < kF; ++u)
+    for (int j = 0; j < 64; j += kF) {
+      if constexpr (DH != 64) {
 #pragma unroll
-        for (int e = 0; e < DH / 64; ++e) vv[u][e] = vb[static_cast<size_t>(j + u) * DH + 64 * e];
+        for (int u = 0; u < kF; ++u)
+#pragma unroll
+          for (int e = 0; e < DH / 64; ++e) vv[u][e] = vload(k0 + j + u, e);
+      }
 #pragma unroll
       for (int u = 0; u < kF; ++u) {
         const float pb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), j + u));
 #pragma unroll
         for (int e = 0; e < DH / 64; ++e) acc[e] = pb != 0.f ? fmaf(pb, vv[u][e], acc[e]) : acc[e];
-      }
-    }
-    for (; j < cnt; ++j) {
-      const float pb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), j));
-#pragma unroll
-      for (int e = 0; e < DH / 64; ++e) {
-        const float v = vb[static_cast<size_t>(j) * DH + 64 * e];
-        acc[e] = pb != 0.f ? fmaf(pb, v, acc[e]) : acc[e];
       }
     }
   }
