@@ -71,6 +71,27 @@ def test_attention_bf16_shapes(parents, B, Hq, Hkv, dh, lens):
     _run(wl, 21, lens)
 
 
+def _f32(parents, B, Hq, Hkv, dh, L):
+    return W.Workload(name="f32-case", dtype="f32", B=B, Hq=Hq, Hkv=Hkv, dh=dh,
+                      parents=tuple(parents), prefix=(L, L), depth_widths=(1,))
+
+
+@pytest.mark.parametrize("parents,B,Hq,Hkv,dh,lens", [
+    ([-1], 2, 8, 2, 128, [37, 300]),                        # one node, several chunks of keys
+    (chain_tree(9), 1, 4, 1, 64, [20]),
+    (branching_tree((4, 3, 2, 1)), 1, 8, 2, 128, [0]),      # empty prefix: exactly 64 keys
+    (branching_tree((2, 2)), 2, 8, 8, 64, [59, 60]),        # 65 and 66 keys: one-key tail chunk
+    (branching_tree((4, 4, 4, 2)), 1, 4, 2, 128, [77]),     # 212 nodes, 7 mask words
+    ([-1, 0, 1, 1, 0, -1, 5], 3, 8, 4, 64, [3, 64, 129]),   # forest (two roots), ragged batch
+])
+def test_attention_fp32_shapes(parents, B, Hq, Hkv, dh, lens):
+    """The fp32 path (one wave per query row, P.V in batches of V rows) at both head sizes,
+    across chunk boundaries of its 64-key loop."""
+    require_gpu()
+    wl = _f32(parents, B, Hq, Hkv, dh, max(lens))
+    _run(wl, 23, lens)
+
+
 def _random_forest(n, seed):
     """Parent array of n nodes in topological order, roots (-1) allowed anywhere."""
     rng = np.random.default_rng(seed)
