@@ -71,6 +71,14 @@ def test_heads_fp32_batched():
     _run_and_check(wl, 7, [3, 2])
 
 
+def test_heads_fp32_large_vocab():
+    """fp32 heads over 4 x 32000 rows (d = 64): enough row blocks that the projection runs
+    4 waves per workgroup, so each wave takes two groups of rows."""
+    require_gpu()
+    wl = W.WORKLOADS["c1"].scaled(B=1, d=64, V=32000, K=4, head_widths=(4, 3, 2, 1))
+    _run_and_check(wl, 9, [4, 3, 2, 1])
+
+
 def test_heads_llama8b_shape_full():
     """d=4096, V=32000, 4 heads, widths (4,3,2,1), batch 1 (the full Llama-3-8B shape)."""
     require_gpu()
