@@ -426,7 +426,8 @@ def main():
         dur_s = seg_mean["heads_projection"] / 1000.0
         ach = b_head / dur_s / 1e9
         src = os.path.join(ROOT, "medusa_tree_attention_verify_amd", "csrc", "heads.hip")
-        roof = {"kernel": "gemv_bf16_kernel<head projection>", "bound": "hbm",
+        kname = "gemv_bf16_kernel" if wl.dtype == "bf16" else "gemv_f32_kernel"
+        roof = {"kernel": f"{kname}<head projection>", "bound": "hbm",
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4),
                 "traffic": _traffic("head_projection", DESCR[args.workload].split(":")[0], src),
