@@ -17,8 +17,9 @@
  *         greedy longest-path rule).
  *   [MTP] "Multi-Token Prediction: Draft-Model-Free Speculative Decoding" (globaltechdigest
  *         blog): "The 2D Tree Attention Mask", "Tree-Structured Attention Verification"
- *         (figure box: longest valid path + 1 bonus token), and the verification-engine code
- *         (parent array, -1 = root; index-order acceptance; longest path, first wins ties).
+ *         (Figure 1's text box: the target adds one token after the committed path), and the
+ *         verification-engine code (parent-array trees with -1 roots; the first of equally
+ *         long accepted paths is kept).
  *   [SD]  "Speculative Decoding & Medusa Tree Attention" (akmalkhaniub blog), section 2,
  *         "The Acceptance Sampling Rule" (alpha and the residual distribution).
  *
@@ -276,11 +277,10 @@ MV_API int mv_lm_head_argmax(int dt, int T, int d, int V, const void* x, const v
 
 /* ---------------------------------------------------------------------------------------
  * (a6)+(a7) Acceptance and the extra token.  Row 0 of target/draft is the distribution after
- * the last prefix token; row i+1 the one after node i.  Node i (index order) is tested
- * against the row of its parent and is accepted iff it passes and its parent is -1 or
- * accepted.  The committed path ends at the deepest accepted node, the lowest index winning
- * ties ([MTP] engine code keeps the first longest path); one extra token follows it
- * ([MTP] figure box "longest valid path + 1 bonus token").
+ * the last prefix token; row i+1 the one after node i.  Each node is tested against the row
+ * of its parent, and is accepted when it and all of its ancestors pass.  The committed path ends at the deepest accepted node, the lowest index winning
+ * ties (the [MTP] engine code keeps the first of equally long paths); the target then adds
+ * one more token after it (the text box of [MTP] Figure 1).
  *
  * MV_ACCEPT_GREEDY ([MX] "2. Single-Pass Tree Attention Verification", step 3): target holds
  *   logits (dt); node i passes iff its token equals the argmax of its parent's row (lowest

@@ -9,7 +9,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmedusa_verify.so")
+LIB_NAME = "libmedusa_verify.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 MV_OK = 0
 MV_ERR_INVALID_ARG = -1
@@ -79,15 +80,44 @@ class MVError(RuntimeError):
         self.status = status
 
 
+def _hip_runtimes():
+    """Distinct files of the HIP runtime mapped into this process."""
+    found = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) >= 6 and os.path.basename(parts[5]).startswith("libamdhip64.so"):
+                    found.add(os.path.realpath(parts[5]))
+    except OSError:  # pragma: no cover - no procfs
+        pass
+    return sorted(found)
+
+
 def lib() -> ctypes.CDLL:
-    """The loaded library (raises ImportError when it has not been built)."""
+    """The loaded library (raises ImportError when it has not been built).
+
+    PyTorch ships its own copy of the HIP runtime (same soname as the system one, different
+    file).  The library is linked against the system runtime by soname, so it binds to
+    whichever copy is already loaded; loaded before torch, it would pull in the system copy
+    and torch would then load its own next to it: two HIP (and HSA) runtimes in one process,
+    each with its own device state, and calls of one failing on the other's initialisation.
+    torch is therefore imported first, and a second runtime is an error."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(
                 f"{LIB_PATH} is missing: build the HIP library first "
                 "(python -c 'import __graft_entry__ as g; g.build()')")
+        try:
+            import torch  # noqa: F401  (binds the HIP runtime torch loads)
+        except ImportError:  # pragma: no cover - the binding is always used with torch
+            pass
         L = ctypes.CDLL(LIB_PATH)
+        rts = _hip_runtimes()
+        if len(rts) > 1:
+            raise ImportError(f"two HIP runtimes are loaded in this process: {rts}; load "
+                              f"torch (or any HIP user) before {LIB_NAME}, not after it")
         for name, res, args in SIGNATURES:
             f = getattr(L, name)
             f.restype = res

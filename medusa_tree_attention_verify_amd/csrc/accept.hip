@@ -6,9 +6,9 @@
 // choice); "Speculative Decoding & Medusa Tree Attention", section 2, "The Acceptance
 // Sampling Rule" (accept with probability min(1, P_t/P_d), else sample from
 // normalize(max(0, P_t - P_d))); "Multi-Token Prediction: Draft-Model-Free Speculative
-// Decoding", the verification engine (nodes tested in index order, a node counts only under
-// an accepted parent, the first longest path wins) and the figure box (longest valid path
-// plus one bonus token).
+// Decoding", the verification engine (a node counts only when its whole root path passes;
+// among equally long accepted paths the first is kept) and the text box of its Figure 1 (the
+// target adds one token after the committed path).
 //
 // Greedy: the target rows are scanned once by many workgroups (row segments -> partial
 // argmax), then one workgroup per sequence merges them and walks the tree.

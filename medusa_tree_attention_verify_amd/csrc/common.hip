@@ -22,12 +22,7 @@ MV_API int mv_device_check(int device) {
   int n = 0;
   if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return MV_ERR_HIP;
   hipDeviceProp_t prop;
-  hipError_t e = hipGetDeviceProperties(&prop, device);
-  if (e != hipSuccess) {  // retry once after clearing a stale error left by an earlier call
-    (void)hipGetLastError();
-    e = hipGetDeviceProperties(&prop, device);
-  }
-  if (e != hipSuccess) return MV_ERR_HIP;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return MV_ERR_HIP;
   return strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? MV_OK : MV_ERR_UNSUPPORTED;
 }
 

@@ -38,9 +38,6 @@ constexpr int kRows = 32;  // weight rows per workgroup
 #ifndef MV_GEMV_WAVES
 #define MV_GEMV_WAVES 12288    // waves per launch to aim for (1024 SIMDs on the chip)
 #endif
-#ifndef MV_GEMV_NT
-#define MV_GEMV_NT 0           // non-temporal weight loads (measured slower when on)
-#endif
 
 struct GemvParams {
   int B, d, R, K, T, nrb;   // R = rows per head, T = d / 32, nrb = ceil(R / kRows)
@@ -68,13 +65,7 @@ struct GemvParams {
   int s[MV_MAX_HEADS];
 };
 
-__device__ __forceinline__ u32x4 wload(const u32x4* p) {
-#if MV_GEMV_NT
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
-}
+__device__ __forceinline__ u32x4 wload(const u32x4* p) { return *p; }
 
 template <bool BF16>
 __device__ __forceinline__ float load_elem(const void* base, size_t i) {

@@ -2,10 +2,11 @@
 // bitmask and the token of every node.
 //
 // Sources: "Multi-Token Prediction: Draft-Model-Free Speculative Decoding", the verification
-// engine's parent array (-1 = a root hanging off the prefix) and its mask walk (follow the
-// parents up to -1, marking every node met), and "The 2D Tree Attention Mask" (ancestor or
-// self); "Medusa Explained: Multi-Head Speculative Decoding Guide", "1. Combinatorial Tree
-// Construction" (the depth-k nodes are the top-s_k tokens of the depth-k head).
+// engine's tree format (a parent array; -1 marks a root that hangs off the prefix) and "The
+// 2D Tree Attention Mask" (a node sees its ancestors and itself); "Medusa Explained:
+// Multi-Head Speculative Decoding Guide", "1. Combinatorial Tree Construction" (the depth-k
+// nodes are the top-s_k tokens of the depth-k head).  Each thread collects its node's
+// ancestor-or-self set by following parent links until it leaves the tree.
 //
 // One workgroup, one thread per node.  Every walk checks parents[c] in [-1, c), so it moves
 // to strictly smaller indices and ends within N steps even on a malformed array.

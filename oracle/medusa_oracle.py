@@ -16,9 +16,10 @@ verification):
   5-candidate mask example, greedy longest-accepted-path rule).
 * "Multi-Token Prediction: Draft-Model-Free Speculative Decoding"
   (globaltechdigest blog): "The 2D Tree Attention Mask" (boolean mask,
-  ancestor-or-self), the verification-engine code (parent array with -1
-  roots, index-order acceptance, longest path with first-wins ties) and the
-  Figure-1 text box (longest valid path plus one bonus token), and
+  ancestor-or-self), the verification-engine code (a parent array with -1
+  roots; the committed path is the longest accepted one, the first of equal
+  ones) and the text box of Figure 1 (the target adds one token after the
+  committed path), and
   "Production Deployment Guidelines" (unselected branches culled from the KV
   cache after verification).
 * "Speculative Decoding & Medusa Tree Attention" (akmalkhaniub blog):
@@ -83,9 +84,9 @@ def medusa_heads(h, w_res, w_head, widths: Sequence[int]) -> Dict[str, np.ndarra
     Returns hk [B,K,d], logits [B,K,V], topk_ids/topk_vals [B,K,s_max]
     (-1 / -inf padded past widths[k]), lse [B,K] = log sum exp(logits).
     """
-    h, w_res, w_head = _f64(h), _f64(w_res), _f64(w_head)
+    h = _f64(h)
     B, d = h.shape
-    K, V, _ = w_head.shape
+    K, V, _ = np.shape(w_head)
     s_max = max(widths)
     hk = np.empty((B, K, d))
     logits = np.empty((B, K, V))
@@ -93,10 +94,11 @@ def medusa_heads(h, w_res, w_head, widths: Sequence[int]) -> Dict[str, np.ndarra
     vals = np.full((B, K, s_max), -np.inf)
     lse = np.empty((B, K))
     for k in range(K):
+        wr, wh = _f64(w_res[k]), _f64(w_head[k])   # one head at a time in host memory
         for b in range(B):
-            u = w_res[k] @ h[b]
+            u = wr @ h[b]
             hk[b, k] = silu(u) + h[b]
-            z = w_head[k] @ hk[b, k]
+            z = wh @ hk[b, k]
             logits[b, k] = z
             t = topk_rows(z, widths[k])
             ids[b, k, :widths[k]] = t["ids"]
@@ -177,7 +179,8 @@ def build_tree(parents: Sequence[int], cand: Optional[Sequence[np.ndarray]] = No
 
 
 def mask_matrix(anc: Sequence[Sequence[int]]) -> np.ndarray:
-    """Dense boolean N x N mask: M[i, j] = j is an ancestor of i or j == i."""
+    """The ancestor-or-self sets as an N x N boolean matrix (row i is True exactly at the
+    columns listed in anc[i])."""
     N = len(anc)
     m = np.zeros((N, N), dtype=bool)
     for i, a in enumerate(anc):
@@ -237,29 +240,28 @@ def tree_attention(q, k_cache, v_cache, prefix_len, anc: Sequence[Sequence[int]]
 
 # --------------------------------------------------------------------------
 # 4a. Greedy acceptance ("2. Single-Pass Tree Attention Verification", step 3:
-#     longest path whose every token equals the target's greedy choice;
-#     verification-engine code: index-order acceptance, first-wins ties;
-#     Figure-1 box: one bonus token from the target after the path)
+#     the committed path is the longest one on which every token equals the
+#     target's greedy choice; the verification-engine code keeps the first of
+#     equally long paths; the Figure-1 text box adds one token from the target
+#     after the path)
 # --------------------------------------------------------------------------
-def _longest_path(parents, accepted):
-    """Deepest accepted node (first in index order on ties) and its root path."""
-    best, best_len = -1, 0
-    for i in range(len(parents)):
-        if not accepted[i]:
-            continue
-        path = []
-        c = i
-        while c != -1 and accepted[c]:
-            path.append(c)
-            c = int(parents[c])
-        if len(path) > best_len:
-            best, best_len = i, len(path)
-    path = []
-    c = best
-    while c != -1:
-        path.append(c)
-        c = int(parents[c])
-    return best, path[::-1]
+def _committed_path(parents, passes):
+    """Accepted nodes and the committed path of one sequence, from each node's own test.
+
+    passes[i] is node i's own test (token match, or u < alpha).  A node is accepted when it
+    and every node of its ancestor-or-self set pass, i.e. when the whole chain of candidate
+    tokens from the prefix down to it is taken.  The ancestor-or-self set of a node has as
+    many members as the node's depth, so among the accepted nodes the committed one is the
+    one with the largest set, the lowest node index among equals.  Its path, root first, is
+    that set in increasing index order (a parent always has a smaller index than its child).
+    Returns (accepted [N] bool, terminal node or -1 for the prefix, path list)."""
+    anc = build_tree(parents)["anc"]
+    accepted = np.array([all(bool(passes[j]) for j in a) for a in anc], dtype=bool)
+    size = np.where(accepted, [len(a) for a in anc], 0)
+    if size.size == 0 or size.max() == 0:
+        return accepted, -1, []
+    term = int(np.flatnonzero(size == size.max())[0])
+    return accepted, term, sorted(anc[term])
 
 
 def _pack(paths_tokens, B, D):
@@ -279,23 +281,21 @@ def accept_greedy(target, node_tokens, parents, D: int) -> Dict[str, np.ndarray]
 
     target [B, N+1, V]: row 0 is the distribution after the last prefix token,
     row i+1 the one after node i.  pred[r] = argmax of row r (first index on
-    ties).  Node i (index order, parents first) is accepted iff its parent is
-    the prefix or an accepted node, and its token equals pred[parent row].
-    The committed path ends at the deepest accepted node (lowest index on
-    ties); the bonus token is pred at that node's row (row 0 if none).
+    ties).  Node i passes when its token equals pred at its parent's row, and
+    is accepted when every node from its root down to it passes.  The
+    committed path ends at the deepest accepted node (lowest index on ties);
+    the bonus token is pred at that node's row (row 0 if none).
     """
     target = _f64(target)
     B, R, V = target.shape
     N = len(parents)
     pred = np.argmax(target, axis=-1)          # first maximal index
+    prow = np.asarray(parents, dtype=np.int64) + 1   # row of each node's parent
     accepted = np.zeros((B, N), dtype=bool)
     res = []
     for b in range(B):
-        for i in range(N):
-            p = int(parents[i])
-            ok = (p == -1) or accepted[b, p]
-            accepted[b, i] = ok and int(node_tokens[b, i]) == int(pred[b, p + 1])
-        term, path = _longest_path(parents, accepted[b])
+        passes = np.asarray(node_tokens[b], dtype=np.int64) == pred[b, prow]
+        accepted[b], term, path = _committed_path(parents, passes)
         res.append((path, [int(node_tokens[b, n]) for n in path], int(pred[b, term + 1])))
     acc_len, path_nodes, out_tokens = _pack(res, B, D)
     return {"accept_len": acc_len, "path_nodes": path_nodes, "out_tokens": out_tokens,
@@ -325,8 +325,8 @@ def accept_speculative(p_target, p_draft, node_tokens, parents, uniforms,
     p_target/p_draft [B, N+1, V] probabilities (row 0 = after the prefix, row
     i+1 = after node i); uniforms [B, N+1] in [0, 1).
     alpha_i = min(1, P_t[parent row, x_i] / P_d[parent row, x_i]) (1 when
-    P_d = 0); node i passes iff u[b, i] < alpha_i and is accepted iff it
-    passes and its parent is the prefix or accepted.  The path ends at the
+    P_d = 0); node i passes iff u[b, i] < alpha_i and is accepted iff every
+    node from its root down to it passes.  The path ends at the
     deepest accepted node e (lowest index on ties; e = prefix if none).  The
     extra token is drawn with u[b, N] by inverse CDF from
     normalize(max(0, P_t[e] - P_d[e])) when e has children (all of them were
@@ -340,18 +340,16 @@ def accept_speculative(p_target, p_draft, node_tokens, parents, uniforms,
     has_child = np.zeros(N + 1, dtype=bool)    # index = row (node + 1); row 0 = prefix
     for i in range(N):
         has_child[int(parents[i]) + 1] = True
+    prow = np.asarray(parents, dtype=np.int64) + 1   # row of each node's parent
     alpha = np.zeros((B, N))
     accepted = np.zeros((B, N), dtype=bool)
     res = []
     for b in range(B):
-        for i in range(N):
-            p = int(parents[i])
-            x = int(node_tokens[b, i])
-            pt, pd = p_t[b, p + 1, x], p_d[b, p + 1, x]
-            alpha[b, i] = 1.0 if pd == 0.0 else min(1.0, pt / pd)
-            ok = (p == -1) or accepted[b, p]
-            accepted[b, i] = ok and (u[b, i] < alpha[b, i])
-        term, path = _longest_path(parents, accepted[b])
+        x = np.asarray(node_tokens[b], dtype=np.int64)
+        pt, pd = p_t[b, prow, x], p_d[b, prow, x]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            alpha[b] = np.where(pd == 0.0, 1.0, np.minimum(1.0, pt / np.where(pd == 0.0, 1.0, pd)))
+        accepted[b], term, path = _committed_path(parents, u[b, :N] < alpha[b])
         row = term + 1
         if has_child[row]:
             r = np.maximum(0.0, p_t[b, row] - p_d[b, row])
