@@ -12,7 +12,8 @@ Prints one JSON line: steps/s (and verified tree tokens/s), the roofline of the 
 kernel (the vocabulary-streaming head projection) timed with HIP events on the stream it
 runs on, and the CPU oracle timed on the host cores on a bounded sample.
 
-    python bench.py [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload c3] [--no-cpu-baseline]
+    python bench.py --workload c3 --tau 1024   # mean accepted length over a decode loop
     python bench.py --copy-calibration      # plain device copy of known size (for counters)
 """
 from __future__ import annotations
@@ -121,98 +122,175 @@ def step_bytes(wl, x):
 
 
 # --------------------------------------------------------------------------- CPU oracle
-def cpu_baseline(wl, x, seed, budget_s):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+def _host_info():
+    """CPU model (first /proc/cpuinfo entry), usable cores and the BLAS thread count."""
     from threadpoolctl import threadpool_info
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return model, cores, blas
 
+
+def _oracle_step(wl, x, seed, attn_rows=None):
+    """One oracle step of the workload on its inputs; returns seconds per part.
+
+    attn_rows = (b, h, i) query rows: the attention is computed for those rows only (None:
+    every row).  Planting the target is input generation and is not timed."""
     from medusa_tree_attention_verify_amd import workloads as W
     from oracle import medusa_oracle as O
 
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     parents = list(wl.parents)
-    t_total = 0.0
-    steps = 0
-    sample = None
-    while True:
-        t0 = time.perf_counter()
-        cand = []
-        if wl.has_heads:
-            heads = O.medusa_heads(x["h"], x["w_res"], x["w_head"], list(wl.head_widths))
-            if wl.lm_width:
-                cand.append(np.stack([O.topk_rows(x["target"][b, 0], wl.lm_width)["ids"]
-                                      for b in range(wl.B)]))
-            cand += [heads["topk_ids"][:, k, :wl.head_widths[k]] for k in range(wl.K)]
-        elif wl.accept == "speculative":
-            cand = None
-        if wl.dynamic_nodes:         # one tree per sequence: its most probable head paths
-            dyn = O.dynamic_tree(heads["topk_ids"], heads["topk_vals"], heads["lse"],
-                                 list(wl.head_widths), wl.dynamic_nodes)
-            trees = [{"parents": dyn["parents"][b], "anc": dyn["anc"][b],
-                      "tokens": np.array([dyn["tokens"][b]])} for b in range(wl.B)]
-        else:
-            tree = (O.build_tree(parents, cand, list(wl.depth_widths)) if cand
-                    else O.build_tree(parents))
-            trees = [{"parents": parents, "anc": tree["anc"],
-                      "tokens": tree["tokens"][b:b + 1] if "tokens" in tree else None}
-                     for b in range(wl.B)]
-        t1 = time.perf_counter()
-        target = None
-        x_t = None
-        if wl.target_head:           # input generation (planting) is not timed
-            x_t = x["x_t"].copy()
-            if wl.plant_p > 0:
-                x_t = W.plant_target_head(x_t, x["w_lm"], parents, tree["tokens"], seed, wl.plant_p)
-        elif wl.accept == "greedy":  # input generation (planting) is not timed
-            target = x["target"].copy()
-            if wl.plant_p > 0 and wl.dynamic_nodes:
-                for b, t in enumerate(trees):
-                    target[b:b + 1] = W.plant_greedy(target[b:b + 1], t["parents"], t["tokens"],
-                                                     seed + b, wl.plant_p)
-            elif wl.plant_p > 0:
-                target = W.plant_greedy(target, parents, tree["tokens"], seed, wl.plant_p)
-            if wl.dtype == "bf16":
-                target = W.round_bf16(target)
-        t2 = time.perf_counter()
-        # attention: whole batch when it fits the budget, else a slice of the query rows
-        if sample is None:
-            sample = "1 full step"
-        if wl.dynamic_nodes:
-            for b, t in enumerate(trees):
-                sl = slice(b, b + 1)
-                O.tree_attention(x["q"][sl], x["k_cache"][sl], x["v_cache"][sl],
-                                 x["prefix_len"][sl], t["anc"])
-        else:
-            O.tree_attention(x["q"], x["k_cache"], x["v_cache"], x["prefix_len"], tree["anc"])
-        if wl.target_head:
-            z = O.lm_head_argmax(x_t.reshape(-1, wl.d), x["w_lm"])["logits"]
-            target = z.reshape(wl.B, wl.N + 1, wl.accept_V)
-        if wl.accept == "greedy" and wl.dynamic_nodes:
-            per = [O.accept_greedy(target[b:b + 1], t["tokens"], t["parents"], wl.D)
-                   for b, t in enumerate(trees)]
-            acc = {k: np.concatenate([a[k] for a in per]) for k in ("accept_len", "path_nodes")}
-        elif wl.accept == "greedy":
-            acc = O.accept_greedy(target, tree["tokens"], parents, wl.D)
-        elif wl.accept == "multicand":
-            acc = O.accept_multicandidate(x["p_target"], x["p_draft"], x["node_tokens"], parents,
-                                          x["uniforms"], wl.D)
-        elif wl.accept == "speculative":
-            acc = O.accept_speculative(x["p_target"], x["p_draft"], x["node_tokens"], parents,
-                                       x["uniforms"], wl.D)
-        if wl.accept != "none":     # commit, on each sequence's tree block
-            for b in range(wl.B):
-                Lb = int(x["prefix_len"][b])
-                blk = slice(Lb, Lb + wl.N)
-                O.kv_commit(x["k_cache"][b:b + 1, :, blk], x["v_cache"][b:b + 1, :, blk],
-                            np.zeros(1, np.int64), acc["path_nodes"][b:b + 1],
-                            acc["accept_len"][b:b + 1], wl.N)
-        t3 = time.perf_counter()
-        t_total += (t1 - t0) + (t3 - t2)
-        steps += 1
-        if t_total >= budget_s or steps >= 100:
-            break
-    return {"value": steps / t_total, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{steps} full step(s) of the same workload (seed {seed}), "
-                      f"{t_total:.1f} s, NumPy fp64"}
+    t = {}
+    t0 = time.perf_counter()
+    cand = []
+    if wl.has_heads:
+        heads = O.medusa_heads(x["h"], x["w_res"], x["w_head"], list(wl.head_widths))
+        if wl.lm_width:
+            cand.append(np.stack([O.topk_rows(x["target"][b, 0], wl.lm_width)["ids"]
+                                  for b in range(wl.B)]))
+        cand += [heads["topk_ids"][:, k, :wl.head_widths[k]] for k in range(wl.K)]
+    t1 = time.perf_counter()
+    if wl.dynamic_nodes:         # one tree per sequence: its most probable head paths
+        dyn = O.dynamic_tree(heads["topk_ids"], heads["topk_vals"], heads["lse"],
+                             list(wl.head_widths), wl.dynamic_nodes)
+        trees = [{"parents": dyn["parents"][b], "anc": dyn["anc"][b],
+                  "tokens": np.array([dyn["tokens"][b]])} for b in range(wl.B)]
+    else:
+        tree = (O.build_tree(parents, cand, list(wl.depth_widths)) if cand
+                else O.build_tree(parents))
+        trees = [{"parents": parents, "anc": tree["anc"],
+                  "tokens": tree["tokens"][b:b + 1] if "tokens" in tree else None}
+                 for b in range(wl.B)]
+    t2 = time.perf_counter()
+    t["heads"], t["tree"] = t1 - t0, t2 - t1
+    target = None
+    x_t = None
+    if wl.target_head:
+        x_t = x["x_t"].copy()
+        if wl.plant_p > 0:
+            x_t = W.plant_target_head(x_t, x["w_lm"], parents, tree["tokens"], seed, wl.plant_p)
+    elif wl.accept == "greedy":
+        target = x["target"].copy()
+        if wl.plant_p > 0 and wl.dynamic_nodes:
+            for b, tr in enumerate(trees):
+                target[b:b + 1] = W.plant_greedy(target[b:b + 1], tr["parents"], tr["tokens"],
+                                                 seed + b, wl.plant_p)
+        elif wl.plant_p > 0:
+            target = W.plant_greedy(target, parents, tree["tokens"], seed, wl.plant_p)
+        if wl.dtype == "bf16":
+            target = W.round_bf16(target)
+    t3 = time.perf_counter()
+    if wl.dynamic_nodes:
+        for b, tr in enumerate(trees):
+            sl = slice(b, b + 1)
+            O.tree_attention(x["q"][sl], x["k_cache"][sl], x["v_cache"][sl],
+                             x["prefix_len"][sl], tr["anc"])
+    else:
+        O.tree_attention(x["q"], x["k_cache"], x["v_cache"], x["prefix_len"], tree["anc"],
+                         select=attn_rows)
+    t4 = time.perf_counter()
+    if wl.target_head:
+        z = O.lm_head_argmax(x_t.reshape(-1, wl.d), x["w_lm"])["logits"]
+        target = z.reshape(wl.B, wl.N + 1, wl.accept_V)
+    if wl.accept == "greedy" and wl.dynamic_nodes:
+        per = [O.accept_greedy(target[b:b + 1], tr["tokens"], tr["parents"], wl.D)
+               for b, tr in enumerate(trees)]
+        acc = {k: np.concatenate([a[k] for a in per]) for k in ("accept_len", "path_nodes")}
+    elif wl.accept == "greedy":
+        acc = O.accept_greedy(target, tree["tokens"], parents, wl.D)
+    elif wl.accept == "multicand":
+        acc = O.accept_multicandidate(x["p_target"], x["p_draft"], x["node_tokens"], parents,
+                                      x["uniforms"], wl.D)
+    elif wl.accept == "speculative":
+        acc = O.accept_speculative(x["p_target"], x["p_draft"], x["node_tokens"], parents,
+                                   x["uniforms"], wl.D)
+    if wl.accept != "none":     # commit, on each sequence's tree block
+        for b in range(wl.B):
+            Lb = int(x["prefix_len"][b])
+            blk = slice(Lb, Lb + wl.N)
+            O.kv_commit(x["k_cache"][b:b + 1, :, blk], x["v_cache"][b:b + 1, :, blk],
+                        np.zeros(1, np.int64), acc["path_nodes"][b:b + 1],
+                        acc["accept_len"][b:b + 1], wl.N)
+    t5 = time.perf_counter()
+    t["attention"], t["accept_commit"] = t4 - t3, t5 - t4
+    return t
+
+
+# query-row x key products above which one oracle step is sampled instead of run whole
+ORACLE_FULL_STEP_WORK = 5e7
+ORACLE_SAMPLE_WORK = 1.5e7
+
+
+def cpu_baseline(wl, x, seed, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same workload.
+
+    Small steps run whole, repeatedly, until ``budget_s`` seconds of oracle work.  Larger ones
+    run one step in which every part is whole except the attention, which is computed for the
+    query rows of one (sequence, KV head) slice (at most ORACLE_SAMPLE_WORK row x key
+    products) and scaled to the whole batch by its share of row x key products (the oracle's
+    attention costs one pass over the visible keys per query row)."""
+    model, cores, blas = _host_info()
+    N, G = wl.N, wl.Hq // wl.Hkv
+    keys = x["prefix_len"].astype(np.int64) + N
+    work = float(np.sum(keys)) * wl.Hq * N
+    res = {"unit": "steps/s", "cores": int(blas), "kind": "oracle", "cpu_model": model,
+           "host_cores": int(cores), "blas_threads": int(blas)}
+    if work <= ORACLE_FULL_STEP_WORK:
+        t_total, steps = 0.0, 0
+        while True:
+            t_total += sum(_oracle_step(wl, x, seed).values())
+            steps += 1
+            if t_total >= budget_s or steps >= 100:
+                break
+        res.update(value=steps / t_total,
+                   sample=f"{steps} full oracle step(s) of the same workload (seed {seed}), "
+                          f"{t_total:.1f} s, NumPy fp64")
+        return res
+    b0 = int(np.argmax(keys))                 # the longest sequence's first KV head
+    nrows = int(min(G * N, max(1, ORACLE_SAMPLE_WORK // int(keys[b0]))))
+    rows = [(b0, h, i) for h in range(G) for i in range(N)][:nrows]
+    parts = _oracle_step(wl, x, seed, attn_rows=rows)
+    scale = work / (float(keys[b0]) * nrows)
+    t_step = parts["heads"] + parts["tree"] + parts["accept_commit"] + parts["attention"] * scale
+    res.update(value=1.0 / t_step,
+               sample=f"one oracle step (seed {seed}, NumPy fp64) with heads, tree, acceptance "
+                      f"and commit whole and the attention of {nrows} of {wl.B * wl.Hq * N} "
+                      f"query rows (sequence {b0}, KV head 0), scaled x{scale:.1f} by query-row "
+                      f"x key products; measured {sum(parts.values()):.1f} s",
+               parts_s={k: round(v * (scale if k == "attention" else 1.0), 3)
+                        for k, v in parts.items()})
+    return res
+
+
+def cpu_single_thread(names=("c1", "c2"), budget_s=5.0):
+    """Whole oracle steps of the small workloads with one BLAS thread (steps/s)."""
+    from threadpoolctl import threadpool_limits
+
+    from medusa_tree_attention_verify_amd import workloads as W
+    out = {}
+    for n in names:
+        wl = W.WORKLOADS[n]
+        seed = int(n[1:])
+        x = make_inputs(wl, seed)
+        with threadpool_limits(limits=1):
+            t_total, steps = 0.0, 0
+            while t_total < budget_s and steps < 100:
+                t_total += sum(_oracle_step(wl, x, seed).values())
+                steps += 1
+        out[DESCR[n].split(":")[0]] = round(steps / t_total, 3)
+        del x
+    return out
 
 
 # --------------------------------------------------------------------------- main
@@ -246,15 +324,89 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
 
 
+def tau_loop(n_seq_steps, wl, seed, step, inputs, x):
+    """Committed decode loop for the mean accepted length (tau) of the planted generator.
+
+    Every step verifies the same candidate tree (the heads' input is fixed) against a target
+    planted afresh (its own seed): each parent row's greedy token is one of its children with
+    probability p, independently.  The step commits its accepted path and the next step starts
+    from the grown prefix (the prefixes start D x steps below the drawn ones, so they stay
+    inside the cache).  On a tree that is full to depth D this gives P(accepted >= k) = p^k
+    and a mean accepted length of sum_{k=1..D} p^k (the page's tau with one extra token per
+    step is that plus one).  Prints one JSON line; nothing here is timed."""
+    import torch
+
+    from medusa_tree_attention_verify_amd import workloads as W
+    if wl.accept != "greedy" or wl.plant_p <= 0 or wl.target_head or wl.dynamic_nodes:
+        raise SystemExit("--tau needs a greedy workload with a planted target and a fixed tree")
+    parents = list(wl.parents)
+    depth = []
+    for p_ in parents:
+        depth.append(1 if p_ < 0 else depth[p_] + 1)
+    has_kids = {p_ for p_ in parents}
+    full = all(i in has_kids for i, dd in enumerate(depth) if dd < wl.D)
+    steps = -(-n_seq_steps // wl.B)
+    calls = step.sequence(step.bind(inputs))
+    toks = step.tree["node_tokens"].cpu().numpy()
+    pl = inputs["prefix_len"]
+    start = np.maximum(0, x["prefix_len"].astype(np.int64) - wl.D * steps).astype(np.int32)
+    pl.copy_(torch.from_numpy(start))
+    lens = []
+    for it in range(steps):
+        tgt = W.plant_greedy(x["target"].copy(), parents, toks, seed * 100003 + it + 1,
+                             wl.plant_p)
+        if wl.dtype == "bf16":
+            tgt = W.round_bf16(tgt)
+        inputs["target"].copy_(torch.from_numpy(tgt))
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        lens.append(step.acc["accept_len"].cpu().numpy().copy())
+        pl.copy_(step.prefix_next)
+    torch.cuda.synchronize()
+    if int(step.status.item()) != 0:
+        raise RuntimeError(f"device status flags {int(step.status.item())}")
+    a = np.concatenate(lens).astype(np.float64)
+    n = a.size
+    mean, se = float(a.mean()), float(a.std(ddof=1) / np.sqrt(n))
+    p = wl.plant_p
+    cf = sum(p ** k for k in range(1, wl.D + 1)) if full else None
+    grew = (pl.cpu().numpy().astype(np.int64) - start).tolist()
+    print(json.dumps({
+        "metric": "mean accepted length per verify step (tau, planted greedy target)",
+        "value": round(mean, 4), "unit": "tokens", "sequence_steps": int(n), "steps": steps,
+        "std_err": round(se, 4), "ci95": [round(mean - 1.96 * se, 4), round(mean + 1.96 * se, 4)],
+        "closed_form": None if cf is None else round(cf, 4),
+        "z_vs_closed_form": None if cf is None else round((mean - cf) / se, 2),
+        "emitted_per_step": round(mean + 1.0, 4),
+        "emitted_closed_form": None if cf is None else round(cf + 1.0, 4),
+        "p_len_ge_k": {str(k): [round(float((a >= k).mean()), 4), round(p ** k, 4)]
+                       for k in range(1, wl.D + 1)},
+        "prefix_growth_per_sequence": grew,
+        "config": {"workload": DESCR[wl_key(wl)], "plant_p": p, "seed": seed},
+    }), flush=True)
+
+
+def wl_key(wl):
+    from medusa_tree_attention_verify_amd import workloads as W
+    return next(k for k, v in W.WORKLOADS.items() if v == wl)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=1000,
                     help="untimed steps before each timed pass (the clocks settle after ~600)")
-    ap.add_argument("--workload", default="c2", choices=sorted(DESCR))
+    ap.add_argument("--workload", default="c3", choices=sorted(DESCR))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-single-thread", action="store_true",
+                    help="skip the one-thread oracle timings of the two small workloads")
+    ap.add_argument("--tau", type=int, default=0,
+                    help="instead of timing: run a committed decode loop of this many "
+                         "sequence-steps with freshly planted targets and report the mean "
+                         "accepted length against the planted closed form")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work timed for cpu_baseline (whole steps, at least one)")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -347,6 +499,9 @@ def main():
             else:
                 tgt = W.plant_greedy(x["target"].copy(), list(wl.parents), toks, seed, wl.plant_p)
             base["target"] = d(W.round_bf16(tgt) if wl.dtype == "bf16" else tgt)
+    if args.tau:
+        tau_loop(args.tau, wl, seed, step, dict(static, **base), x)
+        return
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
     seqs = [step.sequence(step.bind(dict(static, **s))) for s in sets]
     present = [p for p in step.PARTS if p in step.bind(dict(static, **base))]
@@ -463,15 +618,24 @@ def main():
         "config": {"workload": DESCR[args.workload], "global_batch": wl.B, "tree_nodes": wl.N,
                    "seq_len": max_L, "rotating_input_sets": R},
         "verified_tree_tokens_per_s": round(steps_per_s * wl.B * wl.N, 1),
-        "mean_accept_len": (round(float(step.acc["accept_len"].float().mean().item()), 3)
-                            if wl.accept != "none" else None),
-        # accepted tokens + one bonus token per sequence, per second of replayed steps
-        "emitted_tokens_per_s": (round(steps_per_s * float((step.acc["accept_len"] + 1).sum()
-                                                             .item()), 1)
+        # acceptance of the last timed step: one draw of the planted target per sequence (every
+        # replay accepts the same path); a many-step mean is what `--tau` measures
+        "last_step_accept_len": ({"mean": round(float(step.acc["accept_len"].float().mean().item()), 3),
+                                  "sequences": wl.B}
                                  if wl.accept != "none" else None),
+        # accepted tokens + one bonus token per sequence, per second of replayed steps
+        "last_step_emitted_tokens_per_s": (round(steps_per_s * float((step.acc["accept_len"] + 1)
+                                                                      .sum().item()), 1)
+                                           if wl.accept != "none" else None),
         "step_roofline_frac": round(t_roof / (ms / 1000.0), 4),
         "step_algorithmic_bytes": int(step_total),
         "parts_ms": parts_ms,
+        # each part's roofline fraction: its algorithmic bytes / 8 TB/s or FLOPs / bf16 peak,
+        # whichever is larger, over its eager HIP-event time
+        "parts_roofline_frac": {n: round(max(parts[n][0] / (HBM_PEAK_GBS * 1e9),
+                                             parts[n][1] / (BF16_PEAK_TFLOPS * 1e12))
+                                         / (seg_mean[n] / 1000.0), 4)
+                                for n in parts if n in seg_mean and seg_mean[n] > 0},
         "roofline": roof,
         "launch": args.launch,
         "eager_steps_per_s": round(1000.0 / ms_eager, 2),
@@ -486,6 +650,9 @@ def main():
     if not args.no_cpu_baseline:
         t0 = time.time()
         out["cpu_baseline"] = cpu_baseline(wl, x, seed, args.cpu_budget)
+        if not args.no_single_thread:
+            del x
+            out["cpu_baseline"]["single_thread_steps_per_s"] = cpu_single_thread()
         print(f"# cpu baseline took {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 

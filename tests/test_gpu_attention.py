@@ -23,10 +23,17 @@ def _run(wl, seed, lens=None, select=None):
     anc = ops.build_tree_mask(parents)["anc_mask"]
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     max_L = int(x["prefix_len"].max())
-    out, lse = ops.tree_attn_verify(dev(x["q"], dt), dev(x["k_cache"], dt), dev(x["v_cache"], dt),
-                                    dev_i32(x["prefix_len"]), anc, max_L, status=status)
+    q = dev(x["q"], dt)
+    # outputs start as NaN, so a row the kernels never write is caught below
+    out0 = torch.full_like(q, float("nan"))
+    lse0 = torch.full((wl.B, wl.Hq, wl.N), float("nan"), dtype=torch.float32, device="cuda")
+    out, lse = ops.tree_attn_verify(q, dev(x["k_cache"], dt), dev(x["v_cache"], dt),
+                                    dev_i32(x["prefix_len"]), anc, max_L, status=status,
+                                    out=out0, lse=lse0)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
+    assert bool(torch.isfinite(out).all()), "an output row was not written"
+    assert bool(torch.isfinite(lse).all()), "an LSE entry was not written"
     ref = O.tree_attention(x["q"], x["k_cache"], x["v_cache"], x["prefix_len"], tree["anc"],
                            select=select)
     got_o, got_l = host(out), host(lse)
@@ -142,6 +149,28 @@ def test_attention_70b_share_sampled():
     rng = np.random.default_rng(3)
     sel = [(b, int(rng.integers(64)), int(rng.integers(64))) for b in range(8) for _ in range(3)]
     _run(wl, 3, select=sel)
+
+
+def test_attention_serving_b64_full_shape():
+    """The spec-serving attention shape at full size: batch 64, 32/8 heads, dh 128, the 64-node
+    (4,3,2,1) tree, prefixes drawn in [512, 8192], with several equal lengths (the length
+    ordering's tie rule), one empty prefix and one at the maximum.  Every output row must be
+    written (NaN-filled beforehand); sampled rows of every one of the 64 sequences are compared
+    with the oracle, including the first and the deepest node."""
+    require_gpu()
+    wl = W.WORKLOADS["c5"]
+    lens = W.gen_prefix_lens(wl, 5).copy()
+    lens[[3, 10, 20]] = lens[3]           # a three-way tie
+    lens[[40, 41]] = 4096                 # a two-way tie, adjacent
+    lens[[7, 50]] = lens[50]              # a tie far apart
+    lens[63] = 0                          # no prefix: the tree alone
+    lens[5] = 8192                        # the longest possible prefix
+    rng = np.random.default_rng(55)
+    sel = []
+    for b in range(wl.B):
+        sel += [(b, int(rng.integers(wl.Hq)), int(rng.integers(wl.N))) for _ in range(4)]
+        sel += [(b, int(rng.integers(wl.Hq)), 0), (b, int(rng.integers(wl.Hq)), wl.N - 1)]
+    _run(wl, 5, lens.tolist(), select=sel)
 
 
 def test_attention_bad_prefix_flags():

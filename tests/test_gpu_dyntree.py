@@ -120,6 +120,23 @@ def test_per_sequence_trees_attention_and_acceptance():
     print("accept lengths", host(acc["accept_len"]).tolist())
 
 
+def _boundary_gap(logits, widths, N):
+    """fp64 joint log-probability of the N-th most probable candidate path minus that of the
+    (N+1)-th (every path of ranks r_k < widths[k]; log-probabilities from the heads' own
+    logits, clamped at 0)."""
+    logp = []
+    for k, z in enumerate(logits):
+        m = z.max()
+        lse = m + np.log(np.exp(z - m).sum())
+        logp.append(np.minimum(0.0, np.sort(z)[::-1][:widths[k]] - lse))
+    scores, level = [], np.zeros(1)
+    for k in range(len(widths)):
+        level = (level[:, None] + logp[k][None, :]).ravel()
+        scores.append(level)
+    s = np.sort(np.concatenate(scores))[::-1]
+    return float(s[N - 1] - s[N]) if len(s) > N else float("inf")
+
+
 @pytest.mark.parametrize("name,scale", [("c8", dict(d=512, V=3000, accept_V=3000, prefix=(700, 700))),
                                         ("c8", None)])
 def test_step_with_dynamic_tree(name, scale):
@@ -161,9 +178,14 @@ def test_step_with_dynamic_tree(name, scale):
     # those same values (exact parity), and it is also compared with the fp64 heads' tree
     ref = O.dynamic_tree(host(step.cand), host(step.cand_vals), host(step.head_lse),
                          list(wl.head_widths), N)
-    same = sum(ref["parents"][b] == dyn["parents"][b] and ref["tokens"][b] == dyn["tokens"][b]
-               for b in range(wl.B))
-    print(f"trees equal to the fp64 heads' trees: {same} of {wl.B}")
+    # ... and equal to the tree of the fp64 heads whenever no two candidate paths are so close
+    # in fp64 score that fp32 logits could reorder them at the N-th place
+    for b in range(wl.B):
+        gap = _boundary_gap(heads["logits"][b], list(wl.head_widths), N)
+        print(f"b={b}: score gap at the N-th path {gap:.3g}")
+        if gap > 1e-3:
+            assert ref["parents"][b] == dyn["parents"][b], f"b={b}: tree shape"
+            assert ref["tokens"][b] == dyn["tokens"][b], f"b={b}: tree tokens"
     for b in range(wl.B):
         sl = slice(b, b + 1)
         np.testing.assert_array_equal(host(step.parents)[b], ref["parents"][b])

@@ -25,7 +25,9 @@ def _oracle_step(wl, x, target):
     return heads, cand, tree
 
 
-def _check_step(wl, seed):
+def _check_step(wl, seed, attn_select=None):
+    """One GPU step vs the oracle.  ``attn_select`` = (b, h, i) rows whose attention output
+    is compared (all rows when None); everything else is compared in full."""
     parents = list(wl.parents)
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     xh = W.gen_heads(wl, seed)
@@ -72,13 +74,19 @@ def _check_step(wl, seed):
     assert ties == 0, "a near-tie changes the tree; the step comparison below would not hold"
     np.testing.assert_array_equal(host(step.tree["node_tokens"]), tree["tokens"])
     np.testing.assert_array_equal(host(step.tree["depth"]), tree["depth"])
-    ref_att = O.tree_attention(xa["q"], xa["k_cache"], xa["v_cache"], xa["prefix_len"], tree["anc"])
+    ref_att = O.tree_attention(xa["q"], xa["k_cache"], xa["v_cache"], xa["prefix_len"], tree["anc"],
+                               select=attn_select)
+    got_o, got_l = host(step.attn_out), host(step.attn_lse)
+    ref_o, ref_l = ref_att["out"], ref_att["lse"]
+    if attn_select is not None:
+        bb, hh, ii = np.array(attn_select).T
+        got_o, ref_o = got_o[bb, ii, hh], ref_o[bb, ii, hh]
+        got_l, ref_l = got_l[bb, hh, ii], ref_l[bb, hh, ii]
     if wl.dtype == "f32":
-        assert_fp32(host(step.attn_out), ref_att["out"], what="attention")
+        assert_fp32(got_o, ref_o, what="attention")
     else:
-        assert_bf16(host(step.attn_out), ref_att["out"], what="attention")
-    assert_fp32(host(step.attn_lse), ref_att["lse"], atol=1e-4 if wl.dtype == "f32" else 1e-3,
-                what="lse")
+        assert_bf16(got_o, ref_o, what="attention")
+    assert_fp32(got_l, ref_l, atol=1e-4 if wl.dtype == "f32" else 1e-3, what="lse")
     ref_acc = O.accept_greedy(target, tree["tokens"], parents, wl.D)
     for k in ("accept_len", "path_nodes", "out_tokens"):
         np.testing.assert_array_equal(host(step.acc[k]), ref_acc[k], err_msg=k)
@@ -116,3 +124,20 @@ def test_step_target_head_llama8b_full():
     require_gpu()
     lens = _check_step(W.WORKLOADS["c6"], 6)
     print("accept lengths", lens.tolist())
+
+
+def test_step_70b_share_full():
+    """The 70B-shaped one-GPU share at full size (batch 8, 64/8 heads, prefixes in
+    [8192, 32768], d = 8192, 4 heads over V = 32000): all 32 (sequence, head) candidate lists,
+    the tree tokens, the accepted lengths, paths and tokens of all 8 sequences and the
+    committed caches exactly; the attention on sampled rows of every sequence (the oracle
+    computes each row from the whole prefix, one (sequence, KV head) slice at a time)."""
+    require_gpu()
+    wl = W.WORKLOADS["c3"]
+    rng = np.random.default_rng(33)
+    sel = []
+    for b in range(wl.B):
+        sel += [(b, int(rng.integers(wl.Hq)), int(rng.integers(wl.N))) for _ in range(3)]
+        sel += [(b, int(rng.integers(wl.Hq)), wl.N - 1)]
+    lens = _check_step(wl, 3, attn_select=sel)
+    print("accepted lengths", lens.tolist())
