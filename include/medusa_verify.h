@@ -155,6 +155,26 @@ MV_API int mv_medusa_heads(int dt, int B, int d, int V, int K, const int* s_per_
                     void* logits, int32_t* topk_ids, float* topk_vals, int ld_topk, float* lse,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* Allocation-free variant of mv_medusa_heads, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, outputs and results as mv_medusa_heads, without the workspace: its scratch lives
+ * in a device array inside the library (MV_HEADS_NOALLOC_SCRATCH_BYTES, 32 MiB), one copy per
+ * GPU, held until the process ends.  The first call on a device looks the array's address up
+ * on that device (the current one); no call allocates or frees memory.
+ *   Sizes whose mv_medusa_heads_workspace(dt, B, d, V, K, s_max) exceeds the array are
+ *   rejected with MV_ERR_UNSUPPORTED before anything is launched; argument errors are those
+ *   of mv_medusa_heads.
+ *   Every call on one GPU shares that GPU's array, which keeps the last call's contents (no
+ *   part of it needs clearing: each call writes what it reads).  Calls that overlap on one
+ *   GPU (other streams, other host threads) race on it: serialise them. */
+#define MV_HEADS_NOALLOC_SCRATCH_BYTES (32 << 20)
+
+MV_API int mv_medusa_heads_noalloc(int dt, int B, int d, int V, int K, const int* s_per_head,
+                                   int s_max, const void* h, const void* w_res,
+                                   const void* w_head, float* hk, void* logits,
+                                   int32_t* topk_ids, float* topk_vals, int ld_topk, float* lse,
+                                   void* stream);
+
 /* Top-s entries of each of R rows of a logit matrix (the same selection rule as the heads),
  * for candidates that come from logits the caller already has -- e.g. the base model's own
  * head ("Head 0", which predicts the next token in [MX] "The Architectural Blueprint").

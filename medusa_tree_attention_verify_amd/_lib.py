@@ -38,6 +38,7 @@ MV_MAX_DEPTH = 16
 MV_MAX_TOPK = 16
 MV_MAX_BATCH_HEADS = 32
 MV_MAX_HEADS = 16
+MV_HEADS_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -57,6 +58,8 @@ SIGNATURES = [
     ("mv_medusa_head_select", _I, [_I, _I, _I, _I, _I, _IP, _I, _P, _P, _I, _P, _P, _Z, _P]),
     ("mv_medusa_heads", _I, [_I, _I, _I, _I, _I, _IP, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                              _Z, _P]),
+    ("mv_medusa_heads_noalloc", _I, [_I, _I, _I, _I, _I, _IP, _I, _P, _P, _P, _P, _P, _P, _P, _I,
+                                     _P, _P]),
     ("mv_topk_rows", _I, [_I, _I, _I, _I, _P, _LL, _P, _P, _I, _P]),
     ("mv_build_tree_mask", _I, [_I, _P, _I, _I, _I, _IP, _P, _P, _P, _P, _P, _P]),
     ("mv_tree_attn_verify_workspace", _Z, [_I, _I, _I, _I, _I, _I, _I]),

@@ -23,8 +23,16 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "mv_device.h"
 #include "mv_host.h"
+
+// Scratch of the allocation-free entry point (mv_medusa_heads_noalloc): every GPU the library
+// runs on holds one copy for the life of the process.  Host code never passes this name to a
+// kernel (on the host it only stands in for the symbol); it uses the per-device address that
+// hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[MV_HEADS_NOALLOC_SCRATCH_BYTES];
 
 namespace mv {
 namespace {
@@ -770,6 +778,51 @@ MV_API int mv_medusa_heads(int dt, int B, int d, int V, int K, const int* s_per_
                                 stream));
   return mv_medusa_head_select(dt, B, d, V, K, s_per_head, s_max, topk_ids, topk_vals, ld_topk,
                                lse, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kScratchMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchMaxDevices) return MV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return MV_ERR_HIP;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return MV_OK;
+}
+}  // namespace
+
+extern "C" {
+
+MV_API int mv_medusa_heads_noalloc(int dt, int B, int d, int V, int K, const int* s_per_head,
+                                   int s_max, const void* h, const void* w_res,
+                                   const void* w_head, float* hk, void* logits,
+                                   int32_t* topk_ids, float* topk_vals, int ld_topk, float* lse,
+                                   void* stream) {
+  MV_TRY(check_common(dt, B, d, K));
+  if (V < 1) return MV_ERR_INVALID_ARG;
+  if (s_max < 1 || s_max > MV_MAX_TOPK || s_max > V) return MV_ERR_UNSUPPORTED;
+  // the size check comes before anything touches the device
+  const size_t need = heads_layout(nullptr, dt, B, d, V, K, s_max).bytes;
+  if (need > static_cast<size_t>(MV_HEADS_NOALLOC_SCRATCH_BYTES)) return MV_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  MV_TRY(scratch_address(&ws));
+  // the three kernels write every scratch byte they later read, so nothing is cleared
+  return mv_medusa_heads(dt, B, d, V, K, s_per_head, s_max, h, w_res, w_head, hk, logits,
+                         topk_ids, topk_vals, ld_topk, lse, ws,
+                         static_cast<size_t>(MV_HEADS_NOALLOC_SCRATCH_BYTES), stream);
 }
 
 MV_API int mv_topk_rows(int dt, int R, int V, int s, const void* x, long long ldx, int32_t* ids,

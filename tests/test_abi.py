@@ -19,7 +19,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -37,6 +37,12 @@ def test_header_constants_match_binding():
                  "MV_ACCEPT_MULTICAND"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(L, name), name
+
+
+def test_noalloc_scratch_size_matches_binding():
+    text = open(HEADER).read()
+    m = re.search(r"#define MV_HEADS_NOALLOC_SCRATCH_BYTES\s+\((\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == L.MV_HEADS_NOALLOC_SCRATCH_BYTES
 
 
 def test_status_strings():
@@ -84,6 +90,17 @@ def test_host_argument_checks():
                                      None) == L.MV_ERR_INVALID_ARG                 # ld_topk
     assert lib.mv_medusa_head_select(L.MV_BF16, 1, 64, 100, 2, s, 4, None, P, 0, None, P,
                                      1 << 20, None) == L.MV_ERR_INVALID_ARG
+    # allocation-free heads: sizes beyond the device scratch are refused before any device
+    # call (every pointer below is null, so nothing could have been launched)
+    big = L.int_array([16] * 16)
+    assert (lib.mv_medusa_heads_workspace(L.MV_BF16, 32, 8192, 128256, 16, 16)
+            > L.MV_HEADS_NOALLOC_SCRATCH_BYTES)
+    assert lib.mv_medusa_heads_noalloc(L.MV_BF16, 32, 8192, 128256, 16, big, 16, None, None, None,
+                                       None, None, None, None, 0, None, None) == L.MV_ERR_UNSUPPORTED
+    assert lib.mv_medusa_heads_noalloc(7, 1, 64, 100, 1, big, 4, None, None, None, None, None,
+                                       None, None, 0, None, None) == L.MV_ERR_INVALID_ARG
+    assert lib.mv_medusa_heads_noalloc(L.MV_BF16, 1, 64, 100, 1, big, 17, None, None, None, None,
+                                       None, None, None, 0, None, None) == L.MV_ERR_UNSUPPORTED
     # top-k rows
     assert lib.mv_topk_rows(L.MV_F32, 1, 10, 11, P, 10, P, None, 11, None) == L.MV_ERR_UNSUPPORTED
     assert lib.mv_topk_rows(L.MV_F32, 1, 10, 2, P, 9, P, None, 2, None) == L.MV_ERR_INVALID_ARG
