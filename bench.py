@@ -409,6 +409,9 @@ def main():
                          "accepted length against the planted closed form")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work timed for cpu_baseline (whole steps, at least one)")
+    ap.add_argument("--fork", default="off", choices=["on", "off"],
+                    help="graph launch: run the attention branch beside the heads (a parallel "
+                         "branch of the graph) or after them")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="time the step replayed as one HIP graph (default) or as eager launches")
@@ -540,8 +543,9 @@ def main():
     # Pass 2 (the timed region of the metric): the same K steps, each replayed as one graph.
     t_wall = None
     ms = ms_eager
+    fork = args.fork == "on" and step.can_fork()
     if args.launch == "graph":
-        graphs = [step.capture(dict(static, **s_)) for s_ in sets]
+        graphs = [step.capture(dict(static, **s_), fork=fork) for s_ in sets]
         for i in range(args.warmup):
             graphs[i % R].replay()
         torch.cuda.synchronize()
@@ -638,6 +642,7 @@ def main():
                                 for n in parts if n in seg_mean and seg_mean[n] > 0},
         "roofline": roof,
         "launch": args.launch,
+        "graph_fork": bool(fork and args.launch == "graph"),
         "eager_steps_per_s": round(1000.0 / ms_eager, 2),
         "wall_s_timed_region": None if t_wall is None else round(t_wall, 4),
         "repeats_steps_per_s": [round(v, 1) for v in repeats],

@@ -28,8 +28,11 @@ def _p(t: Optional[torch.Tensor]):
 
 
 class VerifyStep:
-    PARTS = ("heads_residual", "heads_projection", "heads_select", "tree", "attention",
-             "target_head", "accept", "commit")
+    PARTS = ("heads_residual", "heads_projection", "heads_select", "tree", "attn_mask",
+             "attention", "target_head", "accept", "commit")
+    # the attention branch of a forked step: it needs only the tree's static ancestor mask,
+    # not the heads' candidates, so it can run beside the heads on a second stream
+    BRANCH = ("attn_mask", "attention")
 
     def __init__(self, *, parents: Optional[Sequence[int]], depth_widths: Sequence[int],
                  dtype: torch.dtype, B: int, Hq: int, Hkv: int, dh: int, max_L: int,
@@ -85,6 +88,10 @@ class VerifyStep:
             self.tree = {"anc_mask": torch.empty((N, W), dtype=torch.int32, device=dev),
                          "depth": torch.empty(N, dtype=torch.int32, device=dev),
                          "node_tokens": torch.empty((B, N), dtype=torch.int32, device=dev)}
+        # a second ancestor mask, written by the attention branch of a forked step (the main
+        # branch's tree call writes its own copy together with the tokens)
+        self.attn_anc = (torch.empty((N, W), dtype=torch.int32, device=dev)
+                         if not self.dynamic else None)
         self.attn_out = torch.empty((B, N, Hq, dh), dtype=dtype, device=dev)
         self.attn_lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
         self.ws_heads = ops.Workspace(dev)
@@ -120,13 +127,23 @@ class VerifyStep:
     def _ws(w: ops.Workspace):
         return (None, 0) if w.buf is None else (w.buf.data_ptr(), w.buf.numel())
 
-    def bind(self, inp: Dict[str, torch.Tensor]) -> Dict[str, Callable[[], None]]:
+    def can_fork(self) -> bool:
+        return not self.dynamic
+
+    def bind(self, inp: Dict[str, torch.Tensor], branch_stream=None) -> Dict[str, Callable[[], None]]:
         """Pre-marshalled calls of one step on ``inp`` (device tensors: h, w_res, w_head when
         the step has heads; q, k_cache, v_cache, prefix_len; target (+ draft, uniforms);
         node_tokens when the tokens are given; x_t, w_lm with the target LM head).  Each callable
-        raises on a non-zero status."""
+        raises on a non-zero status.
+
+        With ``branch_stream`` (a torch stream) the attention branch (its own mask build, then
+        the attention) is enqueued there, everything else on the current stream."""
         lib = L.lib()
         st = torch.cuda.current_stream(self.device).cuda_stream
+        fork = branch_stream is not None
+        if fork and not self.can_fork():
+            raise ValueError("a dynamic tree depends on the heads: the step cannot fork")
+        st_b = branch_stream.cuda_stream if fork else st
         calls: Dict[str, Callable[[], None]] = {}
         B, N, D, s_max = self.B, self.N, self.D, self.s_max
 
@@ -185,13 +202,18 @@ class VerifyStep:
             tokens = self.tree["node_tokens"]
         wsp, wsn = self._ws(self.ws_attn)
         Lcap = inp["k_cache"].shape[2]
+        anc = self.tree["anc_mask"]
+        if fork:
+            anc = self.attn_anc
+            calls["attn_mask"] = wrap("mv_build_tree_mask", lib.mv_build_tree_mask, N,
+                                      _p(self.parents), 0, 0, 0, None, None, _p(anc), None, None,
+                                      _p(self.status), st_b)
         calls["attention"] = wrap("mv_tree_attn_verify", lib.mv_tree_attn_verify, self.dt, B, N,
                                   self.Hq, self.Hkv, self.dh, Lcap, self.max_L, _p(inp["q"]),
                                   _p(inp["k_cache"]), _p(inp["v_cache"]), _p(inp["prefix_len"]),
-                                  _p(self.tree["anc_mask"]),
-                                  N * ((N + 31) // 32) if self.dynamic else 0, 0.0,
+                                  _p(anc), N * ((N + 31) // 32) if self.dynamic else 0, 0.0,
                                   _p(self.attn_out),
-                                  _p(self.attn_lse), _p(self.status), wsp, wsn, st)
+                                  _p(self.attn_lse), _p(self.status), wsp, wsn, st_b)
         if self.target_head:
             wsp, wsn = self._ws(self.ws_lm)
             calls["target_head"] = wrap("mv_lm_head_argmax", lib.mv_lm_head_argmax, L.MV_BF16,
@@ -230,23 +252,51 @@ class VerifyStep:
         for c in self.sequence(self.bind(inp)):
             c()
 
-    def capture(self, inp: Dict[str, torch.Tensor]) -> "torch.cuda.CUDAGraph":
+    def _run_forked(self, inp: Dict[str, torch.Tensor], side: "torch.cuda.Stream") -> None:
+        """One step with the attention branch on ``side``: it forks from the current stream at
+        the start and joins before the acceptance (whose commit moves K/V rows the attention
+        reads)."""
+        main = torch.cuda.current_stream(self.device)
+        calls = self.bind(inp, branch_stream=side)
+        side.wait_stream(main)
+        for name in self.BRANCH:
+            calls[name]()
+        joined = False
+        for name in self.PARTS:
+            if name in self.BRANCH or name not in calls:
+                continue
+            if name in ("accept", "commit") and not joined:
+                main.wait_stream(side)
+                joined = True
+            calls[name]()
+        if not joined:
+            main.wait_stream(side)
+
+    def capture(self, inp: Dict[str, torch.Tensor], fork: bool = False) -> "torch.cuda.CUDAGraph":
         """A HIP graph of one whole step on ``inp`` (replay with ``graph.replay()``).
 
         The calls are bound inside the capture so that they are enqueued on the capture
         stream; the step allocates nothing and issues no memset, so every replay repeats
-        exactly the kernels of an eager step on the same buffers."""
-        calls = None
+        exactly the kernels of an eager step on the same buffers.  With ``fork=True`` the
+        attention branch is a parallel branch of the graph beside the heads and the tree."""
+        if fork and not self.can_fork():
+            fork = False
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream(device=self.device)
+        side = torch.cuda.Stream(device=self.device) if fork else None
         s.wait_stream(torch.cuda.current_stream(self.device))
-        with torch.cuda.stream(s):
-            calls = self.sequence(self.bind(inp))   # warm-up on the side stream
-            for c in calls:
-                c()
+        with torch.cuda.stream(s):       # warm-up on the side stream
+            if fork:
+                self._run_forked(inp, side)
+            else:
+                for c in self.sequence(self.bind(inp)):
+                    c()
         torch.cuda.current_stream(self.device).wait_stream(s)
         torch.cuda.synchronize(self.device)
         with torch.cuda.graph(g):
-            for c in self.sequence(self.bind(inp)):
-                c()
+            if fork:
+                self._run_forked(inp, side)
+            else:
+                for c in self.sequence(self.bind(inp)):
+                    c()
         return g

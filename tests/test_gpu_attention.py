@@ -173,6 +173,38 @@ def test_attention_serving_b64_full_shape():
     _run(wl, 5, lens.tolist(), select=sel)
 
 
+@pytest.mark.parametrize("B,lens,boost_rows", [
+    (1, [3000], (2000, 2010)),        # one chunk: the jump comes after 31 ordinary tiles
+    (2, [9000, 300], (8990, 9000)),   # several chunks: the jump sits in the last prefix tile
+])
+def test_attention_large_score_jump(B, lens, boost_rows):
+    """Scores that jump far above everything seen before in a chunk (a few keys scaled by
+    40): the softmax reference of the first tiles would overflow, so the kernel has to take
+    its second pass from the true chunk max; the result must still match the oracle."""
+    require_gpu()
+    wl = _bf16(branching_tree((4, 3, 2, 1)), B, 32, 8, 128, max(lens))
+    x = W.gen_attention(wl, 61, np.asarray(lens, np.int32))
+    lo, hi = boost_rows
+    x["k_cache"][0, :, lo:hi] = W.round_bf16(x["k_cache"][0, :, lo:hi] * np.float32(40.0))
+    dt = torch.bfloat16
+    anc = ops.build_tree_mask(dev_i32(wl.parents))["anc_mask"]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, lse = ops.tree_attn_verify(dev(x["q"], dt), dev(x["k_cache"], dt), dev(x["v_cache"], dt),
+                                    dev_i32(x["prefix_len"]), anc, max(lens), status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    rng = np.random.default_rng(62)
+    sel = [(b, int(rng.integers(32)), int(rng.integers(64))) for b in range(B) for _ in range(12)]
+    ref = O.tree_attention(x["q"], x["k_cache"], x["v_cache"], x["prefix_len"],
+                           O.build_tree(list(wl.parents))["anc"], select=sel)
+    bb, hh, ii = np.array(sel).T
+    s_max = float(np.max(ref["lse"][bb, hh, ii]))
+    print(f"largest selected lse {s_max:.1f} (natural log units)")
+    assert s_max > 64 * np.log(2.0)   # the jump really exceeds the first-pass slack
+    assert_bf16(host(out)[bb, ii, hh], ref["out"][bb, ii, hh], what="out")
+    assert_fp32(host(lse)[bb, hh, ii], ref["lse"][bb, hh, ii], atol=1e-3, what="lse")
+
+
 def test_attention_bad_prefix_flags():
     require_gpu()
     wl = _bf16([-1, 0], 2, 4, 2, 64, 10)

@@ -19,7 +19,10 @@ def _outputs(step):
                                 step.acc["accept_len"], step.acc["out_tokens"])]
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("fork", [False, True])
+def test_graph_replays_match_eager(fork):
+    """fork=True: the attention branch (its own mask build and the attention) is a parallel
+    branch of the graph beside the heads and the tree."""
     require_gpu()
     wl = W.WORKLOADS["c2"].scaled(d=512, V=3000, prefix=(700, 700))
     dt = torch.bfloat16
@@ -29,7 +32,7 @@ def test_graph_replays_match_eager():
     step = VerifyStep(parents=wl.parents, depth_widths=wl.depth_widths, dtype=dt, B=wl.B,
                       Hq=wl.Hq, Hkv=wl.Hkv, dh=wl.dh, max_L=int(xa["prefix_len"].max()),
                       heads={"d": wl.d, "V": wl.V, "K": wl.K, "widths": list(wl.head_widths)},
-                      accept="greedy", V=wl.accept_V)
+                      accept="greedy", V=wl.accept_V, commit=fork)
     inp = {"h": dev(xh["h"], dt), "w_res": dev(xh["w_res"], dt), "w_head": dev(xh["w_head"], dt),
            "q": dev(xa["q"], dt), "k_cache": dev(xa["k_cache"], dt),
            "v_cache": dev(xa["v_cache"], dt), "prefix_len": dev_i32(xa["prefix_len"]),
@@ -37,7 +40,7 @@ def test_graph_replays_match_eager():
     step.run(inp)
     torch.cuda.synchronize()
     ref = _outputs(step)
-    g = step.capture(inp)
+    g = step.capture(inp, fork=fork)
     for rep in range(4):
         # eager work in between: clobber the outputs, then replay the graph
         for t in (step.cand, step.tree["node_tokens"], step.acc["accept_len"]):
