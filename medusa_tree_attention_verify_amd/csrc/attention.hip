@@ -72,7 +72,7 @@ __device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool re
 #define MV_ATTN_TARGET_WG 2048  // split-KV: aim for this many workgroups (one sequence)
 #endif
 #ifndef MV_ATTN_TARGET_WG_BATCH
-#define MV_ATTN_TARGET_WG_BATCH 256  // ... and with several sequences
+#define MV_ATTN_TARGET_WG_BATCH 768  // ... and with several sequences (at most)
 #endif
 #ifndef MV_ATTN_MIN_CHUNK
 #define MV_ATTN_MIN_CHUNK 256   // but never chunks shorter than this many keys
@@ -560,10 +560,13 @@ AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L) {
   const int M = N * (Hq / Hkv);
   a.qtiles = ceil_div(M, kNWV * 32);
   const long long base = static_cast<long long>(B) * Hkv * a.qtiles;
-  // Several sequences of different lengths already balance across the chip, and every extra
-  // chunk writes M x dh partials that the combine reads back: aim lower for batches.
+  // A batch splits only as far as its (sequence, KV head, query tile) jobs stay within the
+  // batch target (rounding down): the jobs of a large batch already fill the chip, and every
+  // extra chunk writes M x dh partials that the combine reads back.  A small batch of long
+  // sequences (a few jobs per CU) does split, so that the longest jobs do not set the tail.
   const long long target = B > 1 ? MV_ATTN_TARGET_WG_BATCH : MV_ATTN_TARGET_WG;
-  int want = static_cast<int>(std::max<long long>(1, (target + base - 1) / base));
+  int want = static_cast<int>(B > 1 ? std::max<long long>(1, target / base)
+                                    : std::max<long long>(1, (target + base - 1) / base));
   const int cap = std::max(1, ceil_div(max_L, MV_ATTN_MIN_CHUNK));
   want = std::min(want, cap);
   int ck = ceil_div(std::max(max_L, 1), want);
