@@ -44,7 +44,7 @@ import numpy as np
 __all__ = [
     "silu", "medusa_heads", "topk_rows", "build_tree", "tree_attention",
     "accept_greedy", "accept_speculative", "paths_to_parents", "lm_head_argmax", "kv_commit",
-    "accept_multicandidate", "dynamic_tree",
+    "accept_multicandidate", "dynamic_tree", "accept_speculative_lm",
 ]
 
 
@@ -381,6 +381,40 @@ def lm_head_argmax(x, w) -> Dict[str, np.ndarray]:
     mx = z[np.arange(z.shape[0]), ids]
     lse = mx + np.log(np.exp(z - mx[:, None]).sum(axis=1))
     return {"ids": ids.astype(np.int64), "max": mx, "lse": lse, "logits": z}
+
+
+# --------------------------------------------------------------------------
+# 6b. Speculative acceptance with the target from the LM head and the draft
+#     from the Medusa heads ("The Acceptance Sampling Rule": P_target is the
+#     softmax of the target's logits; "2. Single-Pass Tree Attention
+#     Verification", step 2: the target gives a distribution at every
+#     candidate node; "The Architectural Blueprint": head k's softmax is the
+#     draft distribution of the depth-k tokens, and all heads read the same
+#     hidden state, so every depth-k node of a sequence shares it)
+# --------------------------------------------------------------------------
+def _softmax_rows(z: np.ndarray) -> np.ndarray:
+    z = _f64(z)
+    e = np.exp(z - z.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def accept_speculative_lm(x_t, w_lm, draft_logits, node_tokens, parents, uniforms,
+                          D: int) -> Dict[str, np.ndarray]:
+    """accept_speculative with P_t[b, r] = softmax(W_lm x_t[b, r]) (x_t [B, N+1, d], W_lm
+    [V, d]) and P_d[b, r] = softmax(draft_logits[b, k]) where k = depth of the node of row r
+    (0 for the prefix row; draft_logits [B, D, V], row k for the nodes at depth k+1).  Rows of
+    nodes at depth D have no children; their draft row is never read (zeros here)."""
+    x_t, w_lm, dl = _f64(x_t), _f64(w_lm), _f64(draft_logits)
+    B, R, _ = x_t.shape
+    N = R - 1
+    p_t = _softmax_rows(x_t @ w_lm.T)
+    depth = build_tree(parents)["depth"]
+    p_d = np.zeros_like(p_t)
+    for r in range(R):
+        k = 0 if r == 0 else int(depth[r - 1])
+        if k < D:
+            p_d[:, r] = _softmax_rows(dl[:, k])
+    return accept_speculative(p_t, p_d, node_tokens, parents, uniforms, D)
 
 
 # --------------------------------------------------------------------------
