@@ -348,6 +348,44 @@ MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D,
                     int32_t* dev_status, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Speculative acceptance fed by the target LM head and the Medusa heads' logits, without any
+ * [B][N+1][V] probability tensor.  [SD] "The Acceptance Sampling Rule" (the rule, P_target =
+ * softmax of the target's logits); [MX] "2. Single-Pass Tree Attention Verification", step 2
+ * (the target outputs a distribution at every candidate node); [MX] "The Architectural
+ * Blueprint" (head k's softmax is the draft distribution of the depth-k tokens; every head reads
+ * the same hidden state, so all depth-k nodes of a sequence share it).
+ *   P_t at row r (row 0 = after the prefix, row i+1 = after node i) = softmax(W_lm x_t[b][r]);
+ *   P_d at row r = softmax(draft_logits[b][depth(r)]) with depth(row 0) = 0 and depth(row i+1)
+ *   = depth of node i.  Node i's test uses its parent's row: alpha_i = min(1, P_t(x_i)/P_d(x_i))
+ *   (1 when P_d(x_i) = 0), accepted iff uniforms[b][i] < alpha_i and every ancestor is accepted.
+ *   The path, its tokens and the extra token follow mv_accept_paths(MV_ACCEPT_SPECULATIVE):
+ *   the extra token is drawn with uniforms[b][N] from normalize(max(0, P_t - P_d)) at the
+ *   terminal's row when it has children (P_t if that is all zero), else from P_t.
+ * How it is computed: P_t(x_i) from one dot product W_lm[x_i] . x_t[parent row] (fp32
+ * accumulation) against lse_t, P_d(x_i) from one draft logit against draft_lse, both in fp64;
+ * after the walk one streaming pass over W_lm makes each sequence's terminal target row (and its
+ * draft row from the draft logits), and the fp64 segment sums / inverse CDF of mv_accept_paths
+ * draw the extra token.  With fp32 dot products the decisions can differ from an exact one only
+ * where |u - alpha| is within the dot product's rounding (~1e-5 relative).
+ *   draft_dt      MV_F32 or MV_BF16: type of draft_logits [B][D][V] (row k = depth k+1).
+ *   x_t [B][N+1][d] bf16, w_lm [V][d] bf16 (d % 8 == 0); lse_t [B][N+1] fp32 natural-log
+ *   log-sum-exp of the target logits (mv_lm_head_argmax gives it); draft_lse [B][D] fp32 the
+ *   log-sum-exp of each draft row.  Other arguments, outputs and errors as mv_accept_paths.
+ *   ws from mv_accept_speculative_lm_workspace(B, N, V).
+ * ------------------------------------------------------------------------------------- */
+MV_API size_t mv_accept_speculative_lm_workspace(int B, int N, int V);
+
+MV_API int mv_accept_speculative_lm(int draft_dt, int B, int N, int V, int d, int D,
+                                    const int32_t* parents, int parents_stride,
+                                    const int32_t* node_tokens, const void* x_t,
+                                    const void* w_lm, const float* lse_t,
+                                    const void* draft_logits, const float* draft_lse,
+                                    const float* uniforms, int32_t* accept_len,
+                                    int32_t* path_nodes, int32_t* out_tokens,
+                                    uint8_t* node_accept, float* alpha, int32_t* dev_status,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Commit of the accepted path (the step after acceptance).  [MTP] "The 2D Tree Attention
  * Mask": the engine commits the longest accepted path, and a node sees exactly its ancestors,
  * so the kept path is an ordinary causal continuation of the prefix; [MTP] "Production

@@ -72,6 +72,9 @@ SIGNATURES = [
     ("mv_kv_commit", _I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     ("mv_accept_paths", _I, [_I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                              _P, _P, _Z, _P]),
+    ("mv_accept_speculative_lm_workspace", _Z, [_I, _I, _I]),
+    ("mv_accept_speculative_lm", _I, [_I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P,
+                                      _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
 ]
 
 _lib = None

@@ -59,7 +59,17 @@ struct AcceptParams {
   double* seg_t;
   int* seg_lr;    // last index with a positive entry in the segment (-1 if none)
   int* seg_lt;
+  // speculative rule fed by the target LM head: per-node P_t(x_i), P_d(x_i) at the parent's row
+  // (fp64, [B][N]); the terminal rows are then one row per sequence ([B][V], compact = 1)
+  const double* node_pt;
+  const double* node_pd;
+  int compact;
 };
+
+// First element of the terminal row of sequence b in target (or draft).
+__device__ __forceinline__ size_t term_row_offset(const AcceptParams& p, int b, int row) {
+  return p.compact ? static_cast<size_t>(b) * p.V : (static_cast<size_t>(b) * p.R + row) * p.V;
+}
 
 // ---- greedy: partial argmax of one row segment.
 template <bool BF16>
@@ -152,8 +162,9 @@ __global__ __launch_bounds__(256) void accept_path_kernel(const AcceptParams p) 
         if (SPEC && p.alpha) p.alpha[static_cast<size_t>(b) * N + tid] = 0.f;
       } else if constexpr (SPEC) {
         const size_t o = (static_cast<size_t>(b) * R + (pn + 1)) * p.V + tok;
-        const double pt = static_cast<const float*>(p.target)[o];
-        const double pd = p.draft[o];
+        const size_t on = static_cast<size_t>(b) * N + tid;
+        const double pt = p.node_pt ? p.node_pt[on] : static_cast<double>(static_cast<const float*>(p.target)[o]);
+        const double pd = p.node_pd ? p.node_pd[on] : static_cast<double>(p.draft[o]);
         const double u = p.uniforms[static_cast<size_t>(b) * R + tid];
         const double a = pd == 0.0 ? 1.0 : fmin(1.0, pt / pd);
         ok = pd == 0.0 ? (u < 1.0) : (u < 1.0 && u * pd < pt);
@@ -238,7 +249,7 @@ __global__ __launch_bounds__(256) void residual_segsum_kernel(const AcceptParams
   const int row = p.term[b * 4 + 0];
   const double cres = p.term_c[b];
   const bool resid = cres > 0.0;
-  const size_t off = (static_cast<size_t>(b) * p.R + row) * p.V;
+  const size_t off = term_row_offset(p, b, row);
   const float* pt = static_cast<const float*>(p.target) + off;
   const float* pd = p.draft + off;
   const int j0 = s * p.segLen, j1 = min(p.V, j0 + p.segLen);
@@ -311,7 +322,7 @@ __global__ __launch_bounds__(256) void residual_sample_kernel(const AcceptParams
   const int row = p.term[b * 4 + 0], len = p.term[b * 4 + 2];
   const double cres = p.term_c[b];
   const int resid = cres > 0.0;
-  const size_t off = (static_cast<size_t>(b) * p.R + row) * p.V;
+  const size_t off = term_row_offset(p, b, row);
   const float* pt = static_cast<const float*>(p.target) + off;
   const float* pd = p.draft + off;
   const size_t sq = static_cast<size_t>(b) * p.S;
@@ -637,6 +648,123 @@ __global__ __launch_bounds__(kWalkThreads) void multicand_walk_kernel(const Acce
   if (flags && p.status) atomicOr(p.status, flags);
 }
 
+// ---- speculative rule fed by the target LM head and the Medusa heads' logits ------------------
+// The target distribution at row r is softmax(W_lm x_t[r]) and the draft distribution of the
+// nodes at depth k is softmax of head k's logits (one row per depth and sequence: the heads
+// all read the same hidden state).  Nothing of size [B][N+1][V] exists: a node's P_t(x_i) is one
+// dot product W_lm[x_i] . x_t[parent row] against the row's LSE, its P_d(x_i) one entry of the
+// draft logits against their LSE, and the terminal's two rows are produced after the walk
+// (one GEMV over W_lm for the target row).
+struct SpecLmParams {
+  int B, N, V, d, D, pstride, draft_bf16;
+  const int32_t* parents;
+  const int32_t* tokens;
+  const uint16_t* x;      // [B][N+1][d] bf16 hidden states of the verify rows
+  const uint16_t* w;      // [V][d] bf16 LM head
+  const float* lse_t;     // [B][N+1] log-sum-exp of the target logits
+  const void* dlog;       // [B][D][V] draft logits (fp32 or bf16)
+  const float* dlse;      // [B][D]
+  double* node_pt;        // [B][N]
+  double* node_pd;
+  const int* term;        // [B][4] from the walk: {terminal row, -, accepted length, -}
+  const double* term_c;
+  float* row_t;           // [B][V] target row of the terminal
+  float* row_d;           // [B][V] draft row of the terminal's children (when it has any)
+};
+
+__device__ __forceinline__ float dot8_bf16(const uint4 a, const uint4 b, float acc) {
+  const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = fmaf(__uint_as_float(av[i] << 16), __uint_as_float(bv[i] << 16), acc);
+    acc = fmaf(__uint_as_float(av[i] & 0xffff0000u), __uint_as_float(bv[i] & 0xffff0000u), acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ double draft_logit(const SpecLmParams& q, int b, int k, int v) {
+  const size_t o = (static_cast<size_t>(b) * q.D + k) * q.V + v;
+  return q.draft_bf16 ? static_cast<double>(bf16_to_f32(static_cast<const uint16_t*>(q.dlog)[o]))
+                      : static_cast<double>(static_cast<const float*>(q.dlog)[o]);
+}
+
+// One wave per node (b, i): P_t(x_i) = exp(W_lm[x_i] . x_t[b][p_i + 1] - LSE_t) and
+// P_d(x_i) = exp(draft logit of depth(i) at x_i - its LSE), both in fp64 from the fp32 dot.
+// Malformed parents or tokens leave 0 / 0 (the walk flags them).
+__global__ __launch_bounds__(256) void spec_lm_nodes_kernel(const SpecLmParams q) {
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wid >= q.B * q.N) return;
+  const int b = wid / q.N, i = wid % q.N;
+  const int32_t* par = q.parents + static_cast<size_t>(b) * q.pstride;
+  const int tok = q.tokens[static_cast<size_t>(b) * q.N + i];
+  int dep = 0, c = i;
+  bool ok = tok >= 0 && tok < q.V;
+  while (c != -1 && ok) {  // strictly decreasing indices: at most N steps
+    ++dep;
+    const int nx = par[c];
+    if (nx < -1 || nx >= c) ok = false;
+    c = nx;
+  }
+  ok = ok && dep <= q.D;
+  double pt = 0.0, pd = 0.0;
+  if (ok) {
+    const int row = par[i] + 1;
+    const uint16_t* wr = q.w + static_cast<size_t>(tok) * q.d;
+    const uint16_t* xr = q.x + (static_cast<size_t>(b) * (q.N + 1) + row) * q.d;
+    float acc = 0.f;
+    for (int j = 8 * lane; j < q.d; j += 512)
+      acc = dot8_bf16(*reinterpret_cast<const uint4*>(wr + j), *reinterpret_cast<const uint4*>(xr + j), acc);
+    const float dotv = wave_sum(acc);
+    pt = exp(static_cast<double>(dotv) - static_cast<double>(q.lse_t[static_cast<size_t>(b) * (q.N + 1) + row]));
+    pd = exp(draft_logit(q, b, dep - 1, tok) - static_cast<double>(q.dlse[static_cast<size_t>(b) * q.D + dep - 1]));
+  }
+  if (lane == 0) {
+    q.node_pt[wid] = pt;
+    q.node_pd[wid] = pd;
+  }
+}
+
+// Terminal rows after the walk.  Target: row_t[b][v] = exp(W_lm[v] . x_t[b][row_b] - LSE_t),
+// one streaming pass over W_lm for all sequences (each wave takes 4 vocabulary rows, the lanes
+// split d).  Draft, when the terminal has children (they were all rejected): row_d[b][v] =
+// exp(draft logit of depth len_b + 1 at v - its LSE).
+constexpr int kLmRowsPerWave = 4;
+
+__global__ __launch_bounds__(256) void spec_lm_rows_kernel(const SpecLmParams q) {
+  const int lane = threadIdx.x & 63;
+  const int v0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kLmRowsPerWave;
+  if (v0 >= q.V) return;
+  const uint16_t* wr[kLmRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kLmRowsPerWave; ++r) wr[r] = q.w + static_cast<size_t>(min(v0 + r, q.V - 1)) * q.d;
+  for (int b = 0; b < q.B; ++b) {
+    const int row = q.term[b * 4 + 0];
+    const uint16_t* xr = q.x + (static_cast<size_t>(b) * (q.N + 1) + row) * q.d;
+    float acc[kLmRowsPerWave] = {};
+    for (int j = 8 * lane; j < q.d; j += 512) {
+      const uint4 xv = *reinterpret_cast<const uint4*>(xr + j);
+#pragma unroll
+      for (int r = 0; r < kLmRowsPerWave; ++r)
+        acc[r] = dot8_bf16(*reinterpret_cast<const uint4*>(wr[r] + j), xv, acc[r]);
+    }
+    const double lse = q.lse_t[static_cast<size_t>(b) * (q.N + 1) + row];
+    const bool child = q.term_c[b] > 0.0;
+    const int k = q.term[b * 4 + 2];  // depth of the terminal = draft row of its children
+#pragma unroll
+    for (int r = 0; r < kLmRowsPerWave; ++r) {
+      const float dotv = wave_sum(acc[r]);
+      const int v = v0 + r;
+      if (lane == 0 && v < q.V) {
+        q.row_t[static_cast<size_t>(b) * q.V + v] = static_cast<float>(exp(static_cast<double>(dotv) - lse));
+        q.row_d[static_cast<size_t>(b) * q.V + v] =
+            (child && k < q.D)
+                ? static_cast<float>(exp(draft_logit(q, b, k, v) - static_cast<double>(q.dlse[static_cast<size_t>(b) * q.D + k])))
+                : 0.f;
+      }
+    }
+  }
+}
+
 struct AcceptPlan {
   int S = 1, segLen = 1;
   size_t ws_bytes = 0;
@@ -742,6 +870,73 @@ MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D,
   }
   if (mode == MV_ACCEPT_MULTICAND) multicand_walk_kernel<<<B, kWalkThreads, 0, st>>>(p);
   else accept_path_kernel<true><<<B, 256, 0, st>>>(p);
+  MV_TRY(launch_status());
+  residual_segsum_kernel<<<B * a.S, 256, 0, st>>>(p);
+  MV_TRY(launch_status());
+  residual_sample_kernel<<<B, 256, 0, st>>>(p);
+  return launch_status();
+}
+
+MV_API size_t mv_accept_speculative_lm_workspace(int B, int N, int V) {
+  if (B < 1 || N < 1 || V < 1 || N > MV_MAX_NODES) return 0;
+  const AcceptPlan a = plan_accept(MV_ACCEPT_SPECULATIVE, B, N, V, nullptr, nullptr);
+  Carver c(nullptr);
+  c.take<char>(a.ws_bytes);
+  c.take<double>(static_cast<size_t>(B) * N * 2);
+  c.take<float>(static_cast<size_t>(B) * V * 2);
+  return c.bytes();
+}
+
+MV_API int mv_accept_speculative_lm(int draft_dt, int B, int N, int V, int d, int D,
+                                    const int32_t* parents, int parents_stride,
+                                    const int32_t* node_tokens, const void* x_t,
+                                    const void* w_lm, const float* lse_t,
+                                    const void* draft_logits, const float* draft_lse,
+                                    const float* uniforms, int32_t* accept_len,
+                                    int32_t* path_nodes, int32_t* out_tokens,
+                                    uint8_t* node_accept, float* alpha, int32_t* dev_status,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  if (draft_dt != MV_F32 && draft_dt != MV_BF16) return MV_ERR_INVALID_ARG;
+  if (B < 1 || N < 1 || V < 1 || D < 1 || d < 8) return MV_ERR_INVALID_ARG;
+  if (parents_stride != 0 && parents_stride < N) return MV_ERR_INVALID_ARG;
+  if (N > MV_MAX_NODES || D > MV_MAX_DEPTH) return MV_ERR_UNSUPPORTED;
+  if (d % 8 != 0) return MV_ERR_UNSUPPORTED;
+  if (!parents || !node_tokens || !x_t || !w_lm || !lse_t || !draft_logits || !draft_lse ||
+      !uniforms || !accept_len || !path_nodes || !out_tokens)
+    return MV_ERR_INVALID_ARG;
+  MV_TRY(check_ws(ws, ws_bytes, mv_accept_speculative_lm_workspace(B, N, V)));
+  AcceptParams p{};
+  p.B = B; p.N = N; p.V = V; p.D = D; p.R = N + 1;
+  p.parents = parents; p.pstride = parents_stride; p.tokens = node_tokens;
+  p.uniforms = uniforms; p.accept_len = accept_len; p.path_nodes = path_nodes;
+  p.out_tokens = out_tokens; p.node_accept = node_accept; p.alpha = alpha; p.status = dev_status;
+  const AcceptPlan a = plan_accept(MV_ACCEPT_SPECULATIVE, B, N, V, ws, &p);
+  Carver c(ws);
+  c.take<char>(a.ws_bytes);
+  double* npt = c.take<double>(static_cast<size_t>(B) * N);
+  double* npd = c.take<double>(static_cast<size_t>(B) * N);
+  float* rt = c.take<float>(static_cast<size_t>(B) * V);
+  float* rd = c.take<float>(static_cast<size_t>(B) * V);
+  p.node_pt = npt; p.node_pd = npd;
+  p.compact = 1;
+  p.target = rt; p.draft = rd;
+  p.S = a.S;
+  p.segLen = a.segLen;
+  p.vec4 = (V % 4 == 0 && a.segLen % 4 == 0) ? 1 : 0;  // carved rows are 256-byte aligned
+  SpecLmParams q{};
+  q.B = B; q.N = N; q.V = V; q.d = d; q.D = D;
+  q.pstride = parents_stride; q.draft_bf16 = draft_dt == MV_BF16;
+  q.parents = parents; q.tokens = node_tokens;
+  q.x = static_cast<const uint16_t*>(x_t); q.w = static_cast<const uint16_t*>(w_lm);
+  q.lse_t = lse_t; q.dlog = draft_logits; q.dlse = draft_lse;
+  q.node_pt = npt; q.node_pd = npd; q.term = p.term; q.term_c = p.term_c;
+  q.row_t = rt; q.row_d = rd;
+  hipStream_t st = as_stream(stream);
+  spec_lm_nodes_kernel<<<ceil_div(static_cast<long long>(B) * N, 4), 256, 0, st>>>(q);
+  MV_TRY(launch_status());
+  accept_path_kernel<true><<<B, 256, 0, st>>>(p);
+  MV_TRY(launch_status());
+  spec_lm_rows_kernel<<<ceil_div(V, 4 * kLmRowsPerWave), 256, 0, st>>>(q);
   MV_TRY(launch_status());
   residual_segsum_kernel<<<B * a.S, 256, 0, st>>>(p);
   MV_TRY(launch_status());

@@ -360,6 +360,49 @@ def accept_paths(mode: int, parents: torch.Tensor, node_tokens: torch.Tensor,
     return out
 
 
+def accept_speculative_lm(parents: torch.Tensor, node_tokens: torch.Tensor, x_t: torch.Tensor,
+                          w_lm: torch.Tensor, lse_t: torch.Tensor, draft_logits: torch.Tensor,
+                          draft_lse: torch.Tensor, uniforms: torch.Tensor, D: int,
+                          status: Optional[torch.Tensor] = None,
+                          out: Optional[Dict[str, torch.Tensor]] = None,
+                          ws: Optional[Workspace] = None) -> Dict[str, torch.Tensor]:
+    """Speculative acceptance with the target from the LM head (x_t [B, N+1, d] bf16, w_lm
+    [V, d] bf16, lse_t [B, N+1]) and the draft from per-depth logits (draft_logits [B, D, V]
+    fp32 or bf16, draft_lse [B, D]); no [B, N+1, V] probabilities."""
+    B, R, d = x_t.shape
+    N = R - 1
+    V = w_lm.shape[0]
+    if parents.dim() == 2:
+        _need(parents, "parents", torch.int32, (B, N))
+        pstride = N
+    else:
+        _need(parents, "parents", torch.int32, (N,))
+        pstride = 0
+    _need(node_tokens, "node_tokens", torch.int32, (B, N))
+    _need(x_t, "x_t", torch.bfloat16, (B, R, d))
+    _need(w_lm, "w_lm", torch.bfloat16, (V, d))
+    _need(lse_t, "lse_t", torch.float32, (B, R))
+    _need(draft_logits, "draft_logits", None, (B, D, V))
+    _need(draft_lse, "draft_lse", torch.float32, (B, D))
+    _need(uniforms, "uniforms", torch.float32, (B, R))
+    ddt = _dt(draft_logits)
+    dev = x_t.device
+    if out is None:
+        out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+               "path_nodes": torch.empty((B, D), dtype=torch.int32, device=dev),
+               "out_tokens": torch.empty((B, D + 1), dtype=torch.int32, device=dev),
+               "node_accept": torch.empty((B, N), dtype=torch.uint8, device=dev),
+               "alpha": torch.empty((B, N), dtype=torch.float32, device=dev)}
+    w = _ws("accept_lm", ws)
+    ptr, n = w.get(L.lib().mv_accept_speculative_lm_workspace(B, N, V))
+    L.check("mv_accept_speculative_lm", L.lib().mv_accept_speculative_lm(
+        ddt, B, N, V, d, D, _ptr(parents), pstride, _ptr(node_tokens), _ptr(x_t), _ptr(w_lm),
+        _ptr(lse_t), _ptr(draft_logits), _ptr(draft_lse), _ptr(uniforms),
+        _ptr(out["accept_len"]), _ptr(out["path_nodes"]), _ptr(out["out_tokens"]),
+        _ptr(out.get("node_accept")), _ptr(out.get("alpha")), _ptr(status), ptr, n, _stream()))
+    return out
+
+
 def kv_commit(k_cache: torch.Tensor, v_cache: torch.Tensor, prefix_len: torch.Tensor, N: int,
               path_nodes: torch.Tensor, accept_len: torch.Tensor,
               status: Optional[torch.Tensor] = None,

@@ -19,7 +19,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -139,6 +139,15 @@ def test_host_argument_checks():
     # argmax-id targets: greedy only
     assert lib.mv_accept_paths(L.MV_ACCEPT_SPECULATIVE, L.MV_TARGET_IDS, 1, 4, 10, 2, P, 0, P, P, P, P,
                                P, P, P, None, None, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
+    # speculative acceptance from the LM head
+    lm = lambda ddt, d, **kw: lib.mv_accept_speculative_lm(
+        ddt, 1, 4, 100, d, 2, kw.get("par", P), 0, P, P, P, P, P, P, P, P, P, P, None, None, None,
+        kw.get("ws", P), kw.get("wsn", 1 << 20), None)
+    assert lm(7, 64) == L.MV_ERR_INVALID_ARG                   # draft dtype
+    assert lm(L.MV_F32, 60) == L.MV_ERR_UNSUPPORTED            # d % 8
+    assert lm(L.MV_F32, 64, par=None) == L.MV_ERR_INVALID_ARG
+    assert lm(L.MV_F32, 64, ws=None, wsn=0) == L.MV_ERR_WORKSPACE
+    assert lib.mv_accept_speculative_lm_workspace(64, 64, 128256) > 64 * 128256 * 8
     # dynamic tree
     dyn = lambda D, smax, s, N: lib.mv_build_dynamic_tree(
         1, D, smax, L.int_array(s) if s else None, N, P, P, None, P, P, P, P, None, None, None)
