@@ -53,6 +53,9 @@ DESCR = {
           "per-sequence dynamic tree of the 64 most probable candidate paths",
     "c6": "llama3-8b-layer-lmhead: the llama3-8b-layer step with the greedy target computed by "
           "the target LM head (W_lm 32000 x 4096 bf16 over the 65 verify rows, argmax fused)",
+    "c9": "llama3-8b-layer-lmhead-spec: the llama3-8b-layer step with speculative acceptance, "
+          "the target from the LM head (W_lm 32000 x 4096 bf16, LSE per verify row) and the "
+          "draft of depth k from Medusa head k's logits; no [N+1, V] probabilities",
 }
 
 
@@ -83,6 +86,8 @@ def make_inputs(wl, seed):
     x.update(W.gen_attention(wl, seed))
     if wl.target_head:
         x.update(W.gen_target_head(wl, seed))
+        if wl.accept == "speculative":
+            x["uniforms"] = W.gen_uniforms(wl, seed)
     elif wl.accept == "greedy":
         x["target"] = W.gen_target_logits(wl, seed)
     elif wl.accept in ("speculative", "multicand"):
@@ -111,7 +116,14 @@ def step_bytes(wl, x):
     if wl.target_head:
         T = wl.B * (N + 1)
         parts["target_head"] = (wl.accept_V * wl.d * 2 + T * wl.d * 2, 2.0 * T * wl.accept_V * wl.d)
-        parts["accept"] = (T * 4, 0.0)
+        if wl.accept == "speculative":
+            # per node: its W_lm row and its parent's hidden state; the terminal's target row
+            # is one more pass over W_lm; the draft row and the two rows' residual passes
+            parts["accept"] = (wl.B * N * 4 * wl.d + wl.accept_V * wl.d * 2
+                               + wl.B * wl.accept_V * (2 + 3 * 2 * 4),
+                               2.0 * wl.B * (N + wl.accept_V) * wl.d)
+        else:
+            parts["accept"] = (T * 4, 0.0)
     elif wl.accept == "greedy":
         parts["accept"] = (wl.B * (N + 1) * wl.accept_V * esz, 0.0)
     elif wl.accept in ("speculative", "multicand"):
@@ -200,10 +212,15 @@ def _oracle_step(wl, x, seed, attn_rows=None):
         O.tree_attention(x["q"], x["k_cache"], x["v_cache"], x["prefix_len"], tree["anc"],
                          select=attn_rows)
     t4 = time.perf_counter()
-    if wl.target_head:
+    if wl.target_head and wl.accept == "speculative":
+        acc = O.accept_speculative_lm(x_t, x["w_lm"], heads["logits"], tree["tokens"], parents,
+                                      x["uniforms"], wl.D)
+    elif wl.target_head:
         z = O.lm_head_argmax(x_t.reshape(-1, wl.d), x["w_lm"])["logits"]
         target = z.reshape(wl.B, wl.N + 1, wl.accept_V)
-    if wl.accept == "greedy" and wl.dynamic_nodes:
+    if wl.target_head and wl.accept == "speculative":
+        pass
+    elif wl.accept == "greedy" and wl.dynamic_nodes:
         per = [O.accept_greedy(target[b:b + 1], tr["tokens"], tr["parents"], wl.D)
                for b, tr in enumerate(trees)]
         acc = {k: np.concatenate([a[k] for a in per]) for k in ("accept_len", "path_nodes")}
@@ -445,7 +462,7 @@ def main():
     step_total = sum(b for b, _ in parts.values())
 
     max_L = int(x["prefix_len"].max())
-    spec = wl.accept in ("speculative", "multicand")
+    spec = wl.accept in ("speculative", "multicand") and not wl.target_head
     step = VerifyStep(parents=wl.parents, depth_widths=wl.depth_widths, dtype=dt, B=wl.B,
                       Hq=wl.Hq, Hkv=wl.Hkv, dh=wl.dh, max_L=max_L,
                       heads={"d": wl.d, "V": wl.V, "K": wl.K, "widths": list(wl.head_widths)}
@@ -474,6 +491,8 @@ def main():
         # the target rows' hidden states are planted against the node tokens this step
         # produces (the heads and the tree run once, untimed, to get them)
         base["x_t"] = d(x["x_t"], torch.bfloat16)
+        if "uniforms" in x:
+            base["uniforms"] = d(x["uniforms"], torch.float32)
         if wl.plant_p > 0:
             c = step.bind(dict(static, **base))
             for part in ("heads_residual", "heads_projection", "heads_select", "tree"):

@@ -66,8 +66,10 @@ class VerifyStep:
         self.lm_width = lm_width
         self.heads = heads  # {"d":, "V":, "K":, "widths":}
         self.tokens_given = tokens_given  # node tokens come with the inputs (no heads)
-        # greedy target from the LM head (hidden width target_head): inputs x_t [B, N+1, d]
-        # and w_lm [V, d]; its argmax ids feed greedy acceptance (no logits materialised)
+        # target from the LM head (hidden width target_head): inputs x_t [B, N+1, d] and
+        # w_lm [V, d].  Greedy: its argmax ids feed greedy acceptance.  Speculative: its LSE per
+        # row and the heads' own logits (the draft of each depth) feed the speculative rule;
+        # no [B, N+1, V] tensor is made either way
         self.target_head = target_head
         dev = torch.device(device)
         self.device = dev
@@ -105,17 +107,28 @@ class VerifyStep:
         self.ws_attn.get(ops.attn_workspace_bytes(self.dt, B, N, Hq, Hkv, dh, max_L))
         self._s_depth = L.int_array(self.depth_widths)
         if target_head:
-            if accept != "greedy" or dtype != torch.bfloat16:
-                raise ValueError("the target LM head feeds bf16 greedy acceptance")
+            if accept not in ("greedy", "speculative") or dtype != torch.bfloat16:
+                raise ValueError("the target LM head feeds bf16 greedy or speculative acceptance")
+            if accept == "speculative" and (heads is None or lm_width or dynamic_nodes):
+                raise ValueError("speculative acceptance from the LM head takes its draft from "
+                                 "the Medusa heads (one head per depth)")
             self.ws_lm = ops.Workspace(dev)
             self.ws_lm.get(ops.lm_head_workspace_bytes(B * (N + 1), target_head, V))
             self.target_ids = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
+            self.target_lse = torch.empty((B, N + 1), dtype=torch.float32, device=dev)
+            if accept == "speculative":  # the heads' logits: draft row of depth k = head k
+                self.draft_logits = torch.empty((B, heads["K"], heads["V"]), dtype=dtype,
+                                                device=dev)
         if commit and accept == "none":
             raise ValueError("the commit needs an acceptance rule")
         self.commit = commit
         self.prefix_next = torch.empty(B, dtype=torch.int32, device=dev) if commit else None
-        if accept != "none":
+        self.spec_lm = bool(target_head) and accept == "speculative"
+        if self.spec_lm:
+            self.ws_accept.get(L.lib().mv_accept_speculative_lm_workspace(B, N, V))
+        elif accept != "none":
             self.ws_accept.get(ops.accept_workspace_bytes(self.mode, B, N, V))
+        if accept != "none":
             self.acc = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
                         "path_nodes": torch.empty((B, self.D), dtype=torch.int32, device=dev),
                         "out_tokens": torch.empty((B, self.D + 1), dtype=torch.int32, device=dev),
@@ -164,7 +177,8 @@ class VerifyStep:
             ld = D * s_max
             esz = 4
             proj = wrap("mv_medusa_head_project", lib.mv_medusa_head_project, self.dt, B, d, Vh,
-                        K, self._s_heads, s_max, _p(inp["w_head"]), None, wsp, wsn, st)
+                        K, self._s_heads, s_max, _p(inp["w_head"]),
+                        _p(self.draft_logits) if self.spec_lm else None, wsp, wsn, st)
             calls["heads_select"] = wrap("mv_medusa_head_select", lib.mv_medusa_head_select,
                                          self.dt, B, d, Vh, K, self._s_heads, s_max,
                                          self.cand.data_ptr() + off * s_max * esz,
@@ -218,9 +232,20 @@ class VerifyStep:
             wsp, wsn = self._ws(self.ws_lm)
             calls["target_head"] = wrap("mv_lm_head_argmax", lib.mv_lm_head_argmax, L.MV_BF16,
                                         B * (N + 1), self.target_head, self.V, _p(inp["x_t"]),
-                                        _p(inp["w_lm"]), self.target_ids.data_ptr(), None, None,
+                                        _p(inp["w_lm"]), self.target_ids.data_ptr(), None,
+                                        _p(self.target_lse) if self.spec_lm else None,
                                         wsp, wsn, st)
-        if self.accept != "none":
+        if self.spec_lm:
+            wsp, wsn = self._ws(self.ws_accept)
+            a = self.acc
+            calls["accept"] = wrap("mv_accept_speculative_lm", lib.mv_accept_speculative_lm,
+                                   self.dt, B, N, self.V, self.target_head, D, _p(self.parents),
+                                   0, _p(tokens), _p(inp["x_t"]), _p(inp["w_lm"]),
+                                   _p(self.target_lse), _p(self.draft_logits), _p(self.head_lse),
+                                   _p(inp["uniforms"]), _p(a["accept_len"]), _p(a["path_nodes"]),
+                                   _p(a["out_tokens"]), _p(a["node_accept"]), _p(a["alpha"]),
+                                   _p(self.status), wsp, wsn, st)
+        elif self.accept != "none":
             wsp, wsn = self._ws(self.ws_accept)
             if self.target_head:
                 tgt, tdt, Vt = self.target_ids, L.MV_TARGET_IDS, self.V

@@ -166,6 +166,12 @@ WORKLOADS: Dict[str, Workload] = {
                    parents=_T4321, prefix=(4096, 4096), depth_widths=(4, 3, 2, 1),
                    d=4096, V=32000, K=4, head_widths=(4, 3, 2, 1), weight_std=0.02,
                    accept="greedy", accept_V=32000, plant_p=0.6, target_head=True),
+    # the same step with speculative acceptance: the target from the LM head, the draft of
+    # depth k from Medusa head k's logits, seeded uniforms
+    "c9": Workload(name="llama3-8b-layer-lmhead-spec", dtype="bf16", B=1, Hq=32, Hkv=8, dh=128,
+                   parents=_T4321, prefix=(4096, 4096), depth_widths=(4, 3, 2, 1),
+                   d=4096, V=32000, K=4, head_widths=(4, 3, 2, 1), weight_std=0.02,
+                   accept="speculative", accept_V=32000, target_head=True),
 }
 
 
@@ -280,6 +286,11 @@ def gen_target_head(w: Workload, seed: int) -> Dict[str, np.ndarray]:
     W_lm [accept_V, d] ~ N(0, 1/d) (rows of norm ~1), both rounded to bf16."""
     return {"x_t": normal(seed, "x_t", (w.B, w.N + 1, w.d), 1.0, True),
             "w_lm": normal(seed, "w_lm", (w.accept_V, w.d), 1.0 / np.sqrt(w.d), True)}
+
+
+def gen_uniforms(w: Workload, seed: int) -> np.ndarray:
+    """Uniforms [B, N+1] in [0, 1) for a speculative step (float32)."""
+    return rng_for(seed, "uniforms").random((w.B, w.N + 1), dtype=np.float32)
 
 
 def plant_target_head(x_t: np.ndarray, w_lm: np.ndarray, parents: Sequence[int],

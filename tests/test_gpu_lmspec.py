@@ -87,7 +87,9 @@ def _run(B, V, d, widths, seed, noise, draft_bf16=False):
     dep = _depths(parents)
     ties = 0
     for b in range(B):
-        if np.any(np.abs(u[b, :N] - ref["alpha"][b]) < ALPHA_TIE):
+        # only nodes whose parent is the prefix or accepted decide anything
+        live = np.array([p < 0 or ref["node_accept"][b][p] for p in parents])
+        if np.any(live & (np.abs(u[b, :N] - ref["alpha"][b]) < ALPHA_TIE)):
             ties += 1
             continue
         np.testing.assert_array_equal(g["node_accept"][b].astype(bool), ref["node_accept"][b])
@@ -150,3 +152,72 @@ def test_lmspec_bad_token_flags():
                               dev(draft), dev(draft_lse), dev(u), D, status=status)
     torch.cuda.synchronize()
     assert int(status.item()) & L.MV_DEV_BAD_TOKEN
+
+
+def _step_check(wl, seed):
+    """The whole step with speculative acceptance from the LM head: heads -> tree -> attention ->
+    LM head (LSE per verify row) -> speculative acceptance with the heads' logits as the draft ->
+    commit.  The step stores the heads' logits in bf16 and takes their LSE from the fp32 logits,
+    so the oracle's draft rows are its fp64 head logits rounded to bf16 (its own softmax), and a
+    node within 1e-3 of its threshold (or an extra token within 1e-3 of a CDF boundary) is a
+    counted near-tie."""
+    from medusa_tree_attention_verify_amd.step import VerifyStep
+    parents = list(wl.parents)
+    N, D = wl.N, wl.D
+    bf = torch.bfloat16
+    xh, xa, xt = W.gen_heads(wl, seed), W.gen_attention(wl, seed), W.gen_target_head(wl, seed)
+    u = W.gen_uniforms(wl, seed)
+    heads = O.medusa_heads(xh["h"], xh["w_res"], xh["w_head"], list(wl.head_widths))
+    cand = [heads["topk_ids"][:, k, :wl.head_widths[k]] for k in range(wl.K)]
+    tree = O.build_tree(parents, cand, list(wl.depth_widths))
+    step = VerifyStep(parents=parents, depth_widths=wl.depth_widths, dtype=bf, B=wl.B, Hq=wl.Hq,
+                      Hkv=wl.Hkv, dh=wl.dh, max_L=int(xa["prefix_len"].max()),
+                      heads={"d": wl.d, "V": wl.V, "K": wl.K, "widths": list(wl.head_widths)},
+                      accept="speculative", V=wl.accept_V, target_head=wl.d, commit=True)
+    inp = {"h": dev(xh["h"], bf), "w_res": dev(xh["w_res"], bf), "w_head": dev(xh["w_head"], bf),
+           "q": dev(xa["q"], bf), "k_cache": dev(xa["k_cache"], bf), "v_cache": dev(xa["v_cache"], bf),
+           "prefix_len": dev_i32(xa["prefix_len"]), "x_t": dev(xt["x_t"], bf),
+           "w_lm": dev(xt["w_lm"], bf), "uniforms": dev(u)}
+    print(f"lmspec step {wl.name} d={wl.d} V={wl.V} seed={seed}", flush=True)
+    step.run(inp)
+    torch.cuda.synchronize()
+    assert int(step.status.item()) == 0
+    from tests.gpu_util import check_topk, assert_fp32
+    assert check_topk(host(step.cand), heads["logits"], list(wl.head_widths)) == 0
+    np.testing.assert_array_equal(host(step.tree["node_tokens"]), tree["tokens"])
+    lm = O.lm_head_argmax(xt["x_t"].reshape(-1, wl.d), xt["w_lm"])
+    assert_fp32(host(step.target_lse).ravel(), lm["lse"], atol=1e-3, what="target lse")
+    draft = W.round_bf16(heads["logits"].astype(np.float32))
+    ref = O.accept_speculative_lm(xt["x_t"], xt["w_lm"], draft, tree["tokens"], parents, u, D)
+    g = {k: host(v) for k, v in step.acc.items() if v is not None}
+    np.testing.assert_allclose(g["alpha"], ref["alpha"], rtol=0, atol=1e-2)
+    ties = 0
+    for b in range(wl.B):
+        # only nodes whose parent is the prefix or accepted decide anything
+        live = np.array([p < 0 or ref["node_accept"][b][p] for p in parents])
+        if np.any(live & (np.abs(u[b, :N] - ref["alpha"][b]) < 1e-3)):
+            ties += 1
+            continue
+        n = int(ref["accept_len"][b])
+        assert g["accept_len"][b] == n
+        np.testing.assert_array_equal(g["path_nodes"][b], ref["path_nodes"][b])
+        np.testing.assert_array_equal(g["out_tokens"][b][:n], ref["out_tokens"][b][:n])
+    if ties == 0:  # the commit of the oracle's accepted paths (a copy: bit-exact)
+        k2, v2, p2 = O.kv_commit(xa["k_cache"], xa["v_cache"], xa["prefix_len"],
+                                 ref["path_nodes"], ref["accept_len"], N)
+        np.testing.assert_array_equal(host(step.prefix_next), p2)
+        np.testing.assert_array_equal(host(inp["k_cache"]), k2)
+        np.testing.assert_array_equal(host(inp["v_cache"]), v2)
+    print("accepted lengths", g["accept_len"].tolist(), "near-ties", ties)
+    assert ties <= max(1, wl.B // 4)
+
+
+def test_step_lmhead_speculative_small():
+    require_gpu()
+    wl = W.WORKLOADS["c9"].scaled(B=3, d=512, V=3000, accept_V=3000, prefix=(700, 700))
+    _step_check(wl, 33)
+
+
+def test_step_lmhead_speculative_llama8b():
+    require_gpu()
+    _step_check(W.WORKLOADS["c9"], 9)
