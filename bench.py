@@ -56,6 +56,10 @@ DESCR = {
     "c9": "llama3-8b-layer-lmhead-spec: the llama3-8b-layer step with speculative acceptance, "
           "the target from the LM head (W_lm 32000 x 4096 bf16, LSE per verify row) and the "
           "draft of depth k from Medusa head k's logits; no [N+1, V] probabilities",
+    "c10": "spec-serving-b64-lmhead: the spec-serving-b64 attention (B=64, prefix U[512,8192]) "
+           "with speculative acceptance driven by the target LM head (W_lm 128256 x 4096 bf16 "
+           "over 64 x 65 verify rows, LSE per row) and a draft's per-depth logits [64, 4, 128256] "
+           "(candidates = their top tokens); no [B, N+1, V] probabilities",
 }
 
 
@@ -88,6 +92,8 @@ def make_inputs(wl, seed):
         x.update(W.gen_target_head(wl, seed))
         if wl.accept == "speculative":
             x["uniforms"] = W.gen_uniforms(wl, seed)
+            if not wl.has_heads:
+                x["draft_logits"] = W.gen_draft_logits(wl, seed)
     elif wl.accept == "greedy":
         x["target"] = W.gen_target_logits(wl, seed)
     elif wl.accept in ("speculative", "multicand"):
@@ -113,6 +119,9 @@ def step_bytes(wl, x):
         depth.append(1 if p < 0 else depth[p] + 1)
     flops = float(np.sum(4.0 * wl.dh * wl.Hq * (N * L + sum(depth))))
     parts["attention"] = (kv + qo, flops)
+    if wl.target_head and wl.accept == "speculative" and not wl.has_heads:
+        # candidates and LSE of the draft's per-depth rows
+        parts["heads_select"] = (wl.B * wl.D * wl.accept_V * 2, 0.0)
     if wl.target_head:
         T = wl.B * (N + 1)
         parts["target_head"] = (wl.accept_V * wl.d * 2 + T * wl.d * 2, 2.0 * T * wl.accept_V * wl.d)
@@ -172,6 +181,9 @@ def _oracle_step(wl, x, seed, attn_rows=None):
             cand.append(np.stack([O.topk_rows(x["target"][b, 0], wl.lm_width)["ids"]
                                   for b in range(wl.B)]))
         cand += [heads["topk_ids"][:, k, :wl.head_widths[k]] for k in range(wl.K)]
+    elif "draft_logits" in x:    # a draft's per-depth logits: their top tokens are the candidates
+        cand = [np.stack([O.topk_rows(x["draft_logits"][b, k], wl.depth_widths[k])["ids"]
+                          for b in range(wl.B)]) for k in range(wl.D)]
     t1 = time.perf_counter()
     if wl.dynamic_nodes:         # one tree per sequence: its most probable head paths
         dyn = O.dynamic_tree(heads["topk_ids"], heads["topk_vals"], heads["lse"],
@@ -213,7 +225,8 @@ def _oracle_step(wl, x, seed, attn_rows=None):
                          select=attn_rows)
     t4 = time.perf_counter()
     if wl.target_head and wl.accept == "speculative":
-        acc = O.accept_speculative_lm(x_t, x["w_lm"], heads["logits"], tree["tokens"], parents,
+        draft = heads["logits"] if wl.has_heads else x["draft_logits"]
+        acc = O.accept_speculative_lm(x_t, x["w_lm"], draft, tree["tokens"], parents,
                                       x["uniforms"], wl.D)
     elif wl.target_head:
         z = O.lm_head_argmax(x_t.reshape(-1, wl.d), x["w_lm"])["logits"]
@@ -468,7 +481,8 @@ def main():
                       heads={"d": wl.d, "V": wl.V, "K": wl.K, "widths": list(wl.head_widths)}
                       if wl.has_heads else None,
                       lm_width=wl.lm_width, accept=wl.accept, V=wl.accept_V,
-                      tokens_given=not wl.has_heads, target_head=wl.d if wl.target_head else None,
+                      tokens_given=not wl.has_heads and not wl.target_head,
+                      target_head=wl.d if wl.target_head else None,
                       commit=wl.accept != "none", dynamic_nodes=wl.dynamic_nodes or None)
     d = lambda a, t=dt: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
     static = {}
@@ -493,6 +507,8 @@ def main():
         base["x_t"] = d(x["x_t"], torch.bfloat16)
         if "uniforms" in x:
             base["uniforms"] = d(x["uniforms"], torch.float32)
+        if "draft_logits" in x:
+            base["draft_logits"] = d(x["draft_logits"], torch.bfloat16)
         if wl.plant_p > 0:
             c = step.bind(dict(static, **base))
             for part in ("heads_residual", "heads_projection", "heads_select", "tree"):
@@ -610,6 +626,26 @@ def main():
                 "frac": round(ach / HBM_PEAK_GBS, 4),
                 "traffic": _traffic("head_projection", DESCR[args.workload].split(":")[0], src),
                 "algorithmic_bytes": int(b_head), "avg_launch_us": round(seg_mean["heads_projection"] * 1000, 2)}
+    elif wl.target_head:
+        # dominant: the target LM head over all verify rows (tiled kernel + merge, one call);
+        # at B*(N+1) = 4160 rows it is bound by the matrix cores
+        b_lm, f_lm = parts["target_head"]
+        dur_s = seg_mean["target_head"] / 1000.0
+        src = os.path.join(ROOT, "medusa_tree_attention_verify_amd", "csrc", "lmhead.hip")
+        traffic = _traffic("lm_head", DESCR[args.workload].split(":")[0], src)
+        if f_lm / b_lm > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+            ach = f_lm / dur_s / 1e12
+            roof = {"kernel": "lm_head_gemm_kernel + lm_head_merge_kernel", "bound": "mfma",
+                    "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                    "algorithmic_flops": f_lm}
+        else:
+            ach = b_lm / dur_s / 1e9
+            roof = {"kernel": "lm_head_kernel + lm_head_merge_kernel", "bound": "hbm",
+                    "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+        roof["algorithmic_bytes"] = int(b_lm)
+        roof["avg_launch_us"] = round(seg_mean["target_head"] * 1000, 2)
     else:
         # dominant: the tree-attention call (attention kernel, plus the combine when the keys
         # are split and the length ordering for batches), timed as one part

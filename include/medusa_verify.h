@@ -178,11 +178,14 @@ MV_API int mv_medusa_heads_noalloc(int dt, int B, int d, int V, int K, const int
 /* Top-s entries of each of R rows of a logit matrix (the same selection rule as the heads),
  * for candidates that come from logits the caller already has -- e.g. the base model's own
  * head ("Head 0", which predicts the next token in [MX] "The Architectural Blueprint").
+ * Also a draft model's per-depth logits, whose softmax is the draft distribution P_draft of
+ * [SD] "The Acceptance Sampling Rule": lse then gives each row's log-sum-exp.
  *   x      row r starts at x + r*ldx elements (dt), V entries per row.
  *   ids    int32, vals fp32 (vals may be NULL): row r at r*ld_out, s entries.
+ *   lse    fp32 [R] or NULL: log sum_v exp(x[r][v]), accumulated in fp32.
  * 1 <= s <= MV_MAX_TOPK, s <= V.  No workspace. */
 MV_API int mv_topk_rows(int dt, int R, int V, int s, const void* x, long long ldx, int32_t* ids,
-                 float* vals, int ld_out, void* stream);
+                 float* vals, int ld_out, float* lse, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * (a3) Candidate-tree assembly.  [MTP] verification-engine code: the tree is a parent array,
@@ -363,12 +366,13 @@ MV_API int mv_accept_paths(int mode, int target_dt, int B, int N, int V, int D,
  *   terminal's row when it has children (P_t if that is all zero), else from P_t.
  * How it is computed: P_t(x_i) from one dot product W_lm[x_i] . x_t[parent row] (fp32
  * accumulation) against lse_t, P_d(x_i) from one draft logit against draft_lse, both in fp64;
- * after the walk one streaming pass over W_lm makes each sequence's terminal target row (and its
- * draft row from the draft logits), and the fp64 segment sums / inverse CDF of mv_accept_paths
+ * after the walk one streaming pass over W_lm (per 128 sequences, on the matrix cores) makes
+ * each sequence's terminal target row, the draft logits its draft row, and the fp64 segment
+ * sums / inverse CDF of mv_accept_paths
  * draw the extra token.  With fp32 dot products the decisions can differ from an exact one only
  * where |u - alpha| is within the dot product's rounding (~1e-5 relative).
  *   draft_dt      MV_F32 or MV_BF16: type of draft_logits [B][D][V] (row k = depth k+1).
- *   x_t [B][N+1][d] bf16, w_lm [V][d] bf16 (d % 8 == 0); lse_t [B][N+1] fp32 natural-log
+ *   x_t [B][N+1][d] bf16, w_lm [V][d] bf16 (d % 32 == 0); lse_t [B][N+1] fp32 natural-log
  *   log-sum-exp of the target logits (mv_lm_head_argmax gives it); draft_lse [B][D] fp32 the
  *   log-sum-exp of each draft row.  Other arguments, outputs and errors as mv_accept_paths.
  *   ws from mv_accept_speculative_lm_workspace(B, N, V).

@@ -60,7 +60,7 @@ SIGNATURES = [
                              _Z, _P]),
     ("mv_medusa_heads_noalloc", _I, [_I, _I, _I, _I, _I, _IP, _I, _P, _P, _P, _P, _P, _P, _P, _I,
                                      _P, _P]),
-    ("mv_topk_rows", _I, [_I, _I, _I, _I, _P, _LL, _P, _P, _I, _P]),
+    ("mv_topk_rows", _I, [_I, _I, _I, _I, _P, _LL, _P, _P, _I, _P, _P]),
     ("mv_build_tree_mask", _I, [_I, _P, _I, _I, _I, _IP, _P, _P, _P, _P, _P, _P]),
     ("mv_tree_attn_verify_workspace", _Z, [_I, _I, _I, _I, _I, _I, _I]),
     ("mv_tree_attn_verify", _I, [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _F, _P,

@@ -724,45 +724,20 @@ __global__ __launch_bounds__(256) void spec_lm_nodes_kernel(const SpecLmParams q
   }
 }
 
-// Terminal rows after the walk.  Target: row_t[b][v] = exp(W_lm[v] . x_t[b][row_b] - LSE_t),
-// one streaming pass over W_lm for all sequences (each wave takes 4 vocabulary rows, the lanes
-// split d).  Draft, when the terminal has children (they were all rejected): row_d[b][v] =
-// exp(draft logit of depth len_b + 1 at v - its LSE).
-constexpr int kLmRowsPerWave = 4;
-
-__global__ __launch_bounds__(256) void spec_lm_rows_kernel(const SpecLmParams q) {
-  const int lane = threadIdx.x & 63;
-  const int v0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kLmRowsPerWave;
-  if (v0 >= q.V) return;
-  const uint16_t* wr[kLmRowsPerWave];
-#pragma unroll
-  for (int r = 0; r < kLmRowsPerWave; ++r) wr[r] = q.w + static_cast<size_t>(min(v0 + r, q.V - 1)) * q.d;
-  for (int b = 0; b < q.B; ++b) {
-    const int row = q.term[b * 4 + 0];
-    const uint16_t* xr = q.x + (static_cast<size_t>(b) * (q.N + 1) + row) * q.d;
-    float acc[kLmRowsPerWave] = {};
-    for (int j = 8 * lane; j < q.d; j += 512) {
-      const uint4 xv = *reinterpret_cast<const uint4*>(xr + j);
-#pragma unroll
-      for (int r = 0; r < kLmRowsPerWave; ++r)
-        acc[r] = dot8_bf16(*reinterpret_cast<const uint4*>(wr[r] + j), xv, acc[r]);
-    }
-    const double lse = q.lse_t[static_cast<size_t>(b) * (q.N + 1) + row];
-    const bool child = q.term_c[b] > 0.0;
-    const int k = q.term[b * 4 + 2];  // depth of the terminal = draft row of its children
-#pragma unroll
-    for (int r = 0; r < kLmRowsPerWave; ++r) {
-      const float dotv = wave_sum(acc[r]);
-      const int v = v0 + r;
-      if (lane == 0 && v < q.V) {
-        q.row_t[static_cast<size_t>(b) * q.V + v] = static_cast<float>(exp(static_cast<double>(dotv) - lse));
-        q.row_d[static_cast<size_t>(b) * q.V + v] =
-            (child && k < q.D)
-                ? static_cast<float>(exp(draft_logit(q, b, k, v) - static_cast<double>(q.dlse[static_cast<size_t>(b) * q.D + k])))
-                : 0.f;
-      }
-    }
-  }
+// Terminal rows after the walk.  The target row row_t[b][v] = exp(W_lm[v] . x_t[b][row_b] -
+// LSE_t) comes from the LM head's streaming kernel in its rows mode (one pass over W_lm for up
+// to 128 sequences, on the matrix cores).  The draft row, when the terminal has children (they
+// were all rejected): row_d[b][v] = exp(draft logit of depth len_b + 1 at v - its LSE), else 0.
+__global__ __launch_bounds__(256) void spec_lm_draft_rows_kernel(const SpecLmParams q) {
+  const int b = blockIdx.y;
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  if (v >= q.V) return;
+  const bool child = q.term_c[b] > 0.0;
+  const int k = q.term[b * 4 + 2];  // depth of the terminal = draft row of its children
+  q.row_d[static_cast<size_t>(b) * q.V + v] =
+      (child && k < q.D)
+          ? static_cast<float>(exp(draft_logit(q, b, k, v) - static_cast<double>(q.dlse[static_cast<size_t>(b) * q.D + k])))
+          : 0.f;
 }
 
 struct AcceptPlan {
@@ -900,7 +875,7 @@ MV_API int mv_accept_speculative_lm(int draft_dt, int B, int N, int V, int d, in
   if (B < 1 || N < 1 || V < 1 || D < 1 || d < 8) return MV_ERR_INVALID_ARG;
   if (parents_stride != 0 && parents_stride < N) return MV_ERR_INVALID_ARG;
   if (N > MV_MAX_NODES || D > MV_MAX_DEPTH) return MV_ERR_UNSUPPORTED;
-  if (d % 8 != 0) return MV_ERR_UNSUPPORTED;
+  if (d % 32 != 0) return MV_ERR_UNSUPPORTED;
   if (!parents || !node_tokens || !x_t || !w_lm || !lse_t || !draft_logits || !draft_lse ||
       !uniforms || !accept_len || !path_nodes || !out_tokens)
     return MV_ERR_INVALID_ARG;
@@ -936,7 +911,8 @@ MV_API int mv_accept_speculative_lm(int draft_dt, int B, int N, int V, int d, in
   MV_TRY(launch_status());
   accept_path_kernel<true><<<B, 256, 0, st>>>(p);
   MV_TRY(launch_status());
-  spec_lm_rows_kernel<<<ceil_div(V, 4 * kLmRowsPerWave), 256, 0, st>>>(q);
+  MV_TRY(lm_head_prob_rows(B, d, V, q.x, p.term, 4, N + 1, lse_t, q.w, rt, st));
+  spec_lm_draft_rows_kernel<<<dim3(ceil_div(V, 256), B), 256, 0, st>>>(q);
   MV_TRY(launch_status());
   residual_segsum_kernel<<<B * a.S, 256, 0, st>>>(p);
   MV_TRY(launch_status());

@@ -550,33 +550,127 @@ __global__ __launch_bounds__(NW * 64) void gemv_f32_kernel(const GemvParams p) {
   else head_epilogue<false, NW, BC>(p, k, rb, ys);
 }
 
-// ---- top-s of each row of a logit matrix (one workgroup per row).
-template <bool BF16>
-__global__ __launch_bounds__(256) void topk_rows_kernel(int V, int s, const void* x, long long ldx,
-                                                        int32_t* ids, float* vals, int ld_out) {
-  __shared__ float sv[4];
-  __shared__ int si[4];
+// ---- top-s of each row of a logit matrix (one workgroup per row), optionally the row's
+// log-sum-exp.  One pass over the row: every thread keeps its S best (value, id) pairs sorted
+// in registers and a running (max, sum exp(x - max)) pair; then s workgroup-wide arg-bests over
+// the threads' current heads, the owner of each winner popping it.  Rows whose elements are
+// 16-byte aligned are read with 16-byte loads.
+constexpr int kTopkThreads = 1024;
+
+template <bool BF16, int S>
+__global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(int V, int s, const void* x, long long ldx,
+                                                        int32_t* ids, float* vals, int ld_out,
+                                                        float* lse, int vec) {
+  constexpr int NW = kTopkThreads / 64;
+  __shared__ float sv[NW];
+  __shared__ int si[NW];
+  __shared__ float sm[NW], sl[NW];
   const size_t rowoff = static_cast<size_t>(blockIdx.x) * ldx;
-  float pv = INFINITY;
-  int pi = -1;
-  for (int r = 0; r < s; ++r) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-    for (int j = threadIdx.x; j < V; j += 256) {
-      const float v = load_elem<BF16>(x, rowoff + j);
-      if (kv_after(v, j, pv, pi) && kv_better(v, j, bv, bi)) {
-        bv = v;
-        bi = j;
+  float lv[S];
+  int li[S];
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    lv[k] = -INFINITY;
+    li[k] = INT_MAX;
+  }
+  float m = -INFINITY, l = 0.f;
+  auto take = [&](float v, int j) {
+    if (lse) {
+      if (v > m) {
+        l = l * __expf(m - v) + 1.f;
+        m = v;
+      } else if (v != -INFINITY) {
+        l += __expf(v - m);
       }
     }
+    // insert, keeping the list sorted (after the first few elements almost never taken)
+    if (__builtin_expect(v >= lv[S - 1], 0) && kv_better(v, j, lv[S - 1], li[S - 1])) {
+#pragma unroll
+      for (int k = S - 1; k > 0; --k) {
+        const bool shift = kv_better(v, j, lv[k - 1], li[k - 1]);
+        const bool here = !shift && kv_better(v, j, lv[k], li[k]);
+        lv[k] = shift ? lv[k - 1] : (here ? v : lv[k]);
+        li[k] = shift ? li[k - 1] : (here ? j : li[k]);
+      }
+      if (kv_better(v, j, lv[0], li[0])) {
+        lv[0] = v;
+        li[0] = j;
+      }
+    }
+  };
+  constexpr int EPV = BF16 ? 8 : 4;  // elements per 16-byte load
+  constexpr int U = 8;                // loads in flight per thread
+  if (vec) {
+    const uint4* row = reinterpret_cast<const uint4*>(static_cast<const char*>(x) + rowoff * (BF16 ? 2 : 4));
+    const int nv = V / EPV;
+    for (int q0 = threadIdx.x; q0 < nv; q0 += kTopkThreads * U) {
+      uint4 t4[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int q = q0 + u * kTopkThreads;
+        t4[u] = q < nv ? row[q] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int q = q0 + u * kTopkThreads;
+        if (q >= nv) break;
+        const uint32_t w4[4] = {t4[u].x, t4[u].y, t4[u].z, t4[u].w};
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const uint32_t word = w4[BF16 ? e / 2 : e];
+          const float v = BF16 ? __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16))
+                               : __uint_as_float(word);
+          take(v, q * EPV + e);
+        }
+      }
+    }
+  } else {
+    for (int j0 = threadIdx.x; j0 < V; j0 += kTopkThreads * U) {
+      float tv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * kTopkThreads;
+        tv[u] = j < V ? load_elem<BF16>(x, rowoff + j) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * kTopkThreads;
+        if (j >= V) break;
+        take(tv[u], j);
+      }
+    }
+  }
+  if (lse) {
+    wave_ml_merge(m, l);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) {
+      sm[w] = m;
+      sl[w] = l;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int k = 1; k < NW; ++k) ml_merge(m, l, sm[k], sl[k]);
+      lse[blockIdx.x] = m + logf(l);
+    }
+  }
+  for (int r = 0; r < s; ++r) {
+    float bv = lv[0];
+    int bi = li[0];
     block_argbest(bv, bi, sv, si);
     if (threadIdx.x == 0) {
       const size_t o = static_cast<size_t>(blockIdx.x) * ld_out + r;
       ids[o] = bi == INT_MAX ? -1 : bi;
       if (vals) vals[o] = bv;
     }
-    pv = bv;
-    pi = bi;
+    if (bi != INT_MAX && li[0] == bi) {  // the owner pops its head (ids are unique per row)
+#pragma unroll
+      for (int k = 0; k < S - 1; ++k) {
+        lv[k] = lv[k + 1];
+        li[k] = li[k + 1];
+      }
+      lv[S - 1] = -INFINITY;
+      li[S - 1] = INT_MAX;
+    }
   }
 }
 
@@ -826,15 +920,23 @@ MV_API int mv_medusa_heads_noalloc(int dt, int B, int d, int V, int K, const int
 }
 
 MV_API int mv_topk_rows(int dt, int R, int V, int s, const void* x, long long ldx, int32_t* ids,
-                        float* vals, int ld_out, void* stream) {
+                        float* vals, int ld_out, float* lse, void* stream) {
   if (dt != MV_F32 && dt != MV_BF16) return MV_ERR_INVALID_ARG;
   if (R < 1 || V < 1 || !x || !ids) return MV_ERR_INVALID_ARG;
   if (s < 1 || s > MV_MAX_TOPK || s > V) return MV_ERR_UNSUPPORTED;
   if (ldx < V || ld_out < s) return MV_ERR_INVALID_ARG;
   hipStream_t st = as_stream(stream);
-  if (dt == MV_BF16) topk_rows_kernel<true><<<R, 256, 0, st>>>(V, s, x, ldx, ids, vals, ld_out);
-  else topk_rows_kernel<false><<<R, 256, 0, st>>>(V, s, x, ldx, ids, vals, ld_out);
-  return launch_status();
+  const int epv = dt == MV_BF16 ? 8 : 4;
+  const int vec = (V % epv == 0 && ldx % epv == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0) ? 1 : 0;
+#define MV_TOPK_CASE(S_)                                                                          \
+  if (s <= S_) {                                                                                  \
+    if (dt == MV_BF16) topk_rows_kernel<true, S_><<<R, kTopkThreads, 0, st>>>(V, s, x, ldx, ids, vals, ld_out, lse, vec); \
+    else topk_rows_kernel<false, S_><<<R, kTopkThreads, 0, st>>>(V, s, x, ldx, ids, vals, ld_out, lse, vec); \
+    return launch_status();                                                                       \
+  }
+  MV_TOPK_CASE(4) MV_TOPK_CASE(8) MV_TOPK_CASE(16)
+#undef MV_TOPK_CASE
+  return MV_ERR_UNSUPPORTED;
 }
 
 }  // extern "C"

@@ -12,8 +12,10 @@
 // per row the greedy token argmax_v logits[t][v] (ties: lowest id), optionally that logit and
 // LSE[t] = log sum_v exp(logits[t][v]), and never writes the [T][V] logits.
 //
-// One streaming pass over W per group of up to 128 target rows (the kernel below), then a
-// second kernel merges each row's ceil(V/64) block partials into the greedy id and the LSE.
+// Up to 128 target rows: one streaming pass over W per group of rows (lm_head_kernel).  More
+// rows: a tiled GEMM over 256-row vocabulary blocks (lm_head_gemm_kernel), which reads W once
+// per block of 128 or 256 target rows through LDS.  Both write per (row, vocabulary block)
+// partials; a second kernel merges each row's partials into the greedy id and the LSE.
 
 #include <math.h>
 
@@ -29,7 +31,7 @@ constexpr int kLmRows = 64;        // vocabulary rows per workgroup
 constexpr int kLmMergeThreads = 256;
 
 struct LmParams {
-  int T, d, V, KT, nrb;         // KT = d / 32, nrb = ceil(V / 64)
+  int T, d, V, KT, nrb;         // KT = d / 32, nrb = vocabulary blocks (of 64 or 256 rows)
   const uint16_t* x;            // [T][d] bf16
   const uint16_t* w;            // [V][d] bf16
   float* pm;                    // [T][nrb] partial max
@@ -38,7 +40,18 @@ struct LmParams {
   int32_t* ids;                 // [T]
   float* maxv;                  // [T] or null
   float* lse;                   // [T] or null
+  // Rows mode (terminal rows of speculative acceptance): target row t is x row
+  // t * xrow_mul + xrow[t * xrow_stride] (xrow null: row t), and the kernel writes
+  // rows_out[t][v] = exp(logit - lse_in[that row]) instead of partials.
+  const int* xrow;
+  int xrow_stride, xrow_mul;
+  const float* lse_in;
+  float* rows_out;              // [T][V]
 };
+
+__device__ __forceinline__ int lm_xrow(const LmParams& p, int t) {
+  return p.xrow ? t * p.xrow_mul + p.xrow[static_cast<size_t>(t) * p.xrow_stride] : t;
+}
 
 // Streaming kernel.  A workgroup owns 64 vocabulary rows, one 16-row MFMA tile per wave, and a
 // group of up to 128 target rows (NCT column tiles of 16).  Each wave streams its 16 weight rows
@@ -53,7 +66,7 @@ struct LmParams {
 constexpr int kLmThreads = 256;
 constexpr int kLmXPitch = 40;  // bf16 elements per staged target row (32 + 8 padding)
 
-template <int NCT, int U>
+template <int NCT, int U, bool ROWS>
 __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const LmParams p) {
   constexpr int NCOL = 16 * NCT;
   constexpr int XP = NCOL * 4 * U;                           // 16-byte pieces of one x batch
@@ -79,7 +92,8 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const LmParams p) {
       const int q = tid + i * kLmThreads;
       if (XP % kLmThreads == 0 || q < XP) {
         const int u = q / (NCOL * 4), c = (q / 4) % NCOL, qq = q % 4;
-        xr[i] = *reinterpret_cast<const u32x4*>(p.x + static_cast<size_t>(min(col0 + c, p.T - 1)) * p.d +
+        const int t = min(col0 + c, p.T - 1);
+        xr[i] = *reinterpret_cast<const u32x4*>(p.x + static_cast<size_t>(ROWS ? lm_xrow(p, t) : t) * p.d +
                                                 32 * (bt * U + u) + 8 * qq);
       }
     }
@@ -142,6 +156,22 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const LmParams p) {
   // Epilogue.  acc[ct][v]: vocabulary row row0 + 16w + 4*(lane/16) + v, target row
   // col0 + 16ct + lane%16; the four 16-lane groups hold the other rows of the same target rows.
   const int c16 = lane & 15;
+  if constexpr (ROWS) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int t = col0 + 16 * ct + c16;
+      if (t >= p.T) continue;
+      const double lse = static_cast<double>(p.lse_in[lm_xrow(p, t)]);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = row0 + 16 * w + 4 * (lane >> 4) + v;
+        if (r < p.V)
+          p.rows_out[static_cast<size_t>(t) * p.V + r] =
+              static_cast<float>(exp(static_cast<double>(acc[ct][v]) - lse));
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     float bv = -INFINITY;
@@ -207,6 +237,195 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const LmParams p) {
   }
 }
 
+// Tiled kernel for many target rows (batched verify steps).  Streaming W once per 128 rows
+// re-reads it ceil(T/128) times; past that the product is a GEMM whose matrix-core work
+// (2*T*V*d FLOPs) outweighs the weight bytes, so both operands go through LDS in large tiles.
+// A workgroup owns 256 vocabulary rows x BN target rows, split over WM x WN waves (two per
+// SIMD, so one wave's MFMAs run while the other waits on its LDS operand reads); each wave owns
+// a (256/WM) x (BN/WN) block of v_mfma_f32_32x32x16_bf16 accumulators (A operand: weight rows,
+// B operand: target rows, both K-contiguous).  d advances 64 columns per stage through two
+// LDS buffers; the global loads run two stages ahead in two register sets.  Loads are buffer
+// loads over the workgroup's own weight and target slabs, so rows past V or T read as zeros
+// with no load under a branch.  The epilogue writes the same per-(target row, vocabulary
+// block) partials as the streaming kernel, with 256-row blocks.  Jobs (vocabulary block,
+// target block) are dealt to the 8 XCDs in contiguous runs, target block fastest, so the
+// workgroups resident on one XCD share weight slabs in L2.
+constexpr int kLgRows = 256;                 // vocabulary rows per workgroup
+constexpr int kLgBK = 64;                    // columns of d per stage
+constexpr int kLgPitch = kLgBK + 8;          // LDS row pitch (elements): conflict-free 16-byte reads
+constexpr int kXcds = 8;                     // MI355X hands workgroups to its 8 XCDs round-robin
+
+template <int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void lm_head_gemm_kernel(const LmParams p, int ntb, int jobs) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int RM = kLgRows / WM, RN = BN / WN;     // rows of a wave's block
+  constexpr int NI = RM / 32, NJ = RN / 32;          // 32-row blocks per wave
+  constexpr int PA = kLgRows * kLgBK / 8 / NT;       // 16-byte pieces per thread and stage
+  constexpr int PB = BN * kLgBK / 8 / NT;
+  static_assert(NI >= 1 && NJ >= 1 && PA >= 1 && PB >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kLgRows * kLgPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kLgPitch];
+  __shared__ float em[WM][BN], es[WM][BN];
+  __shared__ int ei[WM][BN];
+  // The accumulators live in the matrix-core register file.
+  asm volatile("" ::: "a0");
+
+  const int per = (jobs + kXcds - 1) / kXcds;
+  const int job = static_cast<int>(blockIdx.x % kXcds) * per + static_cast<int>(blockIdx.x / kXcds);
+  if (job >= jobs) return;
+  const int vb = job / ntb, tb = job % ntb;
+  const int row0 = vb * kLgRows, col0 = tb * BN;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w % WM, wn = w / WM, l32 = lane & 31, half = lane >> 5;
+
+  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.w + static_cast<size_t>(row0) * p.d), 0,
+      min(kLgRows, p.V - row0) * p.d * 2, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.x + static_cast<size_t>(col0) * p.d), 0,
+      min(BN, p.T - col0) * p.d * 2, kBufferRsrcWord3);
+  const int nk = p.d / kLgBK;
+  // piece q = tid + NT i: row q / 8, 16-byte chunk q % 8 of the stage's 64 columns.  The two
+  // requests past the last stage re-read it (never used), so the loads carry no condition.
+  auto gload = [&](int s, u32x4 (&ra)[PA], u32x4 (&rb)[PB]) {
+    const int k0 = min(s, nk - 1) * kLgBK;
+#pragma unroll
+    for (int i = 0; i < PA; ++i) {
+      const int q = tid + i * NT;
+      const int off = ((q >> 3) * p.d + k0 + (q & 7) * 8) * 2;
+      ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, off, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int q = tid + i * NT;
+      const int off = ((q >> 3) * p.d + k0 + (q & 7) * 8) * 2;
+      rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, 0));
+    }
+  };
+  auto swrite = [&](int buf, const u32x4 (&ra)[PA], const u32x4 (&rb)[PB]) {
+#pragma unroll
+    for (int i = 0; i < PA; ++i) {
+      const int q = tid + i * NT;
+      *reinterpret_cast<u32x4*>(&As[buf][(q >> 3) * kLgPitch + (q & 7) * 8]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int q = tid + i * NT;
+      *reinterpret_cast<u32x4*>(&Bs[buf][(q >> 3) * kLgPitch + (q & 7) * 8]) = rb[i];
+    }
+  };
+  f32x16 acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  // Operands of one 16-column k-step: lane (row l32, column group half) reads 8 consecutive
+  // columns of its weight row (A) and of its target row (B).
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < kLgBK / 16; ++ks) {
+      bf16x8 a[NI], b[NJ];
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(RM * wm + 32 * i + l32) * kLgPitch + ks * 16 + half * 8]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        b[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(RN * wn + 32 * j + l32) * kLgPitch + ks * 16 + half * 8]);
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // Stage s computes from LDS buffer s & 1.  Registers: set 0 holds stage s + 2 (requested at
+  // the top of the iteration), set 1 stage s + 1 (arrived), stored once buffer 1 is free.
+  u32x4 ra0[PA], rb0[PB], ra1[PA], rb1[PB];
+  gload(0, ra0, rb0);
+  gload(1, ra1, rb1);
+  swrite(0, ra0, rb0);
+  __syncthreads();
+  for (int s = 0; s < nk; s += 2) {  // nk is even (d % 128 == 0)
+    gload(s + 2, ra0, rb0);
+    compute(0);
+    swrite(1, ra1, rb1);
+    __syncthreads();
+    gload(s + 3, ra1, rb1);
+    compute(1);
+    swrite(0, ra0, rb0);
+    __syncthreads();
+  }
+
+  // Epilogue.  acc[i][j][v]: vocabulary row row0 + RM wm + 32 i + 8 (v / 4) + 4 half + v % 4,
+  // target row col0 + RN wn + 32 j + l32; lanes l and l ^ 32 hold the two row halves.
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = row0 + RM * wm + 32 * i + 8 * (v >> 2) + 4 * half + (v & 3);
+        const float val = r < p.V ? acc[i][j][v] : -INFINITY;
+        if (kv_better(val, r, bv, bi)) {
+          bv = val;
+          bi = r;
+        }
+      }
+    {
+      const LanePair tv = swap32(__float_as_uint(bv)), ti = swap32(static_cast<uint32_t>(bi));
+      bv = __uint_as_float(tv.a);
+      bi = static_cast<int>(ti.a);
+      if (kv_better(__uint_as_float(tv.b), static_cast<int>(ti.b), bv, bi)) {
+        bv = __uint_as_float(tv.b);
+        bi = static_cast<int>(ti.b);
+      }
+    }
+    float sm = 0.f;
+    if (bv != -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = row0 + RM * wm + 32 * i + 8 * (v >> 2) + 4 * half + (v & 3);
+          sm += r < p.V ? expf(acc[i][j][v] - bv) : 0.f;
+        }
+    }
+    {
+      const LanePair t2 = swap32(__float_as_uint(sm));
+      sm = __uint_as_float(t2.a) + __uint_as_float(t2.b);
+    }
+    if (half == 0) {
+      const int c = RN * wn + 32 * j + l32;
+      em[wm][c] = bv;
+      ei[wm][c] = bi;
+      es[wm][c] = sm;
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < BN; c += NT) {
+    const int tok = col0 + c;
+    if (tok >= p.T) break;
+    float m = em[0][c], l = es[0][c], bv = em[0][c];
+    int bi = ei[0][c];
+#pragma unroll
+    for (int q = 1; q < WM; ++q) {
+      if (kv_better(em[q][c], ei[q][c], bv, bi)) {
+        bv = em[q][c];
+        bi = ei[q][c];
+      }
+      ml_merge(m, l, em[q][c], es[q][c]);
+    }
+    const size_t o = static_cast<size_t>(tok) * p.nrb + vb;
+    p.pm[o] = m;
+    p.pl[o] = l;
+    p.pidx[o] = bi;
+  }
+}
+
 // One workgroup per target row: argmax (lowest id on ties) and LSE from the block partials.
 __global__ __launch_bounds__(kLmMergeThreads) void lm_head_merge_kernel(const LmParams p) {
   __shared__ float sv[kLmMergeThreads / 64], sm[kLmMergeThreads / 64], sl[kLmMergeThreads / 64];
@@ -261,6 +480,8 @@ __global__ __launch_bounds__(kLmMergeThreads) void lm_head_merge_kernel(const Lm
 
 struct LmPlan {
   int nrb = 1, nct = 1, ncols = 16, ngrp = 1, u = 1;
+  int gemm_bn = 0;  // > 0: the tiled kernel with this many target rows per workgroup
+  int ntb = 0, jobs = 0;
   size_t ws_bytes = 0;
 };
 
@@ -273,8 +494,41 @@ struct LmPlan {
 constexpr int kLmNct[] = {1, 2, 3, 4, 5, 6, 7, 8};
 constexpr int kLmMaxNct = 8;
 
+// Tiled-kernel choices, from a sweep over T = 130..4160 (d = 4096 and 8192): 8 waves (two per
+// SIMD) beat 4 waves with one per SIMD by 10-20%, 4 x 2 wave grids beat 2 x 4 by up to 7%, and
+// 256-row target tiles only pay once the 128-row tiles' extra weight re-reads outweigh the
+// padding of the last tile (equal at 2080 rows, 1.5% ahead at 4160).
+#ifndef MV_LG256_WM
+#define MV_LG256_WM 4  // wave grid of the tiled kernel: 4 x 2 waves for 256 target rows
+#define MV_LG256_WN 2
+#endif
+#ifndef MV_LG128_WM
+#define MV_LG128_WM 4  // ... and for 128
+#define MV_LG128_WN 2
+#endif
+#ifndef MV_LM_GEMM_MIN_T
+#define MV_LM_GEMM_MIN_T 129  // target rows from which the tiled kernel runs
+#endif
+#ifndef MV_LM_GEMM_BN256_MIN_T
+#define MV_LM_GEMM_BN256_MIN_T 2049  // ... and from which it takes 256 target rows per workgroup
+#endif
+
 LmPlan plan_lm(int T, int d, int V) {
   LmPlan a;
+  // (the tiled kernel's buffer ranges cover 256 rows x d bf16, so d stays far below 2^22)
+  if (T >= MV_LM_GEMM_MIN_T && d % (2 * kLgBK) == 0 && d <= (1 << 20)) {
+    a.gemm_bn = T >= MV_LM_GEMM_BN256_MIN_T ? 256 : 128;
+    a.nrb = ceil_div(V, kLgRows);
+    a.ntb = ceil_div(T, a.gemm_bn);
+    a.jobs = a.nrb * a.ntb;
+    Carver c(nullptr);
+    const size_t np = static_cast<size_t>(T) * a.nrb;
+    c.take<float>(np);
+    c.take<float>(np);
+    c.take<int>(np);
+    a.ws_bytes = c.bytes();
+    return a;
+  }
   a.nrb = ceil_div(V, kLmRows);
   const int need = ceil_div(std::min(T, 16 * kLmMaxNct), 16);
   for (int n : kLmNct)
@@ -334,10 +588,20 @@ MV_API int mv_lm_head_argmax(int dt, int T, int d, int V, const void* x, const v
   p.maxv = max_logit;
   p.lse = lse;
   hipStream_t st = as_stream(stream);
+  if (a.gemm_bn > 0) {
+    const int grid = ceil_div(a.jobs, kXcds) * kXcds;
+    if (a.gemm_bn == 256)
+      lm_head_gemm_kernel<256, MV_LG256_WM, MV_LG256_WN><<<grid, MV_LG256_WM * MV_LG256_WN * 64, 0, st>>>(p, a.ntb, a.jobs);
+    else
+      lm_head_gemm_kernel<128, MV_LG128_WM, MV_LG128_WN><<<grid, MV_LG128_WM * MV_LG128_WN * 64, 0, st>>>(p, a.ntb, a.jobs);
+    MV_TRY(launch_status());
+    lm_head_merge_kernel<<<T, kLmMergeThreads, 0, st>>>(p);
+    return launch_status();
+  }
   const dim3 grid(a.nrb, a.ngrp);
   bool launched = false;
 #define MV_LM_CASE(NCT_, U_) \
-  if (!launched && a.nct == NCT_ && a.u == U_) { lm_head_kernel<NCT_, U_><<<grid, kLmThreads, 0, st>>>(p); launched = true; }
+  if (!launched && a.nct == NCT_ && a.u == U_) { lm_head_kernel<NCT_, U_, false><<<grid, kLmThreads, 0, st>>>(p); launched = true; }
   MV_LM_CASE(1, 4) MV_LM_CASE(2, 4) MV_LM_CASE(3, 4) MV_LM_CASE(4, 4)
   MV_LM_CASE(5, 4) MV_LM_CASE(6, 4) MV_LM_CASE(7, 4) MV_LM_CASE(8, 4)
   MV_LM_CASE(1, 2) MV_LM_CASE(2, 2) MV_LM_CASE(3, 2) MV_LM_CASE(4, 2)
@@ -352,3 +616,35 @@ MV_API int mv_lm_head_argmax(int dt, int T, int d, int V, const void* x, const v
 }
 
 }  // extern "C"
+
+namespace mv {
+
+// Probability rows exp(W x - LSE) of T gathered target rows (one streaming pass over W per
+// group of up to 128 rows): the terminal rows of speculative acceptance from the LM head.
+int lm_head_prob_rows(int T, int d, int V, const uint16_t* x, const int* xrow, int xrow_stride,
+                      int xrow_mul, const float* lse_in, const uint16_t* w, float* rows_out,
+                      hipStream_t st) {
+  if (T < 1 || V < 1 || d < 32 || d % 32 != 0) return MV_ERR_UNSUPPORTED;
+  LmParams p{};
+  p.T = T; p.d = d; p.V = V; p.KT = d / 32; p.nrb = ceil_div(V, kLmRows);
+  p.x = x; p.w = w;
+  p.xrow = xrow; p.xrow_stride = xrow_stride; p.xrow_mul = xrow_mul;
+  p.lse_in = lse_in; p.rows_out = rows_out;
+  const int nct = ceil_div(std::min(T, 16 * kLmMaxNct), 16);
+  const int u = p.KT % 4 == 0 ? 4 : (p.KT % 2 == 0 ? 2 : 1);
+  const dim3 grid(p.nrb, ceil_div(T, 16 * nct));
+  bool launched = false;
+#define MV_LMR_CASE(NCT_, U_) \
+  if (!launched && nct == NCT_ && u == U_) { lm_head_kernel<NCT_, U_, true><<<grid, kLmThreads, 0, st>>>(p); launched = true; }
+  MV_LMR_CASE(1, 4) MV_LMR_CASE(2, 4) MV_LMR_CASE(3, 4) MV_LMR_CASE(4, 4)
+  MV_LMR_CASE(5, 4) MV_LMR_CASE(6, 4) MV_LMR_CASE(7, 4) MV_LMR_CASE(8, 4)
+  MV_LMR_CASE(1, 2) MV_LMR_CASE(2, 2) MV_LMR_CASE(3, 2) MV_LMR_CASE(4, 2)
+  MV_LMR_CASE(5, 2) MV_LMR_CASE(6, 2) MV_LMR_CASE(7, 2) MV_LMR_CASE(8, 2)
+  MV_LMR_CASE(1, 1) MV_LMR_CASE(2, 1) MV_LMR_CASE(3, 1) MV_LMR_CASE(4, 1)
+  MV_LMR_CASE(5, 1) MV_LMR_CASE(6, 1) MV_LMR_CASE(7, 1) MV_LMR_CASE(8, 1)
+#undef MV_LMR_CASE
+  if (!launched) return MV_ERR_UNSUPPORTED;
+  return launch_status();
+}
+
+}  // namespace mv

@@ -45,6 +45,12 @@ inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 inline int ceil_div(long long a, long long b) { return static_cast<int>((a + b - 1) / b); }
 
+// Internal (lmhead.hip): rows_out[t][v] = exp(W[v] . x[row(t)] - lse_in[row(t)]) for T target
+// rows, row(t) = t * xrow_mul + xrow[t * xrow_stride] (xrow null: t); bf16 x and W, d % 32 == 0.
+int lm_head_prob_rows(int T, int d, int V, const uint16_t* x, const int* xrow, int xrow_stride,
+                      int xrow_mul, const float* lse_in, const uint16_t* w, float* rows_out,
+                      hipStream_t st);
+
 }  // namespace mv
 
 #define MV_TRY(expr)            \

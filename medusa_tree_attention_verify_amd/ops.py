@@ -162,8 +162,10 @@ def medusa_heads(h: torch.Tensor, w_res: torch.Tensor, w_head: torch.Tensor,
 
 def topk_rows(x: torch.Tensor, s: int, R: Optional[int] = None, V: Optional[int] = None,
               ldx: Optional[int] = None, ids: Optional[torch.Tensor] = None,
-              vals: Optional[torch.Tensor] = None, ld_out: Optional[int] = None):
-    """Top-s of R rows of x (row r at r*ldx elements).  Defaults: x is [R, V] contiguous."""
+              vals: Optional[torch.Tensor] = None, ld_out: Optional[int] = None,
+              lse: Optional[torch.Tensor] = None):
+    """Top-s of R rows of x (row r at r*ldx elements), and each row's log-sum-exp into ``lse``
+    (fp32 [R]) when given.  Defaults: x is [R, V] contiguous."""
     dt = _dt(x)
     if R is None or V is None:
         R, V = x.shape[-2], x.shape[-1]
@@ -173,7 +175,8 @@ def topk_rows(x: torch.Tensor, s: int, R: Optional[int] = None, V: Optional[int]
         vals = torch.empty((R, s), dtype=torch.float32, device=x.device) if vals is None else vals
         ld_out = s
     L.check("mv_topk_rows", L.lib().mv_topk_rows(dt, R, V, s, _ptr(x), int(ldx), _ptr(ids),
-                                                 _ptr(vals), int(ld_out or s), _stream()))
+                                                 _ptr(vals), int(ld_out or s), _ptr(lse),
+                                                 _stream()))
     return ids, vals
 
 

@@ -68,9 +68,12 @@ class VerifyStep:
         self.tokens_given = tokens_given  # node tokens come with the inputs (no heads)
         # target from the LM head (hidden width target_head): inputs x_t [B, N+1, d] and
         # w_lm [V, d].  Greedy: its argmax ids feed greedy acceptance.  Speculative: its LSE per
-        # row and the heads' own logits (the draft of each depth) feed the speculative rule;
-        # no [B, N+1, V] tensor is made either way
+        # row and the draft logits of each depth feed the speculative rule; the draft rows are
+        # the heads' own logits, or without heads an input draft_logits [B, D, V] (a separate
+        # draft's per-depth logits), whose top candidates then build the tree.  No
+        # [B, N+1, V] tensor is made either way
         self.target_head = target_head
+        self.draft_input = bool(target_head) and accept == "speculative" and heads is None
         dev = torch.device(device)
         self.device = dev
         if self.dynamic:
@@ -109,16 +112,21 @@ class VerifyStep:
         if target_head:
             if accept not in ("greedy", "speculative") or dtype != torch.bfloat16:
                 raise ValueError("the target LM head feeds bf16 greedy or speculative acceptance")
-            if accept == "speculative" and (heads is None or lm_width or dynamic_nodes):
-                raise ValueError("speculative acceptance from the LM head takes its draft from "
-                                 "the Medusa heads (one head per depth)")
+            if accept == "speculative" and (lm_width or dynamic_nodes or tokens_given or
+                                            (heads is not None and heads["K"] != self.D)):
+                raise ValueError("speculative acceptance from the LM head takes its draft and "
+                                 "candidates from per-depth logits: the Medusa heads (one head "
+                                 "per depth) or an input draft_logits [B, D, V]")
             self.ws_lm = ops.Workspace(dev)
             self.ws_lm.get(ops.lm_head_workspace_bytes(B * (N + 1), target_head, V))
             self.target_ids = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
             self.target_lse = torch.empty((B, N + 1), dtype=torch.float32, device=dev)
-            if accept == "speculative":  # the heads' logits: draft row of depth k = head k
+            if accept == "speculative" and heads is not None:
+                # the heads' logits: draft row of depth k = head k
                 self.draft_logits = torch.empty((B, heads["K"], heads["V"]), dtype=dtype,
                                                 device=dev)
+            elif accept == "speculative":  # LSE of each input draft row
+                self.head_lse = torch.empty((B, self.D), dtype=torch.float32, device=dev)
         if commit and accept == "none":
             raise ValueError("the commit needs an acceptance rule")
         self.commit = commit
@@ -146,8 +154,9 @@ class VerifyStep:
     def bind(self, inp: Dict[str, torch.Tensor], branch_stream=None) -> Dict[str, Callable[[], None]]:
         """Pre-marshalled calls of one step on ``inp`` (device tensors: h, w_res, w_head when
         the step has heads; q, k_cache, v_cache, prefix_len; target (+ draft, uniforms);
-        node_tokens when the tokens are given; x_t, w_lm with the target LM head).  Each callable
-        raises on a non-zero status.
+        node_tokens when the tokens are given; x_t, w_lm with the target LM head, and
+        draft_logits [B, D, V] for its speculative rule without heads).  Each callable raises
+        on a non-zero status.
 
         With ``branch_stream`` (a torch stream) the attention branch (its own mask build, then
         the attention) is enqueued there, everything else on the current stream."""
@@ -188,7 +197,7 @@ class VerifyStep:
                 tgt = inp["target"]
                 R1, Vt = tgt.shape[1], tgt.shape[2]
                 lm = wrap("mv_topk_rows", lib.mv_topk_rows, self.dt, B, Vt, self.lm_width, _p(tgt),
-                          R1 * Vt, self.cand.data_ptr(), self.cand_vals.data_ptr(), ld, st)
+                          R1 * Vt, self.cand.data_ptr(), self.cand_vals.data_ptr(), ld, None, st)
 
                 def both():
                     lm()
@@ -196,6 +205,11 @@ class VerifyStep:
                 calls["heads_projection"] = both
             else:
                 calls["heads_projection"] = proj
+        if self.draft_input:
+            dl = inp["draft_logits"]
+            calls["heads_select"] = wrap("mv_topk_rows", lib.mv_topk_rows, self.dt, B * D, self.V,
+                                         s_max, _p(dl), self.V, _p(self.cand),
+                                         _p(self.cand_vals), s_max, _p(self.head_lse), st)
         if self.tokens_given:
             calls["tree"] = wrap("mv_build_tree_mask", lib.mv_build_tree_mask, N, _p(self.parents),
                                  0, 0, 0, None, None, _p(self.tree["anc_mask"]),
@@ -241,7 +255,9 @@ class VerifyStep:
             calls["accept"] = wrap("mv_accept_speculative_lm", lib.mv_accept_speculative_lm,
                                    self.dt, B, N, self.V, self.target_head, D, _p(self.parents),
                                    0, _p(tokens), _p(inp["x_t"]), _p(inp["w_lm"]),
-                                   _p(self.target_lse), _p(self.draft_logits), _p(self.head_lse),
+                                   _p(self.target_lse),
+                                   _p(inp["draft_logits"] if self.draft_input else self.draft_logits),
+                                   _p(self.head_lse),
                                    _p(inp["uniforms"]), _p(a["accept_len"]), _p(a["path_nodes"]),
                                    _p(a["out_tokens"]), _p(a["node_accept"]), _p(a["alpha"]),
                                    _p(self.status), wsp, wsn, st)

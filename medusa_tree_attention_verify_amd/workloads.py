@@ -172,6 +172,12 @@ WORKLOADS: Dict[str, Workload] = {
                    parents=_T4321, prefix=(4096, 4096), depth_widths=(4, 3, 2, 1),
                    d=4096, V=32000, K=4, head_widths=(4, 3, 2, 1), weight_std=0.02,
                    accept="speculative", accept_V=32000, target_head=True),
+    # the batched serving step driven by the target LM head: 64 sequences x 65 verify rows
+    # through W_lm [128256, 4096]; the draft of depth k is a separate draft's logits row
+    # [B, D, V] (no Medusa heads at this batch), whose top candidates also build the tree
+    "c10": Workload(name="spec-serving-b64-lmhead", dtype="bf16", B=64, Hq=32, Hkv=8, dh=128,
+                    parents=_T4321, prefix=(512, 8192), depth_widths=(4, 3, 2, 1), d=4096,
+                    accept="speculative", accept_V=128256, target_head=True),
 }
 
 
@@ -286,6 +292,12 @@ def gen_target_head(w: Workload, seed: int) -> Dict[str, np.ndarray]:
     W_lm [accept_V, d] ~ N(0, 1/d) (rows of norm ~1), both rounded to bf16."""
     return {"x_t": normal(seed, "x_t", (w.B, w.N + 1, w.d), 1.0, True),
             "w_lm": normal(seed, "w_lm", (w.accept_V, w.d), 1.0 / np.sqrt(w.d), True)}
+
+
+def gen_draft_logits(w: Workload, seed: int) -> np.ndarray:
+    """A draft's logits for depths 1..D of every sequence, [B, D, accept_V] ~ N(0, 1) rounded
+    to bf16 (the draft distribution of depth k is the softmax of row k)."""
+    return normal(seed, "draft_logits", (w.B, w.D, w.accept_V), 1.0, True)
 
 
 def gen_uniforms(w: Workload, seed: int) -> np.ndarray:

@@ -64,6 +64,9 @@ def test_workspace_queries():
             == lib.mv_accept_paths_workspace(L.MV_ACCEPT_SPECULATIVE, 64, 64, 128256))
     assert lib.mv_accept_paths_workspace(3, 64, 64, 128256) == 0
     assert lib.mv_lm_head_workspace(L.MV_BF16, 65, 4096, 32000) >= 65 * 500 * 12  # 3 x [T][V/64]
+    # from 129 rows (d % 128 == 0) the tiled kernel keeps partials per 256-row vocabulary block
+    assert 520 * 125 * 12 <= lib.mv_lm_head_workspace(L.MV_BF16, 520, 4096, 32000) < 520 * 500 * 12
+    assert lib.mv_lm_head_workspace(L.MV_BF16, 520, 4064, 32000) >= 520 * 500 * 12  # d % 128 != 0
     assert lib.mv_lm_head_workspace(L.MV_F32, 65, 4096, 32000) == 0               # bf16 only
     assert lib.mv_lm_head_workspace(L.MV_BF16, 65, 4080, 32000) == 0              # d % 32
 
@@ -102,8 +105,8 @@ def test_host_argument_checks():
     assert lib.mv_medusa_heads_noalloc(L.MV_BF16, 1, 64, 100, 1, big, 17, None, None, None, None,
                                        None, None, None, 0, None, None) == L.MV_ERR_UNSUPPORTED
     # top-k rows
-    assert lib.mv_topk_rows(L.MV_F32, 1, 10, 11, P, 10, P, None, 11, None) == L.MV_ERR_UNSUPPORTED
-    assert lib.mv_topk_rows(L.MV_F32, 1, 10, 2, P, 9, P, None, 2, None) == L.MV_ERR_INVALID_ARG
+    assert lib.mv_topk_rows(L.MV_F32, 1, 10, 11, P, 10, P, None, 11, None, None) == L.MV_ERR_UNSUPPORTED
+    assert lib.mv_topk_rows(L.MV_F32, 1, 10, 2, P, 9, P, None, 2, None, None) == L.MV_ERR_INVALID_ARG
     # tree
     assert lib.mv_build_tree_mask(0, P, 0, 0, 0, None, None, P, None, None, None, None) == L.MV_ERR_INVALID_ARG
     assert lib.mv_build_tree_mask(257, P, 0, 0, 0, None, None, P, None, None, None, None) == L.MV_ERR_UNSUPPORTED
@@ -144,7 +147,8 @@ def test_host_argument_checks():
         ddt, 1, 4, 100, d, 2, kw.get("par", P), 0, P, P, P, P, P, P, P, P, P, P, None, None, None,
         kw.get("ws", P), kw.get("wsn", 1 << 20), None)
     assert lm(7, 64) == L.MV_ERR_INVALID_ARG                   # draft dtype
-    assert lm(L.MV_F32, 60) == L.MV_ERR_UNSUPPORTED            # d % 8
+    assert lm(L.MV_F32, 60) == L.MV_ERR_UNSUPPORTED            # d % 32
+    assert lm(L.MV_F32, 40) == L.MV_ERR_UNSUPPORTED
     assert lm(L.MV_F32, 64, par=None) == L.MV_ERR_INVALID_ARG
     assert lm(L.MV_F32, 64, ws=None, wsn=0) == L.MV_ERR_WORKSPACE
     assert lib.mv_accept_speculative_lm_workspace(64, 64, 128256) > 64 * 128256 * 8

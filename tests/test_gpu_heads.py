@@ -141,18 +141,22 @@ def test_split_calls_match_fused_and_repeat():
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_topk_rows_ties_and_strides(dtype):
+@pytest.mark.parametrize("V,s", [(3001, 5), (3000, 4), (3000, 12)])  # scalar / 16-byte loads
+def test_topk_rows_ties_and_strides(dtype, V, s):
     require_gpu()
-    rng = np.random.default_rng(5)
-    R, V, s = 6, 3001, 5
+    rng = np.random.default_rng(5 + V + s)
+    R = 6
     x = rng.integers(-4, 5, size=(R, V)).astype(np.float32)   # many exact ties
     xt = dev(x, dtype)
-    ids, vals = ops.topk_rows(xt, s)
+    lse = torch.full((R,), float("nan"), dtype=torch.float32, device="cuda")
+    ids, vals = ops.topk_rows(xt, s, lse=lse)
     torch.cuda.synchronize()
     for r in range(R):
         ref = O.topk_rows(x[r], s)
         np.testing.assert_array_equal(host(ids)[r], ref["ids"])
         np.testing.assert_array_equal(host(vals)[r], ref["vals"])
+    # each row's log-sum-exp: the oracle's LM head with an identity weight has the rows as logits
+    assert_fp32(host(lse), O.lm_head_argmax(x, np.eye(V))["lse"], atol=1e-4, what="row lse")
     # strided rows: every other row of a [2R, V] matrix, written with an output stride
     x2 = np.repeat(x, 2, axis=0)
     x2[1::2] = -100

@@ -36,9 +36,13 @@ def _check_ids(got, z, rows=None):
 
 
 @pytest.mark.parametrize("T,d,V", [(1, 256, 1000), (5, 256, 999), (33, 512, 777),
-                                   (128, 256, 1500), (129, 512, 999), (130, 256, 1500),
-                                   (300, 256, 1500), (65, 1024, 5000),
-                                   (17, 96, 500), (40, 192, 777)])   # 3 and 6 k-steps: batches of 1 and 2
+                                   (128, 256, 1500), (65, 1024, 5000),
+                                   (17, 96, 500), (40, 192, 777),   # 3 and 6 k-steps: batches of 1 and 2
+                                   # from 129 rows the tiled kernel (128 target rows per tile; 256 from
+                                   # 2049): ragged target and vocabulary tiles, 2 and 6 stages of d
+                                   (129, 512, 999), (130, 256, 1500), (300, 256, 1500),
+                                   (2100, 128, 300), (1100, 256, 999), (200, 384, 2000),
+                                   (150, 160, 500)])   # d % 128 != 0: streaming kernel in groups of 128
 def test_lm_head_small_shapes(T, d, V):
     require_gpu()
     print(f"lm head T={T} d={d} V={V}", flush=True)
@@ -66,19 +70,21 @@ def test_lm_head_llama8b_shape():
     assert_fp32(host(got["lse"]), ref["lse"], atol=1e-3, what="lse")
 
 
-@pytest.mark.parametrize("B", [8, 64])
-def test_lm_head_batched_verify_rows_sampled(B):
-    """A batch of verify steps (B x 65 rows: T = 520 and 4160 take the tiled-GEMM kernel),
-    d = 4096, V = 32000: the GPU computes every row, the oracle recomputes 16 sampled rows
-    spread over the 128-row tiles, including the last (ragged) one."""
+@pytest.mark.parametrize("B,d,V", [(8, 4096, 32000), (8, 8192, 32000), (64, 4096, 32000),
+                                   (64, 4096, 128256)])
+def test_lm_head_batched_verify_rows_sampled(B, d, V):
+    """A batch of verify steps (B x 65 rows: T = 520 takes the tiled kernel with 128-row target
+    tiles, T = 4160 with 256-row tiles), up to the 64-sequence serving batch over the Llama-3
+    vocabulary and the 70B share's d = 8192: the GPU computes every row, the oracle recomputes
+    16 sampled rows spread over the tiles, including tile edges and the last (ragged) tile."""
     require_gpu()
     T = B * 65
-    print(f"lm head batched T={T}", flush=True)
-    x, w = _inputs(T, 4096, 32000, 10 + B)
+    print(f"lm head batched T={T} d={d} V={V}", flush=True)
+    x, w = _inputs(T, d, V, 10 + B + d + V)
     got = ops.lm_head_argmax(dev(x, torch.bfloat16), dev(w, torch.bfloat16))
     torch.cuda.synchronize()
     rng = np.random.default_rng(B)
-    rows = sorted(set([0, 127, 128, T - 1] + rng.choice(T, 12, replace=False).tolist()))
+    rows = sorted(set([0, 127, 128, 255, 256, T - 1] + rng.choice(T, 10, replace=False).tolist()))
     ref = O.lm_head_argmax(x[rows], w)
     ids, mx, lse = host(got["ids"]), host(got["max"]), host(got["lse"])
     assert _check_ids(ids, ref["logits"], rows) <= 1

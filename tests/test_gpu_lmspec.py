@@ -124,6 +124,8 @@ def _run(B, V, d, widths, seed, noise, draft_bf16=False):
     (4, 4096, (4, 3, 2, 1), 0.3),     # float4 row passes
     (2, 1000, (2, 2, 2), 2.0),        # mostly rejected: residuals at shallow rows
     (2, 2048, (3, 1, 1, 1, 1), 0.05), # nearly equal distributions: long accepted paths, leaf draws
+    (20, 1000, (4, 3, 2, 1), 0.5),    # terminal rows over two 16-row column tiles
+    (130, 777, (2, 2), 1.0),          # ... and over two groups of 128 rows
 ])
 def test_lmspec_matches_oracle(B, V, widths, noise):
     require_gpu()
@@ -154,62 +156,85 @@ def test_lmspec_bad_token_flags():
     assert int(status.item()) & L.MV_DEV_BAD_TOKEN
 
 
-def _step_check(wl, seed):
-    """The whole step with speculative acceptance from the LM head: heads -> tree -> attention ->
-    LM head (LSE per verify row) -> speculative acceptance with the heads' logits as the draft ->
-    commit.  The step stores the heads' logits in bf16 and takes their LSE from the fp32 logits,
-    so the oracle's draft rows are its fp64 head logits rounded to bf16 (its own softmax), and a
-    node within 1e-3 of its threshold (or an extra token within 1e-3 of a CDF boundary) is a
-    counted near-tie."""
+def _step_check(wl, seed, seqs=None):
+    """The whole step with speculative acceptance from the LM head: candidates -> tree ->
+    attention -> LM head (LSE per verify row) -> speculative acceptance -> commit.
+
+    With Medusa heads the draft of depth k is head k's logits: the step stores them in bf16 and
+    takes their LSE from the fp32 logits, so the oracle's draft rows are its fp64 head logits
+    rounded to bf16 (its own softmax).  Without heads the draft is an input [B, D, V] of bf16
+    logits, which both sides read as given, and the candidates are its rows' top tokens.  A
+    node within 1e-3 of its threshold is a counted near-tie.  ``seqs`` restricts the oracle to
+    those sequences (every sequence is independent of the others)."""
     from medusa_tree_attention_verify_amd.step import VerifyStep
+    from tests.gpu_util import check_topk, assert_fp32
     parents = list(wl.parents)
     N, D = wl.N, wl.D
     bf = torch.bfloat16
-    xh, xa, xt = W.gen_heads(wl, seed), W.gen_attention(wl, seed), W.gen_target_head(wl, seed)
+    seqs = list(range(wl.B)) if seqs is None else list(seqs)
+    xa, xt = W.gen_attention(wl, seed), W.gen_target_head(wl, seed)
     u = W.gen_uniforms(wl, seed)
-    heads = O.medusa_heads(xh["h"], xh["w_res"], xh["w_head"], list(wl.head_widths))
-    cand = [heads["topk_ids"][:, k, :wl.head_widths[k]] for k in range(wl.K)]
-    tree = O.build_tree(parents, cand, list(wl.depth_widths))
-    step = VerifyStep(parents=parents, depth_widths=wl.depth_widths, dtype=bf, B=wl.B, Hq=wl.Hq,
-                      Hkv=wl.Hkv, dh=wl.dh, max_L=int(xa["prefix_len"].max()),
-                      heads={"d": wl.d, "V": wl.V, "K": wl.K, "widths": list(wl.head_widths)},
-                      accept="speculative", V=wl.accept_V, target_head=wl.d, commit=True)
-    inp = {"h": dev(xh["h"], bf), "w_res": dev(xh["w_res"], bf), "w_head": dev(xh["w_head"], bf),
-           "q": dev(xa["q"], bf), "k_cache": dev(xa["k_cache"], bf), "v_cache": dev(xa["v_cache"], bf),
+    inp = {"q": dev(xa["q"], bf), "k_cache": dev(xa["k_cache"], bf), "v_cache": dev(xa["v_cache"], bf),
            "prefix_len": dev_i32(xa["prefix_len"]), "x_t": dev(xt["x_t"], bf),
            "w_lm": dev(xt["w_lm"], bf), "uniforms": dev(u)}
-    print(f"lmspec step {wl.name} d={wl.d} V={wl.V} seed={seed}", flush=True)
+    if wl.has_heads:
+        xh = W.gen_heads(wl, seed)
+        heads = O.medusa_heads(xh["h"][seqs], xh["w_res"], xh["w_head"], list(wl.head_widths))
+        cand = [heads["topk_ids"][:, k, :wl.head_widths[k]] for k in range(wl.K)]
+        draft = W.round_bf16(heads["logits"].astype(np.float32))
+        inp.update(h=dev(xh["h"], bf), w_res=dev(xh["w_res"], bf), w_head=dev(xh["w_head"], bf))
+        hd = {"d": wl.d, "V": wl.V, "K": wl.K, "widths": list(wl.head_widths)}
+    else:
+        dl = W.gen_draft_logits(wl, seed)
+        draft = dl[seqs]
+        cand = [np.stack([O.topk_rows(draft[i, k], wl.depth_widths[k])["ids"]
+                          for i in range(len(seqs))]) for k in range(D)]
+        inp["draft_logits"] = dev(dl, bf)
+        hd = None
+    tree = O.build_tree(parents, cand, list(wl.depth_widths))
+    step = VerifyStep(parents=parents, depth_widths=wl.depth_widths, dtype=bf, B=wl.B, Hq=wl.Hq,
+                      Hkv=wl.Hkv, dh=wl.dh, max_L=int(xa["prefix_len"].max()), heads=hd,
+                      accept="speculative", V=wl.accept_V, target_head=wl.d, commit=True)
+    print(f"lmspec step {wl.name} B={wl.B} d={wl.d} V={wl.accept_V} seed={seed} "
+          f"sequences {len(seqs)}", flush=True)
     step.run(inp)
     torch.cuda.synchronize()
     assert int(step.status.item()) == 0
-    from tests.gpu_util import check_topk, assert_fp32
-    assert check_topk(host(step.cand), heads["logits"], list(wl.head_widths)) == 0
-    np.testing.assert_array_equal(host(step.tree["node_tokens"]), tree["tokens"])
-    lm = O.lm_head_argmax(xt["x_t"].reshape(-1, wl.d), xt["w_lm"])
-    assert_fp32(host(step.target_lse).ravel(), lm["lse"], atol=1e-3, what="target lse")
-    draft = W.round_bf16(heads["logits"].astype(np.float32))
-    ref = O.accept_speculative_lm(xt["x_t"], xt["w_lm"], draft, tree["tokens"], parents, u, D)
-    g = {k: host(v) for k, v in step.acc.items() if v is not None}
+    if wl.has_heads:
+        assert check_topk(host(step.cand)[seqs], heads["logits"], list(wl.head_widths)) == 0
+    else:   # top tokens of the given bf16 rows: exact on both sides
+        for k in range(D):
+            np.testing.assert_array_equal(host(step.cand)[seqs, k, :wl.depth_widths[k]], cand[k])
+    np.testing.assert_array_equal(host(step.tree["node_tokens"])[seqs], tree["tokens"])
+    x_t = xt["x_t"][seqs]
+    lm = O.lm_head_argmax(x_t.reshape(-1, wl.d), xt["w_lm"])
+    assert_fp32(host(step.target_lse)[seqs].ravel(), lm["lse"], atol=1e-3, what="target lse")
+    ref = O.accept_speculative_lm(x_t, xt["w_lm"], draft, tree["tokens"], parents, u[seqs], D)
+    g = {k: host(v)[seqs] for k, v in step.acc.items() if v is not None}
     np.testing.assert_allclose(g["alpha"], ref["alpha"], rtol=0, atol=1e-2)
     ties = 0
-    for b in range(wl.B):
+    for i, b in enumerate(seqs):
         # only nodes whose parent is the prefix or accepted decide anything
-        live = np.array([p < 0 or ref["node_accept"][b][p] for p in parents])
-        if np.any(live & (np.abs(u[b, :N] - ref["alpha"][b]) < 1e-3)):
+        live = np.array([p < 0 or ref["node_accept"][i][p] for p in parents])
+        if np.any(live & (np.abs(u[b, :N] - ref["alpha"][i]) < 1e-3)):
             ties += 1
             continue
-        n = int(ref["accept_len"][b])
-        assert g["accept_len"][b] == n
-        np.testing.assert_array_equal(g["path_nodes"][b], ref["path_nodes"][b])
-        np.testing.assert_array_equal(g["out_tokens"][b][:n], ref["out_tokens"][b][:n])
+        n = int(ref["accept_len"][i])
+        assert g["accept_len"][i] == n
+        np.testing.assert_array_equal(g["path_nodes"][i], ref["path_nodes"][i])
+        np.testing.assert_array_equal(g["out_tokens"][i][:n], ref["out_tokens"][i][:n])
+        # the extra token: the inverse CDF of the residual (or target) row at u[b, N], the same
+        # up to a draw that lands within rounding of a CDF step (counted with the near-ties)
+        if g["out_tokens"][i][n] != ref["out_tokens"][i][n]:
+            ties += 1
     if ties == 0:  # the commit of the oracle's accepted paths (a copy: bit-exact)
-        k2, v2, p2 = O.kv_commit(xa["k_cache"], xa["v_cache"], xa["prefix_len"],
+        k2, v2, p2 = O.kv_commit(xa["k_cache"][seqs], xa["v_cache"][seqs], xa["prefix_len"][seqs],
                                  ref["path_nodes"], ref["accept_len"], N)
-        np.testing.assert_array_equal(host(step.prefix_next), p2)
-        np.testing.assert_array_equal(host(inp["k_cache"]), k2)
-        np.testing.assert_array_equal(host(inp["v_cache"]), v2)
+        np.testing.assert_array_equal(host(step.prefix_next)[seqs], p2)
+        np.testing.assert_array_equal(host(inp["k_cache"])[seqs], k2)
+        np.testing.assert_array_equal(host(inp["v_cache"])[seqs], v2)
     print("accepted lengths", g["accept_len"].tolist(), "near-ties", ties)
-    assert ties <= max(1, wl.B // 4)
+    assert ties <= max(1, len(seqs) // 4)
 
 
 def test_step_lmhead_speculative_small():
@@ -221,3 +246,21 @@ def test_step_lmhead_speculative_small():
 def test_step_lmhead_speculative_llama8b():
     require_gpu()
     _step_check(W.WORKLOADS["c9"], 9)
+
+
+def test_step_lmhead_speculative_draft_input_small():
+    """The batched serving step driven by the LM head, scaled down: 5 sequences (325 verify
+    rows, so the LM head runs its tiled kernel), d = 512, V = 3000, ragged prefixes; the draft
+    is an input of per-depth logits."""
+    require_gpu()
+    wl = W.WORKLOADS["c10"].scaled(B=5, d=512, accept_V=3000, prefix=(300, 900))
+    _step_check(wl, 41)
+
+
+def test_step_lmhead_speculative_serving_b64_sampled():
+    """The full serving step driven by the LM head (64 sequences, W_lm 128256 x 4096, 4160
+    verify rows through the tiled kernel with 256-row target tiles): the GPU runs every
+    sequence, the oracle recomputes 8 of them."""
+    require_gpu()
+    wl = W.WORKLOADS["c10"]
+    _step_check(wl, 10, seqs=[0, 9, 17, 31, 40, 52, 60, 63])
