@@ -257,9 +257,10 @@ def _oracle_step(wl, x, seed, attn_rows=None):
     return t
 
 
-# query-row x key products above which one oracle step is sampled instead of run whole
+# query-row x key products above which one oracle step is sampled instead of run whole, and
+# the products of the sampled attention (whole (sequence, KV head) slices, ~10 s of the oracle)
 ORACLE_FULL_STEP_WORK = 5e7
-ORACLE_SAMPLE_WORK = 1.5e7
+ORACLE_SAMPLE_WORK = 5e8
 
 
 def cpu_baseline(wl, x, seed, budget_s):
@@ -267,9 +268,9 @@ def cpu_baseline(wl, x, seed, budget_s):
 
     Small steps run whole, repeatedly, until ``budget_s`` seconds of oracle work.  Larger ones
     run one step in which every part is whole except the attention, which is computed for the
-    query rows of one (sequence, KV head) slice (at most ORACLE_SAMPLE_WORK row x key
-    products) and scaled to the whole batch by its share of row x key products (the oracle's
-    attention costs one pass over the visible keys per query row)."""
+    query rows of whole (sequence, KV head) slices, longest sequences first, until about
+    ORACLE_SAMPLE_WORK row x key products, and scaled to the whole batch by its share of row x
+    key products (the oracle's attention costs one pass over the visible keys per query row)."""
     model, cores, blas = _host_info()
     N, G = wl.N, wl.Hq // wl.Hkv
     keys = x["prefix_len"].astype(np.int64) + N
@@ -287,17 +288,23 @@ def cpu_baseline(wl, x, seed, budget_s):
                    sample=f"{steps} full oracle step(s) of the same workload (seed {seed}), "
                           f"{t_total:.1f} s, NumPy fp64")
         return res
-    b0 = int(np.argmax(keys))                 # the longest sequence's first KV head
-    nrows = int(min(G * N, max(1, ORACLE_SAMPLE_WORK // int(keys[b0]))))
-    rows = [(b0, h, i) for h in range(G) for i in range(N)][:nrows]
+    rows, sampled, slices = [], 0.0, []
+    for b in np.argsort(-keys, kind="stable"):   # whole slices, longest sequences first
+        for g in range(wl.Hkv):
+            if sampled >= ORACLE_SAMPLE_WORK:
+                break
+            rows += [(int(b), g * G + j, i) for j in range(G) for i in range(N)]
+            sampled += float(keys[b]) * G * N
+            slices.append((int(b), g))
     parts = _oracle_step(wl, x, seed, attn_rows=rows)
-    scale = work / (float(keys[b0]) * nrows)
+    scale = work / sampled
     t_step = parts["heads"] + parts["tree"] + parts["accept_commit"] + parts["attention"] * scale
     res.update(value=1.0 / t_step,
                sample=f"one oracle step (seed {seed}, NumPy fp64) with heads, tree, acceptance "
-                      f"and commit whole and the attention of {nrows} of {wl.B * wl.Hq * N} "
-                      f"query rows (sequence {b0}, KV head 0), scaled x{scale:.1f} by query-row "
-                      f"x key products; measured {sum(parts.values()):.1f} s",
+                      f"and commit whole and the attention of {len(rows)} of {wl.B * wl.Hq * N} "
+                      f"query rows ({len(slices)} whole (sequence, KV head) slices, longest "
+                      f"sequences first), scaled x{scale:.2f} by query-row x key products; "
+                      f"measured {sum(parts.values()):.1f} s",
                parts_s={k: round(v * (scale if k == "attention" else 1.0), 3)
                         for k, v in parts.items()})
     return res

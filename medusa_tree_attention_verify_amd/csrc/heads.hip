@@ -555,9 +555,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_f32_kernel(const GemvParams p) {
 // in registers and a running (max, sum exp(x - max)) pair; then s workgroup-wide arg-bests over
 // the threads' current heads, the owner of each winner popping it.  Rows whose elements are
 // 16-byte aligned are read with 16-byte loads.
-constexpr int kTopkThreads = 1024;
-
-template <bool BF16, int S>
+template <bool BF16, int S, int kTopkThreads>
 __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(int V, int s, const void* x, long long ldx,
                                                         int32_t* ids, float* vals, int ld_out,
                                                         float* lse, int vec) {
@@ -928,13 +926,19 @@ MV_API int mv_topk_rows(int dt, int R, int V, int s, const void* x, long long ld
   hipStream_t st = as_stream(stream);
   const int epv = dt == MV_BF16 ? 8 : 4;
   const int vec = (V % epv == 0 && ldx % epv == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0) ? 1 : 0;
-#define MV_TOPK_CASE(S_)                                                                          \
+  // 1024 threads per row for long rows (the Llama-3 vocabulary: 79 us against 137 us with 256
+  // for 256 rows), 256 for short ones, where the launch and the final arg-bests dominate
+#define MV_TOPK_CASE(S_, NT_)                                                                     \
   if (s <= S_) {                                                                                  \
-    if (dt == MV_BF16) topk_rows_kernel<true, S_><<<R, kTopkThreads, 0, st>>>(V, s, x, ldx, ids, vals, ld_out, lse, vec); \
-    else topk_rows_kernel<false, S_><<<R, kTopkThreads, 0, st>>>(V, s, x, ldx, ids, vals, ld_out, lse, vec); \
+    if (dt == MV_BF16) topk_rows_kernel<true, S_, NT_><<<R, NT_, 0, st>>>(V, s, x, ldx, ids, vals, ld_out, lse, vec); \
+    else topk_rows_kernel<false, S_, NT_><<<R, NT_, 0, st>>>(V, s, x, ldx, ids, vals, ld_out, lse, vec); \
     return launch_status();                                                                       \
   }
-  MV_TOPK_CASE(4) MV_TOPK_CASE(8) MV_TOPK_CASE(16)
+  if (V >= 32768) {
+    MV_TOPK_CASE(4, 1024) MV_TOPK_CASE(8, 1024) MV_TOPK_CASE(16, 1024)
+  } else {
+    MV_TOPK_CASE(4, 256) MV_TOPK_CASE(8, 256) MV_TOPK_CASE(16, 256)
+  }
 #undef MV_TOPK_CASE
   return MV_ERR_UNSUPPORTED;
 }
