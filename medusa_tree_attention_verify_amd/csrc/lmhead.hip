@@ -322,22 +322,49 @@ __global__ __launch_bounds__(WM * WN * 64) void lm_head_gemm_kernel(const LmPara
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   // Operands of one 16-column k-step: lane (row l32, column group half) reads 8 consecutive
-  // columns of its weight row (A) and of its target row (B).
-  auto compute = [&](int buf) {
+  // columns of its weight row (A) and of its target row (B).  The next k-step's operands are
+  // read while this one's MFMAs run (two fragment sets), one LDS read placed after each MFMA
+  // by scheduling groups: 5% over the compiler's own order, which waited on each read just
+  // before its first use.
+  auto ldf = [&](int buf, int ks, bf16x8 (&a)[NI], bf16x8 (&b)[NJ]) {
 #pragma unroll
-    for (int ks = 0; ks < kLgBK / 16; ++ks) {
-      bf16x8 a[NI], b[NJ];
+    for (int i = 0; i < NI; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(RM * wm + 32 * i + l32) * kLgPitch + ks * 16 + half * 8]);
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(RM * wm + 32 * i + l32) * kLgPitch + ks * 16 + half * 8]);
+    for (int j = 0; j < NJ; ++j)
+      b[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(RN * wn + 32 * j + l32) * kLgPitch + ks * 16 + half * 8]);
+  };
+  auto mm = [&](const bf16x8 (&a)[NI], const bf16x8 (&b)[NJ]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(RN * wn + 32 * j + l32) * kLgPitch + ks * 16 + half * 8]);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+  auto interleave = [&]() {  // DS read / MFMA alternation, then the remaining MFMAs
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
+    for (int q = 0; q < NI + NJ; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NI * NJ - (NI + NJ), 0);
+  };
+  static_assert(NI * NJ >= NI + NJ && (kLgBK / 16) % 2 == 0, "interleave shape");
+  auto compute = [&](int buf) {
+    bf16x8 a0[NI], b0[NJ], a1[NI], b1[NJ];
+    ldf(buf, 0, a0, b0);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int ks = 0; ks < kLgBK / 16; ks += 2) {
+      ldf(buf, ks + 1, a1, b1);
+      mm(a0, b0);
+      interleave();
+      if (ks + 2 < kLgBK / 16) {
+        ldf(buf, ks + 2, a0, b0);
+        mm(a1, b1);
+        interleave();
+      } else {
+        mm(a1, b1);
+      }
     }
   };
   // Stage s computes from LDS buffer s & 1.  Registers: set 0 holds stage s + 2 (requested at
