@@ -248,15 +248,21 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const LmParams p) {
 // loads over the workgroup's own weight and target slabs, so rows past V or T read as zeros
 // with no load under a branch.  The epilogue writes the same per-(target row, vocabulary
 // block) partials as the streaming kernel, with 256-row blocks.  Jobs (vocabulary block,
-// target block) are dealt to the 8 XCDs in contiguous runs, target block fastest, so the
-// workgroups resident on one XCD share weight slabs in L2.
+// target block) are dealt to the 8 XCDs in contiguous runs, in an order chosen so that the
+// workgroups resident on one XCD share operand slabs in L2 (below).
 constexpr int kLgRows = 256;                 // vocabulary rows per workgroup
 constexpr int kLgBK = 64;                    // columns of d per stage
 constexpr int kLgPitch = kLgBK + 8;          // LDS row pitch (elements): conflict-free 16-byte reads
 constexpr int kXcds = 8;                     // MI355X hands workgroups to its 8 XCDs round-robin
+// Job order: strips of 8 vocabulary blocks when the target rows' hidden states exceed 24 MB
+// (4160 x 4096: 4195 -> 4046 us, their re-fetches from beyond L2 being the larger stream),
+// else target block fastest (520 x 8192, where the 4 MB weight slabs are the operand worth
+// sharing: 397 us against 439 us with strips of 8).
+constexpr int kLgStrip = 8;
+constexpr size_t kLgStripMinXBytes = 24u << 20;
 
 template <int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) void lm_head_gemm_kernel(const LmParams p, int ntb, int jobs) {
+__global__ __launch_bounds__(WM * WN * 64) void lm_head_gemm_kernel(const LmParams p, int ntb, int jobs, int sv) {
   constexpr int NT = WM * WN * 64;
   constexpr int RM = kLgRows / WM, RN = BN / WN;     // rows of a wave's block
   constexpr int NI = RM / 32, NJ = RN / 32;          // 32-row blocks per wave
@@ -273,7 +279,13 @@ __global__ __launch_bounds__(WM * WN * 64) void lm_head_gemm_kernel(const LmPara
   const int per = (jobs + kXcds - 1) / kXcds;
   const int job = static_cast<int>(blockIdx.x % kXcds) * per + static_cast<int>(blockIdx.x / kXcds);
   if (job >= jobs) return;
-  const int vb = job / ntb, tb = job % ntb;
+  // strips of sv vocabulary blocks x every target block, vocabulary block fastest: with sv = 8
+  // the ~32 workgroups resident on an XCD cover 8 vocabulary x 4 target blocks and share both
+  // slabs; sv = 1 is target block fastest (the weight slab shared, the target slabs streamed)
+  const int nvb = p.nrb;
+  const int strip = job / (sv * ntb), r = job - strip * sv * ntb;
+  const int gv = min(sv, nvb - strip * sv);
+  const int vb = strip * sv + r % gv, tb = r / gv;
   const int row0 = vb * kLgRows, col0 = tb * BN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w % WM, wn = w / WM, l32 = lane & 31, half = lane >> 5;
@@ -617,10 +629,11 @@ MV_API int mv_lm_head_argmax(int dt, int T, int d, int V, const void* x, const v
   hipStream_t st = as_stream(stream);
   if (a.gemm_bn > 0) {
     const int grid = ceil_div(a.jobs, kXcds) * kXcds;
+    const int sv = static_cast<size_t>(T) * d * 2 > kLgStripMinXBytes ? kLgStrip : 1;
     if (a.gemm_bn == 256)
-      lm_head_gemm_kernel<256, MV_LG256_WM, MV_LG256_WN><<<grid, MV_LG256_WM * MV_LG256_WN * 64, 0, st>>>(p, a.ntb, a.jobs);
+      lm_head_gemm_kernel<256, MV_LG256_WM, MV_LG256_WN><<<grid, MV_LG256_WM * MV_LG256_WN * 64, 0, st>>>(p, a.ntb, a.jobs, sv);
     else
-      lm_head_gemm_kernel<128, MV_LG128_WM, MV_LG128_WN><<<grid, MV_LG128_WM * MV_LG128_WN * 64, 0, st>>>(p, a.ntb, a.jobs);
+      lm_head_gemm_kernel<128, MV_LG128_WM, MV_LG128_WN><<<grid, MV_LG128_WM * MV_LG128_WN * 64, 0, st>>>(p, a.ntb, a.jobs, sv);
     MV_TRY(launch_status());
     lm_head_merge_kernel<<<T, kLmMergeThreads, 0, st>>>(p);
     return launch_status();
