@@ -736,7 +736,7 @@ __global__ __launch_bounds__(256) void spec_lm_draft_rows_kernel(const SpecLmPar
   const int k = q.term[b * 4 + 2];  // depth of the terminal = draft row of its children
   q.row_d[static_cast<size_t>(b) * q.V + v] =
       (child && k < q.D)
-          ? static_cast<float>(exp(draft_logit(q, b, k, v) - static_cast<double>(q.dlse[static_cast<size_t>(b) * q.D + k])))
+          ? expf(static_cast<float>(draft_logit(q, b, k, v)) - q.dlse[static_cast<size_t>(b) * q.D + k])
           : 0.f;
 }
 

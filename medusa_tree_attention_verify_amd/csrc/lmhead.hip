@@ -161,13 +161,12 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const LmParams p) {
     for (int ct = 0; ct < NCT; ++ct) {
       const int t = col0 + 16 * ct + c16;
       if (t >= p.T) continue;
-      const double lse = static_cast<double>(p.lse_in[lm_xrow(p, t)]);
+      // exp in fp32: the rows are stored in fp32 (the residual sums over them run in fp64)
+      const float lse = p.lse_in[lm_xrow(p, t)];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int r = row0 + 16 * w + 4 * (lane >> 4) + v;
-        if (r < p.V)
-          p.rows_out[static_cast<size_t>(t) * p.V + r] =
-              static_cast<float>(exp(static_cast<double>(acc[ct][v]) - lse));
+        if (r < p.V) p.rows_out[static_cast<size_t>(t) * p.V + r] = expf(acc[ct][v] - lse);
       }
     }
     return;
