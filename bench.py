@@ -454,9 +454,9 @@ def main():
                     help="time the step replayed as one HIP graph (default) or as eager launches")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
-              "the path shards per sequence / KV head / vocabulary slice, but no multi-GPU "
-              "code is built", file=sys.stderr)
+        print(f"bench.py: this benchmark runs on one GPU only (asked for {args.gpus}); "
+              "the path would shard per sequence / KV head / vocabulary slice, but the library "
+              "has no multi-GPU code", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -65,7 +65,7 @@ typedef enum {
   MV_OK = 0,
   MV_ERR_INVALID_ARG = -1,   /* NULL required pointer, non-positive size, bad enum value */
   MV_ERR_INVALID_TREE = -2,  /* reserved for host-validated tree specs (binding level) */
-  MV_ERR_UNSUPPORTED = -3,   /* a size or dtype this build does not implement (see each call) */
+  MV_ERR_UNSUPPORTED = -3,   /* a size or dtype the library does not implement (see each call) */
   MV_ERR_WORKSPACE = -4,     /* ws is NULL/misaligned or ws_bytes is below the query */
   MV_ERR_HIP = -5            /* a HIP launch or runtime call failed */
 } mv_status;
@@ -88,7 +88,7 @@ typedef enum {
 #define MV_DEV_BAD_TOKEN    0x10 /* a node token is outside [0, V) */
 #define MV_DEV_BAD_PATH     0x20 /* a committed path node outside [j, N), or a length outside [0, D] */
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define MV_MAX_NODES 256   /* N: tree nodes */
 #define MV_MAX_DEPTH 16    /* D: tree depth */
 #define MV_MAX_TOPK  16    /* s: candidates per head / per depth */
