@@ -55,7 +55,16 @@ struct AttnParams {
   float2* part_ml;
   int32_t* status;
   const int32_t* order;  // sequences by decreasing prefix length (null: batch order)
+  // Balanced split of a batch (null: every sequence in chunks of CK keys): plan[3b] = chunks
+  // of sequence b, plan[3b + 1] = its chunk length, plan[3b + 2] = the chunk-job index of its
+  // first chunk; jtab[j] = (b << 16) | chunk for the chunk-jobs j in launch order, kNoJob past
+  // the last.  The partials of chunk-job j then sit at chunk slot j (nchunks = slots per
+  // (sequence, KV head) otherwise, total slots here).
+  const int32_t* plan;
+  const uint32_t* jtab;
 };
+
+constexpr uint32_t kNoJob = 0xffffffffu;
 
 constexpr int kXcds = 8;  // MI355X: workgroups are handed to the 8 XCDs round-robin
 
@@ -73,6 +82,9 @@ __device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool re
 #endif
 #ifndef MV_ATTN_TARGET_WG_BATCH
 #define MV_ATTN_TARGET_WG_BATCH 768  // ... and with several sequences (at most)
+#endif
+#ifndef MV_ATTN_BALANCED
+#define MV_ATTN_BALANCED 1  // batches that split: chunk plan from the actual lengths
 #endif
 #ifndef MV_ATTN_MIN_CHUNK
 #define MV_ATTN_MIN_CHUNK 256   // but never chunks shorter than this many keys
@@ -109,14 +121,26 @@ void tree_attn_bf16_kernel(const AttnParams p) {
   const int job = (pos / p.qtiles) * kXcds + xcd;
   if (job >= p.jobs) return;
   const int g = job % p.Hkv;
-  const int c = (job / p.Hkv) % p.nchunks;
-  const int rank = job / (p.Hkv * p.nchunks);
-  const int b = p.order ? p.order[rank] : rank;
+  int b, c, ncb, ck;
+  if (p.jtab) {
+    const uint32_t e = p.jtab[job / p.Hkv];
+    if (e == kNoJob) return;
+    b = static_cast<int>(e >> 16);
+    c = static_cast<int>(e & 0xffffu);
+    ncb = p.plan[3 * b];
+    ck = p.plan[3 * b + 1];
+  } else {
+    c = (job / p.Hkv) % p.nchunks;
+    const int rank = job / (p.Hkv * p.nchunks);
+    b = p.order ? p.order[rank] : rank;
+    ck = p.CK;
+    ncb = -1;
+  }
 
   const int Lb = clamp_prefix(p, p.prefix_len[b], threadIdx.x == 0 && qt == 0 && c == 0 && g == 0);
-  const int ncb = max(1, (Lb + p.CK - 1) / p.CK);
+  if (ncb < 0) ncb = max(1, (Lb + p.CK - 1) / p.CK);
   if (c >= ncb) return;
-  const int kbeg = c * p.CK, kend = min(Lb, kbeg + p.CK);
+  const int kbeg = c * ck, kend = min(Lb, kbeg + ck);
   const bool last = c == ncb - 1;
   const int ntp = kend > kbeg ? (kend - kbeg + kKT - 1) / kKT : 0;
   const int ntiles = ntp + (last ? (p.N + kKT - 1) / kKT : 0);
@@ -354,8 +378,11 @@ void tree_attn_bf16_kernel(const AttnParams p) {
     // The partial output goes out in the MFMA register order: one 16 KB block per (job, query
     // tile, wave), float4 (db, vq) of lane l at [(db*4 + vq)*64 + l], so every store
     // instruction writes 1 KB of consecutive bytes (the combine reads it in the same order).
-    const size_t rowi = (static_cast<size_t>(b * p.Hq + h) * p.N + node) * p.nchunks + c;
-    const size_t slot = ((static_cast<size_t>(b * p.Hkv + g) * p.nchunks + c) * p.qtiles + qt) * NWV + wv;
+    // chunk slot: per (sequence, KV head) chunk c, or the chunk-job index of a balanced plan
+    const size_t rowi = p.plan ? (static_cast<size_t>(job / p.Hkv) * p.Hq + h) * p.N + node
+                               : (static_cast<size_t>(b * p.Hq + h) * p.N + node) * p.nchunks + c;
+    const size_t slot = p.plan ? ((static_cast<size_t>(job / p.Hkv) * p.Hkv + g) * p.qtiles + qt) * NWV + wv
+                               : ((static_cast<size_t>(b * p.Hkv + g) * p.nchunks + c) * p.qtiles + qt) * NWV + wv;
     float4* po = reinterpret_cast<float4*>(p.part_o) + slot * (DB * 4 * 64) + lane;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -390,13 +417,23 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   const int i = m / p.G, h = g * p.G + m % p.G;
   const int d0 = (dbvq / 4) * 32 + 8 * (dbvq % 4) + 4 * half;
   const int Lb = clamp_prefix(p, p.prefix_len[b], false);
-  const int ncb = max(1, (Lb + p.CK - 1) / p.CK);
+  const int ncb = p.plan ? p.plan[3 * b] : max(1, (Lb + p.CK - 1) / p.CK);
   if (ncb == 1) return;  // the attention kernel wrote this row itself
-  const size_t mlbase = (static_cast<size_t>(b * p.Hq + h) * p.N + i) * p.nchunks;
-  const float4* pbase = reinterpret_cast<const float4*>(p.part_o) +
-                        ((bg * p.nchunks) * p.qtiles + qt) * (static_cast<size_t>(NWV) * SLOT) +
-                        static_cast<size_t>(wv) * SLOT + pos;
-  const size_t cstride = static_cast<size_t>(p.qtiles) * NWV * SLOT;  // float4 per chunk
+  // chunk c of this row: slot (b, g, c) per sequence, or slot j0 + c of a balanced plan
+  size_t mlbase, mlstride, pfirst, cstride;
+  if (p.plan) {
+    const size_t j0 = static_cast<size_t>(p.plan[3 * b + 2]);
+    mlbase = (j0 * p.Hq + h) * p.N + i;
+    mlstride = static_cast<size_t>(p.Hq) * p.N;
+    pfirst = ((j0 * p.Hkv + g) * p.qtiles + qt) * (static_cast<size_t>(NWV) * SLOT);
+    cstride = static_cast<size_t>(p.Hkv) * p.qtiles * NWV * SLOT;
+  } else {
+    mlbase = (static_cast<size_t>(b * p.Hq + h) * p.N + i) * p.nchunks;
+    mlstride = 1;
+    pfirst = ((bg * p.nchunks) * p.qtiles + qt) * (static_cast<size_t>(NWV) * SLOT);
+    cstride = static_cast<size_t>(p.qtiles) * NWV * SLOT;  // float4 per chunk
+  }
+  const float4* pbase = reinterpret_cast<const float4*>(p.part_o) + pfirst + static_cast<size_t>(wv) * SLOT + pos;
   float M = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c0 = 0; c0 < ncb; c0 += CB) {
@@ -405,7 +442,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
       const int c = c0 + u;
-      ml[u] = c < ncb ? p.part_ml[mlbase + c] : make_float2(-INFINITY, 0.f);
+      ml[u] = c < ncb ? p.part_ml[mlbase + c * mlstride] : make_float2(-INFINITY, 0.f);
       po[u] = c < ncb ? pbase[c * cstride] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
@@ -530,23 +567,90 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(const AttnParams p) 
 constexpr int kNWV = kNWVCombine;  // waves per workgroup -> 256 query rows
 
 // Sequences ranked by decreasing (clamped) prefix length, ties by index: order[rank] = b.
+//
+// With `plan` (a batch whose host plan splits the keys): a balanced split from the actual
+// lengths.  The host sizes chunks from the longest prefix only, so with uneven lengths the
+// chunk count rarely fills whole rounds of the chip (8 sequences of 9.6k-29.8k keys gave 528
+// workgroups, two full rounds and 16 in a third).  Here the batch's keys are cut into about
+// c_target chunks of near-equal length Lc: each sequence takes floor(L_b / Lc) chunks (at least
+// 1, at most the host's per-sequence count), the remaining chunks go to the largest remainders,
+// each sequence's chunk length is rounded up to whole key tiles and its count recomputed (so no
+// chunk is empty).  The chunk-jobs are tabled longest sequence first, chunks in order.
 constexpr int kOrderMaxB = 1024;
 
-__global__ __launch_bounds__(kOrderMaxB) void seq_order_kernel(const AttnParams p, int32_t* order) {
+__global__ __launch_bounds__(kOrderMaxB) void seq_order_kernel(const AttnParams p, int32_t* order,
+                                                               int32_t* plan, uint32_t* jtab,
+                                                               int c_target) {
   __shared__ int Ls[kOrderMaxB];
+  __shared__ int ns[kOrderMaxB];
+  __shared__ int rk[kOrderMaxB];
+  __shared__ int shared_lc;
   const int b = threadIdx.x;
   if (b < p.B) Ls[b] = clamp_prefix(p, p.prefix_len[b], false);
   __syncthreads();
-  if (b >= p.B) return;
-  const int Lb = Ls[b];
-  int rank = 0;
-  for (int j = 0; j < p.B; ++j) rank += Ls[j] > Lb || (Ls[j] == Lb && j < b);
-  order[rank] = b;
+  int rank = 0, Lb = 0;
+  if (b < p.B) {
+    Lb = Ls[b];
+    for (int j = 0; j < p.B; ++j) rank += Ls[j] > Lb || (Ls[j] == Lb && j < b);
+    order[rank] = b;
+    rk[b] = rank;
+  }
+  if (!plan) return;
+  if (b == 0) {
+    long long tot = 0;
+    for (int j = 0; j < p.B; ++j) tot += Ls[j];
+    const long long lc = (tot + c_target - 1) / c_target;
+    shared_lc = static_cast<int>(std::max<long long>(MV_ATTN_MIN_CHUNK, std::min<long long>(lc, 1 << 30)));
+  }
+  __syncthreads();
+  const int lc = shared_lc;
+  int n = 0, rem = 0;
+  if (b < p.B) {
+    n = std::max(1, Lb / lc);
+    rem = Lb - n * lc;  // > 0 only where a chunk more could go
+    ns[b] = n;
+  }
+  __syncthreads();
+  int given = 0;
+  for (int j = 0; j < p.B; ++j) given += ns[j];
+  const int deficit = c_target - given;
+  // +1 chunk for the `deficit` largest remainders (ties by index)
+  if (b < p.B && deficit > 0 && rem > 0) {
+    int better = 0;
+    for (int j = 0; j < p.B; ++j) {
+      const int rj = Ls[j] - ns[j] * lc;
+      if (rj > 0 && (rj > rem || (rj == rem && j < b))) ++better;
+    }
+    if (better < deficit) ++n;
+  }
+  int ck = kKT;
+  if (b < p.B) {
+    ck = std::max(kKT, (Lb + n - 1) / n);
+    ck = (ck + kKT - 1) / kKT * kKT;
+    n = Lb > 0 ? (Lb + ck - 1) / ck : 1;
+  }
+  __syncthreads();
+  if (b < p.B) ns[b] = n;
+  __syncthreads();
+  if (b < p.B) {
+    int start = 0;
+    for (int j = 0; j < p.B; ++j) start += rk[j] < rank ? ns[j] : 0;
+    plan[3 * b] = n;
+    plan[3 * b + 1] = ck;
+    plan[3 * b + 2] = start;
+    for (int c = 0; c < n; ++c) jtab[start + c] = (static_cast<uint32_t>(b) << 16) | static_cast<uint32_t>(c);
+  }
+  int total = 0;
+  for (int j = 0; j < p.B; ++j) total += ns[j];
+  // p.nchunks is the total of chunk slots here (c_target + B bounds the chunks)
+  for (int j = total + static_cast<int>(threadIdx.x); j < p.nchunks; j += blockDim.x) jtab[j] = kNoJob;
 }
 
 struct AttnPlan {
   int qtiles = 1, CK = 256, nchunks = 1;
   bool ordered = false;  // a length ordering of the sequences in the workspace
+  bool balanced = false;  // ... and a balanced chunk plan from the actual lengths
+  int c_target = 0;       // chunks the balanced plan aims for (whole batch)
   size_t ws_bytes = 0;
 };
 
@@ -574,11 +678,28 @@ AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L) {
   a.CK = ck;
   a.nchunks = std::max(1, ceil_div(max_L, ck));
   a.ordered = B > 1 && B <= kOrderMaxB;
+#if MV_ATTN_BALANCED
+  a.balanced = a.ordered && a.nchunks > 1;
+#endif
+  if (a.balanced) {
+    // chunks aimed for: the batch's workgroup target (at most the host plan's chunk count);
+    // the at-least-one-chunk rule can add up to one per sequence, so slots = target + B
+    const long long per_chunk = static_cast<long long>(Hkv) * a.qtiles;  // workgroups per chunk
+    a.c_target = static_cast<int>(std::min<long long>(static_cast<long long>(B) * a.nchunks,
+                                                      std::max<long long>(B, target / per_chunk)));
+    a.nchunks = a.c_target + B;  // total chunk slots (partials, job table)
+  }
+  // chunk slots of the partials: per (sequence, KV head) nchunks, or nchunks in total
+  const size_t cslots = a.balanced ? static_cast<size_t>(a.nchunks) : static_cast<size_t>(B) * a.nchunks;
   Carver c(nullptr);
   if (a.ordered) c.take<int32_t>(B);
+  if (a.balanced) {
+    c.take<int32_t>(3 * static_cast<size_t>(B));
+    c.take<uint32_t>(static_cast<size_t>(a.nchunks));
+  }
   if (a.nchunks > 1) {
-    const size_t rows = static_cast<size_t>(B) * Hq * N * a.nchunks;
-    const size_t tile_rows = static_cast<size_t>(B) * Hkv * a.nchunks * a.qtiles * kNWV * 32;
+    const size_t rows = cslots * Hq * N;
+    const size_t tile_rows = cslots * Hkv * a.qtiles * kNWV * 32;
     c.take<float>(tile_rows * dh);  // register-order blocks, padded to whole query tiles
     c.take<float2>(rows);
   }
@@ -636,20 +757,25 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
   }
   Carver c(ws);
   int32_t* order = a.ordered ? c.take<int32_t>(B) : nullptr;
+  int32_t* plan = a.balanced ? c.take<int32_t>(3 * static_cast<size_t>(B)) : nullptr;
+  uint32_t* jtab = a.balanced ? c.take<uint32_t>(static_cast<size_t>(a.nchunks)) : nullptr;
+  const size_t cslots = a.balanced ? static_cast<size_t>(a.nchunks) : static_cast<size_t>(B) * a.nchunks;
   if (a.nchunks > 1) {
-    const size_t rows = static_cast<size_t>(B) * Hq * N * a.nchunks;
-    const size_t tile_rows = static_cast<size_t>(B) * Hkv * a.nchunks * a.qtiles * kNWV * 32;
+    const size_t rows = cslots * Hq * N;
+    const size_t tile_rows = cslots * Hkv * a.qtiles * kNWV * 32;
     p.part_o = c.take<float>(tile_rows * dh);
     p.part_ml = c.take<float2>(rows);
   }
-  const long long jobs = static_cast<long long>(B) * Hkv * a.nchunks;
+  const long long jobs = static_cast<long long>(cslots) * Hkv;
   const long long grid = (jobs + kXcds - 1) / kXcds * kXcds * a.qtiles;
   if (grid > (1LL << 30)) return MV_ERR_UNSUPPORTED;
   p.jobs = static_cast<int>(jobs);
   if (order) {
-    seq_order_kernel<<<1, kOrderMaxB, 0, st>>>(p, order);
+    seq_order_kernel<<<1, kOrderMaxB, 0, st>>>(p, order, plan, jtab, a.c_target);
     MV_TRY(launch_status());
     p.order = order;
+    p.plan = plan;
+    p.jtab = jtab;
   }
   if (dh == 64) tree_attn_bf16_kernel<64, kNWV><<<static_cast<int>(grid), kNWV * 64, 0, st>>>(p);
   else tree_attn_bf16_kernel<128, kNWV><<<static_cast<int>(grid), kNWV * 64, 0, st>>>(p);

@@ -126,6 +126,21 @@ def test_attention_multichunk_ragged():
     _run(wl, 22, [6000, 257, 4096, 1])
 
 
+def test_attention_balanced_split_two_query_tiles():
+    """A split batch with two query tiles per KV head (64/8 heads, 64 nodes) and very uneven
+    prefixes (0 to 12000 keys), so the chunk plan is built on the device from the actual
+    lengths: every output row must be written, sampled rows of every sequence (the first and
+    the deepest node among them) match the oracle."""
+    require_gpu()
+    wl = _bf16(branching_tree((4, 3, 2, 1)), 6, 64, 8, 128, 12000)
+    rng = np.random.default_rng(26)
+    sel = []
+    for b in range(wl.B):
+        sel += [(b, int(rng.integers(wl.Hq)), int(rng.integers(wl.N))) for _ in range(4)]
+        sel += [(b, int(rng.integers(wl.Hq)), 0), (b, int(rng.integers(wl.Hq)), wl.N - 1)]
+    _run(wl, 25, [0, 1, 65, 3000, 9000, 12000], select=sel)
+
+
 def test_attention_llama8b_full():
     """B=1, 32/8 heads, dh 128, prefix 4096, (4,3,2,1) tree: every output row."""
     require_gpu()
