@@ -258,9 +258,10 @@ def _oracle_step(wl, x, seed, attn_rows=None):
 
 
 # query-row x key products above which one oracle step is sampled instead of run whole, and
-# the products of the sampled attention (whole (sequence, KV head) slices, ~10 s of the oracle)
+# the products of the sampled attention (whole (sequence, KV head) slices: the 70B share's whole
+# attention, ~10 s of the oracle on a 16-core host)
 ORACLE_FULL_STEP_WORK = 5e7
-ORACLE_SAMPLE_WORK = 5e8
+ORACLE_SAMPLE_WORK = 1e9
 
 
 def cpu_baseline(wl, x, seed, budget_s):
