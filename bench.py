@@ -447,9 +447,11 @@ def main():
                          "accepted length against the planted closed form")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work timed for cpu_baseline (whole steps, at least one)")
-    ap.add_argument("--fork", default="off", choices=["on", "off"],
+    ap.add_argument("--fork", default="auto", choices=["auto", "on", "off"],
                     help="graph launch: run the attention branch beside the heads (a parallel "
-                         "branch of the graph) or after them")
+                         "branch of the graph) or after them; auto = beside them for steps with "
+                         "Medusa heads over a batch (the 70B share: +3%%; one-sequence steps, "
+                         "whose attention is a short latency-bound call, lose)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="time the step replayed as one HIP graph (default) or as eager launches")
@@ -586,7 +588,7 @@ def main():
     # Pass 2 (the timed region of the metric): the same K steps, each replayed as one graph.
     t_wall = None
     ms = ms_eager
-    fork = args.fork == "on" and step.can_fork()
+    fork = (args.fork == "on" or (args.fork == "auto" and wl.has_heads and wl.B > 1)) and step.can_fork()
     if args.launch == "graph":
         graphs = [step.capture(dict(static, **s_), fork=fork) for s_ in sets]
         for i in range(args.warmup):

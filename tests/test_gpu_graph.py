@@ -19,12 +19,16 @@ def _outputs(step):
                                 step.acc["accept_len"], step.acc["out_tokens"])]
 
 
-@pytest.mark.parametrize("fork", [False, True])
-def test_graph_replays_match_eager(fork):
+@pytest.mark.parametrize("fork,batched", [(False, False), (True, False), (True, True)])
+def test_graph_replays_match_eager(fork, batched):
     """fork=True: the attention branch (its own mask build and the attention) is a parallel
-    branch of the graph beside the heads and the tree."""
+    branch of the graph beside the heads and the tree.  batched: 3 sequences with 64/8 heads
+    (two query tiles) and prefixes long enough for the balanced split of the keys."""
     require_gpu()
-    wl = W.WORKLOADS["c2"].scaled(d=512, V=3000, prefix=(700, 700))
+    if batched:
+        wl = W.WORKLOADS["c3"].scaled(B=3, d=512, V=3000, prefix=(700, 3000))
+    else:
+        wl = W.WORKLOADS["c2"].scaled(d=512, V=3000, prefix=(700, 700))
     dt = torch.bfloat16
     xh = W.gen_heads(wl, 9)
     xa = W.gen_attention(wl, 9)
@@ -32,7 +36,7 @@ def test_graph_replays_match_eager(fork):
     step = VerifyStep(parents=wl.parents, depth_widths=wl.depth_widths, dtype=dt, B=wl.B,
                       Hq=wl.Hq, Hkv=wl.Hkv, dh=wl.dh, max_L=int(xa["prefix_len"].max()),
                       heads={"d": wl.d, "V": wl.V, "K": wl.K, "widths": list(wl.head_widths)},
-                      accept="greedy", V=wl.accept_V, commit=fork)
+                      accept="greedy", V=wl.accept_V, commit=fork and not batched)
     inp = {"h": dev(xh["h"], dt), "w_res": dev(xh["w_res"], dt), "w_head": dev(xh["w_head"], dt),
            "q": dev(xa["q"], dt), "k_cache": dev(xa["k_cache"], dt),
            "v_cache": dev(xa["v_cache"], dt), "prefix_len": dev_i32(xa["prefix_len"]),
