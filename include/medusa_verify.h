@@ -276,6 +276,25 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
                         size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * (a4)+(a5) The same tree-masked GQA attention, launched to run beside bandwidth-bound kernels
+ * on another stream (the Medusa heads of the same step; the passages above define it).
+ * Arguments, layouts, results and errors are those of mv_tree_attn_verify; ws must come from
+ * mv_tree_attn_verify_beside_workspace() with the same sizes.  The bf16 path runs as one
+ * persistent workgroup of 4 waves per CU (one wave per SIMD), which leaves half of every SIMD's
+ * registers to the other stream's workgroups, so both progress at once.  On its own it is
+ * about 1.4x slower than mv_tree_attn_verify; fp32 runs the same kernel as mv_tree_attn_verify.
+ * ------------------------------------------------------------------------------------- */
+MV_API size_t mv_tree_attn_verify_beside_workspace(int dt, int B, int N, int Hq, int Hkv, int dh,
+                                                   int max_L);
+
+MV_API int mv_tree_attn_verify_beside(int dt, int B, int N, int Hq, int Hkv, int dh, int L_cap,
+                                      int max_L, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* prefix_len,
+                                      const uint32_t* anc_mask, int mask_stride, float scale,
+                                      void* out, float* lse, int32_t* dev_status, void* ws,
+                                      size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Target LM head over the verification rows (the row before acceptance).  [MX] "2. Single-Pass
  * Tree Attention Verification", step 2: the target model outputs a distribution for every
  * candidate node; step 3 compares each node with the target's greedy prediction.  [SD] "The

@@ -65,6 +65,9 @@ SIGNATURES = [
     ("mv_tree_attn_verify_workspace", _Z, [_I, _I, _I, _I, _I, _I, _I]),
     ("mv_tree_attn_verify", _I, [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _F, _P,
                                  _P, _P, _P, _Z, _P]),
+    ("mv_tree_attn_verify_beside_workspace", _Z, [_I, _I, _I, _I, _I, _I, _I]),
+    ("mv_tree_attn_verify_beside", _I, [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I,
+                                        _F, _P, _P, _P, _P, _Z, _P]),
     ("mv_lm_head_workspace", _Z, [_I, _I, _I, _I]),
     ("mv_lm_head_argmax", _I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     ("mv_accept_paths_workspace", _Z, [_I, _I, _I, _I]),

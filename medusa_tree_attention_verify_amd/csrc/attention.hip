@@ -27,6 +27,12 @@
 //     (ds_read_b64_tr_b16, two per operand).
 // A second kernel merges the chunk partials with their (max, sum) pairs.
 //
+// Co-resident launch (mv_tree_attn_verify_beside), for a step that runs the attention on a
+// second stream beside the bandwidth-bound Medusa heads: the same kernel with 4 waves (128 query
+// rows) per workgroup, launched persistent, one workgroup per CU, so one attention wave per SIMD
+// holds 256 of its 512 registers and the heads' waves (about 56 registers each) fill the rest;
+// both then progress on every CU instead of taking turns on whole CUs.
+//
 // fp32 path: a vector-ALU kernel, one wave per query row, no chunking (the fp32 configuration
 // is a small check case).
 
@@ -42,6 +48,7 @@ namespace {
 
 struct AttnParams {
   int B, N, Hq, Hkv, G, M, L_cap, max_L, CK, nchunks, qtiles, W, jobs;
+  int vblocks;  // workgroup indices of the launch (a persistent grid strides over them)
   float scale_log2;
   const void* q;
   const void* k;
@@ -91,7 +98,11 @@ __device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool re
 #endif
 
 constexpr int kKT = 64;  // keys per tile
-constexpr int kNWVCombine = 8;  // waves per attention workgroup (the partial blocks' layout)
+// Waves per attention workgroup, 32 query rows each: 8 (two per SIMD) for a launch of its own;
+// 4 (one per SIMD, persistent, one workgroup per CU) for a launch that runs beside
+// bandwidth-bound kernels on another stream and leaves half of every SIMD's registers to them.
+constexpr int kNWVAlone = 8;
+constexpr int kNWVBeside = 4;
 constexpr float kLazyLog2 = 8.f;  // running-max slack of the online softmax (log2 units)
 
 
@@ -99,7 +110,7 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-template <int DH, int NWV>
+template <int DH, int NWV, bool PERSIST>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void tree_attn_bf16_kernel(const AttnParams p) {
   constexpr int NT = NWV * 64;
@@ -116,7 +127,9 @@ void tree_attn_bf16_kernel(const AttnParams p) {
   // Job j = (sequence rank, chunk, KV head), longest sequences first (workgroups are dispatched
   // in index order, so the long jobs do not end up in the tail); jobs are dealt round-robin
   // over the XCDs, and the query tiles of one job stay on one XCD, where they share its K/V.
-  const int xcd = static_cast<int>(blockIdx.x % kXcds), pos = static_cast<int>(blockIdx.x / kXcds);
+  // vb is the workgroup index (blockIdx.x, or each index a persistent launch walks).
+  auto run = [&](const int vb) {
+  const int xcd = vb % kXcds, pos = vb / kXcds;
   const int qt = pos % p.qtiles;
   const int job = (pos / p.qtiles) * kXcds + xcd;
   if (job >= p.jobs) return;
@@ -176,16 +189,15 @@ void tree_attn_bf16_kernel(const AttnParams p) {
       nv = min(kKT, p.N - tt * kKT);
     }
   };
-  // Two register sets of prefetched K/V pieces: tile t+2 is requested while tile t computes.
+  // One register set of prefetched K/V pieces: tile t+1 is requested while tile t computes.
   // Buffer loads over this (sequence, KV head)'s slice of the cache: rows past a partial tile
   // and requests past the last tile get an offset beyond the slice, which the hardware's range
-  // check turns into zeros.  No load sits under a branch, so the wait before each LDS store
-  // leaves the other register set in flight.
+  // check turns into zeros, so no load sits under a branch.
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Kg), 0, p.L_cap * DH * 2, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Vg), 0, p.L_cap * DH * 2, kBufferRsrcWord3);
-  uint4 kr0[PPT], vr0[PPT], kr1[PPT], vr1[PPT];
+  uint4 kr[PPT], vr[PPT];
   auto gload = [&](int t, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
     int row0 = 0, nv = 0;
     if (t < ntiles) tile_rows(t, row0, nv);
@@ -337,25 +349,18 @@ void tree_attn_bf16_kernel(const AttnParams p) {
       }
   };
 
-  // Pipeline: LDS holds tile t (computing) and tile t+1 (written at the end of iteration t);
-  // the registers hold tile t+1 (arrived) and tile t+2 (requested at the start of
-  // iteration t), so every load has two tiles of compute to arrive.
-  gload(0, kr0, vr0);
-  gload(1, kr1, vr1);
-  swrite(0, kr0, vr0);
+  // Pipeline: LDS holds tile t (computing) and tile t+1 (stored at the end of iteration t);
+  // tile t+1's loads are issued before tile t's compute, which covers their latency.  (A
+  // second register set, two tiles ahead, measured no faster and cost 22 registers.)
+  gload(0, kr, vr);
+  swrite(0, kr, vr);
   __syncthreads();
-  int t = 0;
-  for (; t + 2 <= ntiles; t += 2) {
-    gload(t + 2, kr0, vr0);
+  for (int t = 0; t < ntiles; ++t) {
+    gload(t + 1, kr, vr);
     compute(t);
-    swrite((t + 1) & 1, kr1, vr1);
-    __syncthreads();
-    gload(t + 3, kr1, vr1);
-    compute(t + 1);
-    swrite(t & 1, kr0, vr0);
+    swrite((t + 1) & 1, kr, vr);
     __syncthreads();
   }
-  if (t < ntiles) compute(t);
 
   if (!qvalid) return;
   // Output layout of O^T: lane holds query l32, dims db*32 + 8*(v/4) + 4*half + v%4.
@@ -392,6 +397,20 @@ void tree_attn_bf16_kernel(const AttnParams p) {
             make_float4(oacc[db][vq * 4 + 0], oacc[db][vq * 4 + 1], oacc[db][vq * 4 + 2], oacc[db][vq * 4 + 3]);
     if (half == 0) p.part_ml[rowi] = make_float2(m_run * p.scale_log2, l_run);
   }
+  };
+  if constexpr (PERSIST) {
+    // Beside the heads' streaming waves on the same SIMDs, this wave wins the issue
+    // arbitration (those mostly wait on their loads): +2% on the forked 70B-share step.
+    __builtin_amdgcn_s_setprio(1);
+    // Persistent: the grid (a multiple of the XCD count) strides over the workgroup indices,
+    // so every index a workgroup takes maps to its own XCD, as in a launch of its own.
+    for (int vb = static_cast<int>(blockIdx.x); vb < p.vblocks; vb += static_cast<int>(gridDim.x)) {
+      __syncthreads();  // the previous index's last tile may still be read from LDS
+      run(vb);
+    }
+  } else {
+    run(static_cast<int>(blockIdx.x));
+  }
 }
 
 // Merge of the chunk partials: O = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c, as an online
@@ -399,10 +418,9 @@ void tree_attn_bf16_kernel(const AttnParams p) {
 // partial blocks (the same position in every chunk's block), so each wave reads 1 KB of
 // consecutive bytes per chunk; the partials of up to CB chunks are requested before any is
 // used (CB covers every chunk of the one-sequence launches: one round trip to memory).
-template <int DH, int CB>
+template <int DH, int CB, int NWV>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   constexpr int DB = DH / 32, SLOT = DB * 4 * 64;  // float4 per (job, query tile, wave) block
-  constexpr int NWV = kNWVCombine;
   const size_t gid = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   const int pos = static_cast<int>(gid % SLOT);
   const size_t slot = gid / SLOT;                   // ((b*Hkv + g)*qtiles + qt)*NWV + wv
@@ -564,7 +582,6 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(const AttnParams p) 
 // ---------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------
-constexpr int kNWV = kNWVCombine;  // waves per workgroup -> 256 query rows
 
 // Sequences ranked by decreasing (clamped) prefix length, ties by index: order[rank] = b.
 //
@@ -647,6 +664,7 @@ __global__ __launch_bounds__(kOrderMaxB) void seq_order_kernel(const AttnParams 
 }
 
 struct AttnPlan {
+  int nwv = kNWVAlone;   // waves per workgroup (32 query rows each)
   int qtiles = 1, CK = 256, nchunks = 1;
   bool ordered = false;  // a length ordering of the sequences in the workspace
   bool balanced = false;  // ... and a balanced chunk plan from the actual lengths
@@ -657,12 +675,14 @@ struct AttnPlan {
 // Chunking (split-KV): aim for MV_ATTN_TARGET_WG workgroups (MV_ATTN_TARGET_WG_BATCH for a
 // batch) so that the chip stays busy, but keep chunks of at least MV_ATTN_MIN_CHUNK keys:
 // every chunk writes an fp32 partial output as large as its query block, so short chunks turn
-// a K/V-streaming kernel into a partial-output-writing one.
-AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L) {
+// a K/V-streaming kernel into a partial-output-writing one.  `beside` plans the persistent
+// 4-wave launch (the targets then count its workgroup indices).
+AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L, bool beside) {
   AttnPlan a;
   if (dt == MV_F32) return a;
+  a.nwv = beside ? kNWVBeside : kNWVAlone;
   const int M = N * (Hq / Hkv);
-  a.qtiles = ceil_div(M, kNWV * 32);
+  a.qtiles = ceil_div(M, a.nwv * 32);
   const long long base = static_cast<long long>(B) * Hkv * a.qtiles;
   // A batch splits only as far as its (sequence, KV head, query tile) jobs stay within the
   // batch target (rounding down): the jobs of a large batch already fill the chip, and every
@@ -699,7 +719,7 @@ AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L) {
   }
   if (a.nchunks > 1) {
     const size_t rows = cslots * Hq * N;
-    const size_t tile_rows = cslots * Hkv * a.qtiles * kNWV * 32;
+    const size_t tile_rows = cslots * Hkv * a.qtiles * a.nwv * 32;
     c.take<float>(tile_rows * dh);  // register-order blocks, padded to whole query tiles
     c.take<float2>(rows);
   }
@@ -707,25 +727,33 @@ AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L) {
   return a;
 }
 
-}  // namespace
-}  // namespace mv
-
-using namespace mv;
-
-extern "C" {
-
-MV_API size_t mv_tree_attn_verify_workspace(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L) {
-  if ((dt != MV_F32 && dt != MV_BF16) || B < 1 || N < 1 || Hq < 1 || Hkv < 1 || max_L < 0) return 0;
-  if (Hq % Hkv != 0 || (dh != 64 && dh != 128) || N > MV_MAX_NODES) return 0;
-  return plan_attn(dt, B, N, Hq, Hkv, dh, max_L).ws_bytes;
+template <int NWV>
+void launch_combine(const AttnParams& p, int dh, int nchunks, hipStream_t st) {
+  const long long slots = static_cast<long long>(p.B) * p.Hkv * p.qtiles * NWV;
+  const dim3 g64(static_cast<unsigned>(ceil_div(slots * (2 * 4 * 64), 256LL))),
+      g128(static_cast<unsigned>(ceil_div(slots * (4 * 4 * 64), 256LL)));
+  if (nchunks <= 4) {
+    if (dh == 64) attn_combine_kernel<64, 4, NWV><<<g64, 256, 0, st>>>(p);
+    else attn_combine_kernel<128, 4, NWV><<<g128, 256, 0, st>>>(p);
+  } else if (nchunks <= 8) {
+    if (dh == 64) attn_combine_kernel<64, 8, NWV><<<g64, 256, 0, st>>>(p);
+    else attn_combine_kernel<128, 8, NWV><<<g128, 256, 0, st>>>(p);
+  } else {
+    if (dh == 64) attn_combine_kernel<64, 16, NWV><<<g64, 256, 0, st>>>(p);
+    else attn_combine_kernel<128, 16, NWV><<<g128, 256, 0, st>>>(p);
+  }
 }
 
-MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, int L_cap, int max_L,
-                               const void* q, const void* k_cache, const void* v_cache,
-                               const int32_t* prefix_len, const uint32_t* anc_mask,
-                               int mask_stride, float scale,
-                               void* out, float* lse, int32_t* dev_status, void* ws,
-                               size_t ws_bytes, void* stream) {
+size_t attn_workspace(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L, bool beside) {
+  if ((dt != MV_F32 && dt != MV_BF16) || B < 1 || N < 1 || Hq < 1 || Hkv < 1 || max_L < 0) return 0;
+  if (Hq % Hkv != 0 || (dh != 64 && dh != 128) || N > MV_MAX_NODES) return 0;
+  return plan_attn(dt, B, N, Hq, Hkv, dh, max_L, beside).ws_bytes;
+}
+
+int tree_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int L_cap, int max_L, const void* q,
+              const void* k_cache, const void* v_cache, const int32_t* prefix_len,
+              const uint32_t* anc_mask, int mask_stride, float scale, void* out, float* lse,
+              int32_t* dev_status, void* ws, size_t ws_bytes, void* stream, bool beside) {
   if (dt != MV_F32 && dt != MV_BF16) return MV_ERR_INVALID_ARG;
   if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || max_L < 0 || L_cap < N) return MV_ERR_INVALID_ARG;
   if (!q || !k_cache || !v_cache || !prefix_len || !anc_mask || !out) return MV_ERR_INVALID_ARG;
@@ -737,7 +765,7 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
   // bf16 K/V are read through buffer resources over one (sequence, KV head) slice, whose
   // byte size must fit the 31-bit offsets.
   if (dt == MV_BF16 && static_cast<long long>(L_cap) * dh * 2 > 0x7fffffffLL) return MV_ERR_UNSUPPORTED;
-  const AttnPlan a = plan_attn(dt, B, N, Hq, Hkv, dh, max_L);
+  const AttnPlan a = plan_attn(dt, B, N, Hq, Hkv, dh, max_L, beside);
   MV_TRY(check_ws(ws, ws_bytes, a.ws_bytes));
   AttnParams p{};
   p.B = B; p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.M = N * p.G;
@@ -755,6 +783,16 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
     else tree_attn_f32_kernel<128><<<blocks, 256, 0, st>>>(p);
     return launch_status();
   }
+  // Persistent grid of the co-resident launch: one 4-wave workgroup per CU (the CU count
+  // rounded down to whole XCDs), striding over the workgroup indices.
+  int pgrid = 0;
+  if (beside) {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return MV_ERR_HIP;
+    pgrid = std::max(kXcds, ncu / kXcds * kXcds);
+  }
   Carver c(ws);
   int32_t* order = a.ordered ? c.take<int32_t>(B) : nullptr;
   int32_t* plan = a.balanced ? c.take<int32_t>(3 * static_cast<size_t>(B)) : nullptr;
@@ -762,7 +800,7 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
   const size_t cslots = a.balanced ? static_cast<size_t>(a.nchunks) : static_cast<size_t>(B) * a.nchunks;
   if (a.nchunks > 1) {
     const size_t rows = cslots * Hq * N;
-    const size_t tile_rows = cslots * Hkv * a.qtiles * kNWV * 32;
+    const size_t tile_rows = cslots * Hkv * a.qtiles * a.nwv * 32;
     p.part_o = c.take<float>(tile_rows * dh);
     p.part_ml = c.take<float2>(rows);
   }
@@ -770,6 +808,7 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
   const long long grid = (jobs + kXcds - 1) / kXcds * kXcds * a.qtiles;
   if (grid > (1LL << 30)) return MV_ERR_UNSUPPORTED;
   p.jobs = static_cast<int>(jobs);
+  p.vblocks = static_cast<int>(grid);
   if (order) {
     seq_order_kernel<<<1, kOrderMaxB, 0, st>>>(p, order, plan, jtab, a.c_target);
     MV_TRY(launch_status());
@@ -777,26 +816,58 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
     p.plan = plan;
     p.jtab = jtab;
   }
-  if (dh == 64) tree_attn_bf16_kernel<64, kNWV><<<static_cast<int>(grid), kNWV * 64, 0, st>>>(p);
-  else tree_attn_bf16_kernel<128, kNWV><<<static_cast<int>(grid), kNWV * 64, 0, st>>>(p);
+  if (beside) {
+    const int g = static_cast<int>(std::min<long long>(grid, pgrid));
+    if (dh == 64) tree_attn_bf16_kernel<64, kNWVBeside, true><<<g, kNWVBeside * 64, 0, st>>>(p);
+    else tree_attn_bf16_kernel<128, kNWVBeside, true><<<g, kNWVBeside * 64, 0, st>>>(p);
+  } else {
+    const int g = static_cast<int>(grid);
+    if (dh == 64) tree_attn_bf16_kernel<64, kNWVAlone, false><<<g, kNWVAlone * 64, 0, st>>>(p);
+    else tree_attn_bf16_kernel<128, kNWVAlone, false><<<g, kNWVAlone * 64, 0, st>>>(p);
+  }
   MV_TRY(launch_status());
   if (a.nchunks > 1) {
-    const long long slots = static_cast<long long>(B) * Hkv * a.qtiles * kNWV;
-    const dim3 g64(static_cast<unsigned>(ceil_div(slots * (2 * 4 * 64), 256LL))),
-        g128(static_cast<unsigned>(ceil_div(slots * (4 * 4 * 64), 256LL)));
-    if (a.nchunks <= 4) {
-      if (dh == 64) attn_combine_kernel<64, 4><<<g64, 256, 0, st>>>(p);
-      else attn_combine_kernel<128, 4><<<g128, 256, 0, st>>>(p);
-    } else if (a.nchunks <= 8) {
-      if (dh == 64) attn_combine_kernel<64, 8><<<g64, 256, 0, st>>>(p);
-      else attn_combine_kernel<128, 8><<<g128, 256, 0, st>>>(p);
-    } else {
-      if (dh == 64) attn_combine_kernel<64, 16><<<g64, 256, 0, st>>>(p);
-      else attn_combine_kernel<128, 16><<<g128, 256, 0, st>>>(p);
-    }
+    if (beside) launch_combine<kNWVBeside>(p, dh, a.nchunks, st);
+    else launch_combine<kNWVAlone>(p, dh, a.nchunks, st);
     MV_TRY(launch_status());
   }
   return MV_OK;
+}
+
+}  // namespace
+}  // namespace mv
+
+using namespace mv;
+
+extern "C" {
+
+MV_API size_t mv_tree_attn_verify_workspace(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L) {
+  return attn_workspace(dt, B, N, Hq, Hkv, dh, max_L, false);
+}
+
+MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, int L_cap, int max_L,
+                               const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* prefix_len, const uint32_t* anc_mask,
+                               int mask_stride, float scale,
+                               void* out, float* lse, int32_t* dev_status, void* ws,
+                               size_t ws_bytes, void* stream) {
+  return tree_attn(dt, B, N, Hq, Hkv, dh, L_cap, max_L, q, k_cache, v_cache, prefix_len, anc_mask,
+                   mask_stride, scale, out, lse, dev_status, ws, ws_bytes, stream, false);
+}
+
+MV_API size_t mv_tree_attn_verify_beside_workspace(int dt, int B, int N, int Hq, int Hkv, int dh,
+                                                   int max_L) {
+  return attn_workspace(dt, B, N, Hq, Hkv, dh, max_L, true);
+}
+
+MV_API int mv_tree_attn_verify_beside(int dt, int B, int N, int Hq, int Hkv, int dh, int L_cap,
+                                      int max_L, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* prefix_len,
+                                      const uint32_t* anc_mask, int mask_stride, float scale,
+                                      void* out, float* lse, int32_t* dev_status, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  return tree_attn(dt, B, N, Hq, Hkv, dh, L_cap, max_L, q, k_cache, v_cache, prefix_len, anc_mask,
+                   mask_stride, scale, out, lse, dev_status, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -237,8 +237,10 @@ def build_dynamic_tree(cand_ids: torch.Tensor, cand_vals: torch.Tensor,
 
 
 # ------------------------------------------------------------------ attention
-def attn_workspace_bytes(dt: int, B: int, N: int, Hq: int, Hkv: int, dh: int, max_L: int) -> int:
-    return int(L.lib().mv_tree_attn_verify_workspace(dt, B, N, Hq, Hkv, dh, max_L))
+def attn_workspace_bytes(dt: int, B: int, N: int, Hq: int, Hkv: int, dh: int, max_L: int,
+                         beside: bool = False) -> int:
+    fn = L.lib().mv_tree_attn_verify_beside_workspace if beside else L.lib().mv_tree_attn_verify_workspace
+    return int(fn(dt, B, N, Hq, Hkv, dh, max_L))
 
 
 def tree_attn_verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -246,10 +248,12 @@ def tree_attn_verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
                      scale: float = 0.0, out: Optional[torch.Tensor] = None,
                      lse: Optional[torch.Tensor] = None, want_lse: bool = True,
                      status: Optional[torch.Tensor] = None,
-                     ws: Optional[Workspace] = None):
+                     ws: Optional[Workspace] = None, beside: bool = False):
     """a4 + a5: tree-masked GQA attention; returns (out [B,N,Hq,dh], lse [B,Hq,N] or None).
 
-    anc_mask [N, W] (one tree for the batch) or [B, N, W] (one tree per sequence)."""
+    anc_mask [N, W] (one tree for the batch) or [B, N, W] (one tree per sequence).
+    ``beside`` takes the co-resident launch (mv_tree_attn_verify_beside), meant to run on one
+    stream while bandwidth-bound kernels run on another."""
     dt = _dt(q)
     B, N, Hq, dh = q.shape
     _, Hkv, L_cap, _ = k_cache.shape
@@ -269,8 +273,9 @@ def tree_attn_verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     w = _ws("attn", ws)
-    ptr, n = w.get(attn_workspace_bytes(dt, B, N, Hq, Hkv, dh, max_L))
-    L.check("mv_tree_attn_verify", L.lib().mv_tree_attn_verify(
+    ptr, n = w.get(attn_workspace_bytes(dt, B, N, Hq, Hkv, dh, max_L, beside))
+    name = "mv_tree_attn_verify_beside" if beside else "mv_tree_attn_verify"
+    L.check(name, getattr(L.lib(), name)(
         dt, B, N, Hq, Hkv, dh, L_cap, int(max_L), _ptr(q), _ptr(k_cache), _ptr(v_cache),
         _ptr(prefix_len), _ptr(anc_mask), mstride, float(scale), _ptr(out), _ptr(lse),
         _ptr(status),

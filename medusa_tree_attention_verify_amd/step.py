@@ -108,6 +108,8 @@ class VerifyStep:
             self.ws_heads.get(ops.heads_workspace_bytes(self.dt, B, d, Vh, K, self.s_max))
             self._s_heads = L.int_array(heads["widths"])
         self.ws_attn.get(ops.attn_workspace_bytes(self.dt, B, N, Hq, Hkv, dh, max_L))
+        if self.can_fork():  # a forked step runs the co-resident attention
+            self.ws_attn.get(ops.attn_workspace_bytes(self.dt, B, N, Hq, Hkv, dh, max_L, True))
         self._s_depth = L.int_array(self.depth_widths)
         if target_head:
             if accept not in ("greedy", "speculative") or dtype != torch.bfloat16:
@@ -236,7 +238,10 @@ class VerifyStep:
             calls["attn_mask"] = wrap("mv_build_tree_mask", lib.mv_build_tree_mask, N,
                                       _p(self.parents), 0, 0, 0, None, None, _p(anc), None, None,
                                       _p(self.status), st_b)
-        calls["attention"] = wrap("mv_tree_attn_verify", lib.mv_tree_attn_verify, self.dt, B, N,
+        # forked: the co-resident launch (one persistent 4-wave workgroup per CU), so that the
+        # attention and the bandwidth-bound heads share every CU instead of taking turns
+        aname = "mv_tree_attn_verify_beside" if fork else "mv_tree_attn_verify"
+        calls["attention"] = wrap(aname, getattr(lib, aname), self.dt, B, N,
                                   self.Hq, self.Hkv, self.dh, Lcap, self.max_L, _p(inp["q"]),
                                   _p(inp["k_cache"]), _p(inp["v_cache"]), _p(inp["prefix_len"]),
                                   _p(anc), N * ((N + 31) // 32) if self.dynamic else 0, 0.0,
@@ -288,8 +293,13 @@ class VerifyStep:
     def sequence(self, calls: Dict[str, Callable[[], None]]) -> List[Callable[[], None]]:
         return [calls[p] for p in self.PARTS if p in calls]
 
-    def run(self, inp: Dict[str, torch.Tensor]) -> None:
-        """One whole step on ``inp`` (binds, then runs its calls in order)."""
+    def run(self, inp: Dict[str, torch.Tensor], branch_stream=None) -> None:
+        """One whole step on ``inp`` (binds, then runs its calls in order).  With
+        ``branch_stream`` (a torch stream) it runs forked, as ``capture(fork=True)`` records it:
+        the attention branch on that stream, with the co-resident attention launch."""
+        if branch_stream is not None and self.can_fork():
+            self._run_forked(inp, branch_stream)
+            return
         for c in self.sequence(self.bind(inp)):
             c()
 

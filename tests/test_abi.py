@@ -19,7 +19,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 21, names
+    assert len(names) == 23, names
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -58,6 +58,11 @@ def test_workspace_queries():
     assert lib.mv_tree_attn_verify_workspace(L.MV_BF16, 1, 64, 32, 8, 128, 4096) > 0
     assert lib.mv_tree_attn_verify_workspace(L.MV_BF16, 1, 64, 32, 8, 96, 4096) == 0  # dh
     assert lib.mv_tree_attn_verify_workspace(L.MV_F32, 1, 8, 4, 4, 64, 128) == 0    # no split
+    # the co-resident launch plans 128-row query tiles: same checks, its own partial layout
+    assert lib.mv_tree_attn_verify_beside_workspace(L.MV_BF16, 1, 64, 32, 8, 128, 4096) > 0
+    assert lib.mv_tree_attn_verify_beside_workspace(L.MV_BF16, 1, 64, 32, 8, 96, 4096) == 0
+    assert lib.mv_tree_attn_verify_beside_workspace(L.MV_F32, 1, 8, 4, 4, 64, 128) == 0
+    assert lib.mv_tree_attn_verify_beside_workspace(L.MV_BF16, 8, 64, 64, 8, 128, 32768) > 0
     assert lib.mv_accept_paths_workspace(L.MV_ACCEPT_GREEDY, 1, 64, 32000) > 0
     assert lib.mv_accept_paths_workspace(L.MV_ACCEPT_SPECULATIVE, 64, 64, 128256) > 0
     assert (lib.mv_accept_paths_workspace(L.MV_ACCEPT_MULTICAND, 64, 64, 128256)
@@ -111,16 +116,17 @@ def test_host_argument_checks():
     assert lib.mv_build_tree_mask(0, P, 0, 0, 0, None, None, P, None, None, None, None) == L.MV_ERR_INVALID_ARG
     assert lib.mv_build_tree_mask(257, P, 0, 0, 0, None, None, P, None, None, None, None) == L.MV_ERR_UNSUPPORTED
     assert lib.mv_build_tree_mask(8, P, 1, 17, 2, None, P, P, None, P, None, None) == L.MV_ERR_UNSUPPORTED
-    # attention
+    # attention (both launches check their arguments the same way)
     args = (P, P, P, P, P, 0, 0.0, P, None, None)
-    assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 6, 4, 128, 200, 100, *args, None, 0, None) == L.MV_ERR_INVALID_ARG
-    assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 8, 4, 96, 200, 100, *args, None, 0, None) == L.MV_ERR_UNSUPPORTED
-    assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 8, 4, 128, 100, 100, *args, None, 0, None) == L.MV_ERR_INVALID_ARG
-    assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 8, 4, 128, 10000, 8000, *args, None, 0, None) == L.MV_ERR_WORKSPACE
-    # a (sequence, KV head) slice of 2 GiB or more does not fit the bf16 path's buffer offsets
-    assert lib.mv_tree_attn_verify(L.MV_BF16, 1, 8, 8, 4, 128, 1 << 23, 100, *args, None, 0, None) == L.MV_ERR_UNSUPPORTED
     bad_stride = (P, P, P, P, P, 7, 0.0, P, None, None)     # N * W = 8 words per sequence
-    assert lib.mv_tree_attn_verify(L.MV_BF16, 2, 8, 8, 4, 128, 200, 100, *bad_stride, None, 0, None) == L.MV_ERR_INVALID_ARG
+    for attn in (lib.mv_tree_attn_verify, lib.mv_tree_attn_verify_beside):
+        assert attn(L.MV_BF16, 1, 8, 6, 4, 128, 200, 100, *args, None, 0, None) == L.MV_ERR_INVALID_ARG
+        assert attn(L.MV_BF16, 1, 8, 8, 4, 96, 200, 100, *args, None, 0, None) == L.MV_ERR_UNSUPPORTED
+        assert attn(L.MV_BF16, 1, 8, 8, 4, 128, 100, 100, *args, None, 0, None) == L.MV_ERR_INVALID_ARG
+        assert attn(L.MV_BF16, 1, 8, 8, 4, 128, 10000, 8000, *args, None, 0, None) == L.MV_ERR_WORKSPACE
+        # a (sequence, KV head) slice of 2 GiB or more does not fit the bf16 path's buffer offsets
+        assert attn(L.MV_BF16, 1, 8, 8, 4, 128, 1 << 23, 100, *args, None, 0, None) == L.MV_ERR_UNSUPPORTED
+        assert attn(L.MV_BF16, 2, 8, 8, 4, 128, 200, 100, *bad_stride, None, 0, None) == L.MV_ERR_INVALID_ARG
     # acceptance
     assert lib.mv_accept_paths(L.MV_ACCEPT_SPECULATIVE, L.MV_BF16, 1, 4, 10, 2, P, 0, P, P, P, P, P, P,
                                P, None, None, None, P, 1 << 20, None) == L.MV_ERR_UNSUPPORTED

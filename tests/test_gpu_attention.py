@@ -1,4 +1,5 @@
-"""GPU parity of tree-masked GQA attention (mv_tree_attn_verify) against the oracle."""
+"""GPU parity of tree-masked GQA attention against the oracle: mv_tree_attn_verify and the
+co-resident launch mv_tree_attn_verify_beside (persistent 4-wave workgroups), on the same cases."""
 import numpy as np
 import pytest
 import torch
@@ -13,9 +14,9 @@ from tests.gpu_util import assert_bf16, assert_fp32, dev, dev_i32, host, require
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, seed, lens=None, select=None):
+def _run(wl, seed, lens=None, select=None, beside=False):
     print(f"attn {wl.name} B={wl.B} N={wl.N} Hq={wl.Hq} Hkv={wl.Hkv} dh={wl.dh} "
-          f"prefix={wl.prefix} lens={lens} seed={seed}", flush=True)
+          f"prefix={wl.prefix} lens={lens} seed={seed} beside={beside}", flush=True)
     x = W.gen_attention(wl, seed, None if lens is None else np.asarray(lens, np.int32))
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     tree = O.build_tree(list(wl.parents))
@@ -29,7 +30,7 @@ def _run(wl, seed, lens=None, select=None):
     lse0 = torch.full((wl.B, wl.Hq, wl.N), float("nan"), dtype=torch.float32, device="cuda")
     out, lse = ops.tree_attn_verify(q, dev(x["k_cache"], dt), dev(x["v_cache"], dt),
                                     dev_i32(x["prefix_len"]), anc, max_L, status=status,
-                                    out=out0, lse=lse0)
+                                    out=out0, lse=lse0, beside=beside)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     assert bool(torch.isfinite(out).all()), "an output row was not written"
@@ -52,9 +53,13 @@ def _run(wl, seed, lens=None, select=None):
         assert_fp32(gl, rl, atol=1e-3, what="lse")
 
 
-def test_attention_tiny_fp32():
+BESIDE = pytest.mark.parametrize("beside", [False, True], ids=["alone", "beside"])
+
+
+@BESIDE
+def test_attention_tiny_fp32(beside):
     require_gpu()
-    _run(W.WORKLOADS["c1"], 1)
+    _run(W.WORKLOADS["c1"], 1, beside=beside)
 
 
 def _bf16(parents, B, Hq, Hkv, dh, L):
@@ -72,10 +77,11 @@ def _bf16(parents, B, Hq, Hkv, dh, L):
     (branching_tree((4, 4, 4, 2)), 1, 16, 2, 128, [77]),    # 212 nodes, 7 mask words
     ([-1, 0, 1, 1, 0, -1, 5], 1, 8, 1, 64, [3]),            # forest (two roots)
 ])
-def test_attention_bf16_shapes(parents, B, Hq, Hkv, dh, lens):
+@BESIDE
+def test_attention_bf16_shapes(parents, B, Hq, Hkv, dh, lens, beside):
     require_gpu()
     wl = _bf16(parents, B, Hq, Hkv, dh, max(lens))
-    _run(wl, 21, lens)
+    _run(wl, 21, lens, beside=beside)
 
 
 def _f32(parents, B, Hq, Hkv, dh, L):
@@ -105,28 +111,45 @@ def _random_forest(n, seed):
     return [-1] + [int(rng.integers(-1, i)) for i in range(1, n)]
 
 
-def test_attention_max_nodes():
+@BESIDE
+def test_attention_max_nodes(beside):
     """256 nodes (the largest tree: 8 mask words, 4 tree tiles), a random forest, G = 4."""
     require_gpu()
     wl = _bf16(_random_forest(256, 7), 2, 8, 2, 64, 700)
-    _run(wl, 23, [100, 700])
+    _run(wl, 23, [100, 700], beside=beside)
 
 
-def test_attention_multichunk_with_empty_prefix():
+@BESIDE
+def test_attention_multichunk_with_empty_prefix(beside):
     """A split batch in which one sequence has no prefix (its rows skip the combine)."""
     require_gpu()
     wl = _bf16(branching_tree((4, 3, 2, 1)), 3, 32, 8, 128, 5000)
-    _run(wl, 24, [0, 5000, 2049])
+    _run(wl, 24, [0, 5000, 2049], beside=beside)
 
 
-def test_attention_multichunk_ragged():
+@BESIDE
+def test_attention_multichunk_ragged(beside):
     """Prefixes long enough to be split into several chunks, ragged across the batch."""
     require_gpu()
     wl = _bf16(branching_tree((4, 3, 2, 1)), 4, 32, 8, 128, 6000)
-    _run(wl, 22, [6000, 257, 4096, 1])
+    _run(wl, 22, [6000, 257, 4096, 1], beside=beside)
 
 
-def test_attention_balanced_split_two_query_tiles():
+def test_attention_beside_more_indices_than_cus():
+    """The persistent launch with far more workgroup indices than CUs (one sequence split
+    into many chunks, 8 KV heads, 4 query tiles each) and with fewer (one short sequence):
+    every row written, every row against the oracle."""
+    require_gpu()
+    wl = _bf16(branching_tree((4, 4, 4, 2)), 1, 32, 8, 64, 20000)
+    rng = np.random.default_rng(27)
+    sel = [(0, int(rng.integers(wl.Hq)), int(rng.integers(wl.N))) for _ in range(40)]
+    sel += [(0, 0, 0), (0, wl.Hq - 1, wl.N - 1)]
+    _run(wl, 28, [20000], select=sel, beside=True)
+    _run(_bf16(branching_tree((2, 2)), 1, 4, 4, 128, 10), 29, [10], beside=True)
+
+
+@BESIDE
+def test_attention_balanced_split_two_query_tiles(beside):
     """A split batch with two query tiles per KV head (64/8 heads, 64 nodes) and very uneven
     prefixes (0 to 12000 keys), so the chunk plan is built on the device from the actual
     lengths: every output row must be written, sampled rows of every sequence (the first and
@@ -138,13 +161,14 @@ def test_attention_balanced_split_two_query_tiles():
     for b in range(wl.B):
         sel += [(b, int(rng.integers(wl.Hq)), int(rng.integers(wl.N))) for _ in range(4)]
         sel += [(b, int(rng.integers(wl.Hq)), 0), (b, int(rng.integers(wl.Hq)), wl.N - 1)]
-    _run(wl, 25, [0, 1, 65, 3000, 9000, 12000], select=sel)
+    _run(wl, 25, [0, 1, 65, 3000, 9000, 12000], select=sel, beside=beside)
 
 
-def test_attention_llama8b_full():
+@BESIDE
+def test_attention_llama8b_full(beside):
     """B=1, 32/8 heads, dh 128, prefix 4096, (4,3,2,1) tree: every output row."""
     require_gpu()
-    _run(W.WORKLOADS["c2"], 2)
+    _run(W.WORKLOADS["c2"], 2, beside=beside)
 
 
 def test_attention_long_context_sampled():
@@ -157,16 +181,18 @@ def test_attention_long_context_sampled():
     _run(wl, 4, select=sel)
 
 
-def test_attention_70b_share_sampled():
+@BESIDE
+def test_attention_70b_share_sampled(beside):
     """Batch 8, 64/8 heads, prefixes drawn in [8192, 32768]: sampled rows of every sequence."""
     require_gpu()
     wl = W.WORKLOADS["c3"]
     rng = np.random.default_rng(3)
     sel = [(b, int(rng.integers(64)), int(rng.integers(64))) for b in range(8) for _ in range(3)]
-    _run(wl, 3, select=sel)
+    _run(wl, 3, select=sel, beside=beside)
 
 
-def test_attention_serving_b64_full_shape():
+@BESIDE
+def test_attention_serving_b64_full_shape(beside):
     """The spec-serving attention shape at full size: batch 64, 32/8 heads, dh 128, the 64-node
     (4,3,2,1) tree, prefixes drawn in [512, 8192], with several equal lengths (the length
     ordering's tie rule), one empty prefix and one at the maximum.  Every output row must be
@@ -185,14 +211,15 @@ def test_attention_serving_b64_full_shape():
     for b in range(wl.B):
         sel += [(b, int(rng.integers(wl.Hq)), int(rng.integers(wl.N))) for _ in range(4)]
         sel += [(b, int(rng.integers(wl.Hq)), 0), (b, int(rng.integers(wl.Hq)), wl.N - 1)]
-    _run(wl, 5, lens.tolist(), select=sel)
+    _run(wl, 5, lens.tolist(), select=sel, beside=beside)
 
 
 @pytest.mark.parametrize("B,lens,boost_rows", [
     (1, [3000], (2000, 2010)),        # one chunk: the jump comes after 31 ordinary tiles
     (2, [9000, 300], (8990, 9000)),   # several chunks: the jump sits in the last prefix tile
 ])
-def test_attention_large_score_jump(B, lens, boost_rows):
+@BESIDE
+def test_attention_large_score_jump(B, lens, boost_rows, beside):
     """Scores that jump far above everything seen before in a chunk (a few keys scaled by
     40): the softmax reference of the first tiles would overflow, so the kernel has to take
     its second pass from the true chunk max; the result must still match the oracle."""
@@ -205,7 +232,8 @@ def test_attention_large_score_jump(B, lens, boost_rows):
     anc = ops.build_tree_mask(dev_i32(wl.parents))["anc_mask"]
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     out, lse = ops.tree_attn_verify(dev(x["q"], dt), dev(x["k_cache"], dt), dev(x["v_cache"], dt),
-                                    dev_i32(x["prefix_len"]), anc, max(lens), status=status)
+                                    dev_i32(x["prefix_len"]), anc, max(lens), status=status,
+                                    beside=beside)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     rng = np.random.default_rng(62)
@@ -220,7 +248,8 @@ def test_attention_large_score_jump(B, lens, boost_rows):
     assert_fp32(host(lse)[bb, hh, ii], ref["lse"][bb, hh, ii], atol=1e-3, what="lse")
 
 
-def test_attention_bad_prefix_flags():
+@BESIDE
+def test_attention_bad_prefix_flags(beside):
     require_gpu()
     wl = _bf16([-1, 0], 2, 4, 2, 64, 10)
     x = W.gen_attention(wl, 5, np.array([10, 10], np.int32))
@@ -228,6 +257,7 @@ def test_attention_bad_prefix_flags():
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     pl = dev_i32([10, 50])                 # 50 > max_L and 50 + N > L_cap
     ops.tree_attn_verify(dev(x["q"], torch.bfloat16), dev(x["k_cache"], torch.bfloat16),
-                         dev(x["v_cache"], torch.bfloat16), pl, anc, 10, status=status)
+                         dev(x["v_cache"], torch.bfloat16), pl, anc, 10, status=status,
+                         beside=beside)
     torch.cuda.synchronize()
     assert int(status.item()) & L.MV_DEV_BAD_PREFIX
