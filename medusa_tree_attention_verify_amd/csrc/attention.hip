@@ -90,6 +90,9 @@ __device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool re
 #ifndef MV_ATTN_TARGET_WG_BATCH
 #define MV_ATTN_TARGET_WG_BATCH 768  // ... and with several sequences (at most)
 #endif
+#ifndef MV_ATTN_TARGET_WG_BESIDE
+#define MV_ATTN_TARGET_WG_BESIDE 768  // ... for a batch in the co-resident launch (indices)
+#endif
 #ifndef MV_ATTN_BALANCED
 #define MV_ATTN_BALANCED 1  // batches that split: chunk plan from the actual lengths
 #endif
@@ -688,7 +691,8 @@ AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L, boo
   // batch target (rounding down): the jobs of a large batch already fill the chip, and every
   // extra chunk writes M x dh partials that the combine reads back.  A small batch of long
   // sequences (a few jobs per CU) does split, so that the longest jobs do not set the tail.
-  const long long target = B > 1 ? MV_ATTN_TARGET_WG_BATCH : MV_ATTN_TARGET_WG;
+  const long long target = B > 1 ? (beside ? MV_ATTN_TARGET_WG_BESIDE : MV_ATTN_TARGET_WG_BATCH)
+                                 : MV_ATTN_TARGET_WG;
   int want = static_cast<int>(B > 1 ? std::max<long long>(1, target / base)
                                     : std::max<long long>(1, (target + base - 1) / base));
   const int cap = std::max(1, ceil_div(max_L, MV_ATTN_MIN_CHUNK));

@@ -305,8 +305,10 @@ class VerifyStep:
 
     def _run_forked(self, inp: Dict[str, torch.Tensor], side: "torch.cuda.Stream") -> None:
         """One step with the attention branch on ``side``: it forks from the current stream at
-        the start and joins before the acceptance (whose commit moves K/V rows the attention
-        reads)."""
+        the start and joins before the commit, which moves K/V rows the attention reads.  The
+        acceptance reads only the tree, the target and the draft, so it runs on the main stream
+        while the attention may still be running (the attention's outputs are not its input in
+        this path; the device status word is OR-ed atomically by both)."""
         main = torch.cuda.current_stream(self.device)
         calls = self.bind(inp, branch_stream=side)
         side.wait_stream(main)
@@ -316,7 +318,7 @@ class VerifyStep:
         for name in self.PARTS:
             if name in self.BRANCH or name not in calls:
                 continue
-            if name in ("accept", "commit") and not joined:
+            if name == "commit" and not joined:
                 main.wait_stream(side)
                 joined = True
             calls[name]()
