@@ -719,6 +719,19 @@ int check_common(int dt, int B, int d, int K) {
   return MV_OK;
 }
 
+// LDS the projection launch requests beyond what its workgroups use, so that each takes
+// kProjLdsFootprint bytes: at most 3 then share a CU with the co-resident tree attention's
+// workgroup (75776 bytes of LDS, one wave per SIMD) while the heads run beside it on another
+// stream; 4 (the register limit) left the attention wave too little issue and the forked
+// 70B-share step 2.4% slower (1268 vs 1237-1241 steps/s; 2 per CU: 1229).  Alone, 5 fit on a
+// CU, more than the 4 that measured full bandwidth, so a serial step is unchanged (1116 both).
+constexpr size_t kProjLdsFootprint = 28 * 1024;
+template <int NW, int NCT, int MODE>
+constexpr size_t gemv_lds_pad() {
+  const size_t used = sizeof(float) * (static_cast<size_t>(NW) * kRows * (16 * NCT + 1) + kRows * 8 * NCT);
+  return MODE == 1 && used < kProjLdsFootprint ? kProjLdsFootprint - used : 0;
+}
+
 // Waves per workgroup: the smallest power of two that gives the launch about MV_GEMV_WAVES
 // waves (12 per SIMD) to cover HBM latency, while each wave keeps at least 8 k-steps.
 int pick_nw(long long nblocks, int T, int cap) {
@@ -743,7 +756,7 @@ int launch_gemv(int dt, const GemvParams& p, int K, hipStream_t st) {
   const int nct = nct_for(p.B);
   const int nw = pick_nw(static_cast<long long>(p.nrb) * K, p.T, 16 / nct > 8 ? 8 : 16 / nct);
 #define MV_GEMV_CASE(NW_, NCT_) \
-  if (nw == NW_ && nct == NCT_) { gemv_bf16_kernel<NW_, NCT_, MODE><<<grid, NW_ * 64, 0, st>>>(p); return launch_status(); }
+  if (nw == NW_ && nct == NCT_) { gemv_bf16_kernel<NW_, NCT_, MODE><<<grid, NW_ * 64, gemv_lds_pad<NW_, NCT_, MODE>(), st>>>(p); return launch_status(); }
   MV_GEMV_CASE(1, 1) MV_GEMV_CASE(2, 1) MV_GEMV_CASE(4, 1) MV_GEMV_CASE(8, 1)
   MV_GEMV_CASE(1, 2) MV_GEMV_CASE(2, 2) MV_GEMV_CASE(4, 2) MV_GEMV_CASE(8, 2)
   MV_GEMV_CASE(1, 4) MV_GEMV_CASE(2, 4) MV_GEMV_CASE(4, 4)
