@@ -25,9 +25,10 @@ def _oracle_step(wl, x, target):
     return heads, cand, tree
 
 
-def _check_step(wl, seed, attn_select=None):
+def _check_step(wl, seed, attn_select=None, fork=False):
     """One GPU step vs the oracle.  ``attn_select`` = (b, h, i) rows whose attention output
-    is compared (all rows when None); everything else is compared in full."""
+    is compared (all rows when None); everything else is compared in full.  ``fork`` runs the
+    step forked (the attention branch, with the co-resident launch, on a second stream)."""
     parents = list(wl.parents)
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     xh = W.gen_heads(wl, seed)
@@ -63,8 +64,8 @@ def _check_step(wl, seed, attn_select=None):
         assert np.all(srt[..., -1] - srt[..., -2] > 1e-4 * np.maximum(1.0, np.abs(srt[..., -1])))
     else:
         inp["target"] = dev(target, dt)
-    print(f"step {wl.name} seed={seed}", flush=True)
-    step.run(inp)
+    print(f"step {wl.name} seed={seed} fork={fork}", flush=True)
+    step.run(inp, torch.cuda.Stream() if fork else None)
     torch.cuda.synchronize()
     assert int(step.status.item()) == 0
     # heads: ids exact (near-ties counted), candidate tokens and tree exact
@@ -105,9 +106,10 @@ def test_step_tiny_fp32():
     _check_step(W.WORKLOADS["c1"], 1)
 
 
-def test_step_llama8b_full():
+@pytest.mark.parametrize("fork", [False, True], ids=["serial", "forked"])
+def test_step_llama8b_full(fork):
     require_gpu()
-    lens = _check_step(W.WORKLOADS["c2"], 2)
+    lens = _check_step(W.WORKLOADS["c2"], 2, fork=fork)
     print("accepted length", lens.tolist())
 
 
@@ -126,7 +128,8 @@ def test_step_target_head_llama8b_full():
     print("accept lengths", lens.tolist())
 
 
-def test_step_70b_share_full():
+@pytest.mark.parametrize("fork", [False, True], ids=["serial", "forked"])
+def test_step_70b_share_full(fork):
     """The 70B-shaped one-GPU share at full size (batch 8, 64/8 heads, prefixes in
     [8192, 32768], d = 8192, 4 heads over V = 32000): all 32 (sequence, head) candidate lists,
     the tree tokens, the accepted lengths, paths and tokens of all 8 sequences and the
@@ -139,5 +142,5 @@ def test_step_70b_share_full():
     for b in range(wl.B):
         sel += [(b, int(rng.integers(wl.Hq)), int(rng.integers(wl.N))) for _ in range(3)]
         sel += [(b, int(rng.integers(wl.Hq)), wl.N - 1)]
-    lens = _check_step(wl, 3, attn_select=sel)
+    lens = _check_step(wl, 3, attn_select=sel, fork=fork)
     print("accepted lengths", lens.tolist())
