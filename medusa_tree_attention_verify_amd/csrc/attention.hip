@@ -132,274 +132,274 @@ void tree_attn_bf16_kernel(const AttnParams p) {
   // over the XCDs, and the query tiles of one job stay on one XCD, where they share its K/V.
   // vb is the workgroup index (blockIdx.x, or each index a persistent launch walks).
   auto run = [&](const int vb) {
-  const int xcd = vb % kXcds, pos = vb / kXcds;
-  const int qt = pos % p.qtiles;
-  const int job = (pos / p.qtiles) * kXcds + xcd;
-  if (job >= p.jobs) return;
-  const int g = job % p.Hkv;
-  int b, c, ncb, ck;
-  if (p.jtab) {
-    const uint32_t e = p.jtab[job / p.Hkv];
-    if (e == kNoJob) return;
-    b = static_cast<int>(e >> 16);
-    c = static_cast<int>(e & 0xffffu);
-    ncb = p.plan[3 * b];
-    ck = p.plan[3 * b + 1];
-  } else {
-    c = (job / p.Hkv) % p.nchunks;
-    const int rank = job / (p.Hkv * p.nchunks);
-    b = p.order ? p.order[rank] : rank;
-    ck = p.CK;
-    ncb = -1;
-  }
-
-  const int Lb = clamp_prefix(p, p.prefix_len[b], threadIdx.x == 0 && qt == 0 && c == 0 && g == 0);
-  if (ncb < 0) ncb = max(1, (Lb + p.CK - 1) / p.CK);
-  if (c >= ncb) return;
-  const int kbeg = c * ck, kend = min(Lb, kbeg + ck);
-  const bool last = c == ncb - 1;
-  const int ntp = kend > kbeg ? (kend - kbeg + kKT - 1) / kKT : 0;
-  const int ntiles = ntp + (last ? (p.N + kKT - 1) / kKT : 0);
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int l32 = lane & 31, half = lane >> 5;
-  const int m = qt * (NWV * 32) + wv * 32 + l32;
-  const bool qvalid = m < p.M;
-  const int node = qvalid ? m / p.G : 0;
-  const int h = g * p.G + (qvalid ? m % p.G : 0);
-
-  // Q is the B operand of S^T = K Q^T: lane holds query l32, dims ks*16 + 8*half .. +8.
-  bf16x8 qreg[KS];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (static_cast<size_t>(b * p.N + node) * p.Hq + h) * DH;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 t4 = qvalid ? *reinterpret_cast<const uint4*>(qrow + ks * 16 + half * 8) : make_uint4(0, 0, 0, 0);
-      qreg[ks] = as_bf16x8(t4);
-    }
-  }
-  const size_t kvbase = (static_cast<size_t>(b) * p.Hkv + g) * p.L_cap * DH;
-  const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + kvbase;
-  const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + kvbase;
-
-  auto tile_rows = [&](int t, int& row0, int& nv) {
-    if (t < ntp) {
-      row0 = kbeg + t * kKT;
-      nv = min(kKT, kend - row0);
+    const int xcd = vb % kXcds, pos = vb / kXcds;
+    const int qt = pos % p.qtiles;
+    const int job = (pos / p.qtiles) * kXcds + xcd;
+    if (job >= p.jobs) return;
+    const int g = job % p.Hkv;
+    int b, c, ncb, ck;
+    if (p.jtab) {
+      const uint32_t e = p.jtab[job / p.Hkv];
+      if (e == kNoJob) return;
+      b = static_cast<int>(e >> 16);
+      c = static_cast<int>(e & 0xffffu);
+      ncb = p.plan[3 * b];
+      ck = p.plan[3 * b + 1];
     } else {
-      const int tt = t - ntp;
-      row0 = Lb + tt * kKT;
-      nv = min(kKT, p.N - tt * kKT);
+      c = (job / p.Hkv) % p.nchunks;
+      const int rank = job / (p.Hkv * p.nchunks);
+      b = p.order ? p.order[rank] : rank;
+      ck = p.CK;
+      ncb = -1;
     }
-  };
-  // One register set of prefetched K/V pieces: tile t+1 is requested while tile t computes.
-  // Buffer loads over this (sequence, KV head)'s slice of the cache: rows past a partial tile
-  // and requests past the last tile get an offset beyond the slice, which the hardware's range
-  // check turns into zeros, so no load sits under a branch.
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Kg), 0, p.L_cap * DH * 2, kBufferRsrcWord3);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Vg), 0, p.L_cap * DH * 2, kBufferRsrcWord3);
-  uint4 kr[PPT], vr[PPT];
-  auto gload = [&](int t, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
-    int row0 = 0, nv = 0;
-    if (t < ntiles) tile_rows(t, row0, nv);
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int pc = tid + i * NT, key = pc / DG, dg = pc % DG;
-      const int off = key < nv ? ((row0 + key) * DH + dg * 8) * 2 : kBufferOutOfRange;
-      kr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
-      vr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
-    }
-  };
-  auto swrite = [&](int buf, const uint4 (&kr)[PPT], const uint4 (&vr)[PPT]) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int pc = tid + i * NT, key = pc / DG, dg = pc % DG;
-      *reinterpret_cast<uint4*>(&Ks[buf][key * KP + dg * 8]) = kr[i];
-      *reinterpret_cast<uint4*>(&Vs[buf][key * VKP + dg * 8]) = vr[i];
-    }
-  };
 
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const float lazy = kLazyLog2 / p.scale_log2;  // in raw score units
+    const int Lb = clamp_prefix(p, p.prefix_len[b], threadIdx.x == 0 && qt == 0 && c == 0 && g == 0);
+    if (ncb < 0) ncb = max(1, (Lb + p.CK - 1) / p.CK);
+    if (c >= ncb) return;
+    const int kbeg = c * ck, kend = min(Lb, kbeg + ck);
+    const bool last = c == ncb - 1;
+    const int ntp = kend > kbeg ? (kend - kbeg + kKT - 1) / kKT : 0;
+    const int ntiles = ntp + (last ? (p.N + kKT - 1) / kKT : 0);
 
-  auto compute = [&](int t) {
-    const int buf = t & 1;
-    f32x16 sacc[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[st][v] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&Ks[buf][(st * 32 + l32) * KP + ks * 16 + half * 8]);
-        sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qreg[ks], sacc[st], 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    int row0, nv;
-    tile_rows(t, row0, nv);
-    const bool tree = t >= ntp;
-    // 32x32 output layout: lane holds query l32 and keys 32*st + 8*(v/4) + 4*half + v%4.
-    f32x16 (&sv)[2] = sacc;  // scores, then probabilities, in place
-    // Visibility of the 32 scores this lane holds, bit 16*st + v: all set for a full prefix
-    // tile; the tail of a partial tile and non-ancestors of a tree tile are cleared.
-    uint32_t vis = 0xffffffffu;
-    if (tree || nv < kKT) {
-      uint32_t aw[2] = {0xffffffffu, 0xffffffffu};
-      if (tree) {
-        const int w0 = 2 * (t - ntp);
-        const uint32_t* arow = p.anc + static_cast<size_t>(b) * p.mask_stride +
-                               static_cast<size_t>(node) * p.W;
-        aw[0] = qvalid ? arow[w0] : 0u;
-        aw[1] = (qvalid && w0 + 1 < p.W) ? arow[w0 + 1] : 0u;
-      }
-      vis = 0u;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kl = 8 * (v >> 2) + 4 * half + (v & 3);
-          const bool ok = st * 32 + kl < nv && ((aw[st] >> kl) & 1u);
-          vis |= static_cast<uint32_t>(ok) << (16 * st + v);
-        }
-    }
-    // Online softmax; the running max is kept in raw score units and the scale is folded into
-    // the exp2 argument: p = 2^(s*c - m*c), c = scale*log2(e), one FMA per score.
-    float tmax = -INFINITY;
-    if (vis == 0xffffffffu) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sv[st][v]);
-    } else {
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          sv[st][v] = ((vis >> (16 * st + v)) & 1u) ? sv[st][v] : -INFINITY;
-          tmax = fmaxf(tmax, sv[st][v]);
-        }
-    }
-    {  // lanes l and l^32 hold the two key halves of one query
-      const LanePair t2 = swap32(__float_as_uint(tmax));
-      tmax = fmaxf(__uint_as_float(t2.a), __uint_as_float(t2.b));
-    }
-    const float c2 = p.scale_log2;
-    // Lazy rescaling: the running max moves only when a score passes it by more than
-    // kLazyLog2 in log2 units.  Until then the stale max keeps every p <= 2^kLazyLog2, well
-    // inside fp32 and bf16 range, and the O rescale below is skipped; (m, l, O) stay an exact
-    // log-sum-exp triple for whatever reference max they carry.
-    const float m_new = tmax > m_run + lazy ? tmax : m_run;
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
-    const float mc = m_use * c2;
-    float lsum = 0.f;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        sv[st][v] = __builtin_amdgcn_exp2f(fmaf(sv[st][v], c2, -mc));
-        lsum += sv[st][v];
-      }
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int l32 = lane & 31, half = lane >> 5;
+    const int m = qt * (NWV * 32) + wv * 32 + l32;
+    const bool qvalid = m < p.M;
+    const int node = qvalid ? m / p.G : 0;
+    const int h = g * p.G + (qvalid ? m % p.G : 0);
+
+    // Q is the B operand of S^T = K Q^T: lane holds query l32, dims ks*16 + 8*half .. +8.
+    bf16x8 qreg[KS];
     {
-      const LanePair t2 = swap32(__float_as_uint(lsum));
-      lsum = __uint_as_float(t2.a) + __uint_as_float(t2.b);
+      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (static_cast<size_t>(b * p.N + node) * p.Hq + h) * DH;
+  #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 t4 = qvalid ? *reinterpret_cast<const uint4*>(qrow + ks * 16 + half * 8) : make_uint4(0, 0, 0, 0);
+        qreg[ks] = as_bf16x8(t4);
+      }
     }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-    // Keep the P.V operand reads below the softmax: hoisting them above it would keep 16
-    // operand registers per lane alive across the exp2 work.
-    __builtin_amdgcn_sched_barrier(0);
-    if (!__all(alpha == 1.0f)) {  // the running max moved for some query of this wave
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
-    }
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int o = 8 * hf;
-        const uint4 pw = make_uint4(pack_bf16x2(sv[st][o + 0], sv[st][o + 1]),
-                                    pack_bf16x2(sv[st][o + 2], sv[st][o + 3]),
-                                    pack_bf16x2(sv[st][o + 4], sv[st][o + 5]),
-                                    pack_bf16x2(sv[st][o + 6], sv[st][o + 7]));
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          // A operand of O^T += V^T P^T: lane (dim 32*db + l32, key group half) needs V[key][dim]
-          // for the 8 keys whose probabilities it holds in pw.  Two transposed LDS reads
-          // (ds_read_b64_tr_b16): in each 16-lane group, output lane j gets element j%4 of the
-          // 4-element read of group lane 4e + j/4, so group lane i reads dims
-          // 16*(G&1) + 4*(i&3) .. +3 of key row 4*half + i/4 (and that row + 8).  With the
-          // V pitch of DH+32 elements the 4 rows x 4 column chunks of two groups land on 64
-          // distinct banks.
-          const int G = lane >> 4, il = lane & 15;
-          const uint16_t* vp = &Vs[buf][(st * 32 + hf * 16 + 4 * half + (il >> 2)) * VKP + db * 32 + 16 * (G & 1) + 4 * (il & 3)];
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp));
-          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 8 * VKP));
-          const v8i16 a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, a16);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pw), oacc[db], 0, 0, 0);
+    const size_t kvbase = (static_cast<size_t>(b) * p.Hkv + g) * p.L_cap * DH;
+    const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + kvbase;
+    const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + kvbase;
+
+    auto tile_rows = [&](int t, int& row0, int& nv) {
+      if (t < ntp) {
+        row0 = kbeg + t * kKT;
+        nv = min(kKT, kend - row0);
+      } else {
+        const int tt = t - ntp;
+        row0 = Lb + tt * kKT;
+        nv = min(kKT, p.N - tt * kKT);
+      }
+    };
+    // One register set of prefetched K/V pieces: tile t+1 is requested while tile t computes.
+    // Buffer loads over this (sequence, KV head)'s slice of the cache: rows past a partial tile
+    // and requests past the last tile get an offset beyond the slice, which the hardware's range
+    // check turns into zeros, so no load sits under a branch.
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(Kg), 0, p.L_cap * DH * 2, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(Vg), 0, p.L_cap * DH * 2, kBufferRsrcWord3);
+    uint4 kr[PPT], vr[PPT];
+    auto gload = [&](int t, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
+      int row0 = 0, nv = 0;
+      if (t < ntiles) tile_rows(t, row0, nv);
+  #pragma unroll
+      for (int i = 0; i < PPT; ++i) {
+        const int pc = tid + i * NT, key = pc / DG, dg = pc % DG;
+        const int off = key < nv ? ((row0 + key) * DH + dg * 8) * 2 : kBufferOutOfRange;
+        kr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+        vr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+      }
+    };
+    auto swrite = [&](int buf, const uint4 (&kr)[PPT], const uint4 (&vr)[PPT]) {
+  #pragma unroll
+      for (int i = 0; i < PPT; ++i) {
+        const int pc = tid + i * NT, key = pc / DG, dg = pc % DG;
+        *reinterpret_cast<uint4*>(&Ks[buf][key * KP + dg * 8]) = kr[i];
+        *reinterpret_cast<uint4*>(&Vs[buf][key * VKP + dg * 8]) = vr[i];
+      }
+    };
+
+    f32x16 oacc[DB];
+  #pragma unroll
+    for (int db = 0; db < DB; ++db)
+  #pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    const float lazy = kLazyLog2 / p.scale_log2;  // in raw score units
+
+    auto compute = [&](int t) {
+      const int buf = t & 1;
+      f32x16 sacc[2];
+  #pragma unroll
+      for (int st = 0; st < 2; ++st) {
+  #pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[st][v] = 0.f;
+  #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 a = *reinterpret_cast<const uint4*>(&Ks[buf][(st * 32 + l32) * KP + ks * 16 + half * 8]);
+          sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qreg[ks], sacc[st], 0, 0, 0);
         }
       }
-  };
-
-  // Pipeline: LDS holds tile t (computing) and tile t+1 (stored at the end of iteration t);
-  // tile t+1's loads are issued before tile t's compute, which covers their latency.  (A
-  // second register set, two tiles ahead, measured no faster and cost 22 registers.)
-  gload(0, kr, vr);
-  swrite(0, kr, vr);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    gload(t + 1, kr, vr);
-    compute(t);
-    swrite((t + 1) & 1, kr, vr);
-    __syncthreads();
-  }
-
-  if (!qvalid) return;
-  // Output layout of O^T: lane holds query l32, dims db*32 + 8*(v/4) + 4*half + v%4.
-  if (ncb == 1) {
-    const float inv = 1.f / l_run;
-    uint16_t* orow = static_cast<uint16_t*>(p.out) + (static_cast<size_t>(b * p.N + node) * p.Hq + h) * DH;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int vq = 0; vq < 4; ++vq) {
-        const int d0 = db * 32 + 8 * vq + 4 * half;
-        uint2 w2;
-        w2.x = pack_bf16x2(oacc[db][vq * 4 + 0] * inv, oacc[db][vq * 4 + 1] * inv);
-        w2.y = pack_bf16x2(oacc[db][vq * 4 + 2] * inv, oacc[db][vq * 4 + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + d0) = w2;
+      __builtin_amdgcn_sched_barrier(0);
+      int row0, nv;
+      tile_rows(t, row0, nv);
+      const bool tree = t >= ntp;
+      // 32x32 output layout: lane holds query l32 and keys 32*st + 8*(v/4) + 4*half + v%4.
+      f32x16 (&sv)[2] = sacc;  // scores, then probabilities, in place
+      // Visibility of the 32 scores this lane holds, bit 16*st + v: all set for a full prefix
+      // tile; the tail of a partial tile and non-ancestors of a tree tile are cleared.
+      uint32_t vis = 0xffffffffu;
+      if (tree || nv < kKT) {
+        uint32_t aw[2] = {0xffffffffu, 0xffffffffu};
+        if (tree) {
+          const int w0 = 2 * (t - ntp);
+          const uint32_t* arow = p.anc + static_cast<size_t>(b) * p.mask_stride +
+                                 static_cast<size_t>(node) * p.W;
+          aw[0] = qvalid ? arow[w0] : 0u;
+          aw[1] = (qvalid && w0 + 1 < p.W) ? arow[w0 + 1] : 0u;
+        }
+        vis = 0u;
+  #pragma unroll
+        for (int st = 0; st < 2; ++st)
+  #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int kl = 8 * (v >> 2) + 4 * half + (v & 3);
+            const bool ok = st * 32 + kl < nv && ((aw[st] >> kl) & 1u);
+            vis |= static_cast<uint32_t>(ok) << (16 * st + v);
+          }
       }
-    if (p.lse && half == 0)
-      p.lse[(static_cast<size_t>(b) * p.Hq + h) * p.N + node] = (m_run * p.scale_log2 + log2f(l_run)) * kLn2;
-  } else {
-    // The partial output goes out in the MFMA register order: one 16 KB block per (job, query
-    // tile, wave), float4 (db, vq) of lane l at [(db*4 + vq)*64 + l], so every store
-    // instruction writes 1 KB of consecutive bytes (the combine reads it in the same order).
-    // chunk slot: per (sequence, KV head) chunk c, or the chunk-job index of a balanced plan
-    const size_t rowi = p.plan ? (static_cast<size_t>(job / p.Hkv) * p.Hq + h) * p.N + node
-                               : (static_cast<size_t>(b * p.Hq + h) * p.N + node) * p.nchunks + c;
-    const size_t slot = p.plan ? ((static_cast<size_t>(job / p.Hkv) * p.Hkv + g) * p.qtiles + qt) * NWV + wv
-                               : ((static_cast<size_t>(b * p.Hkv + g) * p.nchunks + c) * p.qtiles + qt) * NWV + wv;
-    float4* po = reinterpret_cast<float4*>(p.part_o) + slot * (DB * 4 * 64) + lane;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int vq = 0; vq < 4; ++vq)
-        po[(db * 4 + vq) * 64] =
-            make_float4(oacc[db][vq * 4 + 0], oacc[db][vq * 4 + 1], oacc[db][vq * 4 + 2], oacc[db][vq * 4 + 3]);
-    if (half == 0) p.part_ml[rowi] = make_float2(m_run * p.scale_log2, l_run);
-  }
+      // Online softmax; the running max is kept in raw score units and the scale is folded into
+      // the exp2 argument: p = 2^(s*c - m*c), c = scale*log2(e), one FMA per score.
+      float tmax = -INFINITY;
+      if (vis == 0xffffffffu) {
+  #pragma unroll
+        for (int st = 0; st < 2; ++st)
+  #pragma unroll
+          for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sv[st][v]);
+      } else {
+  #pragma unroll
+        for (int st = 0; st < 2; ++st)
+  #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            sv[st][v] = ((vis >> (16 * st + v)) & 1u) ? sv[st][v] : -INFINITY;
+            tmax = fmaxf(tmax, sv[st][v]);
+          }
+      }
+      {  // lanes l and l^32 hold the two key halves of one query
+        const LanePair t2 = swap32(__float_as_uint(tmax));
+        tmax = fmaxf(__uint_as_float(t2.a), __uint_as_float(t2.b));
+      }
+      const float c2 = p.scale_log2;
+      // Lazy rescaling: the running max moves only when a score passes it by more than
+      // kLazyLog2 in log2 units.  Until then the stale max keeps every p <= 2^kLazyLog2, well
+      // inside fp32 and bf16 range, and the O rescale below is skipped; (m, l, O) stay an exact
+      // log-sum-exp triple for whatever reference max they carry.
+      const float m_new = tmax > m_run + lazy ? tmax : m_run;
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+      const float mc = m_use * c2;
+      float lsum = 0.f;
+  #pragma unroll
+      for (int st = 0; st < 2; ++st)
+  #pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          sv[st][v] = __builtin_amdgcn_exp2f(fmaf(sv[st][v], c2, -mc));
+          lsum += sv[st][v];
+        }
+      {
+        const LanePair t2 = swap32(__float_as_uint(lsum));
+        lsum = __uint_as_float(t2.a) + __uint_as_float(t2.b);
+      }
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+      // Keep the P.V operand reads below the softmax: hoisting them above it would keep 16
+      // operand registers per lane alive across the exp2 work.
+      __builtin_amdgcn_sched_barrier(0);
+      if (!__all(alpha == 1.0f)) {  // the running max moved for some query of this wave
+  #pragma unroll
+        for (int db = 0; db < DB; ++db)
+  #pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+      }
+  #pragma unroll
+      for (int st = 0; st < 2; ++st)
+  #pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int o = 8 * hf;
+          const uint4 pw = make_uint4(pack_bf16x2(sv[st][o + 0], sv[st][o + 1]),
+                                      pack_bf16x2(sv[st][o + 2], sv[st][o + 3]),
+                                      pack_bf16x2(sv[st][o + 4], sv[st][o + 5]),
+                                      pack_bf16x2(sv[st][o + 6], sv[st][o + 7]));
+  #pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            // A operand of O^T += V^T P^T: lane (dim 32*db + l32, key group half) needs V[key][dim]
+            // for the 8 keys whose probabilities it holds in pw.  Two transposed LDS reads
+            // (ds_read_b64_tr_b16): in each 16-lane group, output lane j gets element j%4 of the
+            // 4-element read of group lane 4e + j/4, so group lane i reads dims
+            // 16*(G&1) + 4*(i&3) .. +3 of key row 4*half + i/4 (and that row + 8).  With the
+            // V pitch of DH+32 elements the 4 rows x 4 column chunks of two groups land on 64
+            // distinct banks.
+            const int G = lane >> 4, il = lane & 15;
+            const uint16_t* vp = &Vs[buf][(st * 32 + hf * 16 + 4 * half + (il >> 2)) * VKP + db * 32 + 16 * (G & 1) + 4 * (il & 3)];
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 8 * VKP));
+            const v8i16 a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, a16);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pw), oacc[db], 0, 0, 0);
+          }
+        }
+    };
+
+    // Pipeline: LDS holds tile t (computing) and tile t+1 (stored at the end of iteration t);
+    // tile t+1's loads are issued before tile t's compute, which covers their latency.  (A
+    // second register set, two tiles ahead, measured no faster and cost 22 registers.)
+    gload(0, kr, vr);
+    swrite(0, kr, vr);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      gload(t + 1, kr, vr);
+      compute(t);
+      swrite((t + 1) & 1, kr, vr);
+      __syncthreads();
+    }
+
+    if (!qvalid) return;
+    // Output layout of O^T: lane holds query l32, dims db*32 + 8*(v/4) + 4*half + v%4.
+    if (ncb == 1) {
+      const float inv = 1.f / l_run;
+      uint16_t* orow = static_cast<uint16_t*>(p.out) + (static_cast<size_t>(b * p.N + node) * p.Hq + h) * DH;
+  #pragma unroll
+      for (int db = 0; db < DB; ++db)
+  #pragma unroll
+        for (int vq = 0; vq < 4; ++vq) {
+          const int d0 = db * 32 + 8 * vq + 4 * half;
+          uint2 w2;
+          w2.x = pack_bf16x2(oacc[db][vq * 4 + 0] * inv, oacc[db][vq * 4 + 1] * inv);
+          w2.y = pack_bf16x2(oacc[db][vq * 4 + 2] * inv, oacc[db][vq * 4 + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + d0) = w2;
+        }
+      if (p.lse && half == 0)
+        p.lse[(static_cast<size_t>(b) * p.Hq + h) * p.N + node] = (m_run * p.scale_log2 + log2f(l_run)) * kLn2;
+    } else {
+      // The partial output goes out in the MFMA register order: one 16 KB block per (job, query
+      // tile, wave), float4 (db, vq) of lane l at [(db*4 + vq)*64 + l], so every store
+      // instruction writes 1 KB of consecutive bytes (the combine reads it in the same order).
+      // chunk slot: per (sequence, KV head) chunk c, or the chunk-job index of a balanced plan
+      const size_t rowi = p.plan ? (static_cast<size_t>(job / p.Hkv) * p.Hq + h) * p.N + node
+                                 : (static_cast<size_t>(b * p.Hq + h) * p.N + node) * p.nchunks + c;
+      const size_t slot = p.plan ? ((static_cast<size_t>(job / p.Hkv) * p.Hkv + g) * p.qtiles + qt) * NWV + wv
+                                 : ((static_cast<size_t>(b * p.Hkv + g) * p.nchunks + c) * p.qtiles + qt) * NWV + wv;
+      float4* po = reinterpret_cast<float4*>(p.part_o) + slot * (DB * 4 * 64) + lane;
+  #pragma unroll
+      for (int db = 0; db < DB; ++db)
+  #pragma unroll
+        for (int vq = 0; vq < 4; ++vq)
+          po[(db * 4 + vq) * 64] =
+              make_float4(oacc[db][vq * 4 + 0], oacc[db][vq * 4 + 1], oacc[db][vq * 4 + 2], oacc[db][vq * 4 + 3]);
+      if (half == 0) p.part_ml[rowi] = make_float2(m_run * p.scale_log2, l_run);
+    }
   };
   if constexpr (PERSIST) {
     // Beside the heads' streaming waves on the same SIMDs, this wave wins the issue
