@@ -394,11 +394,16 @@ __device__ void head_epilogue(const GemvParams& p, int k, int rb, float (*ys)[BC
 }
 
 // ---- bf16 weights: MFMA streaming loop.
+// LDS arrays of gemv_bf16_kernel: the waves' partial sums and the reduced outputs (the
+// projection launch pads its LDS request from their sizes).
+template <int NW, int NCT> using GemvRed = float[NW][kRows][16 * NCT + 1];
+template <int NCT> using GemvYs = float[kRows][8 * NCT];
+
 template <int NW, int NCT, int MODE>
 __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(const GemvParams p) {
   constexpr int RT = kRows / 16, BC = 8 * NCT, U = MV_GEMV_U;
-  __shared__ float red[NW][kRows][16 * NCT + 1];
-  __shared__ float ys[kRows][BC];
+  __shared__ GemvRed<NW, NCT> red;
+  __shared__ GemvYs<NCT> ys;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int k = blockIdx.y, rb = blockIdx.x, row0 = rb * kRows;
 
@@ -728,7 +733,7 @@ int check_common(int dt, int B, int d, int K) {
 constexpr size_t kProjLdsFootprint = 28 * 1024;
 template <int NW, int NCT, int MODE>
 constexpr size_t gemv_lds_pad() {
-  const size_t used = sizeof(float) * (static_cast<size_t>(NW) * kRows * (16 * NCT + 1) + kRows * 8 * NCT);
+  const size_t used = sizeof(GemvRed<NW, NCT>) + sizeof(GemvYs<NCT>);
   return MODE == 1 && used < kProjLdsFootprint ? kProjLdsFootprint - used : 0;
 }
 
