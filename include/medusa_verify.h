@@ -146,6 +146,14 @@ MV_API int mv_medusa_head_project(int dt, int B, int d, int V, int K, const int*
                                   int s_max, const void* w_head, void* logits, void* ws,
                                   size_t ws_bytes, void* stream);
 
+/* The same projection, launched to run beside the co-resident tree attention
+ * (mv_tree_attn_verify_beside) on another stream: identical arguments, workspace, outputs and
+ * errors.  Its workgroups keep a footprint of which three fit on a CU beside the attention's,
+ * where the plain call's faster row-segment loads would fit only one. */
+MV_API int mv_medusa_head_project_beside(int dt, int B, int d, int V, int K,
+                                         const int* s_per_head, int s_max, const void* w_head,
+                                         void* logits, void* ws, size_t ws_bytes, void* stream);
+
 MV_API int mv_medusa_head_select(int dt, int B, int d, int V, int K, const int* s_per_head,
                                  int s_max, int32_t* topk_ids, float* topk_vals, int ld_topk,
                                  float* lse, void* ws, size_t ws_bytes, void* stream);

@@ -399,11 +399,23 @@ __device__ void head_epilogue(const GemvParams& p, int k, int rb, float (*ys)[BC
 template <int NW, int NCT> using GemvRed = float[NW][kRows][16 * NCT + 1];
 template <int NCT> using GemvYs = float[kRows][8 * NCT];
 
-template <int NW, int NCT, int MODE>
+// Row-segment weight loads (ROWLOAD, the projection when it runs alone).  Loading straight into
+// the MFMA operand layout reads 16 rows x 64 bytes per instruction; with d = 8192 those rows are
+// 16 KB apart and the 70B-share projection streamed at ~5.1 TB/s.  Reading 2 rows x 512
+// contiguous bytes per instruction and going through LDS to the operand layout streams it at
+// ~5.8 TB/s (412 -> 363 us; the Llama-3-8B-shaped projection 188 -> 181 us).  Each wave stages
+// its own k-range, so the LDS region is private to the wave and needs no workgroup barrier; its
+// 77 KB per workgroup leave room for one such workgroup beside the co-resident attention, which
+// is why the forked step keeps the MFMA-layout loads (1079 vs 1272 steps/s with this path).
+constexpr int kRlS = 8;                // k-steps per stage of the row-segment loads
+constexpr int kRlP = kRlS * 32 + 8;    // LDS row pitch (elements): conflict-free operand reads
+
+template <int NW, int NCT, int MODE, bool ROWLOAD = false>
 __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(const GemvParams p) {
   constexpr int RT = kRows / 16, BC = 8 * NCT, U = MV_GEMV_U;
   __shared__ GemvRed<NW, NCT> red;
   __shared__ GemvYs<NCT> ys;
+  __shared__ __attribute__((aligned(16))) uint16_t wst[ROWLOAD ? NW : 1][ROWLOAD ? kRows : 1][ROWLOAD ? kRlP : 8];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int k = blockIdx.y, rb = blockIdx.x, row0 = rb * kRows;
 
@@ -452,6 +464,58 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(const GemvParams p) 
             __builtin_bit_cast(bf16x8, a[rt]), __builtin_bit_cast(bf16x8, bv[ct]), acc[rt][ct], 0, 0, 0);
   };
   int t = t0;
+  if constexpr (ROWLOAD) {
+    // Row segments: each instruction reads 2 rows x 512 contiguous bytes (lanes 0-31 one row,
+    // 32-63 the next); a stage of kRlS k-steps (32 rows) goes through this wave's own LDS
+    // region and is read back in the MFMA operand layout.  Two stages of loads in flight.
+    uint16_t (*ws)[kRlP] = wst[w];
+    const int lr = lane >> 5, lc = (lane & 31) * 8;
+    auto sload = [&](int ts, u32x4 (&r)[kRows / 2]) {
+#pragma unroll
+      for (int i = 0; i < kRows / 2; ++i) {
+        const int row = min(row0 + 2 * i + lr, p.R - 1);
+        r[i] = wload(reinterpret_cast<const u32x4*>(Wk + static_cast<size_t>(row) * p.d + ts * 32 + lc));
+      }
+    };
+    auto sstore = [&](const u32x4 (&r)[kRows / 2]) {
+#pragma unroll
+      for (int i = 0; i < kRows / 2; ++i) *reinterpret_cast<u32x4*>(&ws[2 * i + lr][lc]) = r[i];
+    };
+    auto scompute = [&]() {
+#pragma unroll
+      for (int s = 0; s < kRlS; ++s) {
+        u32x4 a[RT], bv[NCT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          a[rt] = *reinterpret_cast<const u32x4*>(&ws[rt * 16 + (lane & 15)][s * 32 + (lane >> 4) * 8]);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) bv[ct] = bvalid[ct] ? bp[ct][s * BSTEP] : zero;
+        step(a, bv);
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) bp[ct] += kRlS * BSTEP;
+    };
+    const int nst = (t1 - t0) / kRlS;
+    u32x4 r0[kRows / 2], r1[kRows / 2];
+    if (nst > 0) sload(t, r0);
+    if (nst > 1) sload(t + kRlS, r1);
+    int st = 0;
+    for (; st + 2 <= nst; st += 2) {
+      sstore(r0);
+      scompute();
+      if (st + 2 < nst) sload(t + (st + 2) * kRlS, r0);
+      sstore(r1);
+      scompute();
+      if (st + 3 < nst) sload(t + (st + 3) * kRlS, r1);
+    }
+    if (st < nst) {
+      sstore(r0);
+      scompute();
+    }
+    t += nst * kRlS;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) ap[rt] += nst * kRlS * 4;
+  }
   for (; t + U <= t1; t += U) {
     u32x4 a[U][RT], bv[U][NCT];
 #pragma unroll
@@ -724,12 +788,11 @@ int check_common(int dt, int B, int d, int K) {
   return MV_OK;
 }
 
-// LDS the projection launch requests beyond what its workgroups use, so that each takes
-// kProjLdsFootprint bytes: at most 3 then share a CU with the co-resident tree attention's
-// workgroup (75776 bytes of LDS, one wave per SIMD) while the heads run beside it on another
-// stream; 4 (the register limit) left the attention wave too little issue and the forked
-// 70B-share step 2.4% slower (1268 vs 1237-1241 steps/s; 2 per CU: 1229).  Alone, 5 fit on a
-// CU, more than the 4 that measured full bandwidth, so a serial step is unchanged (1116 both).
+// LDS the projection launch beside the co-resident tree attention requests beyond what its
+// workgroups use, so that each takes kProjLdsFootprint bytes: at most 3 then share a CU with
+// the attention's workgroup (75776 bytes of LDS, one wave per SIMD); 4 (the register limit)
+// left the attention wave too little issue and the forked 70B-share step 2.4% slower (1268 vs
+// 1237-1241 steps/s; 2 per CU: 1229).
 constexpr size_t kProjLdsFootprint = 28 * 1024;
 template <int NW, int NCT, int MODE>
 constexpr size_t gemv_lds_pad() {
@@ -745,8 +808,11 @@ int pick_nw(long long nblocks, int T, int cap) {
   return nw;
 }
 
+// `beside`: the projection runs beside the co-resident tree attention on another stream; it then
+// takes the MFMA-layout loads with the LDS footprint above, otherwise (and for the residual) the
+// row-segment loads where the workgroup has at most 4 waves.
 template <int MODE>
-int launch_gemv(int dt, const GemvParams& p, int K, hipStream_t st) {
+int launch_gemv(int dt, const GemvParams& p, int K, hipStream_t st, bool beside = false) {
   const dim3 grid(p.nrb, K);
   if (dt == MV_F32) {
     const int nw = pick_nw(static_cast<long long>(p.nrb) * K, 1 << 30, 8);
@@ -760,8 +826,15 @@ int launch_gemv(int dt, const GemvParams& p, int K, hipStream_t st) {
   }
   const int nct = nct_for(p.B);
   const int nw = pick_nw(static_cast<long long>(p.nrb) * K, p.T, 16 / nct > 8 ? 8 : 16 / nct);
-#define MV_GEMV_CASE(NW_, NCT_) \
-  if (nw == NW_ && nct == NCT_) { gemv_bf16_kernel<NW_, NCT_, MODE><<<grid, NW_ * 64, gemv_lds_pad<NW_, NCT_, MODE>(), st>>>(p); return launch_status(); }
+#define MV_GEMV_CASE(NW_, NCT_)                                                                  \
+  if (nw == NW_ && nct == NCT_) {                                                                \
+    if (MODE == 1 && !beside && NW_ <= 4)                                                        \
+      gemv_bf16_kernel<NW_, NCT_, MODE, MODE == 1 && NW_ <= 4><<<grid, NW_ * 64, 0, st>>>(p);    \
+    else                                                                                         \
+      gemv_bf16_kernel<NW_, NCT_, MODE, false>                                                   \
+          <<<grid, NW_ * 64, beside ? gemv_lds_pad<NW_, NCT_, MODE>() : 0, st>>>(p);             \
+    return launch_status();                                                                      \
+  }
   MV_GEMV_CASE(1, 1) MV_GEMV_CASE(2, 1) MV_GEMV_CASE(4, 1) MV_GEMV_CASE(8, 1)
   MV_GEMV_CASE(1, 2) MV_GEMV_CASE(2, 2) MV_GEMV_CASE(4, 2) MV_GEMV_CASE(8, 2)
   MV_GEMV_CASE(1, 4) MV_GEMV_CASE(2, 4) MV_GEMV_CASE(4, 4)
@@ -831,9 +904,9 @@ static GemvParams head_params(int dt, int B, int d, int V, int K, const int* s_p
   return p;
 }
 
-MV_API int mv_medusa_head_project(int dt, int B, int d, int V, int K, const int* s_per_head,
-                                  int s_max, const void* w_head, void* logits, void* ws,
-                                  size_t ws_bytes, void* stream) {
+static int head_project(int dt, int B, int d, int V, int K, const int* s_per_head, int s_max,
+                        const void* w_head, void* logits, void* ws, size_t ws_bytes, void* stream,
+                        bool beside) {
   MV_TRY(check_common(dt, B, d, K));
   MV_TRY(check_select(V, K, s_per_head, s_max));
   if (!w_head) return MV_ERR_INVALID_ARG;
@@ -842,7 +915,21 @@ MV_API int mv_medusa_head_project(int dt, int B, int d, int V, int K, const int*
   GemvParams p = head_params(dt, B, d, V, K, s_per_head, s_max, L);
   p.W = w_head;
   p.logits = logits;
-  return launch_gemv<1>(dt, p, K, as_stream(stream));
+  return launch_gemv<1>(dt, p, K, as_stream(stream), beside);
+}
+
+MV_API int mv_medusa_head_project(int dt, int B, int d, int V, int K, const int* s_per_head,
+                                  int s_max, const void* w_head, void* logits, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  return head_project(dt, B, d, V, K, s_per_head, s_max, w_head, logits, ws, ws_bytes, stream,
+                      false);
+}
+
+MV_API int mv_medusa_head_project_beside(int dt, int B, int d, int V, int K,
+                                         const int* s_per_head, int s_max, const void* w_head,
+                                         void* logits, void* ws, size_t ws_bytes, void* stream) {
+  return head_project(dt, B, d, V, K, s_per_head, s_max, w_head, logits, ws, ws_bytes, stream,
+                      true);
 }
 
 MV_API int mv_medusa_head_select(int dt, int B, int d, int V, int K, const int* s_per_head,

@@ -187,7 +187,10 @@ class VerifyStep:
             off = 1 if self.lm_width else 0
             ld = D * s_max
             esz = 4
-            proj = wrap("mv_medusa_head_project", lib.mv_medusa_head_project, self.dt, B, d, Vh,
+            # forked: the projection shares the CUs with the co-resident attention, so it takes
+            # the launch sized for that (mv_medusa_head_project_beside)
+            pname = "mv_medusa_head_project_beside" if fork else "mv_medusa_head_project"
+            proj = wrap(pname, getattr(lib, pname), self.dt, B, d, Vh,
                         K, self._s_heads, s_max, _p(inp["w_head"]),
                         _p(self.draft_logits) if self.spec_lm else None, wsp, wsn, st)
             calls["heads_select"] = wrap("mv_medusa_head_select", lib.mv_medusa_head_select,

@@ -19,7 +19,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -87,13 +87,12 @@ def test_host_argument_checks():
     assert lib.mv_medusa_residual(L.MV_BF16, 1, 64, 1, P, P, None, None, 0, None) == L.MV_ERR_WORKSPACE
     assert lib.mv_medusa_residual(L.MV_BF16, 1, 64, 1, None, P, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
     s = L.int_array([4, 3])
-    assert lib.mv_medusa_head_project(L.MV_BF16, 1, 64, 100, 2, s, 17, P, None, P, 1 << 20,
-                                      None) == L.MV_ERR_UNSUPPORTED
     s_bad = L.int_array([5, 3])
-    assert lib.mv_medusa_head_project(L.MV_BF16, 1, 64, 100, 2, s_bad, 4, P, None, P, 1 << 20,
-                                      None) == L.MV_ERR_INVALID_ARG
-    assert lib.mv_medusa_head_project(L.MV_BF16, 1, 64, 100, 2, s, 4, P, None, None, 0,
-                                      None) == L.MV_ERR_WORKSPACE
+    for proj in (lib.mv_medusa_head_project, lib.mv_medusa_head_project_beside):
+        assert proj(L.MV_BF16, 1, 64, 100, 2, s, 17, P, None, P, 1 << 20, None) == L.MV_ERR_UNSUPPORTED
+        assert proj(L.MV_BF16, 1, 64, 100, 2, s_bad, 4, P, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
+        assert proj(L.MV_BF16, 1, 64, 100, 2, s, 4, P, None, None, 0, None) == L.MV_ERR_WORKSPACE
+        assert proj(L.MV_BF16, 1, 64, 100, 2, s, 4, None, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
     assert lib.mv_medusa_head_select(L.MV_BF16, 1, 64, 100, 2, s, 4, P, P, 3, None, P, 1 << 20,
                                      None) == L.MV_ERR_INVALID_ARG                 # ld_topk
     assert lib.mv_medusa_head_select(L.MV_BF16, 1, 64, 100, 2, s, 4, None, P, 0, None, P,
