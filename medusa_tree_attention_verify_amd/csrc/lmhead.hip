@@ -27,11 +27,10 @@
 namespace mv {
 namespace {
 
-constexpr int kLmRows = 64;        // vocabulary rows per workgroup
 constexpr int kLmMergeThreads = 256;
 
 struct LmParams {
-  int T, d, V, KT, nrb;         // KT = d / 32, nrb = vocabulary blocks (of 64 or 256 rows)
+  int T, d, V, KT, nrb;         // KT = d / 32, nrb = vocabulary blocks (of 64, 128 or 256 rows)
   const uint16_t* x;            // [T][d] bf16
   const uint16_t* w;            // [V][d] bf16
   float* pm;                    // [T][nrb] partial max
@@ -53,29 +52,37 @@ __device__ __forceinline__ int lm_xrow(const LmParams& p, int t) {
   return p.xrow ? t * p.xrow_mul + p.xrow[static_cast<size_t>(t) * p.xrow_stride] : t;
 }
 
-// Streaming kernel.  A workgroup owns 64 vocabulary rows, one 16-row MFMA tile per wave, and a
-// group of up to 128 target rows (NCT column tiles of 16).  Each wave streams its 16 weight rows
-// over the whole of d as the A operand of v_mfma_f32_16x16x32_bf16 (one 16-byte load per lane
-// and k-step, U k-steps per batch, the next batch in registers), so every weight byte crosses
-// HBM once per target-row group.  The target rows' slice of x for a batch is staged in LDS once
-// for the four waves (double-buffered, the next batch in registers) and read back as the B
-// operand; an 80-byte row pitch makes those 16-byte reads conflict-free.  Epilogue per column
-// tile: each wave reduces its 16 rows for every target row in registers (lane swaps between the
-// four 16-lane groups), the four waves meet in LDS, and the workgroup writes per target row the
-// partial (max, its id, sum exp(logit - max)) of its 64-row vocabulary block.
-constexpr int kLmThreads = 256;
+// Streaming kernel.  A workgroup owns 64 or 128 vocabulary rows (4 or 8 waves, one 16-row MFMA
+// tile per wave) and a group of up to 128 target rows (NCT column tiles of 16).  Each wave
+// streams its 16 weight rows over the whole of d as the A operand of v_mfma_f32_16x16x32_bf16
+// (one 16-byte load per lane and k-step, U k-steps per batch, the next batch in registers), so
+// every weight byte crosses HBM once per target-row group.  The target rows' slice of x for a
+// batch is staged in LDS once for all the waves (double-buffered, the next batch in registers)
+// and read back as the B operand; an 80-byte row pitch makes those 16-byte reads conflict-free.
+// Epilogue per column tile: each wave reduces its 16 rows for every target row in registers
+// (lane swaps between the four 16-lane groups), the waves meet in LDS, and the workgroup writes
+// per target row the partial (max, its id, sum exp(logit - max)) of its vocabulary block.
 constexpr int kLmXPitch = 40;  // bf16 elements per staged target row (32 + 8 padding)
+constexpr int kLmUPad = 32;    // bf16 elements between the k-step slices of one x batch
+
+// Waves per workgroup (16 vocabulary rows each): 8 in rows mode, and where a workgroup's x
+// buffers exceed 80 KB (8 column tiles with 4-step batches), so that two 4-wave workgroups
+// would not fit one CU's 160 KB of LDS; else 4.
+constexpr int lm_waves(int nct, int u, bool rows) {
+  return rows || 2 * u * (16 * nct * kLmXPitch + kLmUPad) * 2 > 80 * 1024 ? 8 : 4;
+}
 
 template <int NCT, int U, bool ROWS>
-__global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const LmParams p) {
+__global__ __launch_bounds__(64 * lm_waves(NCT, U, ROWS)) void lm_head_kernel(const LmParams p) {
+  constexpr int NWV = lm_waves(NCT, U, ROWS), NT = 64 * NWV;
   constexpr int NCOL = 16 * NCT;
-  constexpr int XP = NCOL * 4 * U;                           // 16-byte pieces of one x batch
-  constexpr int XPT = (XP + kLmThreads - 1) / kLmThreads;    // per thread
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][U][NCOL * kLmXPitch];
-  __shared__ float em[4][NCOL], es[4][NCOL];
-  __shared__ int ei[4][NCOL];
+  constexpr int XP = NCOL * 4 * U;            // 16-byte pieces of one x batch
+  constexpr int XPT = (XP + NT - 1) / NT;     // per thread
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][U][NCOL * kLmXPitch + kLmUPad];
+  __shared__ float em[NWV][NCOL], es[NWV][NCOL];
+  __shared__ int ei[NWV][NCOL];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int rb = blockIdx.x, row0 = rb * kLmRows, col0 = blockIdx.y * NCOL;
+  const int rb = blockIdx.x, row0 = rb * 16 * NWV, col0 = blockIdx.y * NCOL;
   const int nb = p.KT / U;
   // A operand: lane (row r = lane % 16, k-group g = lane / 16) of wave w reads the 16 bytes
   // W[row0 + 16w + r][32t + 8g .. +8] at k-step t; rows past V are clamped (not used).
@@ -84,26 +91,30 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const LmParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) a[u] = *reinterpret_cast<const u32x4*>(wp + static_cast<size_t>(bt * U + u) * 32);
   };
-  // x batch bt: piece q = (u, target row c, quarter qq) is x[col0 + c][32*(bt*U + u) + 8*qq .. +8];
+  // x batch bt: piece q = (target row c, u, quarter qq) is x[col0 + c][32*(bt*U + u) + 8*qq .. +8],
+  // so 4U consecutive lanes read one row's 64U contiguous bytes (16 rows x 64 bytes per load
+  // instruction, the previous order, put every piece of an instruction 8 KB apart at d = 4096);
   // target rows past T read row T-1 (their results are not written).
   auto xload = [&](int bt, u32x4 (&xr)[XPT]) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      const int q = tid + i * kLmThreads;
-      if (XP % kLmThreads == 0 || q < XP) {
-        const int u = q / (NCOL * 4), c = (q / 4) % NCOL, qq = q % 4;
+      const int q = tid + i * NT;
+      if (XP % NT == 0 || q < XP) {
+        const int c = q / (4 * U), u = (q / 4) % U, qq = q % 4;
         const int t = min(col0 + c, p.T - 1);
         xr[i] = *reinterpret_cast<const u32x4*>(p.x + static_cast<size_t>(ROWS ? lm_xrow(p, t) : t) * p.d +
                                                 32 * (bt * U + u) + 8 * qq);
       }
     }
   };
+  // (the k-step slices sit kLmUPad elements further apart than their size, 16 banks, so the
+  // 16 lanes of one row store to distinct banks)
   auto xstore = [&](int buf, const u32x4 (&xr)[XPT]) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      const int q = tid + i * kLmThreads;
-      if (XP % kLmThreads == 0 || q < XP) {
-        const int u = q / (NCOL * 4), c = (q / 4) % NCOL, qq = q % 4;
+      const int q = tid + i * NT;
+      if (XP % NT == 0 || q < XP) {
+        const int c = q / (4 * U), u = (q / 4) % U, qq = q % 4;
         *reinterpret_cast<u32x4*>(&Xs[buf][u][c * kLmXPitch + 8 * qq]) = xr[i];
       }
     }
@@ -216,13 +227,13 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const LmParams p) {
     }
   }
   __syncthreads();
-  for (int c = tid; c < NCOL; c += kLmThreads) {
+  for (int c = tid; c < NCOL; c += NT) {
     const int tok = col0 + c;
     if (tok >= p.T) break;
     float m = em[0][c], l = es[0][c], bv = em[0][c];
     int bi = ei[0][c];
 #pragma unroll
-    for (int q = 1; q < 4; ++q) {
+    for (int q = 1; q < NWV; ++q) {
       if (kv_better(em[q][c], ei[q][c], bv, bi)) {
         bv = em[q][c];
         bi = ei[q][c];
@@ -567,7 +578,6 @@ LmPlan plan_lm(int T, int d, int V) {
     a.ws_bytes = c.bytes();
     return a;
   }
-  a.nrb = ceil_div(V, kLmRows);
   const int need = ceil_div(std::min(T, 16 * kLmMaxNct), 16);
   for (int n : kLmNct)
     if (n >= need) {
@@ -578,6 +588,7 @@ LmPlan plan_lm(int T, int d, int V) {
   a.ngrp = ceil_div(T, a.ncols);
   const int KT = d / 32;
   a.u = KT % 4 == 0 ? 4 : (KT % 2 == 0 ? 2 : 1);
+  a.nrb = ceil_div(V, 16 * lm_waves(a.nct, a.u, false));
   Carver c(nullptr);
   const size_t np = static_cast<size_t>(T) * a.nrb;
   c.take<float>(np);
@@ -640,7 +651,7 @@ MV_API int mv_lm_head_argmax(int dt, int T, int d, int V, const void* x, const v
   const dim3 grid(a.nrb, a.ngrp);
   bool launched = false;
 #define MV_LM_CASE(NCT_, U_) \
-  if (!launched && a.nct == NCT_ && a.u == U_) { lm_head_kernel<NCT_, U_, false><<<grid, kLmThreads, 0, st>>>(p); launched = true; }
+  if (!launched && a.nct == NCT_ && a.u == U_) { lm_head_kernel<NCT_, U_, false><<<grid, 64 * lm_waves(NCT_, U_, false), 0, st>>>(p); launched = true; }
   MV_LM_CASE(1, 4) MV_LM_CASE(2, 4) MV_LM_CASE(3, 4) MV_LM_CASE(4, 4)
   MV_LM_CASE(5, 4) MV_LM_CASE(6, 4) MV_LM_CASE(7, 4) MV_LM_CASE(8, 4)
   MV_LM_CASE(1, 2) MV_LM_CASE(2, 2) MV_LM_CASE(3, 2) MV_LM_CASE(4, 2)
@@ -665,16 +676,17 @@ int lm_head_prob_rows(int T, int d, int V, const uint16_t* x, const int* xrow, i
                       hipStream_t st) {
   if (T < 1 || V < 1 || d < 32 || d % 32 != 0) return MV_ERR_UNSUPPORTED;
   LmParams p{};
-  p.T = T; p.d = d; p.V = V; p.KT = d / 32; p.nrb = ceil_div(V, kLmRows);
+  p.T = T; p.d = d; p.V = V; p.KT = d / 32;
   p.x = x; p.w = w;
   p.xrow = xrow; p.xrow_stride = xrow_stride; p.xrow_mul = xrow_mul;
   p.lse_in = lse_in; p.rows_out = rows_out;
   const int nct = ceil_div(std::min(T, 16 * kLmMaxNct), 16);
   const int u = p.KT % 4 == 0 ? 4 : (p.KT % 2 == 0 ? 2 : 1);
+  p.nrb = ceil_div(V, 16 * lm_waves(nct, u, true));
   const dim3 grid(p.nrb, ceil_div(T, 16 * nct));
   bool launched = false;
 #define MV_LMR_CASE(NCT_, U_) \
-  if (!launched && nct == NCT_ && u == U_) { lm_head_kernel<NCT_, U_, true><<<grid, kLmThreads, 0, st>>>(p); launched = true; }
+  if (!launched && nct == NCT_ && u == U_) { lm_head_kernel<NCT_, U_, true><<<grid, 64 * lm_waves(NCT_, U_, true), 0, st>>>(p); launched = true; }
   MV_LMR_CASE(1, 4) MV_LMR_CASE(2, 4) MV_LMR_CASE(3, 4) MV_LMR_CASE(4, 4)
   MV_LMR_CASE(5, 4) MV_LMR_CASE(6, 4) MV_LMR_CASE(7, 4) MV_LMR_CASE(8, 4)
   MV_LMR_CASE(1, 2) MV_LMR_CASE(2, 2) MV_LMR_CASE(3, 2) MV_LMR_CASE(4, 2)
