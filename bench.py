@@ -449,9 +449,10 @@ def main():
                     help="seconds of oracle work timed for cpu_baseline (whole steps, at least one)")
     ap.add_argument("--fork", default="auto", choices=["auto", "on", "off"],
                     help="graph launch: run the attention branch beside the heads (a parallel "
-                         "branch of the graph) or after them; auto = beside them for steps with "
-                         "Medusa heads over a batch (the 70B share: +3%%; one-sequence steps, "
-                         "whose attention is a short latency-bound call, lose)")
+                         "branch of the graph, the attention on half of the CUs) or after them; "
+                         "auto = beside them for steps with Medusa heads over a batch (the 70B "
+                         "share: 1360 against 1187 steps/s; one-sequence steps, whose attention "
+                         "is a short latency-bound call, lose 2-4%%)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="time the step replayed as one HIP graph (default) or as eager launches")

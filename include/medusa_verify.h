@@ -146,14 +146,6 @@ MV_API int mv_medusa_head_project(int dt, int B, int d, int V, int K, const int*
                                   int s_max, const void* w_head, void* logits, void* ws,
                                   size_t ws_bytes, void* stream);
 
-/* The same projection, launched to run beside the co-resident tree attention
- * (mv_tree_attn_verify_beside) on another stream: identical arguments, workspace, outputs and
- * errors.  Its workgroups keep a footprint of which three fit on a CU beside the attention's,
- * where the plain call's faster row-segment loads would fit only one. */
-MV_API int mv_medusa_head_project_beside(int dt, int B, int d, int V, int K,
-                                         const int* s_per_head, int s_max, const void* w_head,
-                                         void* logits, void* ws, size_t ws_bytes, void* stream);
-
 MV_API int mv_medusa_head_select(int dt, int B, int d, int V, int K, const int* s_per_head,
                                  int s_max, int32_t* topk_ids, float* topk_vals, int ld_topk,
                                  float* lse, void* ws, size_t ws_bytes, void* stream);
@@ -288,9 +280,10 @@ MV_API int mv_tree_attn_verify(int dt, int B, int N, int Hq, int Hkv, int dh, in
  * on another stream (the Medusa heads of the same step; the passages above define it).
  * Arguments, layouts, results and errors are those of mv_tree_attn_verify; ws must come from
  * mv_tree_attn_verify_beside_workspace() with the same sizes.  The bf16 path runs as one
- * persistent workgroup of 4 waves per CU (one wave per SIMD), which leaves half of every SIMD's
- * registers to the other stream's workgroups, so both progress at once.  On its own it is
- * about 1.4x slower than mv_tree_attn_verify; fp32 runs the same kernel as mv_tree_attn_verify.
+ * persistent 8-wave workgroup per CU on half of the CUs; each holds nearly all of its CU's
+ * registers, so the other stream's workgroups run on the other half and both progress at once.
+ * On its own it is about twice as slow as mv_tree_attn_verify; fp32 runs the same kernel as
+ * mv_tree_attn_verify.
  * ------------------------------------------------------------------------------------- */
 MV_API size_t mv_tree_attn_verify_beside_workspace(int dt, int B, int N, int Hq, int Hkv, int dh,
                                                    int max_L);

@@ -55,7 +55,6 @@ SIGNATURES = [
     ("mv_medusa_heads_workspace", _Z, [_I, _I, _I, _I, _I, _I]),
     ("mv_medusa_residual", _I, [_I, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
     ("mv_medusa_head_project", _I, [_I, _I, _I, _I, _I, _IP, _I, _P, _P, _P, _Z, _P]),
-    ("mv_medusa_head_project_beside", _I, [_I, _I, _I, _I, _I, _IP, _I, _P, _P, _P, _Z, _P]),
     ("mv_medusa_head_select", _I, [_I, _I, _I, _I, _I, _IP, _I, _P, _P, _I, _P, _P, _Z, _P]),
     ("mv_medusa_heads", _I, [_I, _I, _I, _I, _I, _IP, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                              _Z, _P]),

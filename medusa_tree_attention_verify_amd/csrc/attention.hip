@@ -27,11 +27,12 @@
 //     (ds_read_b64_tr_b16, two per operand).
 // A second kernel merges the chunk partials with their (max, sum) pairs.
 //
-// Co-resident launch (mv_tree_attn_verify_beside), for a step that runs the attention on a
-// second stream beside the bandwidth-bound Medusa heads: the same kernel with 4 waves (128 query
-// rows) per workgroup, launched persistent, one workgroup per CU, so one attention wave per SIMD
-// holds 256 of its 512 registers and the heads' waves (about 56 registers each) fill the rest;
-// both then progress on every CU instead of taking turns on whole CUs.
+// Launch beside other kernels (mv_tree_attn_verify_beside), for a step that runs the attention
+// on a second stream beside the bandwidth-bound Medusa heads: the same kernel launched
+// persistent on half of the CUs, one workgroup per CU striding over the workgroup indices.  Such
+// a workgroup holds nearly all of its CU's registers (two waves of ~250 per SIMD), so the
+// heads' workgroups stream their weights on the other half of the chip instead of sharing SIMDs
+// with the attention.
 //
 // fp32 path: a vector-ALU kernel, one wave per query row, no chunking (the fp32 configuration
 // is a small check case).
@@ -91,7 +92,7 @@ __device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool re
 #define MV_ATTN_TARGET_WG_BATCH 768  // ... and with several sequences (at most)
 #endif
 #ifndef MV_ATTN_TARGET_WG_BESIDE
-#define MV_ATTN_TARGET_WG_BESIDE 768  // ... for a batch in the co-resident launch (indices)
+#define MV_ATTN_TARGET_WG_BESIDE 768  // ... for a batch in the launch beside other kernels (indices)
 #endif
 #ifndef MV_ATTN_BALANCED
 #define MV_ATTN_BALANCED 1  // batches that split: chunk plan from the actual lengths
@@ -101,11 +102,8 @@ __device__ __forceinline__ int clamp_prefix(const AttnParams& p, int Lb, bool re
 #endif
 
 constexpr int kKT = 64;  // keys per tile
-// Waves per attention workgroup, 32 query rows each: 8 (two per SIMD) for a launch of its own;
-// 4 (one per SIMD, persistent, one workgroup per CU) for a launch that runs beside
-// bandwidth-bound kernels on another stream and leaves half of every SIMD's registers to them.
-constexpr int kNWVAlone = 8;
-constexpr int kNWVBeside = 4;
+// Waves per attention workgroup, 32 query rows each (two per SIMD).
+constexpr int kNWV = 8;
 constexpr float kLazyLog2 = 8.f;  // running-max slack of the online softmax (log2 units)
 
 
@@ -402,9 +400,6 @@ void tree_attn_bf16_kernel(const AttnParams p) {
     }
   };
   if constexpr (PERSIST) {
-    // Beside the heads' streaming waves on the same SIMDs, this wave wins the issue
-    // arbitration (those mostly wait on their loads): +2% on the forked 70B-share step.
-    __builtin_amdgcn_s_setprio(1);
     // Persistent: the grid (a multiple of the XCD count) strides over the workgroup indices,
     // so every index a workgroup takes maps to its own XCD, as in a launch of its own.
     for (int vb = static_cast<int>(blockIdx.x); vb < p.vblocks; vb += static_cast<int>(gridDim.x)) {
@@ -667,7 +662,6 @@ __global__ __launch_bounds__(kOrderMaxB) void seq_order_kernel(const AttnParams 
 }
 
 struct AttnPlan {
-  int nwv = kNWVAlone;   // waves per workgroup (32 query rows each)
   int qtiles = 1, CK = 256, nchunks = 1;
   bool ordered = false;  // a length ordering of the sequences in the workspace
   bool balanced = false;  // ... and a balanced chunk plan from the actual lengths
@@ -679,13 +673,12 @@ struct AttnPlan {
 // batch) so that the chip stays busy, but keep chunks of at least MV_ATTN_MIN_CHUNK keys:
 // every chunk writes an fp32 partial output as large as its query block, so short chunks turn
 // a K/V-streaming kernel into a partial-output-writing one.  `beside` plans the persistent
-// 4-wave launch (the targets then count its workgroup indices).
+// launch on half of the CUs (the targets then count its workgroup indices).
 AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L, bool beside) {
   AttnPlan a;
   if (dt == MV_F32) return a;
-  a.nwv = beside ? kNWVBeside : kNWVAlone;
   const int M = N * (Hq / Hkv);
-  a.qtiles = ceil_div(M, a.nwv * 32);
+  a.qtiles = ceil_div(M, kNWV * 32);
   const long long base = static_cast<long long>(B) * Hkv * a.qtiles;
   // A batch splits only as far as its (sequence, KV head, query tile) jobs stay within the
   // batch target (rounding down): the jobs of a large batch already fill the chip, and every
@@ -723,7 +716,7 @@ AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L, boo
   }
   if (a.nchunks > 1) {
     const size_t rows = cslots * Hq * N;
-    const size_t tile_rows = cslots * Hkv * a.qtiles * a.nwv * 32;
+    const size_t tile_rows = cslots * Hkv * a.qtiles * kNWV * 32;
     c.take<float>(tile_rows * dh);  // register-order blocks, padded to whole query tiles
     c.take<float2>(rows);
   }
@@ -787,15 +780,16 @@ int tree_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int L_cap, int max_
     else tree_attn_f32_kernel<128><<<blocks, 256, 0, st>>>(p);
     return launch_status();
   }
-  // Persistent grid of the co-resident launch: one 4-wave workgroup per CU (the CU count
-  // rounded down to whole XCDs), striding over the workgroup indices.
+  // Persistent grid of the launch beside other kernels: one workgroup per CU on half of the
+  // CUs (rounded down to whole XCDs), striding over the workgroup indices.  (Measured on the
+  // 70B-shaped forked step: 3/8 of the CUs 1194, half 1363, 5/8 1318 steps/s.)
   int pgrid = 0;
   if (beside) {
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return MV_ERR_HIP;
-    pgrid = std::max(kXcds, ncu / kXcds * kXcds);
+    pgrid = std::max(kXcds, ncu / (2 * kXcds) * kXcds);
   }
   Carver c(ws);
   int32_t* order = a.ordered ? c.take<int32_t>(B) : nullptr;
@@ -804,7 +798,7 @@ int tree_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int L_cap, int max_
   const size_t cslots = a.balanced ? static_cast<size_t>(a.nchunks) : static_cast<size_t>(B) * a.nchunks;
   if (a.nchunks > 1) {
     const size_t rows = cslots * Hq * N;
-    const size_t tile_rows = cslots * Hkv * a.qtiles * a.nwv * 32;
+    const size_t tile_rows = cslots * Hkv * a.qtiles * kNWV * 32;
     p.part_o = c.take<float>(tile_rows * dh);
     p.part_ml = c.take<float2>(rows);
   }
@@ -822,17 +816,16 @@ int tree_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int L_cap, int max_
   }
   if (beside) {
     const int g = static_cast<int>(std::min<long long>(grid, pgrid));
-    if (dh == 64) tree_attn_bf16_kernel<64, kNWVBeside, true><<<g, kNWVBeside * 64, 0, st>>>(p);
-    else tree_attn_bf16_kernel<128, kNWVBeside, true><<<g, kNWVBeside * 64, 0, st>>>(p);
+    if (dh == 64) tree_attn_bf16_kernel<64, kNWV, true><<<g, kNWV * 64, 0, st>>>(p);
+    else tree_attn_bf16_kernel<128, kNWV, true><<<g, kNWV * 64, 0, st>>>(p);
   } else {
     const int g = static_cast<int>(grid);
-    if (dh == 64) tree_attn_bf16_kernel<64, kNWVAlone, false><<<g, kNWVAlone * 64, 0, st>>>(p);
-    else tree_attn_bf16_kernel<128, kNWVAlone, false><<<g, kNWVAlone * 64, 0, st>>>(p);
+    if (dh == 64) tree_attn_bf16_kernel<64, kNWV, false><<<g, kNWV * 64, 0, st>>>(p);
+    else tree_attn_bf16_kernel<128, kNWV, false><<<g, kNWV * 64, 0, st>>>(p);
   }
   MV_TRY(launch_status());
   if (a.nchunks > 1) {
-    if (beside) launch_combine<kNWVBeside>(p, dh, a.nchunks, st);
-    else launch_combine<kNWVAlone>(p, dh, a.nchunks, st);
+    launch_combine<kNWV>(p, dh, a.nchunks, st);
     MV_TRY(launch_status());
   }
   return MV_OK;

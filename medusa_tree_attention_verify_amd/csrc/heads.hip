@@ -399,14 +399,13 @@ __device__ void head_epilogue(const GemvParams& p, int k, int rb, float (*ys)[BC
 template <int NW, int NCT> using GemvRed = float[NW][kRows][16 * NCT + 1];
 template <int NCT> using GemvYs = float[kRows][8 * NCT];
 
-// Row-segment weight loads (ROWLOAD, the projection when it runs alone).  Loading straight into
+// Row-segment weight loads (ROWLOAD, the projection).  Loading straight into
 // the MFMA operand layout reads 16 rows x 64 bytes per instruction; with d = 8192 those rows are
 // 16 KB apart and the 70B-share projection streamed at ~5.1 TB/s.  Reading 2 rows x 512
 // contiguous bytes per instruction and going through LDS to the operand layout streams it at
 // ~5.8 TB/s (412 -> 363 us; the Llama-3-8B-shaped projection 188 -> 181 us).  Each wave stages
-// its own k-range, so the LDS region is private to the wave and needs no workgroup barrier; its
-// 77 KB per workgroup leave room for one such workgroup beside the co-resident attention, which
-// is why the forked step keeps the MFMA-layout loads (1079 vs 1272 steps/s with this path).
+// its own k-range, so the LDS region is private to the wave and needs no workgroup barrier
+// (77 KB per 4-wave workgroup).
 constexpr int kRlS = 8;                // k-steps per stage of the row-segment loads
 constexpr int kRlP = kRlS * 32 + 8;    // LDS row pitch (elements): conflict-free operand reads
 
@@ -788,18 +787,6 @@ int check_common(int dt, int B, int d, int K) {
   return MV_OK;
 }
 
-// LDS the projection launch beside the co-resident tree attention requests beyond what its
-// workgroups use, so that each takes kProjLdsFootprint bytes: at most 3 then share a CU with
-// the attention's workgroup (75776 bytes of LDS, one wave per SIMD); 4 (the register limit)
-// left the attention wave too little issue and the forked 70B-share step 2.4% slower (1268 vs
-// 1237-1241 steps/s; 2 per CU: 1229).
-constexpr size_t kProjLdsFootprint = 28 * 1024;
-template <int NW, int NCT, int MODE>
-constexpr size_t gemv_lds_pad() {
-  const size_t used = sizeof(GemvRed<NW, NCT>) + sizeof(GemvYs<NCT>);
-  return MODE == 1 && used < kProjLdsFootprint ? kProjLdsFootprint - used : 0;
-}
-
 // Waves per workgroup: the smallest power of two that gives the launch about MV_GEMV_WAVES
 // waves (12 per SIMD) to cover HBM latency, while each wave keeps at least 8 k-steps.
 int pick_nw(long long nblocks, int T, int cap) {
@@ -808,11 +795,11 @@ int pick_nw(long long nblocks, int T, int cap) {
   return nw;
 }
 
-// `beside`: the projection runs beside the co-resident tree attention on another stream; it then
-// takes the MFMA-layout loads with the LDS footprint above, otherwise (and for the residual) the
-// row-segment loads where the workgroup has at most 4 waves.
+// The projection takes the row-segment loads where the workgroup has at most 4 waves; the
+// residual (8-wave workgroups, which would need 154 KB of staging) loads straight into the
+// operand layout.
 template <int MODE>
-int launch_gemv(int dt, const GemvParams& p, int K, hipStream_t st, bool beside = false) {
+int launch_gemv(int dt, const GemvParams& p, int K, hipStream_t st) {
   const dim3 grid(p.nrb, K);
   if (dt == MV_F32) {
     const int nw = pick_nw(static_cast<long long>(p.nrb) * K, 1 << 30, 8);
@@ -828,11 +815,10 @@ int launch_gemv(int dt, const GemvParams& p, int K, hipStream_t st, bool beside 
   const int nw = pick_nw(static_cast<long long>(p.nrb) * K, p.T, 16 / nct > 8 ? 8 : 16 / nct);
 #define MV_GEMV_CASE(NW_, NCT_)                                                                  \
   if (nw == NW_ && nct == NCT_) {                                                                \
-    if (MODE == 1 && !beside && NW_ <= 4)                                                        \
+    if (MODE == 1 && NW_ <= 4)                                                                   \
       gemv_bf16_kernel<NW_, NCT_, MODE, MODE == 1 && NW_ <= 4><<<grid, NW_ * 64, 0, st>>>(p);    \
     else                                                                                         \
-      gemv_bf16_kernel<NW_, NCT_, MODE, false>                                                   \
-          <<<grid, NW_ * 64, beside ? gemv_lds_pad<NW_, NCT_, MODE>() : 0, st>>>(p);             \
+      gemv_bf16_kernel<NW_, NCT_, MODE, false><<<grid, NW_ * 64, 0, st>>>(p);                    \
     return launch_status();                                                                      \
   }
   MV_GEMV_CASE(1, 1) MV_GEMV_CASE(2, 1) MV_GEMV_CASE(4, 1) MV_GEMV_CASE(8, 1)
@@ -904,9 +890,9 @@ static GemvParams head_params(int dt, int B, int d, int V, int K, const int* s_p
   return p;
 }
 
-static int head_project(int dt, int B, int d, int V, int K, const int* s_per_head, int s_max,
-                        const void* w_head, void* logits, void* ws, size_t ws_bytes, void* stream,
-                        bool beside) {
+MV_API int mv_medusa_head_project(int dt, int B, int d, int V, int K, const int* s_per_head,
+                                  int s_max, const void* w_head, void* logits, void* ws,
+                                  size_t ws_bytes, void* stream) {
   MV_TRY(check_common(dt, B, d, K));
   MV_TRY(check_select(V, K, s_per_head, s_max));
   if (!w_head) return MV_ERR_INVALID_ARG;
@@ -915,21 +901,7 @@ static int head_project(int dt, int B, int d, int V, int K, const int* s_per_hea
   GemvParams p = head_params(dt, B, d, V, K, s_per_head, s_max, L);
   p.W = w_head;
   p.logits = logits;
-  return launch_gemv<1>(dt, p, K, as_stream(stream), beside);
-}
-
-MV_API int mv_medusa_head_project(int dt, int B, int d, int V, int K, const int* s_per_head,
-                                  int s_max, const void* w_head, void* logits, void* ws,
-                                  size_t ws_bytes, void* stream) {
-  return head_project(dt, B, d, V, K, s_per_head, s_max, w_head, logits, ws, ws_bytes, stream,
-                      false);
-}
-
-MV_API int mv_medusa_head_project_beside(int dt, int B, int d, int V, int K,
-                                         const int* s_per_head, int s_max, const void* w_head,
-                                         void* logits, void* ws, size_t ws_bytes, void* stream) {
-  return head_project(dt, B, d, V, K, s_per_head, s_max, w_head, logits, ws, ws_bytes, stream,
-                      true);
+  return launch_gemv<1>(dt, p, K, as_stream(stream));
 }
 
 MV_API int mv_medusa_head_select(int dt, int B, int d, int V, int K, const int* s_per_head,

@@ -107,12 +107,10 @@ def medusa_head_topk(w_head: torch.Tensor, B: int, s_per_head: Sequence[int],
                      topk_ids: Optional[torch.Tensor] = None,
                      topk_vals: Optional[torch.Tensor] = None, ld_topk: int = 0,
                      lse: Optional[torch.Tensor] = None,
-                     ws: Optional[Workspace] = None, beside: bool = False) -> Dict[str, torch.Tensor]:
+                     ws: Optional[Workspace] = None) -> Dict[str, torch.Tensor]:
     """a2: logits_k = W_head^(k) h_k (h_k from medusa_residual's workspace), top-s_k, lse.
 
-    Two C calls: mv_medusa_head_project (the weight stream; ``beside`` takes
-    mv_medusa_head_project_beside, the launch that shares CUs with the co-resident attention)
-    and mv_medusa_head_select."""
+    Two C calls: mv_medusa_head_project (the weight stream) and mv_medusa_head_select."""
     dt = _dt(w_head)
     K, V, d = w_head.shape
     s_max = int(s_max or max(s_per_head))
@@ -129,8 +127,7 @@ def medusa_head_topk(w_head: torch.Tensor, B: int, s_per_head: Sequence[int],
     w = _ws("heads", ws)
     ptr, n = w.get(heads_workspace_bytes(dt, B, d, V, K, s_max))
     sp = L.int_array(s_per_head)
-    pname = "mv_medusa_head_project_beside" if beside else "mv_medusa_head_project"
-    L.check(pname, getattr(L.lib(), pname)(
+    L.check("mv_medusa_head_project", L.lib().mv_medusa_head_project(
         dt, B, d, V, K, sp, s_max, _ptr(w_head), _ptr(logits), ptr, n, _stream()))
     L.check("mv_medusa_head_select", L.lib().mv_medusa_head_select(
         dt, B, d, V, K, sp, s_max, _ptr(topk_ids), _ptr(topk_vals), int(ld_topk), _ptr(lse),
@@ -255,8 +252,8 @@ def tree_attn_verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     """a4 + a5: tree-masked GQA attention; returns (out [B,N,Hq,dh], lse [B,Hq,N] or None).
 
     anc_mask [N, W] (one tree for the batch) or [B, N, W] (one tree per sequence).
-    ``beside`` takes the co-resident launch (mv_tree_attn_verify_beside), meant to run on one
-    stream while bandwidth-bound kernels run on another."""
+    ``beside`` takes the launch on half of the CUs (mv_tree_attn_verify_beside), meant to run
+    on one stream while bandwidth-bound kernels run on another."""
     dt = _dt(q)
     B, N, Hq, dh = q.shape
     _, Hkv, L_cap, _ = k_cache.shape

@@ -108,7 +108,7 @@ class VerifyStep:
             self.ws_heads.get(ops.heads_workspace_bytes(self.dt, B, d, Vh, K, self.s_max))
             self._s_heads = L.int_array(heads["widths"])
         self.ws_attn.get(ops.attn_workspace_bytes(self.dt, B, N, Hq, Hkv, dh, max_L))
-        if self.can_fork():  # a forked step runs the co-resident attention
+        if self.can_fork():  # a forked step runs the attention launch on half of the CUs
             self.ws_attn.get(ops.attn_workspace_bytes(self.dt, B, N, Hq, Hkv, dh, max_L, True))
         self._s_depth = L.int_array(self.depth_widths)
         if target_head:
@@ -187,10 +187,7 @@ class VerifyStep:
             off = 1 if self.lm_width else 0
             ld = D * s_max
             esz = 4
-            # forked: the projection shares the CUs with the co-resident attention, so it takes
-            # the launch sized for that (mv_medusa_head_project_beside)
-            pname = "mv_medusa_head_project_beside" if fork else "mv_medusa_head_project"
-            proj = wrap(pname, getattr(lib, pname), self.dt, B, d, Vh,
+            proj = wrap("mv_medusa_head_project", lib.mv_medusa_head_project, self.dt, B, d, Vh,
                         K, self._s_heads, s_max, _p(inp["w_head"]),
                         _p(self.draft_logits) if self.spec_lm else None, wsp, wsn, st)
             calls["heads_select"] = wrap("mv_medusa_head_select", lib.mv_medusa_head_select,
@@ -241,8 +238,8 @@ class VerifyStep:
             calls["attn_mask"] = wrap("mv_build_tree_mask", lib.mv_build_tree_mask, N,
                                       _p(self.parents), 0, 0, 0, None, None, _p(anc), None, None,
                                       _p(self.status), st_b)
-        # forked: the co-resident launch (one persistent 4-wave workgroup per CU), so that the
-        # attention and the bandwidth-bound heads share every CU instead of taking turns
+        # forked: the launch on half of the CUs (one persistent 8-wave workgroup per CU), so
+        # that the bandwidth-bound heads stream their weights on the other half meanwhile
         aname = "mv_tree_attn_verify_beside" if fork else "mv_tree_attn_verify"
         calls["attention"] = wrap(aname, getattr(lib, aname), self.dt, B, N,
                                   self.Hq, self.Hkv, self.dh, Lcap, self.max_L, _p(inp["q"]),
@@ -299,7 +296,7 @@ class VerifyStep:
     def run(self, inp: Dict[str, torch.Tensor], branch_stream=None) -> None:
         """One whole step on ``inp`` (binds, then runs its calls in order).  With
         ``branch_stream`` (a torch stream) it runs forked, as ``capture(fork=True)`` records it:
-        the attention branch on that stream, with the co-resident attention launch."""
+        the attention branch on that stream, with the attention launch on half of the CUs."""
         if branch_stream is not None and self.can_fork():
             self._run_forked(inp, branch_stream)
             return

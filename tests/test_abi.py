@@ -19,7 +19,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 24, names
+    assert len(names) == 23, names
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -58,7 +58,7 @@ def test_workspace_queries():
     assert lib.mv_tree_attn_verify_workspace(L.MV_BF16, 1, 64, 32, 8, 128, 4096) > 0
     assert lib.mv_tree_attn_verify_workspace(L.MV_BF16, 1, 64, 32, 8, 96, 4096) == 0  # dh
     assert lib.mv_tree_attn_verify_workspace(L.MV_F32, 1, 8, 4, 4, 64, 128) == 0    # no split
-    # the co-resident launch plans 128-row query tiles: same checks, its own partial layout
+    # the launch beside other kernels plans its own split (persistent grid): same checks
     assert lib.mv_tree_attn_verify_beside_workspace(L.MV_BF16, 1, 64, 32, 8, 128, 4096) > 0
     assert lib.mv_tree_attn_verify_beside_workspace(L.MV_BF16, 1, 64, 32, 8, 96, 4096) == 0
     assert lib.mv_tree_attn_verify_beside_workspace(L.MV_F32, 1, 8, 4, 4, 64, 128) == 0
@@ -88,7 +88,7 @@ def test_host_argument_checks():
     assert lib.mv_medusa_residual(L.MV_BF16, 1, 64, 1, None, P, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
     s = L.int_array([4, 3])
     s_bad = L.int_array([5, 3])
-    for proj in (lib.mv_medusa_head_project, lib.mv_medusa_head_project_beside):
+    for proj in (lib.mv_medusa_head_project,):
         assert proj(L.MV_BF16, 1, 64, 100, 2, s, 17, P, None, P, 1 << 20, None) == L.MV_ERR_UNSUPPORTED
         assert proj(L.MV_BF16, 1, 64, 100, 2, s_bad, 4, P, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
         assert proj(L.MV_BF16, 1, 64, 100, 2, s, 4, P, None, None, 0, None) == L.MV_ERR_WORKSPACE

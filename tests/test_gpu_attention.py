@@ -1,5 +1,5 @@
 """GPU parity of tree-masked GQA attention against the oracle: mv_tree_attn_verify and the
-co-resident launch mv_tree_attn_verify_beside (persistent 4-wave workgroups), on the same cases."""
+launch mv_tree_attn_verify_beside (persistent workgroups on half of the CUs), on the same cases."""
 import numpy as np
 import pytest
 import torch

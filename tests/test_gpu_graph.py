@@ -21,10 +21,10 @@ def _outputs(step):
 
 @pytest.mark.parametrize("fork,batched", [(False, False), (True, False), (True, True)])
 def test_graph_replays_match_eager(fork, batched):
-    """fork=True: the attention branch (its own mask build and the co-resident attention) is a
-    parallel branch of the graph beside the heads and the tree; its replays must equal an eager
-    forked step bit for bit (the co-resident launch may cut the keys into other chunks than the
-    serial one, so its rounding can differ from the serial step's).  batched: 3 sequences with
+    """fork=True: the attention branch (its own mask build and the attention launch on half of
+    the CUs) is a parallel branch of the graph beside the heads and the tree; its replays must
+    equal an eager forked step bit for bit (that launch may cut the keys into other chunks than
+    the serial one, so its rounding can differ from the serial step's).  batched: 3 sequences with
     64/8 heads and prefixes long enough for the balanced split of the keys."""
     require_gpu()
     if batched:

@@ -120,11 +120,9 @@ def test_heads_70b_full_sampled():
         assert_fp32(vals[b, k, :s], ref["logits"][0, 0][ids[b, k, :s]], what=f"topk_vals b={b} k={k}")
 
 
-@pytest.mark.parametrize("beside", [False, True], ids=["alone", "beside"])
-def test_split_calls_match_fused_and_repeat(beside):
+def test_split_calls_match_fused_and_repeat():
     """mv_medusa_residual + (mv_medusa_head_project + mv_medusa_head_select) twice equal
-    mv_medusa_heads; so does the projection's co-resident launch (mv_medusa_head_project_beside):
-    both accumulate the same products in the same order."""
+    mv_medusa_heads: they accumulate the same products in the same order."""
     require_gpu()
     wl = W.WORKLOADS["c2"].scaled(B=2, d=512, V=3000, K=4, head_widths=(4, 3, 2, 1))
     x = W.gen_heads(wl, 11)
@@ -134,7 +132,7 @@ def test_split_calls_match_fused_and_repeat(beside):
     ws = ops.Workspace()
     ops.medusa_residual(h, w_res, V=3000, s_max=4, ws=ws)
     runs = [ops.medusa_head_topk(w_head, 2, widths, lse=torch.empty((2, 4), device="cuda"),
-                                 logits=torch.empty_like(fused["logits"]), ws=ws, beside=beside)
+                                 logits=torch.empty_like(fused["logits"]), ws=ws)
             for _ in range(2)]
     torch.cuda.synchronize()
     for r in runs:
@@ -144,32 +142,15 @@ def test_split_calls_match_fused_and_repeat(beside):
         assert torch.equal(r["logits"], fused["logits"])
 
 
-@pytest.mark.parametrize("wl_name,B,d", [("c2", 1, 4096), ("c3", 8, 8192), ("c2", 3, 800),
-                                         ("c2", 2, 96), ("c2", 20, 2080)])
-def test_projection_beside_equals_alone(wl_name, B, d):
-    """The projection alone (row-segment weight loads through LDS where the workgroup has at
-    most 4 waves) and beside the attention (operand-layout loads) give bit-identical logits,
-    top-k and LSE: the full Llama-3-8B and 70B-share shapes, and widths whose per-wave k-range
-    leaves a partial stage (d = 800, 2080) or no full stage (d = 96), with 1 to 4 column tiles.
-    The alone path itself is checked against the oracle by the tests above."""
+@pytest.mark.parametrize("B,d", [(3, 800), (2, 96), (20, 2080)])
+def test_projection_partial_stages(B, d):
+    """The projection's row-segment loads stage 8 k-steps at a time per wave; widths whose
+    per-wave k-range leaves a partial stage (d = 800, 2080) or no full stage (d = 96), with 1 to
+    4 column tiles, against the oracle (logits, top-k, LSE)."""
     require_gpu()
-    V = W.WORKLOADS[wl_name].V if d >= 4096 else 1999
-    wl = W.WORKLOADS[wl_name].scaled(B=B, d=d, V=V)
-    widths = list(wl.head_widths)
-    x = W.gen_heads(wl, 17)
-    print(f"projection beside/alone {wl_name} B={B} d={d} V={V}", flush=True)
-    h, w_res, w_head = (dev(x[k], torch.bfloat16) for k in ("h", "w_res", "w_head"))
-    ws = ops.Workspace()
-    ops.medusa_residual(h, w_res, V=V, s_max=max(widths), ws=ws)
-    out = []
-    for beside in (False, True):
-        out.append(ops.medusa_head_topk(w_head, B, widths, lse=torch.empty((B, wl.K), device="cuda"),
-                                        logits=torch.empty((B, wl.K, V), dtype=torch.bfloat16,
-                                                           device="cuda"),
-                                        ws=ws, beside=beside))
-    torch.cuda.synchronize()
-    for key in ("topk_ids", "topk_vals", "lse", "logits"):
-        assert torch.equal(out[0][key], out[1][key]), key
+    wl = W.WORKLOADS["c2"].scaled(B=B, d=d, V=1999)
+    ties = _run_and_check(wl, 17, list(wl.head_widths), check_logits=True)
+    assert ties <= 1
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])

@@ -28,7 +28,7 @@ def _oracle_step(wl, x, target):
 def _check_step(wl, seed, attn_select=None, fork=False):
     """One GPU step vs the oracle.  ``attn_select`` = (b, h, i) rows whose attention output
     is compared (all rows when None); everything else is compared in full.  ``fork`` runs the
-    step forked (the attention branch, with the co-resident launch, on a second stream)."""
+    step forked (the attention branch, with the launch on half of the CUs, on a second stream)."""
     parents = list(wl.parents)
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     xh = W.gen_heads(wl, seed)
