@@ -312,11 +312,16 @@ class VerifyStep:
         main = torch.cuda.current_stream(self.device)
         calls = self.bind(inp, branch_stream=side)
         side.wait_stream(main)
+        # the main branch's first call is enqueued ahead of the attention branch, so that a
+        # graph of the step starts it first (the heads' chain is the longer branch)
+        first = next((n for n in self.PARTS if n not in self.BRANCH and n in calls), None)
+        if first is not None:
+            calls[first]()
         for name in self.BRANCH:
             calls[name]()
         joined = False
         for name in self.PARTS:
-            if name in self.BRANCH or name not in calls:
+            if name in self.BRANCH or name not in calls or name == first:
                 continue
             if name == "commit" and not joined:
                 main.wait_stream(side)
