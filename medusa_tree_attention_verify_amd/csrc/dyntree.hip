@@ -15,9 +15,14 @@
 // One wave per sequence selects the N paths best-first: the frontier holds, for every selected
 // path, its first child and its next sibling (both score no higher than it), so the best
 // frontier entry is always the next path in the order.  Each round is a wave-wide arg-best over
-// the frontier (at most N + 1 entries in LDS).  The (depth, ranks) key is packed in 64 bits:
-// depth in the top 4 bits, the rank at depth d in bits [60 - 4d, 64 - 4d), so depth <= 15 and
-// ranks < 16.
+// the frontier (at most N + 1 entries in LDS).  For N <= 64 the frontier is instead kept sorted
+// across the lanes, one entry per lane: the best entry is lane 0's, and a round shifts it out
+// and inserts the (at most two) new entries at their ranks (a ballot count, then a one-lane
+// shift of the lanes behind), with no reduction and no LDS round trip.  An entry ranked at or
+// beyond the number of picks still to make can never be picked (every entry ahead of it is
+// smaller and is picked first), so 64 lanes hold every entry that matters.  The (depth, ranks)
+// key is packed in 64 bits: depth in the top 4 bits, the rank at depth d in bits
+// [60 - 4d, 64 - 4d), so depth <= 15 and ranks < 16.
 
 #include <algorithm>
 
@@ -99,6 +104,47 @@ __device__ __forceinline__ int key_rank(uint64_t k, int d) {
   return static_cast<int>((k >> (60 - 4 * d)) & 15u);
 }
 
+// whole-wave one-lane shifts (DPP wave_shr:1 / wave_shl:1): lane i takes lane i - 1 (i + 1);
+// the lane without a source keeps `fill`
+__device__ __forceinline__ uint32_t wave_shr1(uint32_t v, uint32_t fill) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(fill), static_cast<int>(v), 0x138, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t wave_shl1(uint32_t v, uint32_t fill) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(fill), static_cast<int>(v), 0x130, 0xF, 0xF, false));
+}
+
+// One frontier entry per lane (sorted mode): selection key (a, k), score, parent's score,
+// parent's selection index.  An empty entry has a = k = ~0 and sorts last.
+struct DynEntry {
+  uint64_t a, k;
+  double sc, ps;
+  int par;
+};
+
+template <bool LEFT>
+__device__ __forceinline__ DynEntry wave_shift(const DynEntry& e) {
+  auto sh = [](uint32_t v, uint32_t fill) { return LEFT ? wave_shl1(v, fill) : wave_shr1(v, fill); };
+  auto sh64 = [&](uint64_t v, uint64_t fill) {
+    return (static_cast<uint64_t>(sh(static_cast<uint32_t>(v >> 32), static_cast<uint32_t>(fill >> 32))) << 32) |
+           sh(static_cast<uint32_t>(v), static_cast<uint32_t>(fill));
+  };
+  auto shd = [&](double v) {
+    return __longlong_as_double(static_cast<long long>(sh64(static_cast<uint64_t>(__double_as_longlong(v)), 0)));
+  };
+  return {sh64(e.a, ~static_cast<uint64_t>(0)), sh64(e.k, ~static_cast<uint64_t>(0)), shd(e.sc), shd(e.ps),
+          static_cast<int>(sh(static_cast<uint32_t>(e.par), 0xffffffffu))};
+}
+
+__device__ __forceinline__ DynEntry pick(bool f, const DynEntry& u, const DynEntry& v) {
+  return {f ? u.a : v.a, f ? u.k : v.k, f ? u.sc : v.sc, f ? u.ps : v.ps, f ? u.par : v.par};
+}
+
+__device__ __forceinline__ uint64_t first_lane_u64(uint64_t v) {
+  return (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v >> 32)))) << 32) |
+         static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+}
+
+template <bool SORTED>
 __global__ __launch_bounds__(64) void dynamic_tree_kernel(const DynParams p) {
   __shared__ double lp[kDynMaxDepth][MV_MAX_TOPK];
   __shared__ double fs[kDynFrontier], fps[kDynFrontier];  // score, parent's score
@@ -123,62 +169,105 @@ __global__ __launch_bounds__(64) void dynamic_tree_kernel(const DynParams p) {
     lp[d][r] = v;
   }
   __syncthreads();
-  if (lane == 0) {
-    fs[0] = lp[0][0];
-    fps[0] = 0.0;
-    fk[0] = static_cast<uint64_t>(1) << 60;  // depth 1, rank 0
-    fpar[0] = -1;
-    fcount = 1;
-    nsel = 0;
-  }
-  __syncthreads();
-  for (int n = 0; n < N; ++n) {
-    const int fc = fcount;
-    SelKey best = {~static_cast<uint64_t>(0), ~static_cast<uint64_t>(0), 0xffffffffu};
-    for (int j = lane; j < fc; j += 64) take_if_less(best, score_key(fs[j]), fk[j], j);
-    wave_min_key(best);  // keys are distinct: every lane ends with the same entry
-    // an empty frontier means every path is in the tree; the host has checked that there
-    // are at least N paths, so this only guards the loops below
-    if (best.j == 0xffffffffu) break;
-    const int bj = static_cast<int>(best.j);
-    const uint64_t bk = best.k;
+  int ns_sorted = 0;
+  if constexpr (SORTED) {
+    DynEntry e = {~static_cast<uint64_t>(0), ~static_cast<uint64_t>(0), 0.0, 0.0, -1};
     if (lane == 0) {
-      const double bs = fs[bj];
-      const int d = key_depth(bk), r = key_rank(bk, d);
-      const int par = fpar[bj];
-      const double psc = fps[bj];
-      ss[n] = bs;
-      sk[n] = bk;
-      spar[n] = par;
-      int cnt = fc;
-      // first child replaces the chosen entry; without one the last entry moves into its slot
-      if (d < D) {
-        fs[bj] = bs + lp[d][0];
-        fps[bj] = bs;
-        fk[bj] = (bk & ((static_cast<uint64_t>(1) << 60) - 1)) | (static_cast<uint64_t>(d + 1) << 60);
-        fpar[bj] = n;
-      } else {
-        --cnt;
-        if (bj != cnt) {
-          fs[bj] = fs[cnt];
-          fps[bj] = fps[cnt];
-          fk[bj] = fk[cnt];
-          fpar[bj] = fpar[cnt];
-        }
+      e.sc = lp[0][0];
+      e.k = static_cast<uint64_t>(1) << 60;  // depth 1, rank 0
+      e.a = score_key(e.sc);
+    }
+    // put x at its rank: the lanes behind it move back by one lane
+    auto insert = [&](const DynEntry& x) {
+      const bool lt = (e.a < x.a) | ((e.a == x.a) & (e.k < x.k));
+      const int pos = __popcll(__ballot(lt));
+      e = pick(lane == pos, x, pick(lane > pos, wave_shift<false>(e), e));
+    };
+    for (int n = 0; n < N; ++n) {
+      const uint64_t wa = first_lane_u64(e.a), wk = first_lane_u64(e.k);
+      // an empty frontier means every path is in the tree; the host has checked that there
+      // are at least N paths, so this only guards the loops below
+      if (wa == ~static_cast<uint64_t>(0) && wk == ~static_cast<uint64_t>(0)) break;
+      const double wsc = __longlong_as_double(static_cast<long long>(first_lane_u64(static_cast<uint64_t>(__double_as_longlong(e.sc)))));
+      const double wps = __longlong_as_double(static_cast<long long>(first_lane_u64(static_cast<uint64_t>(__double_as_longlong(e.ps)))));
+      const int wpar = __builtin_amdgcn_readfirstlane(e.par);
+      const int d = key_depth(wk), r = key_rank(wk, d);
+      if (lane == 0) {
+        ss[n] = wsc;
+        sk[n] = wk;
+        spar[n] = wpar;
       }
-      if (r + 1 < p.s[d - 1]) {  // next sibling
-        fs[cnt] = psc + lp[d - 1][r + 1];
-        fps[cnt] = psc;
-        fk[cnt] = bk + (static_cast<uint64_t>(1) << (60 - 4 * d));
-        fpar[cnt] = par;
-        ++cnt;
+      e = wave_shift<true>(e);  // the chosen entry leaves
+      if (d < D) {  // its first child
+        const double c = wsc + lp[d][0];
+        insert({score_key(c), (wk & ((static_cast<uint64_t>(1) << 60) - 1)) | (static_cast<uint64_t>(d + 1) << 60),
+                c, wsc, n});
       }
-      fcount = cnt;
-      nsel = n + 1;
+      if (r + 1 < p.s[d - 1]) {  // its next sibling
+        const double c = wps + lp[d - 1][r + 1];
+        insert({score_key(c), wk + (static_cast<uint64_t>(1) << (60 - 4 * d)), c, wps, wpar});
+      }
+      ns_sorted = n + 1;
     }
     __syncthreads();
+  } else {
+    if (lane == 0) {
+      fs[0] = lp[0][0];
+      fps[0] = 0.0;
+      fk[0] = static_cast<uint64_t>(1) << 60;  // depth 1, rank 0
+      fpar[0] = -1;
+      fcount = 1;
+      nsel = 0;
+    }
+    __syncthreads();
+    for (int n = 0; n < N; ++n) {
+      const int fc = fcount;
+      SelKey best = {~static_cast<uint64_t>(0), ~static_cast<uint64_t>(0), 0xffffffffu};
+      for (int j = lane; j < fc; j += 64) take_if_less(best, score_key(fs[j]), fk[j], j);
+      wave_min_key(best);  // keys are distinct: every lane ends with the same entry
+      // an empty frontier means every path is in the tree; the host has checked that there
+      // are at least N paths, so this only guards the loops below
+      if (best.j == 0xffffffffu) break;
+      const int bj = static_cast<int>(best.j);
+      const uint64_t bk = best.k;
+      if (lane == 0) {
+        const double bs = fs[bj];
+        const int d = key_depth(bk), r = key_rank(bk, d);
+        const int par = fpar[bj];
+        const double psc = fps[bj];
+        ss[n] = bs;
+        sk[n] = bk;
+        spar[n] = par;
+        int cnt = fc;
+        // first child replaces the chosen entry; without one the last entry moves into its slot
+        if (d < D) {
+          fs[bj] = bs + lp[d][0];
+          fps[bj] = bs;
+          fk[bj] = (bk & ((static_cast<uint64_t>(1) << 60) - 1)) | (static_cast<uint64_t>(d + 1) << 60);
+          fpar[bj] = n;
+        } else {
+          --cnt;
+          if (bj != cnt) {
+            fs[bj] = fs[cnt];
+            fps[bj] = fps[cnt];
+            fk[bj] = fk[cnt];
+            fpar[bj] = fpar[cnt];
+          }
+        }
+        if (r + 1 < p.s[d - 1]) {  // next sibling
+          fs[cnt] = psc + lp[d - 1][r + 1];
+          fps[cnt] = psc;
+          fk[cnt] = bk + (static_cast<uint64_t>(1) << (60 - 4 * d));
+          fpar[cnt] = par;
+          ++cnt;
+        }
+        fcount = cnt;
+        nsel = n + 1;
+      }
+      __syncthreads();
+    }
   }
-  const int ns = nsel;
+  const int ns = SORTED ? ns_sorted : nsel;
   // breadth-first position = rank of (depth, ranks) among the selected keys
   for (int i = lane; i < ns; i += 64) {
     const uint64_t k = sk[i];
@@ -248,7 +337,8 @@ MV_API int mv_build_dynamic_tree(int B, int D, int s_max, const int* s_per_depth
   p.ids = cand_ids; p.vals = cand_vals; p.lse = cand_lse;
   p.parents = parents; p.depth = depth; p.tokens = node_tokens; p.anc = anc_mask;
   p.logp = node_logp; p.status = dev_status;
-  dynamic_tree_kernel<<<B, 64, 0, as_stream(stream)>>>(p);
+  if (N <= 64) dynamic_tree_kernel<true><<<B, 64, 0, as_stream(stream)>>>(p);
+  else dynamic_tree_kernel<false><<<B, 64, 0, as_stream(stream)>>>(p);
   return launch_status();
 }
 

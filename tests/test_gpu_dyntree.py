@@ -52,6 +52,8 @@ def _check(got, ref, N):
     (2, 15, (2,) * 15, 256, 300),        # deepest trees, the largest node count
     (1, 1, (16,), 16, 100),              # every path
     (5, 6, (4, 3, 3, 2, 2, 2), 40, 700),
+    (2, 15, (2,) * 15, 64, 300),         # the sorted-frontier selection (N <= 64), deepest keys
+    (3, 4, (16, 16, 16, 16), 65, 4000),  # the smallest N of the LDS-frontier selection
 ])
 def test_dynamic_tree_matches_oracle(B, D, s, N, V):
     require_gpu()
