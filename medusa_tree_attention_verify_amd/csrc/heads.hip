@@ -357,6 +357,114 @@ __global__ __launch_bounds__(kMergeThreads) void heads_tournament_kernel(const G
   if (lane == 0 && p.lse) p.lse[static_cast<size_t>(b) * p.K + k] = M + logf(Ls);
 }
 
+// Merge of the blocks' sorted lists (each 32-row block's list is its top s, best first): a
+// k-way merge over the list heads.  Each thread holds the lists of BPT blocks in registers and
+// their current heads; per rank the workgroup takes the best head (a wave arg-best, one LDS
+// exchange between the waves) and only the thread owning the winner advances that list.  A
+// rank then costs a comparison of BPT heads per thread instead of a scan of every candidate
+// the thread holds.
+template <int BPT, int SMX>
+__global__ __launch_bounds__(kMergeThreads) void heads_kmerge_kernel(const GemvParams p) {
+  __shared__ float rv[2][kMergeWaves];
+  __shared__ int ri[2][kMergeWaves];
+  __shared__ float wm[kMergeWaves], wl[kMergeWaves];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int k = blockIdx.x % p.K, b = blockIdx.x / p.K;
+  const int nrb = p.nrb, s = p.s[k], smax = p.s_max;
+  const size_t base = (static_cast<size_t>(k) * p.B + b) * nrb;
+  const int* pidx = p.pidx + base * smax;
+  const float* pval = p.pval + base * smax;
+  float lv[BPT][SMX];
+  int li[BPT][SMX];
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {  // all requested before any is used
+    const int blk = tid + q * kMergeThreads;
+#pragma unroll
+    for (int r = 0; r < SMX; ++r) {
+      const bool ok = blk < nrb && r < s;
+      const int id = ok ? pidx[static_cast<size_t>(blk) * smax + r] : -1;
+      const float v = ok ? pval[static_cast<size_t>(blk) * smax + r] : -INFINITY;
+      li[q][r] = id >= 0 ? id : INT_MAX;
+      lv[q][r] = id >= 0 ? v : -INFINITY;
+    }
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int j = tid; j < nrb; j += kMergeThreads) ml_merge(m, l, p.pm[base + j], p.pl[base + j]);
+  wave_ml_merge(m, l);
+  if (lane == 0) {
+    wm[w] = m;
+    wl[w] = l;
+  }
+  int ptr[BPT];
+  float hv[BPT];
+  int hi[BPT];
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    ptr[q] = 0;
+    hv[q] = lv[q][0];
+    hi[q] = li[q][0];
+  }
+  const size_t o = static_cast<size_t>(b) * p.ld_topk + static_cast<size_t>(k) * smax;
+  for (int r = 0; r < s; ++r) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      const bool c = kv_better(hv[q], hi[q], bv, bi);
+      bv = c ? hv[q] : bv;
+      bi = c ? hi[q] : bi;
+    }
+    wave_argbest(bv, bi);
+    if (lane == 0) {
+      rv[r & 1][w] = bv;
+      ri[r & 1][w] = bi;
+    }
+    __syncthreads();
+    float gv = rv[r & 1][0];
+    int gi = ri[r & 1][0];
+#pragma unroll
+    for (int q = 1; q < kMergeWaves; ++q) {
+      const float ov = rv[r & 1][q];
+      const int oi = ri[r & 1][q];
+      const bool c = kv_better(ov, oi, gv, gi);
+      gv = c ? ov : gv;
+      gi = c ? oi : gi;
+    }
+    if (gi != INT_MAX) {  // token ids are unique: exactly one head of one thread holds it
+#pragma unroll
+      for (int q = 0; q < BPT; ++q) {
+        if (hi[q] == gi) {
+          const int nx = ++ptr[q];
+          float v = -INFINITY;
+          int id = INT_MAX;
+#pragma unroll
+          for (int t = 1; t < SMX; ++t) {
+            v = t == nx ? lv[q][t] : v;
+            id = t == nx ? li[q][t] : id;
+          }
+          hv[q] = v;
+          hi[q] = id;
+        }
+      }
+    }
+    if (tid == 0) {
+      p.topk_ids[o + r] = gi != INT_MAX ? gi : -1;
+      p.topk_vals[o + r] = gi != INT_MAX ? gv : -INFINITY;
+    }
+  }
+  if (tid == 0)
+    for (int r = s; r < smax; ++r) {
+      p.topk_ids[o + r] = -1;
+      p.topk_vals[o + r] = -INFINITY;
+    }
+  __syncthreads();
+  if (w != 0) return;
+  float M = lane < kMergeWaves ? wm[lane] : -INFINITY;
+  float Ls = lane < kMergeWaves ? wl[lane] : 0.f;
+  wave_ml_merge(M, Ls);
+  if (lane == 0 && p.lse) p.lse[static_cast<size_t>(b) * p.K + k] = M + logf(Ls);
+}
+
 // ---- projection epilogue: optional logits, per-workgroup top-s and (max, sum exp).
 template <bool BF16, int NW, int BC>
 __device__ void head_epilogue(const GemvParams& p, int k, int rb, float (*ys)[BC]) {
@@ -920,11 +1028,13 @@ MV_API int mv_medusa_head_select(int dt, int B, int d, int V, int K, const int* 
   p.ld_topk = ld_topk;
   p.lse = lse;
   hipStream_t st = as_stream(stream);
-  // Lists of up to 8 slots: per-thread sorted lists.  Longer (up to 16): a tournament over the
+  // Lists of up to 8 slots: per-thread sorted lists.  Longer (up to 16): a k-way merge of the
+  // blocks' lists when every thread holds at most two of them, else a tournament over the
   // candidates held in registers when they fit (up to 32 per thread), else the 16-slot lists.
   const long long n = static_cast<long long>(p.nrb) * s_max;
   if (s_max <= 4) heads_merge_kernel<4><<<K * B, kMergeThreads, 0, st>>>(p);
   else if (s_max <= 8) heads_merge_kernel<8><<<K * B, kMergeThreads, 0, st>>>(p);
+  else if (p.nrb <= 2 * kMergeThreads) heads_kmerge_kernel<2, MV_MAX_TOPK><<<K * B, kMergeThreads, 0, st>>>(p);
   else if (n <= 16LL * kMergeThreads) heads_tournament_kernel<16><<<K * B, kMergeThreads, 0, st>>>(p);
   else if (n <= 32LL * kMergeThreads) heads_tournament_kernel<32><<<K * B, kMergeThreads, 0, st>>>(p);
   else heads_merge_kernel<MV_MAX_TOPK><<<K * B, kMergeThreads, 0, st>>>(p);
