@@ -808,7 +808,8 @@ int tree_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int L_cap, int max_
   p.jobs = static_cast<int>(jobs);
   p.vblocks = static_cast<int>(grid);
   if (order) {
-    seq_order_kernel<<<1, kOrderMaxB, 0, st>>>(p, order, plan, jtab, a.c_target);
+    // one wave per 64 sequences: a small workgroup is placed at once on a busy chip
+    seq_order_kernel<<<1, std::min(kOrderMaxB, ceil_div(B, 64) * 64), 0, st>>>(p, order, plan, jtab, a.c_target);
     MV_TRY(launch_status());
     p.order = order;
     p.plan = plan;
