@@ -728,16 +728,21 @@ __global__ __launch_bounds__(NW * 64) void gemv_f32_kernel(const GemvParams p) {
 
 // ---- top-s of each row of a logit matrix (one workgroup per row), optionally the row's
 // log-sum-exp.  One pass over the row: every thread keeps its S best (value, id) pairs sorted
-// in registers and a running (max, sum exp(x - max)) pair; then s workgroup-wide arg-bests over
-// the threads' current heads, the owner of each winner popping it.  Rows whose elements are
-// 16-byte aligned are read with 16-byte loads.
+// in registers and a running (max, sum exp(x - max)) pair; then each wave takes its top s by
+// wave arg-bests over the threads' current heads (the owner of each winner popping it), and
+// one wave takes the row's top s from the waves' lists.  Rows whose elements are
+// 16-byte aligned are read with 16-byte loads.  After each batch of loads the wave takes the
+// largest of its lanes' S-th best values: the wave has seen S elements at least that large, so
+// an element below it cannot be among the row's S best and skips the insertion (which, with
+// every thread seeing only V / threads elements, otherwise ran in some lane of almost every
+// step).
 template <bool BF16, int S, int kTopkThreads>
 __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(int V, int s, const void* x, long long ldx,
                                                         int32_t* ids, float* vals, int ld_out,
                                                         float* lse, int vec) {
   constexpr int NW = kTopkThreads / 64;
-  __shared__ float sv[NW];
-  __shared__ int si[NW];
+  __shared__ float cv[NW][S];
+  __shared__ int ci[NW][S];
   __shared__ float sm[NW], sl[NW];
   const size_t rowoff = static_cast<size_t>(blockIdx.x) * ldx;
   float lv[S];
@@ -748,17 +753,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(int V, int s, c
     li[k] = INT_MAX;
   }
   float m = -INFINITY, l = 0.f;
-  auto take = [&](float v, int j) {
-    if (lse) {
-      if (v > m) {
-        l = l * __expf(m - v) + 1.f;
-        m = v;
-      } else if (v != -INFINITY) {
-        l += __expf(v - m);
-      }
-    }
-    // insert, keeping the list sorted (after the first few elements almost never taken)
-    if (__builtin_expect(v >= lv[S - 1], 0) && kv_better(v, j, lv[S - 1], li[S - 1])) {
+  float wthr = -INFINITY;  // a lower bound on the wave's, so on the row's, S-th best value
+  // running (max, sum exp(x - max)) without a branch: one exp of -|v - m| serves both cases
+  // (a new maximum rescales the sum, any other value adds its term); -inf adds nothing
+  auto lse_take = [&](float v) {
+    const bool bigger = v > m;
+    const float t = __expf(-fabsf(v - m));
+    const float up = fmaf(l, t, 1.f);                    // v is the new maximum
+    const float add = l + (v == -INFINITY ? 0.f : t);     // any other value
+    l = bigger ? up : add;
+    m = bigger ? v : m;
+  };
+  // insert, keeping the list sorted (after the first few elements almost never taken)
+  auto insert = [&](float v, int j) {
+    if (v >= lv[S - 1] && v >= wthr && kv_better(v, j, lv[S - 1], li[S - 1])) {
 #pragma unroll
       for (int k = S - 1; k > 0; --k) {
         const bool shift = kv_better(v, j, lv[k - 1], li[k - 1]);
@@ -772,34 +780,81 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(int V, int s, c
       }
     }
   };
+  auto take = [&](float v, int j) {
+    if (lse) lse_take(v);
+    if (__builtin_expect(v >= lv[S - 1] && v >= wthr, 0)) insert(v, j);
+  };
   constexpr int EPV = BF16 ? 8 : 4;  // elements per 16-byte load
   constexpr int U = 8;                // loads in flight per thread
   if (vec) {
-    const uint4* row = reinterpret_cast<const uint4*>(static_cast<const char*>(x) + rowoff * (BF16 ? 2 : 4));
     const int nv = V / EPV;
-    for (int q0 = threadIdx.x; q0 < nv; q0 += kTopkThreads * U) {
+    // buffer loads over the row: a piece past its end reads as zero, so no load sits under a
+    // branch and a batch's U loads are in flight together (a conditional load made the
+    // compiler wait for each one)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(x) + rowoff * (BF16 ? 2 : 4)), 0, nv * 16,
+        kBufferRsrcWord3);
+    // the trip count is the same in every lane, so the wave-wide maximum below has all lanes
+    for (int q0 = threadIdx.x; q0 - static_cast<int>(threadIdx.x) < nv; q0 += kTopkThreads * U) {
       uint4 t4[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int q = q0 + u * kTopkThreads;
-        t4[u] = q < nv ? row[q] : make_uint4(0u, 0u, 0u, 0u);
+        t4[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, q < nv ? 16 * q : kBufferOutOfRange, 0, 0));
+      }
+      auto unpack = [&](const uint4& t, float (&v)[EPV]) {
+        const uint32_t w4[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const uint32_t word = w4[BF16 ? e / 2 : e];
+          v[e] = BF16 ? __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16))
+                      : __uint_as_float(word);
+        }
+      };
+      if (q0 == static_cast<int>(threadIdx.x)) {
+        // First batch: start the wave threshold at the S-th largest of the lanes' maxima over
+        // the batch (S distinct elements reach it, so it bounds the wave's S-th best from
+        // below).  Without it every lane's list fills from -inf and the insertion runs in some
+        // lane of nearly every early step (s = 16 over 128256: 237 us).
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float v[EPV];
+          unpack(t4[u], v);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) mx = q0 + u * kTopkThreads < nv ? fmaxf(mx, v[e]) : mx;
+        }
+        float cur = -INFINITY;
+        for (int k = 0; k < S; ++k) {
+          cur = wave_max(mx);
+          const uint64_t hold = __ballot(mx == cur);  // drop one lane holding it
+          if (static_cast<int>(threadIdx.x & 63) == __ffsll(static_cast<long long>(hold)) - 1) mx = -INFINITY;
+        }
+        wthr = cur;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int q = q0 + u * kTopkThreads;
         if (q >= nv) break;
-        const uint32_t w4[4] = {t4[u].x, t4[u].y, t4[u].z, t4[u].w};
+        float v[EPV];
+        unpack(t4[u], v);
+        if (lse) {
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const uint32_t word = w4[BF16 ? e / 2 : e];
-          const float v = BF16 ? __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16))
-                               : __uint_as_float(word);
-          take(v, q * EPV + e);
+          for (int e = 0; e < EPV; ++e) lse_take(v[e]);
+        }
+        // one branch per 16-byte piece: its largest element against the thresholds
+        float g = v[0];
+#pragma unroll
+        for (int e = 1; e < EPV; ++e) g = fmaxf(g, v[e]);
+        if (__builtin_expect(g >= lv[S - 1] && g >= wthr, 0)) {
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) insert(v[e], q * EPV + e);
         }
       }
+      wthr = fmaxf(wthr, wave_max(lv[S - 1]));
     }
   } else {
-    for (int j0 = threadIdx.x; j0 < V; j0 += kTopkThreads * U) {
+    for (int j0 = threadIdx.x; j0 - static_cast<int>(threadIdx.x) < V; j0 += kTopkThreads * U) {
       float tv[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -812,6 +867,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(int V, int s, c
         if (j >= V) break;
         take(tv[u], j);
       }
+      wthr = fmaxf(wthr, wave_max(lv[S - 1]));
     }
   }
   if (lse) {
@@ -827,16 +883,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(int V, int s, c
       lse[blockIdx.x] = m + logf(l);
     }
   }
+  // Each wave's top s (wave arg-bests over the lanes' list heads, the owner popping each
+  // winner; ids are unique per row), then wave 0 takes the row's top s from the waves' lists.
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int r = 0; r < s; ++r) {
     float bv = lv[0];
     int bi = li[0];
-    block_argbest(bv, bi, sv, si);
-    if (threadIdx.x == 0) {
-      const size_t o = static_cast<size_t>(blockIdx.x) * ld_out + r;
-      ids[o] = bi == INT_MAX ? -1 : bi;
-      if (vals) vals[o] = bv;
+    wave_argbest(bv, bi);
+    if (lane == 0) {
+      cv[w][r] = bv;
+      ci[w][r] = bi;
     }
-    if (bi != INT_MAX && li[0] == bi) {  // the owner pops its head (ids are unique per row)
+    if (bi != INT_MAX && li[0] == bi) {
 #pragma unroll
       for (int k = 0; k < S - 1; ++k) {
         lv[k] = lv[k + 1];
@@ -844,6 +902,42 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(int V, int s, c
       }
       lv[S - 1] = -INFINITY;
       li[S - 1] = INT_MAX;
+    }
+  }
+  __syncthreads();
+  if (w != 0) return;
+  constexpr int CPL = (NW * S + 63) / 64;  // candidates per lane
+  float hv[CPL];
+  int hi[CPL];
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) {
+    const int c = lane + 64 * t;
+    const bool ok = c < NW * s;
+    hv[t] = ok ? cv[c / s][c % s] : -INFINITY;
+    hi[t] = ok ? ci[c / s][c % s] : INT_MAX;
+  }
+  for (int r = 0; r < s; ++r) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      const bool c = kv_better(hv[t], hi[t], bv, bi);
+      bv = c ? hv[t] : bv;
+      bi = c ? hi[t] : bi;
+    }
+    wave_argbest(bv, bi);
+    if (lane == 0) {
+      const size_t o = static_cast<size_t>(blockIdx.x) * ld_out + r;
+      ids[o] = bi == INT_MAX ? -1 : bi;
+      if (vals) vals[o] = bv;
+    }
+    if (bi != INT_MAX) {
+#pragma unroll
+      for (int t = 0; t < CPL; ++t) {
+        const bool hit = hi[t] == bi;
+        hv[t] = hit ? -INFINITY : hv[t];
+        hi[t] = hit ? INT_MAX : hi[t];
+      }
     }
   }
 }
@@ -1112,7 +1206,9 @@ MV_API int mv_topk_rows(int dt, int R, int V, int s, const void* x, long long ld
   if (ldx < V || ld_out < s) return MV_ERR_INVALID_ARG;
   hipStream_t st = as_stream(stream);
   const int epv = dt == MV_BF16 ? 8 : 4;
-  const int vec = (V % epv == 0 && ldx % epv == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0) ? 1 : 0;
+  // (16-byte pieces through a buffer resource over one row: its bytes must fit the 31-bit offsets)
+  const int vec = (V % epv == 0 && ldx % epv == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                   static_cast<long long>(V) * (dt == MV_BF16 ? 2 : 4) < 0x7fffffffLL) ? 1 : 0;
   // 1024 threads per row for long rows (the Llama-3 vocabulary: 79 us against 137 us with 256
   // for 256 rows), 256 for short ones, where the launch and the final arg-bests dominate
 #define MV_TOPK_CASE(S_, NT_)                                                                     \

@@ -154,6 +154,36 @@ def test_projection_partial_stages(B, d):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("V,s", [(128256, 4), (131072, 16), (100003, 9)])
+def test_topk_rows_long_rows(dtype, V, s):
+    """Rows long enough for several load batches per thread, where elements below the wave's
+    running threshold skip the insertion: integer rows (many exact ties across batches) and
+    normal rows with their largest value planted again at scattered positions; ids, values
+    and the row LSE against the oracle."""
+    require_gpu()
+    rng = np.random.default_rng(7 + V + s)
+    x = np.empty((4, V), np.float32)
+    x[:2] = rng.integers(-4, 5, size=(2, V))
+    x[2:] = rng.standard_normal((2, V))
+    if dtype == torch.bfloat16:
+        x = W.round_bf16(x)
+    for r in (2, 3):
+        top = x[r].max()
+        x[r, rng.choice(V, 5, replace=False)] = top
+    print(f"topk rows V={V} s={s} {dtype}", flush=True)
+    lse = torch.full((4,), float("nan"), dtype=torch.float32, device="cuda")
+    ids, vals = ops.topk_rows(dev(x, dtype), s, lse=lse)
+    torch.cuda.synchronize()
+    for r in range(4):
+        ref = O.topk_rows(x[r], s)
+        np.testing.assert_array_equal(host(ids)[r], ref["ids"])
+        np.testing.assert_array_equal(host(vals)[r], ref["vals"])
+        # the row's LSE: the oracle's LM head over V one-column weight rows holding the row
+        want = O.lm_head_argmax(np.ones((1, 1)), x[r][:, None])["lse"]
+        assert_fp32(host(lse)[r:r + 1], want, atol=1e-4, what=f"row {r} lse")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("V,s", [(3001, 5), (3000, 4), (3000, 12)])  # scalar / 16-byte loads
 def test_topk_rows_ties_and_strides(dtype, V, s):
     require_gpu()
