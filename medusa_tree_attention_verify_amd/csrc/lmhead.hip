@@ -95,16 +95,21 @@ __global__ __launch_bounds__(64 * lm_waves(NCT, U, ROWS)) void lm_head_kernel(co
   // so 4U consecutive lanes read one row's 64U contiguous bytes (16 rows x 64 bytes per load
   // instruction, the previous order, put every piece of an instruction 8 KB apart at d = 4096);
   // target rows past T read row T-1 (their results are not written).
+  // a thread's pieces keep their target rows in every batch: their row starts are found once
+  // (in rows mode through the gathered row index, a load the batches then do not repeat)
+  const uint16_t* xrp[XPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int q = tid + i * NT;
+    const int c = q / (4 * U), u = (q / 4) % U, qq = q % 4;
+    const int t = min(col0 + c, p.T - 1);
+    xrp[i] = p.x + static_cast<size_t>(ROWS ? lm_xrow(p, t) : t) * p.d + 32 * u + 8 * qq;
+  }
   auto xload = [&](int bt, u32x4 (&xr)[XPT]) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int q = tid + i * NT;
-      if (XP % NT == 0 || q < XP) {
-        const int c = q / (4 * U), u = (q / 4) % U, qq = q % 4;
-        const int t = min(col0 + c, p.T - 1);
-        xr[i] = *reinterpret_cast<const u32x4*>(p.x + static_cast<size_t>(ROWS ? lm_xrow(p, t) : t) * p.d +
-                                                32 * (bt * U + u) + 8 * qq);
-      }
+      if (XP % NT == 0 || q < XP) xr[i] = *reinterpret_cast<const u32x4*>(xrp[i] + 32 * bt * U);
     }
   };
   // (the k-step slices sit kLmUPad elements further apart than their size, 16 banks, so the
