@@ -130,10 +130,15 @@ __global__ __launch_bounds__(256) void accept_path_kernel(const AcceptParams p) 
   __shared__ int par[MV_MAX_NODES];
   __shared__ int pred[MV_MAX_NODES + 1];
   __shared__ int pass[MV_MAX_NODES];
+  __shared__ int tks[MV_MAX_NODES];  // node tokens, read with the parents (the test and the
+                                     // path output then read LDS)
   __shared__ float sv[4];
   __shared__ int si[4];
   const int b = blockIdx.x, tid = threadIdx.x, N = p.N, R = p.R;
-  if (tid < N) par[tid] = p.parents[static_cast<size_t>(b) * p.pstride + tid];
+  if (tid < N) {
+    par[tid] = p.parents[static_cast<size_t>(b) * p.pstride + tid];
+    tks[tid] = p.tokens[static_cast<size_t>(b) * N + tid];
+  }
   if constexpr (!SPEC) {
     for (int r = tid; r < R && p.pred_ids; r += 256) pred[r] = p.pred_ids[static_cast<size_t>(b) * R + r];
     for (int r = tid; r < R && !p.pred_ids; r += 256) {
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(256) void accept_path_kernel(const AcceptParams p) 
     if (pn < -1 || pn >= tid) {
       flags |= MV_DEV_BAD_PARENT;
     } else {
-      const int tok = p.tokens[static_cast<size_t>(b) * N + tid];
+      const int tok = tks[tid];
       if (tok < 0 || tok >= p.V) {
         flags |= MV_DEV_BAD_TOKEN;
         if (SPEC && p.alpha) p.alpha[static_cast<size_t>(b) * N + tid] = 0.f;
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(256) void accept_path_kernel(const AcceptParams p) 
     for (int c = term; c != -1 && k >= 0; c = par[c], --k) {
       if (k < D) {
         pn_out[k] = c;
-        tk_out[k] = p.tokens[static_cast<size_t>(b) * N + c];
+        tk_out[k] = tks[c];
       }
     }
     const int lc = min(len, D);
@@ -633,8 +638,8 @@ __global__ __launch_bounds__(kWalkThreads) void multicand_walk_kernel(const Acce
     int32_t* pn_out = p.path_nodes + static_cast<size_t>(b) * D;
     int32_t* tk_out = p.out_tokens + static_cast<size_t>(b) * (D + 1);
     for (int k = 0; k < D; ++k) pn_out[k] = k < lc ? path[k] : -1;
-    for (int k = 0; k <= D; ++k)
-      tk_out[k] = k < lc ? p.tokens[static_cast<size_t>(b) * N + path[k]] : -1;
+    for (int k = 0; k <= D; ++k)  // an accepted node's token is in range, so gtok holds it
+      tk_out[k] = k < lc ? gtok[path[k]] : -1;
     p.accept_len[b] = lc;
     p.term[b * 4 + 0] = st_node + 1;
     p.term[b * 4 + 2] = lc;
