@@ -674,6 +674,19 @@ struct AttnPlan {
 // every chunk writes an fp32 partial output as large as its query block, so short chunks turn
 // a K/V-streaming kernel into a partial-output-writing one.  `beside` plans the persistent
 // launch on half of the CUs (the targets then count its workgroup indices).
+// CUs of the current device (cached per device; 0 if the runtime cannot say)
+int current_cus() {
+  constexpr int kMaxDev = 64;
+  static int cus[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDev && cus[dev] > 0) return cus[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < kMaxDev) cus[dev] = n;
+  return n;
+}
+
 AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L, bool beside) {
   AttnPlan a;
   if (dt == MV_F32) return a;
@@ -690,8 +703,30 @@ AttnPlan plan_attn(int dt, int B, int N, int Hq, int Hkv, int dh, int max_L, boo
                                     : std::max<long long>(1, (target + base - 1) / base));
   const int cap = std::max(1, ceil_div(max_L, MV_ATTN_MIN_CHUNK));
   want = std::min(want, cap);
-  int ck = ceil_div(std::max(max_L, 1), want);
-  ck = std::max(MV_ATTN_MIN_CHUNK, (ck + kKT - 1) / kKT * kKT);
+  auto chunk_keys = [&](int w) {
+    const int c = ceil_div(std::max(max_L, 1), w);
+    return std::max(MV_ATTN_MIN_CHUNK, (c + kKT - 1) / kKT * kKT);
+  };
+  // One sequence in a launch of its own: its workgroups run one per CU (the kernel's registers
+  // allow no second), so they go in rounds of the CU count.  Of the chunk counts up to the
+  // target's, take the one whose rounds x tiles per chunk is least (fewer chunks on ties):
+  // 131072 keys x 8 KV heads x 7 query tiles on 256 CUs took 37 chunks, 8 full rounds and a
+  // ninth of 24 workgroups; 32 chunks make 7 rounds of 64 tiles.
+  const int ncu = B == 1 && !beside ? current_cus() : 0;
+  if (ncu > 0 && base * want > ncu) {
+    long long best = -1;
+    int bw = want;
+    for (int w = want; w >= 1; --w) {
+      const int c = chunk_keys(w), nc = std::max(1, ceil_div(max_L, c));
+      const long long cost = ceil_div(base * nc, static_cast<long long>(ncu)) * (c / kKT);
+      if (best < 0 || cost <= best) {
+        best = cost;
+        bw = w;
+      }
+    }
+    want = bw;
+  }
+  const int ck = chunk_keys(want);
   a.CK = ck;
   a.nchunks = std::max(1, ceil_div(max_L, ck));
   a.ordered = B > 1 && B <= kOrderMaxB;
