@@ -92,7 +92,7 @@ typedef enum {
 #define MV_MAX_NODES 256   /* N: tree nodes */
 #define MV_MAX_DEPTH 16    /* D: tree depth */
 #define MV_MAX_TOPK  16    /* s: candidates per head / per depth */
-#define MV_MAX_BATCH_HEADS 32  /* B for the Medusa heads */
+#define MV_MAX_BATCH_HEADS 64  /* B for the Medusa heads (bf16; fp32 takes up to 32) */
 #define MV_MAX_HEADS 16    /* K: Medusa heads */
 
 /* Human-readable text of a mv_status value (static storage). */
@@ -113,7 +113,8 @@ MV_API int mv_version(void);
  * the top-s_k logits, and lse = log sum_v exp(logit_v) gives the distribution itself.
  *
  *   dt        MV_BF16 (weights, h and logits in bf16) or MV_F32.
- *   B         batch (1..MV_MAX_BATCH_HEADS), d model width, V vocabulary, K heads (1..16).
+ *   B         batch (1..MV_MAX_BATCH_HEADS for bf16, 1..32 for fp32), d model width,
+ *             V vocabulary, K heads (1..16).
  *             bf16 needs d % 32 == 0; fp32 needs d % 4 == 0.
  *   h         [B, d] dt.
  *   w_res     [K, d, d] dt, W_res^(k)[out][in] (row-major, out-major).

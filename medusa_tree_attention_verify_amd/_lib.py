@@ -36,7 +36,7 @@ MV_DEV_BAD_PATH = 0x20
 MV_MAX_NODES = 256
 MV_MAX_DEPTH = 16
 MV_MAX_TOPK = 16
-MV_MAX_BATCH_HEADS = 32
+MV_MAX_BATCH_HEADS = 64
 MV_MAX_HEADS = 16
 MV_HEADS_NOALLOC_SCRATCH_BYTES = 32 << 20
 

@@ -38,6 +38,7 @@ namespace mv {
 namespace {
 
 constexpr int kRows = 32;  // weight rows per workgroup
+constexpr int kMaxBatchF32 = 32;  // batch rows of the fp32 heads (a register accumulator each)
 
 // Streaming parameters (measured on MI355X; see the head-projection profile).
 #ifndef MV_GEMV_U
@@ -675,7 +676,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(const GemvParams p) 
 // ---- fp32 weights: vector-ALU loop, one wave per weight row.
 template <int NW, int MODE>
 __global__ __launch_bounds__(NW * 64) void gemv_f32_kernel(const GemvParams p) {
-  constexpr int BC = MV_MAX_BATCH_HEADS;
+  constexpr int BC = kMaxBatchF32;
   __shared__ float ys[kRows][BC];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int k = blockIdx.y, rb = blockIdx.x, row0 = rb * kRows;
@@ -945,7 +946,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(int V, int s, c
 // ---------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------
-int nct_for(int B) { return B <= 8 ? 1 : (B <= 16 ? 2 : 4); }
+int nct_for(int B) { return B <= 8 ? 1 : (B <= 16 ? 2 : (B <= 32 ? 4 : 8)); }
 
 struct HeadsLayout {
   float* hk = nullptr;
@@ -984,6 +985,7 @@ int check_common(int dt, int B, int d, int K) {
   if (dt != MV_F32 && dt != MV_BF16) return MV_ERR_INVALID_ARG;
   if (B < 1 || d < 1 || K < 1) return MV_ERR_INVALID_ARG;
   if (B > MV_MAX_BATCH_HEADS || K > MV_MAX_HEADS) return MV_ERR_UNSUPPORTED;
+  if (dt == MV_F32 && B > kMaxBatchF32) return MV_ERR_UNSUPPORTED;
   if (dt == MV_BF16 && d % 32 != 0) return MV_ERR_UNSUPPORTED;
   if (dt == MV_F32 && d % 4 != 0) return MV_ERR_UNSUPPORTED;
   return MV_OK;
@@ -1026,6 +1028,7 @@ int launch_gemv(int dt, const GemvParams& p, int K, hipStream_t st) {
   MV_GEMV_CASE(1, 1) MV_GEMV_CASE(2, 1) MV_GEMV_CASE(4, 1) MV_GEMV_CASE(8, 1)
   MV_GEMV_CASE(1, 2) MV_GEMV_CASE(2, 2) MV_GEMV_CASE(4, 2) MV_GEMV_CASE(8, 2)
   MV_GEMV_CASE(1, 4) MV_GEMV_CASE(2, 4) MV_GEMV_CASE(4, 4)
+  MV_GEMV_CASE(1, 8) MV_GEMV_CASE(2, 8)
 #undef MV_GEMV_CASE
   return MV_ERR_UNSUPPORTED;
 }

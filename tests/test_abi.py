@@ -83,7 +83,9 @@ def test_host_argument_checks():
     # heads
     assert lib.mv_medusa_residual(7, 1, 64, 1, P, P, None, None, 0, None) == L.MV_ERR_INVALID_ARG
     assert lib.mv_medusa_residual(L.MV_BF16, 1, 48, 1, P, P, None, None, 0, None) == L.MV_ERR_UNSUPPORTED
-    assert lib.mv_medusa_residual(L.MV_BF16, 33, 64, 1, P, P, None, None, 0, None) == L.MV_ERR_UNSUPPORTED
+    assert lib.mv_medusa_residual(L.MV_BF16, 65, 64, 1, P, P, None, None, 0, None) == L.MV_ERR_UNSUPPORTED
+    assert lib.mv_medusa_residual(L.MV_F32, 33, 64, 1, P, P, None, None, 0, None) == L.MV_ERR_UNSUPPORTED
+    assert lib.mv_medusa_residual(L.MV_BF16, 64, 64, 1, P, P, None, None, 0, None) == L.MV_ERR_WORKSPACE
     assert lib.mv_medusa_residual(L.MV_BF16, 1, 64, 1, P, P, None, None, 0, None) == L.MV_ERR_WORKSPACE
     assert lib.mv_medusa_residual(L.MV_BF16, 1, 64, 1, None, P, None, P, 1 << 20, None) == L.MV_ERR_INVALID_ARG
     s = L.int_array([4, 3])

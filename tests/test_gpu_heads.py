@@ -46,7 +46,7 @@ def test_heads_tiny_fp32():
     assert _run_and_check(wl, 1, list(wl.head_widths)) == 0
 
 
-@pytest.mark.parametrize("B", [1, 3, 8, 12, 20])
+@pytest.mark.parametrize("B", [1, 3, 8, 12, 20, 33, 40, 64])  # 33-64: eight column tiles
 def test_heads_bf16_small(B):
     require_gpu()
     wl = W.WORKLOADS["c2"].scaled(B=B, d=256, V=1000, K=3, head_widths=(4, 3, 1))
@@ -95,6 +95,29 @@ def test_heads_70b_width_batch8():
     ties = _run_and_check(wl, 3, list(wl.head_widths), check_logits=True)
     print("near-tie ranks:", ties)
     assert ties <= 2
+
+
+def test_heads_serving_batch64_sampled():
+    """The Llama-3-8B head shape (d=4096, V=32000, 4 heads) at the serving batch of 64 (eight
+    column tiles): the GPU computes every (batch row, head); the oracle recomputes sampled
+    pairs, each from its own slice of the inputs."""
+    require_gpu()
+    wl = W.WORKLOADS["c2"].scaled(B=64)
+    widths = list(wl.head_widths)
+    x = W.gen_heads(wl, 29)
+    print(f"heads B={wl.B} d={wl.d} V={wl.V} K={wl.K}", flush=True)
+    got = ops.medusa_heads(dev(x["h"], torch.bfloat16), dev(x["w_res"], torch.bfloat16),
+                           dev(x["w_head"], torch.bfloat16), widths, want_hk=True)
+    torch.cuda.synchronize()
+    hk, ids, vals, lse = (host(got[n]) for n in ("hk", "topk_ids", "topk_vals", "lse"))
+    for b, k in ((0, 0), (17, 1), (40, 2), (63, 3), (63, 0)):
+        ref = O.medusa_heads(x["h"][b:b + 1], x["w_res"][k:k + 1], x["w_head"][k:k + 1], [widths[k]])
+        s = widths[k]
+        assert_fp32(hk[b, k], ref["hk"][0, 0], what=f"hk b={b} k={k}")
+        assert_fp32(lse[b, k], ref["lse"][0, 0], atol=1e-3, what=f"lse b={b} k={k}")
+        ties = check_topk(ids[b:b + 1, k:k + 1], ref["logits"], [s])
+        assert ties <= 1
+        assert_fp32(vals[b, k, :s], ref["logits"][0, 0][ids[b, k, :s]], what=f"topk_vals b={b} k={k}")
 
 
 def test_heads_70b_full_sampled():
