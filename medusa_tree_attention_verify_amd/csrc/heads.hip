@@ -162,6 +162,53 @@ __device__ __forceinline__ void list_pop(float (&lv)[SM], int (&li)[SM]) {
   li[SM - 1] = INT_MAX;
 }
 
+// Wave 0's final phase of the merges: the waves' top s (wtv/wti, best first), at most
+// kMergeWaves * s <= 128 candidates, two per lane and sorted, give the final s by wave
+// arg-bests; the waves' (max, sum) pairs give the LSE.
+__device__ __forceinline__ void merge_wave_winners(const GemvParams& p, const float (&wtv)[kMergeWaves][MV_MAX_TOPK],
+                                                   const int (&wti)[kMergeWaves][MV_MAX_TOPK],
+                                                   const float (&wm)[kMergeWaves], const float (&wl)[kMergeWaves],
+                                                   int s, int smax, int b, int k, int lane) {
+  float cv[2];
+  int ci[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = lane + 64 * q;
+    const bool ok = c < kMergeWaves * s;
+    cv[q] = ok ? wtv[c / max(s, 1)][c % max(s, 1)] : -INFINITY;
+    ci[q] = ok ? wti[c / max(s, 1)][c % max(s, 1)] : INT_MAX;
+  }
+  if (kv_better(cv[1], ci[1], cv[0], ci[0])) {
+    const float tv = cv[0];
+    const int ti = ci[0];
+    cv[0] = cv[1];
+    ci[0] = ci[1];
+    cv[1] = tv;
+    ci[1] = ti;
+  }
+  for (int r = 0; r < smax; ++r) {
+    float bv = r < s ? cv[0] : -INFINITY;
+    int bi = r < s ? ci[0] : INT_MAX;
+    wave_argbest(bv, bi);
+    if (r < s && bi != INT_MAX && ci[0] == bi) {
+      cv[0] = cv[1];
+      ci[0] = ci[1];
+      cv[1] = -INFINITY;
+      ci[1] = INT_MAX;
+    }
+    if (lane == 0) {
+      const size_t o = static_cast<size_t>(b) * p.ld_topk + static_cast<size_t>(k) * smax + r;
+      const bool ok = r < s && bi != INT_MAX;
+      p.topk_ids[o] = ok ? bi : -1;
+      p.topk_vals[o] = ok ? bv : -INFINITY;
+    }
+  }
+  float M = lane < kMergeWaves ? wm[lane] : -INFINITY;
+  float Ls = lane < kMergeWaves ? wl[lane] : 0.f;
+  wave_ml_merge(M, Ls);
+  if (lane == 0 && p.lse) p.lse[static_cast<size_t>(b) * p.K + k] = M + logf(Ls);
+}
+
 template <int SM>
 __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(const GemvParams p) {
   __shared__ float wtv[kMergeWaves][MV_MAX_TOPK];
@@ -225,45 +272,7 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(const GemvPa
   }
   __syncthreads();
   if (w != 0) return;
-  // wave 0: at most kMergeWaves * s <= 128 candidates, two per lane, sorted
-  float cv[2];
-  int ci[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int c = lane + 64 * q;
-    const bool ok = c < kMergeWaves * s;
-    cv[q] = ok ? wtv[c / max(s, 1)][c % max(s, 1)] : -INFINITY;
-    ci[q] = ok ? wti[c / max(s, 1)][c % max(s, 1)] : INT_MAX;
-  }
-  if (kv_better(cv[1], ci[1], cv[0], ci[0])) {
-    const float tv = cv[0];
-    const int ti = ci[0];
-    cv[0] = cv[1];
-    ci[0] = ci[1];
-    cv[1] = tv;
-    ci[1] = ti;
-  }
-  for (int r = 0; r < smax; ++r) {
-    float bv = r < s ? cv[0] : -INFINITY;
-    int bi = r < s ? ci[0] : INT_MAX;
-    wave_argbest(bv, bi);
-    if (r < s && bi != INT_MAX && ci[0] == bi) {
-      cv[0] = cv[1];
-      ci[0] = ci[1];
-      cv[1] = -INFINITY;
-      ci[1] = INT_MAX;
-    }
-    if (lane == 0) {
-      const size_t o = static_cast<size_t>(b) * p.ld_topk + static_cast<size_t>(k) * smax + r;
-      const bool ok = r < s && bi != INT_MAX;
-      p.topk_ids[o] = ok ? bi : -1;
-      p.topk_vals[o] = ok ? bv : -INFINITY;
-    }
-  }
-  float M = lane < kMergeWaves ? wm[lane] : -INFINITY;
-  float Ls = lane < kMergeWaves ? wl[lane] : 0.f;
-  wave_ml_merge(M, Ls);
-  if (lane == 0 && p.lse) p.lse[static_cast<size_t>(b) * p.K + k] = M + logf(Ls);
+  merge_wave_winners(p, wtv, wti, wm, wl, s, smax, b, k, lane);
 }
 
 // ---- merge as a tournament, for lists longer than 8 (up to kMergeThreads * CPT candidates
@@ -360,14 +369,15 @@ __global__ __launch_bounds__(kMergeThreads) void heads_tournament_kernel(const G
 
 // Merge of the blocks' sorted lists (each 32-row block's list is its top s, best first): a
 // k-way merge over the list heads.  Each thread holds the lists of BPT blocks in registers and
-// their current heads; per rank the workgroup takes the best head (a wave arg-best, one LDS
-// exchange between the waves) and only the thread owning the winner advances that list.  A
-// rank then costs a comparison of BPT heads per thread instead of a scan of every candidate
-// the thread holds.
+// their current heads; per rank a wave takes the best head among its threads (a wave arg-best)
+// and only the thread owning the winner advances that list.  Each wave so draws its own top s
+// with no workgroup barrier per rank; after one barrier wave 0 merges the waves' winners.  A
+// rank costs a comparison of BPT heads per thread instead of a scan of every candidate the
+// thread holds.
 template <int BPT, int SMX>
 __global__ __launch_bounds__(kMergeThreads) void heads_kmerge_kernel(const GemvParams p) {
-  __shared__ float rv[2][kMergeWaves];
-  __shared__ int ri[2][kMergeWaves];
+  __shared__ float wtv[kMergeWaves][MV_MAX_TOPK];
+  __shared__ int wti[kMergeWaves][MV_MAX_TOPK];
   __shared__ float wm[kMergeWaves], wl[kMergeWaves];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int k = blockIdx.x % p.K, b = blockIdx.x / p.K;
@@ -405,7 +415,6 @@ __global__ __launch_bounds__(kMergeThreads) void heads_kmerge_kernel(const GemvP
     hv[q] = lv[q][0];
     hi[q] = li[q][0];
   }
-  const size_t o = static_cast<size_t>(b) * p.ld_topk + static_cast<size_t>(k) * smax;
   for (int r = 0; r < s; ++r) {
     float bv = -INFINITY;
     int bi = INT_MAX;
@@ -416,25 +425,10 @@ __global__ __launch_bounds__(kMergeThreads) void heads_kmerge_kernel(const GemvP
       bi = c ? hi[q] : bi;
     }
     wave_argbest(bv, bi);
-    if (lane == 0) {
-      rv[r & 1][w] = bv;
-      ri[r & 1][w] = bi;
-    }
-    __syncthreads();
-    float gv = rv[r & 1][0];
-    int gi = ri[r & 1][0];
-#pragma unroll
-    for (int q = 1; q < kMergeWaves; ++q) {
-      const float ov = rv[r & 1][q];
-      const int oi = ri[r & 1][q];
-      const bool c = kv_better(ov, oi, gv, gi);
-      gv = c ? ov : gv;
-      gi = c ? oi : gi;
-    }
-    if (gi != INT_MAX) {  // token ids are unique: exactly one head of one thread holds it
+    if (bi != INT_MAX) {  // token ids are unique: exactly one head of one lane holds it
 #pragma unroll
       for (int q = 0; q < BPT; ++q) {
-        if (hi[q] == gi) {
+        if (hi[q] == bi) {
           const int nx = ++ptr[q];
           float v = -INFINITY;
           int id = INT_MAX;
@@ -448,22 +442,14 @@ __global__ __launch_bounds__(kMergeThreads) void heads_kmerge_kernel(const GemvP
         }
       }
     }
-    if (tid == 0) {
-      p.topk_ids[o + r] = gi != INT_MAX ? gi : -1;
-      p.topk_vals[o + r] = gi != INT_MAX ? gv : -INFINITY;
+    if (lane == 0) {
+      wtv[w][r] = bv;
+      wti[w][r] = bi;
     }
   }
-  if (tid == 0)
-    for (int r = s; r < smax; ++r) {
-      p.topk_ids[o + r] = -1;
-      p.topk_vals[o + r] = -INFINITY;
-    }
   __syncthreads();
   if (w != 0) return;
-  float M = lane < kMergeWaves ? wm[lane] : -INFINITY;
-  float Ls = lane < kMergeWaves ? wl[lane] : 0.f;
-  wave_ml_merge(M, Ls);
-  if (lane == 0 && p.lse) p.lse[static_cast<size_t>(b) * p.K + k] = M + logf(Ls);
+  merge_wave_winners(p, wtv, wti, wm, wl, s, smax, b, k, lane);
 }
 
 // ---- projection epilogue: optional logits, per-workgroup top-s and (max, sum exp).
